@@ -1,0 +1,114 @@
+"""Pins for the oracle's DARTree depth-wise builder (CPU only).
+
+The depth-wise super-tree is a heuristic with no closed form; it is pinned by
+reductions: no correction -> the marginal tree; no pruning -> brute-force
+best-first over corrected path scores (the exact "sequential correction with
+heap" the DARTree summary names); width 1 -> the greedy corrected chain.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import depthwise, marginal, rowsweep, treeout
+
+
+def small_head(rng, V, dm, rank, L, scale):
+    E = rng.standard_normal((V, dm)) * scale
+    U = rng.standard_normal((L, dm, rank)) * scale
+    P = rng.standard_normal((rank, V)) * scale
+    return E, U, P
+
+
+def lse(x):
+    m = np.max(x)
+    return m + math.log(np.sum(np.exp(x - m)))
+
+
+def test_bf16_round_matches_generator_rounding():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-8, 8, 20000)).astype(np.float32)
+    x = np.concatenate([x, np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)], dtype=np.float32)])
+    ours = depthwise.bf16_round(x.astype(np.float64))
+    gen = synth.f32_from_bf16(synth.bf16_from_f32(x)).astype(np.float64)
+    np.testing.assert_array_equal(ours, gen)
+
+
+@pytest.mark.parametrize("beta", [0.0, -0.4])
+def test_zero_correction_equals_marginal_tree(beta):
+    rng = np.random.default_rng(1)
+    L, V, B = 4, 40, 12
+    base = rng.standard_normal((L, V)) * 2.0
+    E, U, P = small_head(rng, V, 16, 8, L, 0.3)
+    U[:] = 0.0
+    t = depthwise.build_depthwise(base, E, U, P, root_tok=5, K=B, W=B, B=B, beta=beta)
+    m = marginal.build_marginal(base, B, B, beta)
+    assert t.paths() == m.paths()
+    np.testing.assert_allclose(t.score, m.score, atol=1e-12)
+
+
+def corrected_brute_force(base, E, U, P, root_tok, K, B, beta):
+    """Every prefix over C_1 x ... x C_L scored with its own path's correction, top-B by sort."""
+    L, V = base.shape
+    cands = [list(np.argsort(-base[d], kind="stable")[:K]) for d in range(L)]
+    scored = []
+    for d in range(1, L + 1):
+        for ks in itertools.product(range(K), repeat=d):
+            prev, s = root_tok, 0.0
+            for i, k in enumerate(ks):
+                h = depthwise.bf16_round(E[prev] @ U[i])
+                z = base[i] + h @ P
+                c = cands[i][k]
+                s = min(s + (z[c] - lse(z)) + beta, s)
+                prev = c
+            scored.append((-s, d, tuple(cands[i][k] for i, k in enumerate(ks))))
+    scored.sort()
+    return {p: -ns for ns, _, p in scored[:B]}
+
+
+@pytest.mark.parametrize("seed", [2, 3])
+def test_no_pruning_equals_exact_corrected_best_first(seed):
+    rng = np.random.default_rng(seed)
+    L, V, K, B = 3, 20, 3, 9
+    base = rng.standard_normal((L, V)) * 1.5
+    E, U, P = small_head(rng, V, 8, 4, L, 0.8)
+    t = depthwise.build_depthwise(base, E, U, P, root_tok=3, K=K, W=K ** (L - 1), B=B, beta=-0.1)
+    ref = corrected_brute_force(base, E, U, P, 3, K, B, -0.1)
+    got = {p: s for p, s in zip(t.paths()[1:], t.score[1:])}
+    assert set(got) == set(ref)
+    for p in got:
+        assert abs(got[p] - ref[p]) < 1e-12
+    treeout.check_invariants(t, B, L)
+
+
+def test_width_one_is_greedy_corrected_chain():
+    rng = np.random.default_rng(4)
+    L, V, K = 5, 30, 4
+    base = rng.standard_normal((L, V))
+    E, U, P = small_head(rng, V, 8, 4, L, 0.8)
+    t = depthwise.build_depthwise(base, E, U, P, root_tok=1, K=K, W=1, B=L, beta=0.0)
+    prev, s = 1, 0.0
+    for d in range(L):
+        cands = np.argsort(-base[d], kind="stable")[:K]
+        z = base[d] + depthwise.bf16_round(E[prev] @ U[d]) @ P
+        sc = [s + (z[c] - lse(z)) for c in cands]
+        best = int(np.argmax(sc))
+        assert t.token[d + 1] == int(cands[best]) and t.parent[d + 1] == d
+        s, prev = sc[best], int(cands[best])
+
+
+def test_super_tree_invariants_workload_shape_small():
+    R, L, V, dm, rank = 2, 6, 600, 32, 16
+    base_b = synth.ddtree_logits(seed=2, R=R, L=L, V=V)
+    E, U, P, root = synth.correction_head(seed=3, R=R, L=L, V=V, d_model=dm, rank=rank)
+    base = rowsweep.as_f64(base_b, "bf16")
+    E64, U64, P64 = (synth.f32_from_bf16(a).astype(np.float64) for a in (E, U, P))
+    for r in range(R):
+        t, levels = depthwise.build_depthwise(base[r], E64, U64, P64, int(root[r]), K=8, W=32, B=40,
+                                              beta=-0.5, with_super=True)
+        treeout.check_invariants(t, 40, L)
+        assert len(levels[0]) == 8 and all(len(lv) <= 32 for lv in levels)
+        for d in range(1, len(levels)):
+            assert all(nd["ppos"] < len(levels[d - 1]) for nd in levels[d])
