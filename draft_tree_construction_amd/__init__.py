@@ -1,0 +1,224 @@
+"""Python binding of libdtree.so, the gfx950 draft-tree construction library.
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels behind
+the C ABI declared in include/dtree.h. PyTorch provides device memory and the
+current stream. There is no CPU fallback: if libdtree.so is missing or fails to
+load, every call raises.
+
+Entry points (same names as the C ABI):
+    topk_logsoftmax(logits, K)                          -> (lse, ids, lp)
+    build_tree_marginal(logits, K, B, beta)             -> Tree
+    build_tree_depthwise(logits, E, U, P, root_tok, K, W, B, beta) -> Tree
+    build_tree_gated(logits, K_root, mu, N)             -> Tree
+    accept_tree(tree, target, draft, temperature, seed, trial0, n_trials)
+        -> (accept_len, accept_node, next_token), each [n_trials, R]
+Logits are torch.bfloat16 or torch.float32 device tensors ([R, L, V] for the builders).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdtree.so")
+
+DTREE_BF16, DTREE_F32 = 0, 1
+OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT = range(5)
+STATUS = {0: "DTREE_OK", -1: "DTREE_E_INVAL", -2: "DTREE_E_BETA", -3: "DTREE_E_WORKSPACE",
+          -4: "DTREE_E_UNSUPPORTED", -5: "DTREE_E_HIP"}
+
+# every symbol include/dtree.h declares
+SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_depthwise",
+           "build_tree_gated", "accept_tree", "dtree_status_string", "dtree_last_error")
+
+
+class DTreeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class CTree(ctypes.Structure):
+    _fields_ = [("parent", ctypes.c_void_p), ("token", ctypes.c_void_p), ("depth", ctypes.c_void_p),
+                ("score", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("n_nodes", ctypes.c_void_p),
+                ("cap", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdtree.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m draft_tree_construction_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    u64 = ctypes.c_uint64
+    L.dtree_workspace_size.restype = sz
+    L.dtree_workspace_size.argtypes = [i32] * 8
+    L.dtree_topk_logsoftmax.restype = i32
+    L.dtree_topk_logsoftmax.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.build_tree_marginal.restype = i32
+    L.build_tree_marginal.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, ctypes.POINTER(CTree), vp, sz, vp]
+    L.build_tree_depthwise.restype = i32
+    L.build_tree_depthwise.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32, f32,
+                                       ctypes.POINTER(CTree), vp, sz, vp]
+    L.build_tree_gated.restype = i32
+    L.build_tree_gated.argtypes = [vp, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(CTree), vp, sz, vp]
+    L.accept_tree.restype = i32
+    L.accept_tree.argtypes = [ctypes.POINTER(CTree), vp, vp, i32, i32, i32, i32, f32, u64, u64, i32, vp, vp, vp,
+                              vp, sz, vp]
+    L.dtree_status_string.restype = ctypes.c_char_p
+    L.dtree_status_string.argtypes = [i32]
+    L.dtree_last_error.restype = ctypes.c_char_p
+    L.dtree_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise DTreeError(rc, lib().dtree_last_error().decode())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTREE_BF16
+    if t.dtype == torch.float32:
+        return DTREE_F32
+    raise TypeError("logits must be torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("inputs must be contiguous device tensors")
+
+
+def workspace_size(op: int, R: int, L: int, V: int, K: int = 0, B_or_N: int = 0, W: int = 0, rank: int = 0) -> int:
+    return int(lib().dtree_workspace_size(op, R, L, V, K, B_or_N, W, rank))
+
+
+def _workspace(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+@dataclass
+class Tree:
+    """Device outputs of a builder: per round [cap+1] slots (slot 0 = root)."""
+    parent: torch.Tensor
+    token: torch.Tensor
+    depth: torch.Tensor
+    score: torch.Tensor
+    mask: torch.Tensor
+    n_nodes: torch.Tensor
+    cap: int
+
+    @staticmethod
+    def empty(R: int, cap: int, dev) -> "Tree":
+        words = (cap + 1 + 31) // 32
+        i32 = dict(dtype=torch.int32, device=dev)
+        return Tree(torch.empty(R, cap + 1, **i32), torch.empty(R, cap + 1, **i32), torch.empty(R, cap + 1, **i32),
+                    torch.empty(R, cap + 1, dtype=torch.float32, device=dev),
+                    torch.empty(R, cap + 1, words, dtype=torch.int32, device=dev),
+                    torch.empty(R, **i32), cap)
+
+    def c_struct(self) -> CTree:
+        return CTree(self.parent.data_ptr(), self.token.data_ptr(), self.depth.data_ptr(), self.score.data_ptr(),
+                     self.mask.data_ptr(), self.n_nodes.data_ptr(), self.cap)
+
+
+def topk_logsoftmax(logits: torch.Tensor, K: int, ws: torch.Tensor | None = None):
+    """logits [rows, V] -> lse [rows] f32, ids [rows, K] i32, lp [rows, K] f32."""
+    _require_device(logits)
+    rows, V = logits.shape
+    dev = logits.device
+    lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    ids = torch.empty(rows, K, dtype=torch.int32, device=dev)
+    lp = torch.empty(rows, K, dtype=torch.float32, device=dev)
+    need = workspace_size(OP_TOPK, rows, 1, V, K)
+    ws = _workspace(need, dev) if ws is None else ws
+    _check(lib().dtree_topk_logsoftmax(_ptr(logits), _dtype(logits), rows, V, K, _ptr(lse), _ptr(ids), _ptr(lp),
+                                       _ptr(ws), ws.numel(), _stream(dev)))
+    return lse, ids, lp
+
+
+def build_tree_marginal(logits: torch.Tensor, K: int, B: int, beta: float, ws: torch.Tensor | None = None,
+                        out: Tree | None = None) -> Tree:
+    _require_device(logits)
+    R, L, V = logits.shape
+    dev = logits.device
+    out = Tree.empty(R, B, dev) if out is None else out
+    ws = _workspace(workspace_size(OP_MARGINAL, R, L, V, K, B), dev) if ws is None else ws
+    st = out.c_struct()
+    _check(lib().build_tree_marginal(_ptr(logits), _dtype(logits), R, L, V, K, B, float(beta), ctypes.byref(st),
+                                     _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def build_tree_depthwise(logits: torch.Tensor, E: torch.Tensor, U: torch.Tensor, P: torch.Tensor,
+                         root_tok: torch.Tensor, K: int, W: int, B: int, beta: float,
+                         ws: torch.Tensor | None = None, out: Tree | None = None) -> Tree:
+    """E [V, d_model], U [L, d_model, rank], P [rank, V] bf16; root_tok [R] int32."""
+    _require_device(logits, E, U, P, root_tok)
+    for t in (E, U, P):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("E, U, P must be torch.bfloat16")
+    if root_tok.dtype != torch.int32:
+        raise TypeError("root_tok must be int32")
+    R, L, V = logits.shape
+    d_model, rank = U.shape[1], U.shape[2]
+    dev = logits.device
+    out = Tree.empty(R, B, dev) if out is None else out
+    ws = _workspace(workspace_size(OP_DEPTHWISE, R, L, V, K, B, W, rank), dev) if ws is None else ws
+    st = out.c_struct()
+    _check(lib().build_tree_depthwise(_ptr(logits), _dtype(logits), R, L, V, _ptr(E), _ptr(U), _ptr(P), d_model, rank,
+                                      _ptr(root_tok), K, W, B, float(beta), ctypes.byref(st), _ptr(ws), ws.numel(),
+                                      _stream(dev)))
+    return out
+
+
+def build_tree_gated(logits: torch.Tensor, K_root: int, mu: float, N: int, ws: torch.Tensor | None = None,
+                     out: Tree | None = None) -> Tree:
+    _require_device(logits)
+    R, L, V = logits.shape
+    dev = logits.device
+    out = Tree.empty(R, N, dev) if out is None else out
+    ws = _workspace(workspace_size(OP_GATED, R, L, V, 0, N), dev) if ws is None else ws
+    st = out.c_struct()
+    _check(lib().build_tree_gated(_ptr(logits), _dtype(logits), R, L, V, K_root, float(mu), N, ctypes.byref(st),
+                                  _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def accept_tree(tree: Tree, target: torch.Tensor, draft: torch.Tensor | None, temperature: float, seed: int,
+                trial0: int = 0, n_trials: int = 1, ws: torch.Tensor | None = None, outs=None):
+    """target [R, cap+1, V]; draft [R, L, V] (None allowed at temperature 0)."""
+    _require_device(target, draft)
+    R, rows, V = target.shape
+    if rows != tree.cap + 1:
+        raise ValueError("target must have cap+1 rows per round")
+    L = draft.shape[1] if draft is not None else 1
+    dev = target.device
+    if outs is None:
+        outs = tuple(torch.empty(n_trials, R, dtype=torch.int32, device=dev) for _ in range(3))
+    ws = _workspace(workspace_size(OP_ACCEPT, R, L, V, 0, tree.cap), dev) if ws is None else ws
+    st = tree.c_struct()
+    _check(lib().accept_tree(ctypes.byref(st), _ptr(target), _ptr(draft), _dtype(target), R, L, V, float(temperature),
+                             int(seed), int(trial0), int(n_trials), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                             _ptr(ws), ws.numel(), _stream(dev)))
+    return outs

@@ -1,0 +1,223 @@
+// The C ABI of libdtree.so: argument validation, workspace layout and stream-ordered
+// launches. Every check happens on the host before any launch (no device sync, no
+// device->host copy); see include/dtree.h for the contract of each entry point.
+#include <math.h>
+#include <stdio.h>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return DTREE_E_HIP;
+}
+
+bool dtype_ok(int dtype) { return dtype == DTREE_BF16 || dtype == DTREE_F32; }
+
+// a1 outputs kept in the workspace for the builders
+struct A1Ws {
+  float *zk;
+  int32_t *ids;
+  double *lse;
+  void *rest;  // rowsweep split partials
+};
+
+size_t a1_bytes(int rows, int V, int K) {
+  return dt::align256((size_t)rows * K * sizeof(float)) + dt::align256((size_t)rows * K * sizeof(int32_t)) +
+         dt::align256((size_t)rows * sizeof(double)) + dt::rowsweep_ws_bytes(rows, V, K);
+}
+
+A1Ws a1_carve(void *ws, int rows, int K) {
+  char *w = static_cast<char *>(ws);
+  A1Ws a;
+  a.zk = reinterpret_cast<float *>(w);
+  w += dt::align256((size_t)rows * K * sizeof(float));
+  a.ids = reinterpret_cast<int32_t *>(w);
+  w += dt::align256((size_t)rows * K * sizeof(int32_t));
+  a.lse = reinterpret_cast<double *>(w);
+  w += dt::align256((size_t)rows * sizeof(double));
+  a.rest = w;
+  return a;
+}
+
+int check_tree(const dtree_tree *t, int cap) {
+  if (!t) return fail(DTREE_E_INVAL, "tree struct is NULL");
+  if (t->cap != cap) return fail(DTREE_E_INVAL, "tree cap does not match the budget");
+  if (!t->parent || !t->token || !t->depth || !t->score || !t->mask || !t->n_nodes)
+    return fail(DTREE_E_INVAL, "a tree output array is NULL");
+  return DTREE_OK;
+}
+
+dt::TreeOut tree_out(const dtree_tree *t) {
+  return dt::TreeOut{t->parent, t->token, t->depth, t->score, t->mask, t->n_nodes, t->cap};
+}
+
+int marginal_k(int K, int B, int V) { return K == 0 ? (B < V ? B : V) : K; }
+int gated_k(int V) { return V < DTREE_MAX_K ? V : DTREE_MAX_K; }
+
+}  // namespace
+
+extern "C" {
+
+const char *dtree_status_string(int status) {
+  switch (status) {
+    case DTREE_OK: return "ok";
+    case DTREE_E_INVAL: return "invalid argument";
+    case DTREE_E_BETA: return "beta > 0 breaks the best-first == Top-B equivalence";
+    case DTREE_E_WORKSPACE: return "workspace missing or too small";
+    case DTREE_E_UNSUPPORTED: return "outside the compiled size envelope";
+    case DTREE_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char *dtree_last_error(void) { return g_last_error.c_str(); }
+
+size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank) {
+  if (R < 0 || L < 1 || V < 1) return 0;
+  switch (op) {
+    case DTREE_OP_TOPK:
+      if (K < 1) return 0;
+      return dt::rowsweep_ws_bytes(R * L, V, K);
+    case DTREE_OP_MARGINAL: {
+      const int k = marginal_k(K, B_or_N, V);
+      if (k < 1) return 0;
+      return a1_bytes(R * L, V, k);
+    }
+    case DTREE_OP_GATED:
+      return a1_bytes(R * L, V, gated_k(V));
+    case DTREE_OP_DEPTHWISE:
+      if (K < 1 || W < 1 || B_or_N < 1) return 0;
+      return a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B_or_N, rank);
+    case DTREE_OP_ACCEPT:
+      if (B_or_N < 1) return 0;
+      return dt::accept_ws_bytes(R, L, V, B_or_N);
+    default:
+      return 0;
+  }
+}
+
+int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K, float *lse, int32_t *ids,
+                          float *lp, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (rows < 0 || V < 1 || K < 1 || K > V) return fail(DTREE_E_INVAL, "need rows >= 0, 1 <= K <= V");
+  if (K > DTREE_MAX_K) return fail(DTREE_E_UNSUPPORTED, "K > DTREE_MAX_K");
+  if (rows == 0) return DTREE_OK;
+  if (!logits || !ids) return fail(DTREE_E_INVAL, "logits and ids must not be NULL");
+  const size_t need = dt::rowsweep_ws_bytes(rows, V, K);
+  if (need > 0 && (!ws || ws_bytes < need)) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  dt::RowOut o{nullptr, lse, ids, nullptr, lp};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, rows, V, K, o, ws, static_cast<hipStream_t>(s));
+  if (e != hipSuccess) return hip_fail(e, "dtree_topk_logsoftmax");
+  return DTREE_OK;
+}
+
+int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta,
+                        const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || B < 1 || K < 0) return fail(DTREE_E_INVAL, "need R >= 0, L, V, B >= 1, K >= 0");
+  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
+  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
+  const int k = marginal_k(K, B, V);
+  if (k > V) return fail(DTREE_E_INVAL, "K > V");
+  if (k > DTREE_MAX_K || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "K, B or L beyond the compiled envelope");
+  int rc = check_tree(out, B);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits) return fail(DTREE_E_INVAL, "logits is NULL");
+  const size_t need = a1_bytes(R * L, V, k);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  hipStream_t st = static_cast<hipStream_t>(s);
+  A1Ws a = a1_carve(ws, R * L, k);
+  dt::RowOut o{a.lse, nullptr, a.ids, a.zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, k, o, a.rest, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_marginal (row sweep)");
+  e = dt::launch_marginal(a.zk, a.ids, a.lse, R, L, k, B, beta, tree_out(out), st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_marginal (top-B)");
+  return DTREE_OK;
+}
+
+int build_tree_gated(const void *logits, int dtype, int R, int L, int V, int K_root, float mu, int N,
+                     const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || N < 1 || K_root < 1 || K_root > N || K_root > V)
+    return fail(DTREE_E_INVAL, "need R >= 0, L, V >= 1, 1 <= K_root <= min(N, V)");
+  if (!(mu > 0.f && mu <= 1.f)) return fail(DTREE_E_INVAL, "need 0 < mu <= 1");
+  const int k = gated_k(V);
+  if (K_root > k || (N - K_root > k && k < V) || N > DTREE_MAX_CAP || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "K_root, N - K_root, N or L beyond the compiled envelope");
+  int rc = check_tree(out, N);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits) return fail(DTREE_E_INVAL, "logits is NULL");
+  const size_t need = a1_bytes(R * L, V, k);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  hipStream_t st = static_cast<hipStream_t>(s);
+  A1Ws a = a1_carve(ws, R * L, k);
+  dt::RowOut o{a.lse, nullptr, a.ids, a.zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, k, o, a.rest, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_gated (row sweep)");
+  e = dt::launch_gated(a.zk, a.ids, a.lse, R, L, k, K_root, log((double)mu), N, tree_out(out), st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_gated (gate)");
+  return DTREE_OK;
+}
+
+int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, const uint16_t *E, const uint16_t *U,
+                         const uint16_t *P, int d_model, int rank, const int32_t *root_tok, int K, int W, int B,
+                         float beta, const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || K < 1 || K > V || W < 1 || B < 1 || d_model < 1 || rank < 1)
+    return fail(DTREE_E_INVAL, "need R >= 0, L, V, W, B, d_model, rank >= 1, 1 <= K <= V");
+  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
+  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
+  if (rank != 64 || d_model % 64 != 0 || K > DTREE_MAX_K || W > 64 || W * K > 1024 || B > DTREE_MAX_CAP ||
+      L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "rank, d_model, K, W, B or L beyond the compiled envelope");
+  int rc = check_tree(out, B);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits || !E || !U || !P || !root_tok) return fail(DTREE_E_INVAL, "an input pointer is NULL");
+  const size_t need = a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B, rank);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  dt::DepthwiseArgs a{logits, dtype, R, L, V, K, W, B, d_model, rank, beta, E, U, P, root_tok};
+  hipError_t e = dt::launch_depthwise(a, tree_out(out), ws, static_cast<hipStream_t>(s));
+  if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise");
+  return DTREE_OK;
+}
+
+int accept_tree(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype, int R,
+                int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials, int32_t *accept_len,
+                int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (!tree) return fail(DTREE_E_INVAL, "tree struct is NULL");
+  if (R < 0 || L < 1 || V < 1 || n_trials < 1) return fail(DTREE_E_INVAL, "need R >= 0, L, V, n_trials >= 1");
+  if (!(temperature >= 0.f) || isinf(temperature)) return fail(DTREE_E_INVAL, "need finite temperature >= 0");
+  if (tree->cap < 1) return fail(DTREE_E_INVAL, "tree cap < 1");
+  if (tree->cap > DTREE_MAX_CAP || L > DTREE_MAX_L || V > DTREE_MAX_ACCEPT_V)
+    return fail(DTREE_E_UNSUPPORTED, "cap, L or V beyond the compiled envelope");
+  int rc = check_tree(tree, tree->cap);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!target_logits || !accept_len || !accept_node || !next_token)
+    return fail(DTREE_E_INVAL, "target_logits or an output is NULL");
+  if (temperature > 0.f && !draft_logits) return fail(DTREE_E_INVAL, "draft_logits is NULL with temperature > 0");
+  const size_t need = dt::accept_ws_bytes(R, L, V, tree->cap);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  dt::AcceptArgs a{tree_out(tree), target_logits, draft_logits, dtype, R, L, V, temperature, seed, trial0, n_trials,
+                   accept_len, accept_node, next_token};
+  hipError_t e = dt::launch_accept(a, ws, static_cast<hipStream_t>(s));
+  if (e != hipSuccess) return hip_fail(e, "accept_tree");
+  return DTREE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// Device helpers shared by the gfx950 kernels: element loads, ordered keys, block sorts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DT_INLINE __device__ __forceinline__
+
+namespace dt {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInf = __builtin_huge_valf();
+
+// bf16 bits -> float (exact widening).
+DT_INLINE float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Element loaders: uint16_t means bf16 bits.
+DT_INLINE float load_elt(const uint16_t *p, size_t i) { return bf16_to_f32(p[i]); }
+DT_INLINE float load_elt(const float *p, size_t i) { return p[i]; }
+
+// 16-byte vector of elements and its widening.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  DT_INLINE static void widen(const u32x4 &v, float *x) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  DT_INLINE static void widen(const u32x4 &v, float *x) {
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+  }
+};
+
+// Order-preserving map of a float to uint32 (-0 is mapped like +0). NaN is not expected.
+DT_INLINE uint32_t ord_f32(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+DT_INLINE float unord_f32(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+// Candidate key: larger value first, then smaller id. Key 0 is below every real key.
+DT_INLINE uint64_t make_key(float x, uint32_t id) {
+  return ((uint64_t)ord_f32(x) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+DT_INLINE float key_val(uint64_t k) { return unord_f32((uint32_t)(k >> 32)); }
+DT_INLINE uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
+
+DT_INLINE int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Descending bitonic sort of n keys (n a power of two) in LDS by the whole block.
+// Must be called by every thread of the block; ends with a barrier.
+template <int NT>
+DT_INLINE void block_sort_desc_u64(uint64_t *a, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += NT) {
+        int ixj = i ^ j;
+        if (ixj > i) {
+          uint64_t x = a[i], y = a[ixj];
+          bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            a[i] = y;
+            a[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Wave-level (64 lanes) reductions.
+DT_INLINE float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+DT_INLINE double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Prefix-score record used by the tree builders. Order within one depth:
+// (s desc, Z desc, ppos asc, rank asc); across depths a tie in s goes to the smaller depth.
+struct Pref {
+  double s;    // s_beta of the prefix
+  double Z;    // sum of the path's logits (exact tie detector within a depth)
+  int depth;
+  int ppos;    // parent's position within its own depth's order
+  int rank;    // candidate rank at this depth
+  int pos;     // own position within its depth's order (filled after sorting)
+};
+
+// true iff a precedes b in the global order.
+DT_INLINE bool pref_before(const Pref &a, const Pref &b) {
+  if (a.s != b.s) return a.s > b.s;
+  if (a.depth != b.depth) return a.depth < b.depth;
+  if (a.Z != b.Z) return a.Z > b.Z;
+  if (a.ppos != b.ppos) return a.ppos < b.ppos;
+  return a.rank < b.rank;
+}
+
+}  // namespace dt

@@ -1,0 +1,70 @@
+// Host-side launchers of the gfx950 kernels (internal to libdtree.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dtree.h"
+
+namespace dt {
+
+// ---- a1: fused row log-softmax + top-K ------------------------------------------------
+struct RowOut {
+  double *lse_d;  // [rows] or null
+  float *lse_f;   // [rows] or null
+  int32_t *ids;   // [rows][K]
+  float *zk;      // [rows][K] candidate logits, or null
+  float *lp;      // [rows][K] log-probs, or null
+};
+// Splits per row chosen for `rows`; workspace bytes for the split partials.
+int rowsweep_splits(int rows, int V, int K);
+size_t rowsweep_ws_bytes(int rows, int V, int K);
+hipError_t launch_rowsweep(const void *logits, int dtype, int rows, int V, int K, const RowOut &out,
+                           void *ws, hipStream_t st);
+
+// ---- tree outputs ------------------------------------------------------------------------
+struct TreeOut {
+  int32_t *parent, *token, *depth;
+  float *score;
+  uint32_t *mask;
+  int32_t *n_nodes;
+  int cap;
+};
+
+// ---- a2 + a6: marginal Top-B ---------------------------------------------------------------
+hipError_t launch_marginal(const float *zk, const int32_t *ids, const double *lse, int R, int L, int K,
+                           int B, float beta, const TreeOut &out, hipStream_t st);
+
+// ---- a5 + a6: TALON gated tree --------------------------------------------------------------
+hipError_t launch_gated(const float *zk, const int32_t *ids, const double *lse, int R, int L, int K,
+                        int K_root, double ln_mu, int N, const TreeOut &out, hipStream_t st);
+
+// ---- a3 + a4 + a6: DARTree depth-wise ---------------------------------------------------------
+struct DepthwiseArgs {
+  const void *base;  // [R][L][V]
+  int dtype;
+  int R, L, V, K, W, B, dm, rank;
+  float beta;
+  const uint16_t *E, *U, *P;
+  const int32_t *root_tok;
+};
+size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank);
+hipError_t launch_depthwise(const DepthwiseArgs &a, const TreeOut &out, void *ws, hipStream_t st);
+
+// ---- a7: acceptance walk ------------------------------------------------------------------------
+struct AcceptArgs {
+  TreeOut tree;
+  const void *target, *draft;
+  int dtype, R, L, V;
+  float T;
+  uint64_t seed, trial0;
+  int n_trials;
+  int32_t *accept_len, *accept_node, *next_token;
+};
+size_t accept_ws_bytes(int R, int L, int V, int cap);
+hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st);
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace dt

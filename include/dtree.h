@@ -1,0 +1,183 @@
+/*
+ * dtree.h -- C ABI of the MI355X (gfx950) draft-tree construction library, libdtree.so.
+ *
+ * The operations are those of speculative decoding with block-parallel drafters:
+ *   - "DARTree: Speculative Diffusion Decoding With Autoregressive Draft Trees"
+ *     (papercache summary of arXiv 2608.13524): Algorithm 1, the depth-bonus score
+ *     s_beta, Lemma 1 (best-first == global Top-B when beta <= 0).
+ *   - "DDTree: from theory to practice" (CSDN blog), sections 2-3: the optimal tree
+ *     is the B best prefixes; each position needs only its top K = min(B, V) tokens.
+ *   - "TALON: Confidence-Aware Speculative Decoding with Adaptive Token Trees",
+ *     key designs 1-2: root Top-K, gating against the per-depth anchor m_d, budget N.
+ *   - Course notes "Sampling, speculative decoding and multi-token prediction"
+ *     (unit 11): acceptance min(1, p/q), residual (p - q)_+, bonus token.
+ *
+ * Conventions shared by every entry point
+ *   - Logits are row-major [R][L][V] (rounds, draft positions, vocabulary), V contiguous,
+ *     as bf16 bit patterns (uint16, DTREE_BF16) or IEEE float (DTREE_F32). They must be
+ *     finite; non-finite logits are a precondition violation that is not detected.
+ *   - All array arguments are DEVICE pointers (memory of the current HIP device), except
+ *     the dtree_tree struct itself and scalar arguments, which live on the host.
+ *   - The caller owns every buffer, including the workspace `ws` of at least
+ *     dtree_workspace_size(...) bytes. The library never allocates or frees memory, keeps
+ *     no state between calls and holds no pointer after it returns.
+ *   - Every call only enqueues kernels on stream `s` (a hipStream_t; NULL = null stream)
+ *     and returns; results are valid once the stream reaches that point. Calls are
+ *     reentrant; calls that share an output or workspace buffer must be ordered by the caller.
+ *   - Arguments are validated on the host before anything is launched: on an error the
+ *     call returns a negative dtree_status, launches nothing and leaves outputs untouched.
+ *     dtree_last_error() then gives a thread-local message.
+ *
+ * Tree outputs (dtree_tree, one slot row per round)
+ *   B (or N) counts non-root nodes; node 0 is the root (the verified context). Nodes are
+ *   laid out depth by depth, each depth in its selection order (larger score first), so
+ *   parent[i] < i. Slot i of round r: parent, token (vocabulary id), depth (root 0), score
+ *   (s_beta of the prefix, float; root 0). Unused slots hold -1 and score -inf.
+ *   mask[r][i][w], w < ceil((cap+1)/32): bit (j & 31) of word (j >> 5) is set iff node j
+ *   is node i or an ancestor of i -- the tree-attention mask (DARTree background
+ *   "tree verification"; DDTree blog section 4.2). Unused rows are zero.
+ *   n_nodes[r] = number of non-root nodes of round r.
+ *
+ * Ordering and ties (same rule in every builder)
+ *   A position's candidates are ranked by (logit desc, vocabulary id asc). Prefix scores
+ *   are accumulated in float64. Among prefixes of one depth the order is (score desc,
+ *   sum of path logits desc, parent's position in its depth asc, candidate rank asc);
+ *   across depths a tie in score goes to the shallower prefix (Lemma 1: ancestor first).
+ */
+#ifndef DTREE_H
+#define DTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *dtree_stream_t;
+
+enum dtree_dtype { DTREE_BF16 = 0, DTREE_F32 = 1 };
+
+enum dtree_status {
+  DTREE_OK = 0,
+  DTREE_E_INVAL = -1,       /* bad size/scalar or NULL pointer */
+  DTREE_E_BETA = -2,        /* beta > 0: Lemma 1's precondition fails (DARTree Lemma 1) */
+  DTREE_E_WORKSPACE = -3,   /* ws too small or NULL */
+  DTREE_E_UNSUPPORTED = -4, /* valid, but outside the compiled envelope (limits below) */
+  DTREE_E_HIP = -5          /* a HIP launch failed; detail in dtree_last_error() */
+};
+
+enum dtree_op {
+  DTREE_OP_TOPK = 0,
+  DTREE_OP_MARGINAL = 1,
+  DTREE_OP_DEPTHWISE = 2,
+  DTREE_OP_GATED = 3,
+  DTREE_OP_ACCEPT = 4
+};
+
+/* Compiled envelope (DTREE_E_UNSUPPORTED beyond it). */
+#define DTREE_MAX_K 64      /* per-position candidates */
+#define DTREE_MAX_L 64      /* draft positions */
+#define DTREE_MAX_CAP 128   /* B or N */
+#define DTREE_MAX_ACCEPT_V 262144 /* vocabulary of accept_tree */
+
+typedef struct {
+  int32_t *parent;  /* [R][cap+1] */
+  int32_t *token;   /* [R][cap+1] */
+  int32_t *depth;   /* [R][cap+1] */
+  float *score;     /* [R][cap+1] */
+  uint32_t *mask;   /* [R][cap+1][(cap+1+31)/32] */
+  int32_t *n_nodes; /* [R] */
+  int32_t cap;      /* B or N */
+} dtree_tree;
+
+/*
+ * Bytes of workspace an operation needs. `op` is a dtree_op; unused size arguments are
+ * ignored: TOPK(rows = R*L, V, K), MARGINAL(R, L, V, K, B), DEPTHWISE(R, L, V, K, B, W,
+ * rank), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap). Returns 0 for an
+ * unknown op or invalid sizes.
+ */
+size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank);
+
+/*
+ * Row log-softmax and top-K (DDTree blog 3.3: top-K tokens per position with their
+ * log-probs; DARTree Algorithm 1 step 4: C_d = TopK(L_d^base, K)).
+ * logits [rows][V]; outputs lse [rows] = ln sum_v exp(z_v), ids [rows][K] in rank order
+ * (logit desc, id asc), lp [rows][K] = z - lse. Any of lse / lp may be NULL.
+ * Needs 1 <= K <= min(V, DTREE_MAX_K).
+ */
+int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K, float *lse,
+                          int32_t *ids, float *lp, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * Marginal draft tree (DDTree; DARTree background "tree verification and DDTree"):
+ * the B prefixes u, |u| <= L, with the largest s_beta(u) = sum_i log q_i(u_i) + beta*|u|,
+ * q_i = softmax(logits[r][i-1]), over each position's top K tokens. K = 0 means
+ * min(B, V) (DDTree's S_K lemma), which gives the exact global Top-B. Needs beta <= 0
+ * (else DTREE_E_BETA), 1 <= B <= DTREE_MAX_CAP, K <= DTREE_MAX_K, out->cap == B.
+ */
+int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta,
+                        const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * DARTree depth-wise super-tree + deferred Top-B (DARTree Algorithm 1) with a Markov
+ * correction head: branch state = its last token (root: root_tok[r]);
+ *   h = bf16(E[tok] @ U_d),  z = base_d + h @ P,  log q~_d(c | b) = z[c] - logsumexp(z)
+ * for c in C_d = top-K of base_d (shared by all branches); per depth the global top-W
+ * children are kept, then the B best of the whole super-tree by s_beta.
+ * E [V][d_model], U [L][d_model][rank], P [rank][V] are bf16 bits; root_tok [R] int32.
+ * Needs beta <= 0, rank == 64, d_model % 64 == 0, K <= DTREE_MAX_K, W <= 64, W*K <= 1024,
+ * B <= DTREE_MAX_CAP, out->cap == B.
+ */
+int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, const uint16_t *E,
+                         const uint16_t *U, const uint16_t *P, int d_model, int rank,
+                         const int32_t *root_tok, int K, int W, int B, float beta,
+                         const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * TALON gated tree (TALON key designs 1-2): the root's children are the top K_root
+ * tokens of position 1; then per depth the pool P_d x V is gated by p(u) >= mu * m_d
+ * (m_d = the pool's best path probability) and, when the survivors exceed N - |T|,
+ * truncated to the N - |T| best and growth stops. Growth also stops at depth L or
+ * |T| = N. Needs 1 <= K_root <= N, 0 < mu <= 1, K_root <= DTREE_MAX_K,
+ * N - K_root <= DTREE_MAX_K, N <= DTREE_MAX_CAP, out->cap == N.
+ */
+int build_tree_gated(const void *logits, int dtype, int R, int L, int V, int K_root, float mu, int N,
+                     const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * Tree verification walk (DARTree background "speculative sampling"; course notes unit 11).
+ * tree: a tree from one of the builders (device arrays, cap = tree->cap).
+ * target_logits [R][cap+1][V]: the target's logits at every tree slot (row j = the
+ * distribution after node j's path). draft_logits [R][L][V] (may be NULL when
+ * temperature == 0): q at node j is softmax(draft[r][min(depth(j), L-1)] / T).
+ * temperature == 0: greedy -- descend to the child carrying the target's argmax (smallest
+ * id on ties), else stop and emit that argmax.
+ * temperature > 0: at each node try the children in slot order, accepting child c iff
+ * u * q(c) < p'(c) with p' the current residual (starts at softmax(target/T)); a rejection
+ * sets p' <- (p' - q)_+ / sum (kept as is when that sum is 0). When all children are
+ * rejected, or at a leaf, draw the extra token from p' by inverse CDF (smallest v with
+ * cumsum p'(v) > u * sum p'). Uniforms: Philox4x32-10 (Salmon et al., SC'11) with key
+ * (seed lo, seed hi) and counter (trial lo, round, step, trial hi), u = (out0 >> 8) / 2^24,
+ * trial = trial0 + t for t < n_trials.
+ * Outputs [n_trials][R]: accept_len (accepted draft tokens = depth of accept_node),
+ * accept_node (slot index), next_token (bonus or correction token).
+ * Needs cap <= DTREE_MAX_CAP, L <= DTREE_MAX_L, V <= DTREE_MAX_ACCEPT_V, n_trials >= 1,
+ * temperature >= 0.
+ */
+int accept_tree(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype,
+                int R, int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials,
+                int32_t *accept_len, int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes,
+                dtree_stream_t s);
+
+/* Static string for a dtree_status code. */
+const char *dtree_status_string(int status);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char *dtree_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DTREE_H */

@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every declared symbol, sizes workspaces, and rejects bad
+arguments on the host before any launch (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_tree_construction_amd as dt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "dtree.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = dt.lib()
+    decl = declared_symbols()
+    assert set(decl) == set(dt.SYMBOLS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = dt.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.dtree_status_string(code)
+    assert L.dtree_status_string(7) == b"unknown status"
+
+
+def test_workspace_sizes():
+    ws = dt.workspace_size
+    assert ws(dt.OP_MARGINAL, 64, 16, 151936, 64, 64) > 64 * 16 * 64 * 8
+    assert ws(dt.OP_GATED, 64, 16, 151936, 0, 60) > 0
+    assert ws(dt.OP_ACCEPT, 64, 16, 151936, 0, 64) > 64 * 65 * 2374 * 8
+    assert ws(dt.OP_DEPTHWISE, 64, 16, 151936, 8, 128, 32, 64) > 0
+    assert ws(dt.OP_TOPK, 1024, 1, 151936, 64) == 0          # no split needed
+    assert ws(dt.OP_TOPK, 2, 1, 151936, 64) > 0              # split rows need partials
+    assert ws(99, 1, 1, 1) == 0
+    assert ws(dt.OP_MARGINAL, -1, 16, 100, 8, 8) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def tree(cap):
+    return dt.CTree(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, cap)
+
+
+def marg(**kw):
+    a = dict(logits=FAKE, dtype=0, R=4, L=4, V=32, K=8, B=8, beta=0.0, t=tree(8), ws=FAKE, nbytes=0)
+    a.update(kw)
+    t = a["t"]
+    return dt.lib().build_tree_marginal(a["logits"], a["dtype"], a["R"], a["L"], a["V"], a["K"], a["B"],
+                                        a["beta"], ctypes.byref(t) if t is not None else None, a["ws"],
+                                        a["nbytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(beta=0.5), -2),
+    (dict(beta=float("nan")), -1),
+    (dict(dtype=3), -1),
+    (dict(K=33), -1),
+    (dict(K=65, V=1000), -4),
+    (dict(B=129, t=tree(129)), -4),
+    (dict(L=65), -4),
+    (dict(t=tree(7)), -1),
+    (dict(t=None), -1),
+    (dict(logits=None), -1),
+    (dict(ws=None), -3),
+    (dict(nbytes=10), -3),
+])
+def test_marginal_validation(kw, code):
+    assert marg(**kw) == code
+    assert dt.lib().dtree_last_error()
+
+
+def test_zero_rounds_is_a_no_op():
+    assert marg(R=0, ws=None, logits=None) == 0
+
+
+def test_gated_validation():
+    L = dt.lib()
+    t = tree(60)
+    def call(K_root=10, mu=0.03, N=60, V=151936, cap_t=t):
+        return L.build_tree_gated(FAKE, 0, 4, 16, V, K_root, mu, N, ctypes.byref(cap_t), FAKE, 0, None)
+    assert call(mu=0.0) == -1
+    assert call(mu=1.5) == -1
+    assert call(K_root=61) == -1
+    assert call(K_root=0) == -1
+    assert call(N=200, cap_t=tree(200)) == -4
+    assert call(K_root=65, N=100, cap_t=tree(100)) == -4
+    assert call() == -3
+
+
+def test_depthwise_validation():
+    L = dt.lib()
+    def call(rank=64, dm=1024, K=8, W=32, B=128, beta=-0.5, cap=128):
+        t = tree(cap)
+        return L.build_tree_depthwise(FAKE, 0, 4, 16, 151936, FAKE, FAKE, FAKE, dm, rank, FAKE, K, W, B, beta,
+                                      ctypes.byref(t), FAKE, 0, None)
+    assert call(beta=0.1) == -2
+    assert call(rank=32) == -4
+    assert call(dm=1000) == -4
+    assert call(W=65) == -4
+    assert call(K=9, W=64*2) == -4
+    assert call() == -3
+
+
+def test_accept_validation():
+    L = dt.lib()
+    t = tree(64)
+    def call(T=1.0, n=1, draft=FAKE, V=151936):
+        o = FAKE
+        return L.accept_tree(ctypes.byref(t), FAKE, draft, 0, 4, 16, V, T, 1, 0, n, o, o, o, FAKE, 0, None)
+    assert call(T=-1.0) == -1
+    assert call(T=float("inf")) == -1
+    assert call(n=0) == -1
+    assert call(draft=None) == -1
+    assert call(V=300000) == -4
+    assert call() == -3
+    assert L.accept_tree(None, FAKE, FAKE, 0, 4, 16, 100, 1.0, 1, 0, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+
+
+def test_topk_validation():
+    L = dt.lib()
+    def call(K=8, V=32, rows=4, dtype=0):
+        return L.dtree_topk_logsoftmax(FAKE, dtype, rows, V, K, FAKE, FAKE, FAKE, None, 0, None)
+    assert call(K=0) == -1
+    assert call(K=33) == -1
+    assert call(K=65, V=100) == -4
+    assert call(dtype=5) == -1
+    assert call(rows=2, V=151936, K=8) == -3   # split rows need a workspace
+    assert call(rows=0) == 0
