@@ -1,0 +1,214 @@
+"""Benchmark of the draft-tree construction hot path on one MI355X.
+
+One step = one pass of the whole hot path over a batch of R = 64 rounds
+(L = 16 draft positions, V = 151,936, bf16 logits, synthetic seeded inputs):
+  1. build_tree_marginal   DDTree-shape logits, K = B = 64, beta = 0
+  2. build_tree_depthwise  same logits as base, Markov head E 151936x1024, U 16x1024x64,
+                           P 64x151936, K = 8, W = 32, B = 128, beta = -0.5
+  3. build_tree_gated      TALON-shape logits, K_root = 10, mu = 0.03, N = 60
+  4. accept_tree T = 0     the step's marginal trees against draft-correlated target logits
+  5. accept_tree T = 1     same, one Philox-seeded trial per round (trial index = step)
+value = rounds per second of that whole step (R / step time). Inputs are resident in
+HBM before timing. Prints one JSON line.
+
+The roofline object is for the logits row sweep (fused log-softmax + top-K), the
+kernel every builder runs over its [R, L, V] logits, timed live with HIP events over
+K launches of dtree_topk_logsoftmax on the same stream; algorithmic bytes per launch
+= R*L*V*2 (each bf16 logit read once) + the K-list outputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+R, L, V = 64, 16, 151936
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "rowsweep_traffic.json"))
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(rounds shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import draft_tree_construction_amd as dt
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs (seeded, resident in HBM)
+    draft_h = synth.ddtree_logits(seed=2)
+    draft = bf(draft_h)
+    talon_h = synth.talon_logits(seed=4)
+    talon = bf(talon_h)
+    head = synth.correction_head(seed=3)
+    E_h, U_h, P_h, root_h = head
+    E, U, P = bf(E_h), bf(U_h), bf(P_h)
+    root = torch.from_numpy(root_h).to(dev)
+
+    ws_m = torch.empty(dt.workspace_size(dt.OP_MARGINAL, R, L, V, 64, 64), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(dt.workspace_size(dt.OP_DEPTHWISE, R, L, V, 8, 128, 32, 64), dtype=torch.uint8, device=dev)
+    ws_g = torch.empty(dt.workspace_size(dt.OP_GATED, R, L, V, 0, 60), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(dt.workspace_size(dt.OP_ACCEPT, R, L, V, 0, 64), dtype=torch.uint8, device=dev)
+    t_m, t_d, t_g = dt.Tree.empty(R, 64, dev), dt.Tree.empty(R, 128, dev), dt.Tree.empty(R, 60, dev)
+    o0 = tuple(torch.empty(1, R, dtype=torch.int32, device=dev) for _ in range(3))
+    o1 = tuple(torch.empty(1, R, dtype=torch.int32, device=dev) for _ in range(3))
+
+    # target logits follow the marginal trees' depths (deterministic, so built once)
+    dt.build_tree_marginal(draft, 64, 64, 0.0, ws=ws_m, out=t_m)
+    torch.cuda.synchronize()
+    target = bf(synth.verification_target(draft_h, t_m.depth.cpu().numpy(), seed=5))
+
+    stream = torch.cuda.current_stream(dev)
+    names = ["marginal", "depthwise", "gated", "accept_t0", "accept_t1"]
+
+    def step(i, ev=None):
+        def mark(k):
+            if ev is not None:
+                ev[k].record(stream)
+        mark(0)
+        dt.build_tree_marginal(draft, 64, 64, 0.0, ws=ws_m, out=t_m)
+        mark(1)
+        dt.build_tree_depthwise(draft, E, U, P, root, 8, 32, 128, -0.5, ws=ws_d, out=t_d)
+        mark(2)
+        dt.build_tree_gated(talon, 10, 0.03, 60, ws=ws_g, out=t_g)
+        mark(3)
+        dt.accept_tree(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
+        mark(4)
+        dt.accept_tree(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
+        mark(5)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, synchronised on both sides
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(5)] for i in range(args.steps)])
+    step_ms = float(np.sum(per, axis=1).mean())
+    ms_per_step = wall * 1e3 / args.steps
+    value = R / (ms_per_step / 1e3)
+
+    # ---- roofline: the row sweep kernel, timed live over its own launches on this stream
+    flat = draft.view(R * L, V)
+    K = 64
+    lse = torch.empty(R * L, dtype=torch.float32, device=dev)
+    ids = torch.empty(R * L, K, dtype=torch.int32, device=dev)
+    lp = torch.empty(R * L, K, dtype=torch.float32, device=dev)
+    ws_t = torch.empty(max(dt.workspace_size(dt.OP_TOPK, R * L, 1, V, K), 1), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        dt.topk_logsoftmax(flat, K, ws=ws_t)
+    torch.cuda.synchronize()
+    n_sweep = max(args.steps, 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_sweep):
+        dt.lib().dtree_topk_logsoftmax(flat.data_ptr(), 0, R * L, V, K, lse.data_ptr(), ids.data_ptr(),
+                                       lp.data_ptr(), ws_t.data_ptr(), ws_t.numel(), stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sweep_us = e0.elapsed_time(e1) * 1e3 / n_sweep
+    alg_bytes = R * L * V * 2 + R * L * (4 + K * 8)
+    achieved = alg_bytes / (sweep_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            traffic = json.load(open(args.traffic_json)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "k_rowsweep<bf16> (dtree_topk_logsoftmax, R*L=1024 rows, K=64)",
+                "us_per_launch": round(sweep_us, 2), "alg_bytes_per_launch": alg_bytes}
+
+    out = {
+        "metric": "tree-build rounds/sec + us/round at V=151936,L=16,B=128; HBM GB/s vs peak",
+        "value": round(value, 1), "unit": "rounds/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "us_per_round": round(ms_per_step * 1e3 / R, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "R=64 rounds, L=16, V=151936 bf16: marginal K=B=64 + depthwise K=8,W=32,B=128,"
+                               "beta=-0.5,E 151936x1024,rank 64 + gated K_root=10,mu=0.03,N=60 + "
+                               "accept T=0 and T=1 (1 trial/round) on the marginal trees",
+                   "rounds": R, "L": L, "V": V},
+        "breakdown_us_per_round": {n: round(float(per[:, k].mean()) * 1e3 / R, 3) for k, n in enumerate(names)},
+        "breakdown_ms": {n: round(float(per[:, k].mean()), 4) for k, n in enumerate(names)},
+        "event_ms_per_step": round(step_ms, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(draft_h, talon_h, head)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(draft_h, talon_h, head):
+    """The oracle, as it stands, on a bounded sample: one round of the same step
+    (all five operations) on round 0's inputs, single-threaded numpy."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    import synth
+    from oracle import accept, depthwise, gated, marginal, rowsweep
+
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    try:
+        r = 0
+        z = rowsweep.as_f64(draft_h[r], "bf16")
+        tal = rowsweep.as_f64(talon_h[r], "bf16")
+        E_h, U_h, P_h, root_h = head
+        t0 = time.perf_counter()
+        tm = marginal.build_marginal(z, 64, 64, 0.0)
+        E64 = E_h  # rows are gathered on demand
+        U64 = synth.f32_from_bf16(U_h).astype(np.float64)
+        P64 = synth.f32_from_bf16(P_h).astype(np.float64)
+
+        class Rows:
+            def __getitem__(self, idx):
+                return synth.f32_from_bf16(E64[idx]).astype(np.float64)
+        depthwise.build_depthwise(z, Rows(), U64, P64, int(root_h[r]), 8, 32, 128, -0.5)
+        gated.build_gated(tal, 10, float(np.float32(0.03)), 60, full_pool=False)
+        depth = np.array(tm.arrays(64)[2])[None, :]
+        tgt = rowsweep.as_f64(synth.verification_target(draft_h[:1], depth, seed=5)[0], "bf16")
+        accept.walk_greedy(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1])
+        tab = accept.ResidualTables(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1], z, 1.0)
+        accept.walk_sampled(tab, tm.depth, synth.PHILOX_SEED, 0, 0)
+        dt_s = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {"value": round(1.0 / dt_s, 4), "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": "1 round (round 0) of the full step: marginal + depthwise + gated + accept T=0 + T=1, "
+                      f"float64 numpy, 1 thread; {dt_s:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

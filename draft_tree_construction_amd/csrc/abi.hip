@@ -180,8 +180,8 @@ int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, con
     return fail(DTREE_E_INVAL, "need R >= 0, L, V, W, B, d_model, rank >= 1, 1 <= K <= V");
   if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
   if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
-  if (rank != 64 || d_model % 64 != 0 || K > DTREE_MAX_K || W > 64 || W * K > 1024 || B > DTREE_MAX_CAP ||
-      L > DTREE_MAX_L)
+  if (rank != 64 || d_model % 64 != 0 || K > DTREE_MAX_K || W > 64 || W * K > 1024 || L * W > 2048 ||
+      B > DTREE_MAX_CAP || L > DTREE_MAX_L)
     return fail(DTREE_E_UNSUPPORTED, "rank, d_model, K, W, B or L beyond the compiled envelope");
   int rc = check_tree(out, B);
   if (rc) return rc;
@@ -189,8 +189,13 @@ int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, con
   if (!logits || !E || !U || !P || !root_tok) return fail(DTREE_E_INVAL, "an input pointer is NULL");
   const size_t need = a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B, rank);
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  hipStream_t st = static_cast<hipStream_t>(s);
+  A1Ws a1 = a1_carve(ws, R * L, K);
+  dt::RowOut o{a1.lse, nullptr, a1.ids, a1.zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, K, o, a1.rest, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise (row sweep)");
   dt::DepthwiseArgs a{logits, dtype, R, L, V, K, W, B, d_model, rank, beta, E, U, P, root_tok};
-  hipError_t e = dt::launch_depthwise(a, tree_out(out), ws, static_cast<hipStream_t>(s));
+  e = dt::launch_depthwise(a, a1.zk, a1.ids, tree_out(out), static_cast<char *>(ws) + a1_bytes(R * L, V, K), st);
   if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise");
   return DTREE_OK;
 }

@@ -1,17 +1,575 @@
-// a3 + a4: DARTree depth-wise super-tree (kernels follow).
+// a3 + a4 + a6: DARTree depth-wise super-tree with a Markov correction head, deferred Top-B.
+//
+// What it computes (DARTree summary, Algorithm 1): from the root, depth by depth, every
+// active branch b (state = its last token) is corrected at once,
+//     h_b = bf16(E[tok_b] @ U_d),  z_b = base_d + h_b @ P,  log q~ = z_b[c] - logsumexp(z_b),
+// each child (b, c), c in C_d = top-K of base_d, is scored s = s_b + log q~ + beta, the best
+// W children (over all branches) form S_d, and finally the B best nodes of the super-tree
+// by s are kept (Lemma 1: a sort replaces the best-first heap).
+//
+// Design (gfx950), per depth two launches plus a final one:
+//  * k_dw_corr -- the only O(V) work and the only dense contraction. For a tile of 32
+//    branches of one round and a 32-token block, one v_mfma_f32_32x32x16_bf16 chain
+//    (K = 64 + 16) computes z - ref directly: the A operand is P^T (pre-transposed so each
+//    lane loads 64 contiguous bytes) with two extra columns [1, base(v)], the B operand is
+//    [h_b, -ref_b, 1] and stays in registers for the whole V range. ref_b is a bf16 upper
+//    bound of max_v z_b (max base + sum_j |h_j| max|P_j.|), so exp(z - ref) <= 1 needs no
+//    running max; each lane owns one branch column and 16 rows, so the sum of
+//    exponentials accumulates per lane with no cross-lane reduction until the end.
+//    Workgroups are mapped XCD-aware: all tiles of one V chunk run on one XCD, so that
+//    chunk of P^T is read from HBM once and then served from that XCD's L2.
+//    (If the bound is loose -- over 10 nats -- the tile switches to a running max.)
+//  * k_dw_select -- one workgroup per round: reduce the chunk partials to LSE_b, score the
+//    W*K children (candidate logits recomputed with the same h and P), sort in LDS, keep
+//    the top W as S_d, then compute the next depth's h = E[tok] @ U with MFMA.
+//  * k_dw_final -- one workgroup per round: Top-B over the super-tree, parent array, mask.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "treeio.hpp"
 
 namespace dt {
 
-size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank) {
-  (void)R; (void)L; (void)V; (void)K; (void)W; (void)B; (void)rank;
-  return 0;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int DW_NT = 256;
+constexpr int DW_NC = 64;      // V chunks (partials per branch)
+constexpr int DW_HX = 80;      // branch row: h (64), -ref, 1, zero padding
+constexpr int DW_SUP = 2048;   // super-tree nodes per round (L * W)
+constexpr int DW_CH = 1024;    // children per depth (W * K)
+constexpr float DW_WIDE = 10.f;
+
+DT_INLINE bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+DT_INLINE uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+// smallest bf16 >= x (x finite)
+DT_INLINE uint16_t f32_to_bf16_up(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0xFFFFu) == 0) return (uint16_t)(u >> 16);
+  if (u & 0x80000000u) return (uint16_t)(u >> 16);  // negative: truncation rounds toward +inf
+  return (uint16_t)((u >> 16) + 1);
 }
 
-hipError_t launch_depthwise(const DepthwiseArgs &a, const TreeOut &out, void *ws, hipStream_t st) {
-  (void)a; (void)out; (void)ws; (void)st;
-  return hipErrorNotSupported;
+struct DwState {
+  uint16_t *PT;     // [V][64]: row v holds P[k][v] at slot half*32 + kb*8 + e, k = 16kb + 8half + e
+  float *pmax;      // [64]: max_v |P[j][v]|
+  uint16_t *hx;     // [R][Wp][80]
+  float *bref;      // [R][Wp]: ref of each branch (a bf16 value)
+  double *bs;       // [R][Wp]: branch scores
+  int *nb;          // [R]: branches at the current depth
+  int *wide;        // [R][NG]: tile uses a running max
+  double *part_s;   // [R*Wp][NC]
+  float *part_m;    // [R*Wp][NC]
+  double *sup_s;    // [R][L][W]
+  int *sup_pk;      // [R][L][W]: ppos << 16 | rank
+  int *sup_tok;     // [R][L][W]
+  int *sup_n;       // [R][L]
+};
+
+struct DwDev {
+  const float *zk;     // [R*L][K] candidate base logits
+  const int32_t *ids;  // [R*L][K]
+  const uint16_t *E, *U;
+  const int32_t *root_tok;
+  int R, L, V, K, W, Wp, NG, B, dm;
+  float beta;
+};
+
+// ---------------------------------------------------------------- prep: P^T and column maxima
+__global__ __launch_bounds__(DW_NT) void k_dw_transpose_p(const uint16_t *__restrict__ P, int V, uint16_t *PT) {
+  __shared__ uint16_t tile[64][66];
+  const int v0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += DW_NT) {
+    const int k = i >> 6, vv = i & 63;
+    tile[k][vv] = (v0 + vv < V) ? P[(size_t)k * V + v0 + vv] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += DW_NT) {
+    const int vv = i >> 6, slot = i & 63;
+    const int half = slot >> 5, kb = (slot >> 3) & 3, e = slot & 7;
+    const int k = 16 * kb + 8 * half + e;
+    if (v0 + vv < V) PT[(size_t)(v0 + vv) * 64 + slot] = tile[k][vv];
+  }
+}
+
+__global__ __launch_bounds__(DW_NT) void k_dw_pmax(const uint16_t *__restrict__ P, int V, float *pmax) {
+  __shared__ float red[DW_NT / 64];
+  const int j = blockIdx.x;
+  float m = 0.f;
+  for (int v = threadIdx.x; v < V; v += DW_NT) m = fmaxf(m, fabsf(bf16_to_f32(P[(size_t)j * V + v])));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int i = 1; i < DW_NT / 64; ++i) r = fmaxf(r, red[i]);
+    pmax[j] = r;
+  }
+}
+
+// ---------------------------------------------------------------- the correction sweep
+template <typename T>
+__global__ __launch_bounds__(DW_NT) void k_dw_corr(DwState s, const T *__restrict__ base, int d, int L, int V,
+                                                   int R, int NG) {
+  const int nct = R * NG;
+  const int TG = (nct + 3) >> 2;
+  const int i = blockIdx.x, xcd = i & 7, j = i >> 3;
+  const int c = xcd + 8 * (j / TG);
+  const int g = j - (j / TG) * TG;
+  if (c >= DW_NC) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = g * 4 + wave;
+  if (t >= nct) return;
+  const int r = t / NG;
+  const int col = lane & 31, half = lane >> 5;
+
+  const u32x4 *hrow = reinterpret_cast<const u32x4 *>(s.hx + ((size_t)t * 32 + col) * DW_HX);
+  bf16x8 bfr[5];
+#pragma unroll
+  for (int kb = 0; kb < 5; ++kb) bfr[kb] = as_bf16x8(hrow[2 * kb + half]);
+  const bool wide = s.wide[t] != 0;
+  const T *brow = base + ((size_t)r * L + (d - 1)) * V;
+  const int nb32 = (V + 31) >> 5;
+  const int blk0 = (int)(((long long)nb32 * c) / DW_NC);
+  const int blk1 = (int)(((long long)nb32 * (c + 1)) / DW_NC);
+  constexpr bool kBf16 = sizeof(T) == 2;
+  const bf16x8 zero8 = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+
+  double acc = 0.0;
+  float m = wide ? -kInf : 0.f;
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int v = (blk << 5) + col;
+    bf16x8 a0 = zero8, a1 = zero8, a2 = zero8, a3 = zero8, a4 = zero8;
+    if (v < V) {
+      const u32x4 *pr = reinterpret_cast<const u32x4 *>(s.PT + (size_t)v * 64 + half * 32);
+      a0 = as_bf16x8(pr[0]);
+      a1 = as_bf16x8(pr[1]);
+      a2 = as_bf16x8(pr[2]);
+      a3 = as_bf16x8(pr[3]);
+      if (half == 0) {
+        uint32_t w0 = 0x3F80u;
+        if constexpr (kBf16) w0 |= ((uint32_t)reinterpret_cast<const uint16_t *>(brow)[v]) << 16;
+        a4 = as_bf16x8(u32x4{w0, 0u, 0u, 0u});
+      }
+    }
+    f32x16 z = {};
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfr[0], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfr[1], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, bfr[2], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, bfr[3], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a4, bfr[4], z, 0, 0, 0);
+    // lane holds rows (blk*32 + 8*(q/4) + 4*half + q%4) of its branch column
+    const int vbase = (blk << 5) + 4 * half;
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int vr = vbase + 8 * (q >> 2) + (q & 3);
+      float xv = z[q];
+      if constexpr (!kBf16) {
+        if (vr < V) xv += load_elt(brow, (size_t)vr);
+      }
+      x[q] = (vr < V) ? xv : -kInf;
+    }
+    if (!wide) {
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; q += 2) {
+        a += __builtin_amdgcn_exp2f(x[q] * kLog2e);
+        b += __builtin_amdgcn_exp2f(x[q + 1] * kLog2e);
+      }
+      acc += (double)(a + b);
+    } else {
+      float bm = -kInf;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) bm = fmaxf(bm, x[q]);
+      if (bm > m) {
+        acc = (m == -kInf) ? 0.0 : acc * exp((double)m - (double)bm);
+        m = bm;
+      }
+      if (m != -kInf) {
+        float a = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) a += __builtin_amdgcn_exp2f((x[q] - m) * kLog2e);
+        acc += (double)a;
+      }
+    }
+  }
+  // merge the two row halves of this branch column (lanes l and l ^ 32)
+  const float mo = __shfl_xor(m, 32, 64);
+  const double ao = __shfl_xor(acc, 32, 64);
+  const float mm = fmaxf(m, mo);
+  double tot = 0.0;
+  if (mm != -kInf) {
+    tot = ((m == -kInf) ? 0.0 : acc * exp((double)m - (double)mm)) + ((mo == -kInf) ? 0.0 : ao * exp((double)mo - (double)mm));
+  }
+  if (half == 0) {
+    const size_t o = ((size_t)t * 32 + col) * DW_NC + c;
+    s.part_s[o] = tot;
+    s.part_m[o] = mm;
+  }
+}
+
+// ---------------------------------------------------------------- next-depth branch state
+// For the `keep` new branches of round r (tokens tok[]), h = bf16(E[tok] @ U[dn-1]) via MFMA,
+// the bf16 upper bound ref, and the hx rows / tile flags. Called by the whole block.
+DT_INLINE void dw_branch_state(const DwState &s, const DwDev &a, int r, int dn, int keep, const int *tok,
+                               const double *sc, float (*hacc)[32][65], float *bnd) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int ct = wave & 1, kh = wave >> 1;
+  const int kspan = a.dm >> 1;
+  const uint16_t *Ud = a.U + (size_t)(dn - 1) * a.dm * 64;
+  const float mnext = a.zk[((size_t)r * a.L + (dn - 1)) * a.K];
+  const int nrt = (a.Wp + 31) >> 5;
+  for (int rt = 0; rt < nrt; ++rt) {
+    const int bi = rt * 32 + col;  // A row (branch) for this lane
+    const bool live = bi < keep;
+    const uint16_t *erow = live ? a.E + (size_t)tok[bi] * a.dm : nullptr;
+    f32x16 acc = {};
+    for (int k0 = kh * kspan; k0 < (kh + 1) * kspan; k0 += 16) {
+      bf16x8 av = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      if (live) av = as_bf16x8(*reinterpret_cast<const u32x4 *>(erow + k0 + 8 * half));
+      uint16_t bb[8];
+      const int jc = 32 * ct + col;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bb[e] = Ud[(size_t)(k0 + 8 * half + e) * 64 + jc];
+      bf16x8 bv;
+      __builtin_memcpy(&bv, bb, 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = 8 * (q >> 2) + 4 * half + (q & 3);
+      hacc[kh][row][32 * ct + col] = acc[q];
+    }
+    __syncthreads();
+    // h = bf16(sum of the two k halves); rows x 64 columns, 256 threads
+    for (int idx = threadIdx.x; idx < 32 * 64; idx += DW_NT) {
+      const int row = idx >> 6, jj = idx & 63;
+      const int b = rt * 32 + row;
+      const float hv = hacc[0][row][jj] + hacc[1][row][jj];
+      const uint16_t hb = (b < keep) ? f32_to_bf16_rne(hv) : (uint16_t)0;
+      s.hx[((size_t)r * a.Wp + b) * DW_HX + jj] = hb;
+      hacc[0][row][jj] = fabsf(bf16_to_f32(hb)) * s.pmax[jj];
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int row = threadIdx.x;
+      const int b = rt * 32 + row;
+      float bound = 0.f;
+      for (int jj = 0; jj < 64; ++jj) bound += hacc[0][row][jj];
+      uint16_t *hr = s.hx + ((size_t)r * a.Wp + b) * DW_HX;
+      if (b < keep) {
+        const bool wide = bound > DW_WIDE;
+        const uint16_t ru = f32_to_bf16_up(wide ? mnext : mnext + bound * 1.0001f + 1e-6f);
+        s.bref[(size_t)r * a.Wp + b] = bf16_to_f32(ru);
+        s.bs[(size_t)r * a.Wp + b] = sc[b];
+        hr[64] = (uint16_t)(ru ^ 0x8000u);  // -ref
+        hr[65] = 0x3F80u;                   // 1.0
+        bnd[b] = wide ? 1.f : 0.f;
+      } else {
+        hr[64] = 0;
+        hr[65] = 0;
+      }
+      for (int e = 66; e < DW_HX; ++e) hr[e] = 0;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < a.NG) {
+    int w = 0;
+    for (int b = threadIdx.x * 32; b < (threadIdx.x + 1) * 32; ++b)
+      if (b < keep && bnd[b] != 0.f) w = 1;
+    s.wide[r * a.NG + threadIdx.x] = w;
+  }
+  if (threadIdx.x == 0) s.nb[r] = keep;
+}
+
+__global__ __launch_bounds__(DW_NT) void k_dw_init(DwState s, DwDev a) {
+  __shared__ float hacc[2][32][65];
+  __shared__ float bnd[64];
+  __shared__ int tok[1];
+  __shared__ double sc[1];
+  const int r = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const int t0 = a.root_tok[r];
+    tok[0] = (t0 >= 0 && t0 < a.V) ? t0 : 0;  // out-of-range root tokens are a precondition violation
+    sc[0] = 0.0;
+  }
+  __syncthreads();
+  dw_branch_state(s, a, r, 1, 1, tok, sc, hacc, bnd);
+}
+
+// ---------------------------------------------------------------- per-round selection
+__global__ __launch_bounds__(DW_NT) void k_dw_select(DwState s, DwDev a, int d) {
+  __shared__ float hb[64][65];
+  __shared__ double lse_b[64], s_b[64];
+  __shared__ double cs[DW_CH];
+  __shared__ int cpk[DW_CH];
+  __shared__ uint16_t cidx[DW_CH];
+  __shared__ int ktok[64];
+  __shared__ double ks[64];
+  __shared__ float hacc[2][32][65];
+  __shared__ float bnd[64];
+  const int r = blockIdx.x;
+  const int nbp = s.nb[r];
+  const size_t rowl = (size_t)r * a.L + (d - 1);
+  // 1. LSE of every branch from the chunk partials; old branch state into LDS
+  if (threadIdx.x < nbp) {
+    const int b = threadIdx.x;
+    const size_t o = ((size_t)r * a.Wp + b) * DW_NC;
+    float M = -kInf;
+    for (int c = 0; c < DW_NC; ++c) M = fmaxf(M, s.part_m[o + c]);
+    double S = 0.0;
+    for (int c = 0; c < DW_NC; ++c) {
+      const float mc = s.part_m[o + c];
+      if (mc != -kInf) S += s.part_s[o + c] * exp((double)mc - (double)M);
+    }
+    lse_b[b] = (double)s.bref[(size_t)r * a.Wp + b] + (double)M + log(S);
+    s_b[b] = s.bs[(size_t)r * a.Wp + b];
+  }
+  for (int idx = threadIdx.x; idx < nbp * 64; idx += DW_NT) {
+    const int b = idx >> 6, jj = idx & 63;
+    hb[b][jj] = bf16_to_f32(s.hx[((size_t)r * a.Wp + b) * DW_HX + jj]);
+  }
+  __syncthreads();
+  // 2. score every child (b, k): z = base(c) + h_b . P[:, c]
+  const int nc = nbp * a.K;
+  for (int t = threadIdx.x; t < nc; t += DW_NT) {
+    const int b = t / a.K, k = t - b * a.K;
+    const int cid = a.ids[rowl * a.K + k];
+    const uint16_t *pr = s.PT + (size_t)cid * 64;
+    float corr = 0.f;
+#pragma unroll 8
+    for (int slot = 0; slot < 64; ++slot) {
+      const int half = slot >> 5, kb = (slot >> 3) & 3, e = slot & 7;
+      corr += hb[b][16 * kb + 8 * half + e] * bf16_to_f32(pr[slot]);
+    }
+    const float z = a.zk[rowl * a.K + k] + corr;
+    double sc = (s_b[b] + ((double)z - lse_b[b])) + (double)a.beta;
+    cs[t] = fmin(sc, s_b[b]);
+    cpk[t] = (b << 16) | k;
+  }
+  const int npw = next_pow2(nc > 1 ? nc : 1);
+  for (int i = threadIdx.x; i < npw; i += DW_NT) cidx[i] = (uint16_t)i;
+  __syncthreads();
+  // 3. order children by (s desc, parent position asc, rank asc)
+  for (int kk = 2; kk <= npw; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < npw; i += DW_NT) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const int x = cidx[i], y = cidx[ixj];
+          bool x_first;
+          if (x >= nc) x_first = false;
+          else if (y >= nc) x_first = true;
+          else x_first = (cs[x] != cs[y]) ? (cs[x] > cs[y]) : (cpk[x] < cpk[y]);
+          const bool up = (i & kk) == 0;
+          if (up ? !x_first : x_first) {
+            cidx[i] = (uint16_t)y;
+            cidx[ixj] = (uint16_t)x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // 4. S_d = the first W children
+  const int keep = nc < a.W ? nc : a.W;
+  for (int i = threadIdx.x; i < keep; i += DW_NT) {
+    const int x = cidx[i];
+    const size_t o = rowl * a.W + i;
+    const int k = cpk[x] & 0xFFFF;
+    const int tk = a.ids[rowl * a.K + k];
+    s.sup_s[o] = cs[x];
+    s.sup_pk[o] = cpk[x];
+    s.sup_tok[o] = tk;
+    ktok[i] = tk;
+    ks[i] = cs[x];
+  }
+  if (threadIdx.x == 0) s.sup_n[rowl] = keep;
+  __syncthreads();
+  // 5. state of the new branches for the next depth
+  if (d < a.L) dw_branch_state(s, a, r, d + 1, keep, ktok, ks, hacc, bnd);
+}
+
+// ---------------------------------------------------------------- deferred Top-B + outputs
+__global__ __launch_bounds__(DW_NT) void k_dw_final(DwState s, DwDev a, TreeOut out) {
+  __shared__ double fs[DW_SUP];
+  __shared__ int fdp[DW_SUP];  // depth << 16 | pos
+  __shared__ uint16_t fidx[DW_SUP];
+  __shared__ int off[DTREE_MAX_L + 2], cnt[DTREE_MAX_L + 2];
+  __shared__ int opar[DTREE_MAX_CAP + 1], otok[DTREE_MAX_CAP + 1], odep[DTREE_MAX_CAP + 1];
+  __shared__ float osc[DTREE_MAX_CAP + 1];
+  const int r = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int o = 0;
+    for (int d = 1; d <= a.L; ++d) {
+      off[d] = o;
+      o += s.sup_n[(size_t)r * a.L + d - 1];
+    }
+    off[a.L + 1] = o;
+  }
+  __syncthreads();
+  const int n = off[a.L + 1];
+  for (int d = 1; d <= a.L; ++d) {
+    const int nd = off[d + 1] - off[d];
+    for (int p = threadIdx.x; p < nd; p += DW_NT) {
+      fs[off[d] + p] = s.sup_s[((size_t)r * a.L + d - 1) * a.W + p];
+      fdp[off[d] + p] = (d << 16) | p;
+    }
+  }
+  const int npw = next_pow2(n > 1 ? n : 1);
+  for (int i = threadIdx.x; i < npw; i += DW_NT) fidx[i] = (uint16_t)i;
+  if (threadIdx.x <= a.L + 1) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  for (int kk = 2; kk <= npw; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < npw; i += DW_NT) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const int x = fidx[i], y = fidx[ixj];
+          bool x_first;
+          if (x >= n) x_first = false;
+          else if (y >= n) x_first = true;
+          else x_first = (fs[x] != fs[y]) ? (fs[x] > fs[y]) : (fdp[x] < fdp[y]);
+          const bool up = (i & kk) == 0;
+          if (up ? !x_first : x_first) {
+            fidx[i] = (uint16_t)y;
+            fidx[ixj] = (uint16_t)x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int keep = n < a.B ? n : a.B;
+  for (int i = threadIdx.x; i < keep; i += DW_NT) atomicAdd(&cnt[fdp[fidx[i]] >> 16], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int o = 1;
+    for (int d = 1; d <= a.L; ++d) {
+      const int c = cnt[d];
+      cnt[d] = o;  // reuse as canonical offset of depth d
+      o += c;
+    }
+    opar[0] = -1;
+    otok[0] = -1;
+    odep[0] = 0;
+    osc[0] = 0.f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < keep; i += DW_NT) {
+    const int x = fidx[i];
+    const int d = fdp[x] >> 16, p = fdp[x] & 0xFFFF;
+    const size_t o = ((size_t)r * a.L + d - 1) * a.W + p;
+    const int idx = cnt[d] + p;
+    const int ppos = s.sup_pk[o] >> 16;
+    opar[idx] = (d == 1) ? 0 : cnt[d - 1] + ppos;
+    otok[idx] = s.sup_tok[o];
+    odep[idx] = d;
+    osc[idx] = (float)fs[x];
+  }
+  __syncthreads();
+  write_tree(r, keep, opar, otok, odep, osc, out);
+}
+
+// ---------------------------------------------------------------- host side
+struct DwLayout {
+  size_t PT, pmax, hx, bref, bs, nb, wide, part_s, part_m, sup_s, sup_pk, sup_tok, sup_n, total;
+};
+
+static DwLayout dw_layout(int R, int L, int V, int W) {
+  const int Wp = (W + 31) / 32 * 32, NG = Wp / 32;
+  DwLayout l;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  l.PT = take((size_t)V * 64 * 2);
+  l.pmax = take(64 * sizeof(float));
+  l.hx = take((size_t)R * Wp * DW_HX * 2);
+  l.bref = take((size_t)R * Wp * sizeof(float));
+  l.bs = take((size_t)R * Wp * sizeof(double));
+  l.nb = take((size_t)R * sizeof(int));
+  l.wide = take((size_t)R * NG * sizeof(int));
+  l.part_s = take((size_t)R * Wp * DW_NC * sizeof(double));
+  l.part_m = take((size_t)R * Wp * DW_NC * sizeof(float));
+  l.sup_s = take((size_t)R * L * W * sizeof(double));
+  l.sup_pk = take((size_t)R * L * W * sizeof(int));
+  l.sup_tok = take((size_t)R * L * W * sizeof(int));
+  l.sup_n = take((size_t)R * L * sizeof(int));
+  l.total = o;
+  return l;
+}
+
+size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank) {
+  (void)K;
+  (void)B;
+  (void)rank;
+  return dw_layout(R, L, V, W).total;
+}
+
+hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
+                            void *ws, hipStream_t st) {
+  const DwLayout l = dw_layout(a.R, a.L, a.V, a.W);
+  char *w = static_cast<char *>(ws);
+  DwState s;
+  s.PT = reinterpret_cast<uint16_t *>(w + l.PT);
+  s.pmax = reinterpret_cast<float *>(w + l.pmax);
+  s.hx = reinterpret_cast<uint16_t *>(w + l.hx);
+  s.bref = reinterpret_cast<float *>(w + l.bref);
+  s.bs = reinterpret_cast<double *>(w + l.bs);
+  s.nb = reinterpret_cast<int *>(w + l.nb);
+  s.wide = reinterpret_cast<int *>(w + l.wide);
+  s.part_s = reinterpret_cast<double *>(w + l.part_s);
+  s.part_m = reinterpret_cast<float *>(w + l.part_m);
+  s.sup_s = reinterpret_cast<double *>(w + l.sup_s);
+  s.sup_pk = reinterpret_cast<int *>(w + l.sup_pk);
+  s.sup_tok = reinterpret_cast<int *>(w + l.sup_tok);
+  s.sup_n = reinterpret_cast<int *>(w + l.sup_n);
+  DwDev dv;
+  dv.zk = zk;
+  dv.ids = ids;
+  dv.E = a.E;
+  dv.U = a.U;
+  dv.root_tok = a.root_tok;
+  dv.R = a.R;
+  dv.L = a.L;
+  dv.V = a.V;
+  dv.K = a.K;
+  dv.W = a.W;
+  dv.Wp = (a.W + 31) / 32 * 32;
+  dv.NG = dv.Wp / 32;
+  dv.B = a.B;
+  dv.dm = a.dm;
+  dv.beta = a.beta;
+
+  hipLaunchKernelGGL(k_dw_transpose_p, dim3((a.V + 63) / 64), dim3(DW_NT), 0, st, a.P, a.V, s.PT);
+  hipLaunchKernelGGL(k_dw_pmax, dim3(64), dim3(DW_NT), 0, st, a.P, a.V, s.pmax);
+  hipLaunchKernelGGL(k_dw_init, dim3(a.R), dim3(DW_NT), 0, st, s, dv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nct = a.R * dv.NG;
+  const int TG = (nct + 3) / 4;
+  const dim3 gcorr((unsigned)(8 * TG * (DW_NC / 8)));
+  for (int d = 1; d <= a.L; ++d) {
+    if (a.dtype == DTREE_BF16)
+      hipLaunchKernelGGL(k_dw_corr<uint16_t>, gcorr, dim3(DW_NT), 0, st, s, static_cast<const uint16_t *>(a.base),
+                         d, a.L, a.V, a.R, dv.NG);
+    else
+      hipLaunchKernelGGL(k_dw_corr<float>, gcorr, dim3(DW_NT), 0, st, s, static_cast<const float *>(a.base), d, a.L,
+                         a.V, a.R, dv.NG);
+    hipLaunchKernelGGL(k_dw_select, dim3(a.R), dim3(DW_NT), 0, st, s, dv, d);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_dw_final, dim3(a.R), dim3(DW_NT), 0, st, s, dv, out);
+  return hipGetLastError();
 }
 
 }  // namespace dt

@@ -50,7 +50,8 @@ struct DepthwiseArgs {
   const int32_t *root_tok;
 };
 size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank);
-hipError_t launch_depthwise(const DepthwiseArgs &a, const TreeOut &out, void *ws, hipStream_t st);
+hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
+                            void *ws, hipStream_t st);
 
 // ---- a7: acceptance walk ------------------------------------------------------------------------
 struct AcceptArgs {

@@ -127,7 +127,8 @@ int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int 
  * children are kept, then the B best of the whole super-tree by s_beta.
  * E [V][d_model], U [L][d_model][rank], P [rank][V] are bf16 bits; root_tok [R] int32.
  * Needs beta <= 0, rank == 64, d_model % 64 == 0, K <= DTREE_MAX_K, W <= 64, W*K <= 1024,
- * B <= DTREE_MAX_CAP, out->cap == B.
+ * L*W <= 2048, B <= DTREE_MAX_CAP, out->cap == B. root_tok values must lie in [0, V) (an
+ * out-of-range value is read as token 0).
  */
 int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, const uint16_t *E,
                          const uint16_t *U, const uint16_t *P, int d_model, int rank,

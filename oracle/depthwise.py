@@ -56,7 +56,8 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 def build_depthwise(base_rows: np.ndarray, E: np.ndarray, U: np.ndarray, P: np.ndarray,
                     root_tok: int, K: int, W: int, B: int, beta: float, with_super: bool = False):
     """One round. base_rows float64 [L, V]; E float64-convertible [V, dm] (rows gathered);
-    U [L, dm, rank]; P [rank, V]. Returns the canonical Tree (and the super-tree levels)."""
+    U [L, dm, rank]; P [rank, V]. Returns the canonical Tree; with_super also returns the
+    super-tree levels and the selection gaps (per depth at the width cut, then at the B cut)."""
     L, V = base_rows.shape
     if beta > 0:
         raise ValueError("Lemma 1 needs beta <= 0")
@@ -64,6 +65,7 @@ def build_depthwise(base_rows: np.ndarray, E: np.ndarray, U: np.ndarray, P: np.n
         raise ValueError("bad sizes")
     P64 = np.asarray(P, dtype=np.float64)
     levels = []
+    gaps = []   # per depth: score of the W-th kept child minus the first dropped one
     # S_{d-1} as parallel lists; depth 0 is the root alone
     prev_tok = [int(root_tok)]
     prev_s = [0.0]
@@ -83,11 +85,16 @@ def build_depthwise(base_rows: np.ndarray, E: np.ndarray, U: np.ndarray, P: np.n
                 children.append((-s, b, k, int(c), s))
         children.sort()
         kept = children[:W]
+        gaps.append(kept[-1][4] - children[W][4] if len(children) > W else np.inf)
         levels.append([dict(s=s, ppos=b, rank=k, token=c) for (_, b, k, c, s) in kept])
         prev_tok = [c for (_, _, _, c, _) in kept]
         prev_s = [s for (_, _, _, _, s) in kept]
     tree = deferred_topb(levels, B)
-    return (tree, levels) if with_super else tree
+    if with_super:
+        flat = sorted(-nd["s"] for lev in levels for nd in lev)
+        gaps.append(flat[B] - flat[B - 1] if len(flat) > B else np.inf)
+        return tree, levels, gaps
+    return tree
 
 
 def deferred_topb(levels, B: int) -> Tree:

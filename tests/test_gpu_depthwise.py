@@ -1,0 +1,94 @@
+"""GPU parity: DARTree depth-wise super-tree + deferred Top-B (a3 + a4 + a6) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import draft_tree_construction_amd as dt
+import synth
+from oracle import depthwise, marginal, rowsweep
+from parity_util import TOL, assert_tree_equal, dev_bf16, dev_f32, tree_to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def head_to_device(E, U, P, root):
+    return dev_bf16(E), dev_bf16(U), dev_bf16(P), torch.from_numpy(root.astype(np.int32)).cuda()
+
+
+def check(base_host, dtype, E, U, P, root, K, W, B, beta, rounds=None):
+    """Run all rounds on the GPU; compare the given rounds with the oracle. A round whose
+    oracle selection gap (width cut of any depth, or the B cut) is <= 1e-5 is checked for
+    validity and shared-prefix scores only. Returns (exact rounds, compared rounds)."""
+    R = base_host.shape[0]
+    bd = dev_bf16(base_host) if dtype == "bf16" else dev_f32(base_host)
+    Ed, Ud, Pd, rd = head_to_device(E, U, P, root)
+    tr = dt.build_tree_depthwise(bd, Ed, Ud, Pd, rd, K, W, B, beta)
+    h = tree_to_host(tr)
+    E64, U64, P64 = (synth.f32_from_bf16(x).astype(np.float64) for x in (E, U, P))
+    rounds = range(R) if rounds is None else rounds
+    exact = 0
+    for r in rounds:
+        z = rowsweep.as_f64(base_host[r], dtype)
+        ref, _, gaps = depthwise.build_depthwise(z, E64, U64, P64, int(root[r]), K, W, B, beta, with_super=True)
+        exact += assert_tree_equal(h, r, ref, B, near_tie=min(gaps) <= TOL)
+    return exact, len(list(rounds))
+
+
+@pytest.mark.parametrize("R,L,V,dm,K,W,B,beta,seed", [
+    (4, 6, 600, 64, 8, 32, 40, -0.5, 1),
+    (3, 16, 2000, 128, 8, 32, 128, -0.5, 2),
+    (3, 5, 1001, 64, 4, 16, 30, -0.2, 3),     # odd V: ragged 32-token block
+    (2, 4, 500, 64, 16, 64, 100, 0.0, 4),     # two 32-branch tiles per round
+    (3, 7, 300, 64, 5, 1, 7, -0.1, 5),        # width 1: one corrected chain
+])
+def test_depthwise_small(R, L, V, dm, K, W, B, beta, seed):
+    base = synth.ddtree_logits(seed=seed, R=R, L=L, V=V)
+    E, U, P, root = synth.correction_head(seed=100 + seed, R=R, L=L, V=V, d_model=dm, rank=64)
+    exact, n = check(base, "bf16", E, U, P, root, K, W, B, beta)
+    assert exact >= n - 1
+
+
+def test_depthwise_float32_base():
+    R, L, V, dm = 3, 5, 700, 64
+    rng = np.random.default_rng(8)
+    base = (2.0 * rng.standard_normal((R, L, V))).astype(np.float32)
+    E, U, P, root = synth.correction_head(seed=9, R=R, L=L, V=V, d_model=dm, rank=64)
+    exact, n = check(base, "f32", E, U, P, root, 8, 16, 40, -0.3)
+    assert exact >= n - 1
+
+
+def test_depthwise_loose_bound_uses_running_max():
+    """A head large enough that the max-logit bound exceeds 10 nats switches tiles to the
+    running-max path; results must still match."""
+    R, L, V, dm = 2, 4, 800, 64
+    base = synth.ddtree_logits(seed=6, R=R, L=L, V=V)
+    E, U, P, root = synth.correction_head(seed=7, R=R, L=L, V=V, d_model=dm, rank=64)
+    U = synth.bf16_from_f32(synth.f32_from_bf16(U) * np.float32(40.0))
+    P = synth.bf16_from_f32(synth.f32_from_bf16(P) * np.float32(40.0))
+    exact, n = check(base, "bf16", E, U, P, root, 8, 32, 60, -0.5)
+    assert exact >= n - 1
+
+
+def test_depthwise_zero_correction_is_marginal_tree():
+    """U = 0 makes every branch's correction vanish; with W >= B and K >= B the depth-wise
+    tree is the marginal Top-B tree (fp32 logits: no exact ties)."""
+    R, L, V, B = 3, 6, 500, 32
+    rng = np.random.default_rng(10)
+    base = (2.0 * rng.standard_normal((R, L, V))).astype(np.float32)
+    E, U, P, root = synth.correction_head(seed=11, R=R, L=L, V=V, d_model=64, rank=64)
+    U[:] = 0
+    Ed, Ud, Pd, rd = head_to_device(E, U, P, root)
+    tr = dt.build_tree_depthwise(dev_f32(base), Ed, Ud, Pd, rd, B, B, B, -0.25)
+    h = tree_to_host(tr)
+    for r in range(R):
+        ref = marginal.build_marginal(rowsweep.as_f64(base[r], "f32"), B, B, -0.25)
+        assert_tree_equal(h, r, ref, B)
+
+
+def test_depthwise_full_dartree_config_sampled():
+    """DARTree config at full size: R=64, L=16, V=151936, E 151936x1024, U 16x1024x64,
+    P 64x151936, W=32, K=8, B=128, beta=-0.5; three rounds checked against the oracle."""
+    base = synth.ddtree_logits(seed=2)
+    E, U, P, root = synth.correction_head(seed=3)
+    exact, n = check(base, "bf16", E, U, P, root, 8, 32, 128, -0.5, rounds=(0, 31, 63))
+    assert exact >= n - 1

@@ -106,8 +106,9 @@ def test_super_tree_invariants_workload_shape_small():
     base = rowsweep.as_f64(base_b, "bf16")
     E64, U64, P64 = (synth.f32_from_bf16(a).astype(np.float64) for a in (E, U, P))
     for r in range(R):
-        t, levels = depthwise.build_depthwise(base[r], E64, U64, P64, int(root[r]), K=8, W=32, B=40,
-                                              beta=-0.5, with_super=True)
+        t, levels, gaps = depthwise.build_depthwise(base[r], E64, U64, P64, int(root[r]), K=8, W=32, B=40,
+                                                    beta=-0.5, with_super=True)
+        assert len(gaps) == L + 1 and all(g >= 0 for g in gaps)
         treeout.check_invariants(t, 40, L)
         assert len(levels[0]) == 8 and all(len(lv) <= 32 for lv in levels)
         for d in range(1, len(levels)):
