@@ -99,6 +99,40 @@ DT_INLINE double wave_sum(double v) {
   return v;
 }
 
+// ---- wave-level (64-lane) sorting of 64-bit keys held one per lane, descending
+DT_INLINE uint64_t wave_sort64_desc_u64(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = __shfl_xor(v, j, 64);
+      const bool desc_blk = (lane & k) == 0;
+      const bool lower = (lane & j) == 0;
+      const uint64_t hi = v > o ? v : o, lo = v > o ? o : v;
+      v = (lower == desc_blk) ? hi : lo;
+    }
+  }
+  return v;
+}
+// Top 64 (sorted descending across lanes) of two descending 64-key lists.
+DT_INLINE uint64_t wave_merge_top64_u64(uint64_t a, uint64_t b) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t rb = __shfl(b, 63 - lane, 64);
+  uint64_t v = a > rb ? a : rb;  // bitonic; holds the 64 largest
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1) {
+    const uint64_t o = __shfl_xor(v, j, 64);
+    const bool lower = (lane & j) == 0;
+    v = lower ? (v > o ? v : o) : (v > o ? o : v);
+  }
+  return v;
+}
+// Lane prefix count of set bits below this lane in a 64-bit wave mask.
+DT_INLINE int lane_prefix(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // Prefix-score record used by the tree builders. Order within one depth:
 // (s desc, Z desc, ppos asc, rank asc); across depths a tie in s goes to the smaller depth.
 struct Pref {

@@ -79,7 +79,14 @@ struct DwDev {
 };
 
 // ---------------------------------------------------------------- prep: P^T and column maxima
-__global__ __launch_bounds__(DW_NT) void k_dw_transpose_p(const uint16_t *__restrict__ P, int V, uint16_t *PT) {
+__global__ void k_dw_zero_f32(float *p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0.f;
+}
+
+// PT tile of 64 tokens; also max_v |P[k][v]| per k folded in with an integer atomic max
+// (non-negative floats order like their bit patterns).
+__global__ __launch_bounds__(DW_NT) void k_dw_transpose_p(const uint16_t *__restrict__ P, int V, uint16_t *PT,
+                                                          float *pmax) {
   __shared__ uint16_t tile[64][66];
   const int v0 = blockIdx.x * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += DW_NT) {
@@ -93,20 +100,11 @@ __global__ __launch_bounds__(DW_NT) void k_dw_transpose_p(const uint16_t *__rest
     const int k = 16 * kb + 8 * half + e;
     if (v0 + vv < V) PT[(size_t)(v0 + vv) * 64 + slot] = tile[k][vv];
   }
-}
-
-__global__ __launch_bounds__(DW_NT) void k_dw_pmax(const uint16_t *__restrict__ P, int V, float *pmax) {
-  __shared__ float red[DW_NT / 64];
-  const int j = blockIdx.x;
-  float m = 0.f;
-  for (int v = threadIdx.x; v < V; v += DW_NT) m = fmaxf(m, fabsf(bf16_to_f32(P[(size_t)j * V + v])));
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = red[0];
-    for (int i = 1; i < DW_NT / 64; ++i) r = fmaxf(r, red[i]);
-    pmax[j] = r;
+  if (threadIdx.x < 64) {
+    const int k = threadIdx.x;
+    float m = 0.f;
+    for (int vv = 0; vv < 64; ++vv) m = fmaxf(m, fabsf(bf16_to_f32(tile[k][vv])));
+    atomicMax(reinterpret_cast<unsigned int *>(pmax) + k, __float_as_uint(m));
   }
 }
 
@@ -549,8 +547,8 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   dv.dm = a.dm;
   dv.beta = a.beta;
 
-  hipLaunchKernelGGL(k_dw_transpose_p, dim3((a.V + 63) / 64), dim3(DW_NT), 0, st, a.P, a.V, s.PT);
-  hipLaunchKernelGGL(k_dw_pmax, dim3(64), dim3(DW_NT), 0, st, a.P, a.V, s.pmax);
+  hipLaunchKernelGGL(k_dw_zero_f32, dim3(1), dim3(64), 0, st, s.pmax, 64);
+  hipLaunchKernelGGL(k_dw_transpose_p, dim3((a.V + 63) / 64), dim3(DW_NT), 0, st, a.P, a.V, s.PT, s.pmax);
   hipLaunchKernelGGL(k_dw_init, dim3(a.R), dim3(DW_NT), 0, st, s, dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
