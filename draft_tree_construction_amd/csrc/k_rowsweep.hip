@@ -9,14 +9,16 @@
 // registers); each thread keeps an online (max, sum-exp) pair -- exp2 of one FMA per
 // element, fp32 terms, float64 accumulation -- and records each chunk's maximum in LDS
 // (as bf16 rounded up, which can only over-select). One or two chunks before the end
-// (checkpoint c*), each wave sorts its 64 running lane maxima in registers and takes the
-// ceil(K/4)-th; the smallest over the four waves has at least K distinct elements at or
+// (checkpoint c*), each wave finds the ceil(K/4)-th largest of its 64 running lane
+// maxima with ballots; the smallest over the four waves has at least K distinct elements at or
 // above it, so it bounds the K-th value from below. Only lane-chunks whose maximum
-// reaches the bound can hold top-K elements (about K of them): they are listed in LDS and
-// thread i issues the loads of the i-th 64-byte span right away, consuming it after the
-// last chunks are streamed, so the re-read is one round hidden behind the stream. Elements >= bound are keyed (value desc, id asc) into LDS,
-// each wave takes the top 64 of its share with register bitonic sorts and merges, and
-// one wave merges the four lists. Pathological rows whose candidates overflow the
+// reaches the bound can hold top-K elements (about K of them): each wave lists its own in
+// LDS and its lane j issues the loads of the j-th 64-byte span right away, consuming them
+// after the last chunks are streamed, so the re-read is one round hidden behind the stream.
+// Elements >= bound are keyed (value desc, id asc) into LDS, their slots reserved once
+// per wave; with at most one candidate per thread each thread's rank is the number of
+// keys above its own, else each wave takes the top 64 of a quarter with register
+// bitonic sorts and one wave merges the four lists. Pathological rows whose candidates overflow the
 // buffer are re-streamed with the threshold raised to the K-th key of the full buffer
 // until a pass fits. Rows too short to fill the GPU are split over several workgroups
 // whose partial (max, sum, top-K) are merged by a second kernel.
@@ -30,29 +32,17 @@ constexpr int RS_NW = RS_NT / 64;
 constexpr int RS_U = 4;        // 16-byte vectors per thread per chunk
 constexpr int RS_BUF = 2048;   // LDS candidate keys
 constexpr int RS_NG = 32;      // recorded chunk(-group) maxima per thread
-constexpr int RS_LIST = 512;   // listed re-read spans
+constexpr int RS_WL = 128;     // listed re-read spans per wave
+constexpr int RS_WBUF = RS_BUF / RS_NW;  // candidate keys per wave region
+constexpr int RS_D = 2;        // chunks in flight per wave ahead of the one being consumed
 
 struct RowPart {
   uint64_t *keys;  // [rows*S][K]
-  float *m;        // [rows*S]
-  double *s;       // [rows*S]
+  float *m;        // [rows*S] largest x log2e (fp32) of the split
+  double *s;       // [rows*S] sum of exp2(x log2e - m) over the split
 };
-
-// Descending bitonic sort of one float per lane across the 64 lanes of a wave.
-DT_INLINE float wave_sort_desc(float v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float o = __shfl_xor(v, j, 64);
-      const bool desc_blk = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      v = (lower == desc_blk) ? fmaxf(v, o) : fminf(v, o);
-    }
-  }
-  return v;
-}
+constexpr double kLn2d = 0.6931471805599453;
+constexpr double kLog2ed = 1.4426950408889634;
 
 // Top 64 keys (sorted descending across the lanes) of keys[0..n).
 DT_INLINE uint64_t wave_top64(const uint64_t *keys, int n) {
@@ -64,6 +54,44 @@ DT_INLINE uint64_t wave_top64(const uint64_t *keys, int n) {
     top = (g == 0) ? srt : wave_merge_top64_u64(top, srt);
   }
   return top;
+}
+
+// Exclusive prefix over the wave's lanes of cnt (0 <= cnt < 64) and the wave total, from
+// six ballots and lane counts (no LDS traffic).
+DT_INLINE int wave_prefix(int cnt, int &total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint64_t bal = __ballot((cnt >> b) & 1);
+    pre += lane_prefix(bal) << b;
+    tot += __popcll(bal) << b;
+  }
+  total = tot;
+  return pre;
+}
+// Slots for cnt items per lane from an LDS counter with one atomic per wave: returns this
+// lane's first slot (the lanes' items are consecutive, in lane order). Wave-uniform call.
+DT_INLINE int wave_reserve(int *ctr, int cnt) {
+  int total;
+  const int pre = wave_prefix(cnt, total);
+  int base = 0;
+  if (total > 0) {
+    if ((threadIdx.x & 63) == 0) base = atomicAdd(ctr, total);
+    base = __builtin_amdgcn_readlane(base, 0);
+  }
+  return base + pre;
+}
+// The kw-th largest value (1 <= kw <= 64) among the wave's lanes, found bit by bit on the
+// order-preserving code with ballots (exact; no LDS traffic).
+DT_INLINE float wave_kth_largest(float v, int kw) {
+  const uint32_t key = ord_f32(v);
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    if (__popcll(__ballot(key >= c)) >= kw) t = c;
+  }
+  return unord_f32(t);
 }
 
 // bf16 rounded toward +inf (as an ordered 16-bit code) and back; -inf stays -inf.
@@ -79,71 +107,89 @@ template <typename T>
 __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ logits, int V, int K, int S,
                                                        int seg, RowPart part, RowOut out) {
   constexpr int EPV = Vec<T>::N;
-  constexpr int E = EPV * RS_U;     // elements per thread per chunk
-  constexpr int CH = RS_NT * E;     // elements per chunk
-  __shared__ uint64_t buf[RS_BUF];
+  constexpr int E = RS_U * EPV;           // elements per thread per chunk
+  constexpr int CH = RS_NT * E;           // elements per chunk
+  __shared__ uint64_t buf[RS_BUF];        // candidate keys: one region of RS_WBUF per wave
   __shared__ uint16_t s_gm[RS_NG][RS_NT];
-  __shared__ float s_wb[RS_NW];
-  __shared__ int s_cnt, s_nq;
-  __shared__ int s_list[RS_LIST];
-  __shared__ float s_wm[RS_NW];
+  __shared__ int s_list[RS_NW][RS_WL];
+  __shared__ uint64_t s_top[64];
+  __shared__ float s_wb[2][RS_NW], s_wm[RS_NW];
   __shared__ double s_ws[RS_NW];
+  __shared__ int s_rn[RS_NW];
+  __shared__ int s_cnt;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = blockIdx.x / S;
   const int sp = blockIdx.x - row * S;
   const int v0 = sp * seg;
   const int v1 = min(V, v0 + seg);
+  const int len = max(0, v1 - v0);
   const T *p = logits + (size_t)row * (size_t)V;
-  const bool aligned = ((reinterpret_cast<uintptr_t>(p + v0) & 15) == 0);
-  const int nchunks = (v1 - v0 + CH - 1) / CH;
-  const int nfull = aligned ? (v1 - v0) / CH : 0;     // chunks needing no bounds checks
-  // checkpoint: two chunks before the end (one for short rows); recorded maxima cover [0, c*)
-  const int cstar = nchunks >= 8 ? nchunks - 2 : (nchunks >= 2 ? nchunks - 1 : nchunks);
-  const int cpg = (cstar + RS_NG - 1) / RS_NG;       // chunks per recorded group
-  const int ngroups = cpg > 0 ? (cstar + cpg - 1) / cpg : 0;
+  // vector path: 16-byte aligned segment of whole vectors
+  const bool fast = ((reinterpret_cast<uintptr_t>(p + v0) & 15) == 0) && (len % EPV == 0) && len >= EPV;
+  const int nchunks = (len + CH - 1) / CH;
+  const int nfull = len / CH;  // chunks entirely inside the segment
+  const int nround = (nchunks + RS_D - 1) / RS_D * RS_D;  // whole ring turns (tail chunks masked)
+  const int cpg = (nround + RS_NG - 1) / RS_NG;           // chunks per recorded group
+  const int ngroups = cpg > 0 ? (nround + cpg - 1) / cpg : 0;
 
-  if (tid == 0) s_cnt = 0;
+  float m = -kInf, mh = 0.f;  // running max; mh = fp32(m log2 e) once m is finite
+  double s = 0.0;             // sum of exp2(x log2e - mh): the true sum times 2^(m log2e - mh)
+  float gm = -kInf;           // maximum of the current recorded group
+  int gi = 0, gk = 0;         // recorded group and position in it (wave-uniform)
+  float th = kInf;            // bound once known (elements >= th are candidates)
+  int wn = 0;                 // keys in this wave's region (wave-uniform)
+  uint64_t *const wbuf = buf + w * RS_WBUF;
 
-  float m = -kInf, mh = -kInf;  // running max and fp32(m * log2 e)
-  double s = 0.0;               // sum of exp2(x log2e - mh): the true sum times 2^(m log2e - mh)
-  float gm = -kInf;
-  float th = kInf;              // bound once known (elements >= th are candidates)
-
-  auto load_full = [&](int c, u32x4 *r) {
-    const T *q = p + v0 + c * CH + tid * EPV;
-#pragma unroll
-    for (int u = 0; u < RS_U; ++u) r[u] = *reinterpret_cast<const u32x4 *>(q + u * RS_NT * EPV);
+  // element layout: lane ln holds E consecutive elements of each chunk (one 64-byte span)
+  auto elem0 = [&](int c, int u, int ln) { return v0 + c * CH + ln * E + u * EPV; };
+  // buffer view of the segment (vector path): reads past its end return zero and touch no
+  // memory, so the ring and the re-reads need no address clamping
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(p + v0), (short)0, fast ? len * (int)sizeof(T) : 0, 0x00020000);
+  auto bload = [&](int c, int u, int ln) -> u32x4 {
+    return (u32x4)__builtin_amdgcn_raw_buffer_load_b128(rsrc, (c * CH + ln * E + u * EPV) * (int)sizeof(T), 0, 0);
   };
-  auto widen_full = [&](const u32x4 *r, float *x) {
+  auto gload = [&](int b, float *x) {
 #pragma unroll
-    for (int u = 0; u < RS_U; ++u) Vec<T>::widen(r[u], x + u * EPV);
+    for (int e = 0; e < EPV; ++e) x[e] = (b + e >= 0 && b + e < v1) ? load_elt(p, (size_t)(b + e)) : -kInf;
   };
-  auto load_guarded = [&](int c, float *x) {
-    const int cb = v0 + c * CH;
+  // vectors of a span (chunk c, lane ln) at or past the segment's end, or all of it when
+  // !valid, become -inf
+  auto mask_span = [&](float *x, int c, int ln, bool valid) {
 #pragma unroll
     for (int u = 0; u < RS_U; ++u) {
-      const int b = cb + (u * RS_NT + tid) * EPV;
+      const bool ok = valid && elem0(c, u, ln) < v1;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) x[u * EPV + e] = (b + e < v1) ? load_elt(p, (size_t)(b + e)) : -kInf;
+      for (int e = 0; e < EPV; ++e) x[u * EPV + e] = ok ? x[u * EPV + e] : -kInf;
     }
   };
-  // key every element >= th of a widened chunk into LDS (per lane; hits are rare)
-  auto append_all = [&](int c, const float *x) {
-    const int cb = v0 + c * CH;
+  // key the elements >= th of a span (chunk c, lane ln) into the wave's region (wave-uniform)
+  auto append_span = [&](const float *x, int c, int ln) {
+    int hits = 0;
 #pragma unroll
-    for (int u = 0; u < RS_U; ++u) {
+    for (int e = 0; e < E; ++e) hits += x[e] >= th;
+    if (__ballot(hits > 0)) {
+      int total;
+      int slot = wn + wave_prefix(hits, total);
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float xv = x[u * EPV + e];
-        if (xv >= th) {
-          const int slot = atomicAdd(&s_cnt, 1);
-          if (slot < RS_BUF) buf[slot] = make_key(xv, (uint32_t)(cb + (u * RS_NT + tid) * EPV + e));
+      for (int u = 0; u < RS_U; ++u) {
+        const int b = elem0(c, u, ln);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float xv = x[u * EPV + e];
+          if (xv >= th) {
+            if (slot < RS_WBUF) wbuf[slot] = make_key(xv, (uint32_t)(b + e));
+            ++slot;
+          }
         }
       }
+      wn += total;
     }
   };
-  auto consume = [&](int c, const float *x) {
+  // online (max, sum-exp) over this thread's span of a chunk; the running maximum of the
+  // chunk group is stored every chunk (no branch in the streaming loop)
+  auto consume = [&](const float *x) {
     float cm = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) cm = fmaxf(cm, x[e]);
@@ -154,160 +200,232 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
       m = cm;
       mh = nh;
     }
-    if (m != -kInf) {
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], kLog2e, -mh));
-        a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 1], kLog2e, -mh));
-        a2 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 2], kLog2e, -mh));
-        a3 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 3], kLog2e, -mh));
-      }
-      s += (double)((a0 + a1) + (a2 + a3));
+    for (int e = 0; e < E; e += 4) {
+      a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], kLog2e, -mh));
+      a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 1], kLog2e, -mh));
+      a2 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 2], kLog2e, -mh));
+      a3 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 3], kLog2e, -mh));
     }
-    if (c < cstar) {
-      gm = fmaxf(gm, cm);
-      if ((c + 1) % cpg == 0 || c + 1 == cstar) {
-        s_gm[c / cpg][tid] = up16(gm);
-        gm = -kInf;
-      }
-    } else if (cm >= th) {
-      append_all(c, x);
+    s += (double)((a0 + a1) + (a2 + a3));
+    gm = (gk == 0) ? cm : fmaxf(gm, cm);
+    s_gm[gi][tid] = up16(gm);
+    if (++gk == cpg) {
+      gk = 0;
+      ++gi;
     }
   };
 
-  // re-reads: the qualifying (group, lane) spans are listed in LDS at c*; thread i issues
-  // the loads of entry i right away (single-chunk groups in full chunks) and consumes them
-  // after the stream, so the whole re-read is one round hidden behind the last chunks
-  int my_entry = -1;            // list entry whose loads this thread has in flight
-  u32x4 ra[RS_U];
-  auto span_load = [&](int c, int ln, u32x4 *r) {
-    const T *q = p + v0 + c * CH + ln * EPV;
-#pragma unroll
-    for (int u = 0; u < RS_U; ++u) r[u] = *reinterpret_cast<const u32x4 *>(q + u * RS_NT * EPV);
-  };
-  auto span_append = [&](int c, int ln, const float *x) {
-    const int cb = v0 + c * CH;
-#pragma unroll
-    for (int u = 0; u < RS_U; ++u) {
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float xv = x[u * EPV + e];
-        if (xv >= th) {
-          const int slot = atomicAdd(&s_cnt, 1);
-          if (slot < RS_BUF) buf[slot] = make_key(xv, (uint32_t)(cb + (u * RS_NT + ln) * EPV + e));
-        }
-      }
-    }
-  };
-  auto span_guarded = [&](int c, int ln, float *x) {
-    const int cb = v0 + c * CH;
-#pragma unroll
-    for (int u = 0; u < RS_U; ++u) {
-      const int b = cb + (u * RS_NT + ln) * EPV;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) x[u * EPV + e] = (b + e < v1) ? load_elt(p, (size_t)(b + e)) : -kInf;
-    }
-  };
-  auto checkpoint = [&]() {
+  // ---- bound: the ceil(K/4)-th largest lane maximum of each wave, the smallest over the
+  // waves (every wave has that many distinct elements at or above it). The final one also
+  // exchanges the waves' largest scaled maxima (mh of the lanes that saw data).
+  float MH = -kInf;  // block maximum of mh (final bound only)
+  auto block_bound = [&](int slot) {
     const int kw = (K + RS_NW - 1) / RS_NW;
-    const float srt = wave_sort_desc(m);
-    const float b = (kw <= 64) ? __shfl(srt, kw - 1, 64) : -kInf;
-    if (lane == 0) s_wb[w] = b;
-    if (tid == 0) s_nq = 0;
-    __syncthreads();
-    float t = s_wb[0];
-#pragma unroll
-    for (int i = 1; i < RS_NW; ++i) t = fminf(t, s_wb[i]);
-    th = fmaxf(t, -3.402823466e38f);  // padding (-inf) never qualifies
-    for (int g = 0; g < ngroups; ++g) {
-      if (from16(s_gm[g][tid]) >= th) {
-        const int q = atomicAdd(&s_nq, 1);
-        if (q < RS_LIST) s_list[q] = (g << 8) | tid;
-      }
+    const float b = (kw <= 64) ? wave_kth_largest(m, kw) : -kInf;
+    const float wmh = slot ? wave_max(m == -kInf ? -kInf : mh) : 0.f;
+    if (lane == 0) {
+      s_wb[slot][w] = b;
+      if (slot) s_wm[w] = wmh;
     }
     __syncthreads();
-    if (cpg == 1 && tid < s_nq && tid < RS_LIST) {
-      const int g = s_list[tid] >> 8;
-      if (g < nfull) {
-        my_entry = tid;
-        span_load(g, s_list[tid] & 255, ra);
-      }
+    float t = s_wb[slot][0];
+#pragma unroll
+    for (int i = 1; i < RS_NW; ++i) t = fminf(t, s_wb[slot][i]);
+    if (slot) {
+      MH = s_wm[0];
+#pragma unroll
+      for (int i = 1; i < RS_NW; ++i) MH = fmaxf(MH, s_wm[i]);
+    }
+    return fmaxf(t, -3.402823466e38f);  // padding (-inf) never qualifies
+  };
+  // ---- per-wave list of the (group, lane) spans whose recorded maximum reaches th, over
+  // the groups of chunks [0, climit); lane j may then load its wave's j-th span at once
+  int nlist = 0;           // entries in this wave's list (wave-uniform)
+  int own_q = 0;           // list index of this lane's first qualifying group
+  uint32_t own_qual = 0;   // this lane's qualifying groups
+  int climit = 0;          // listed spans cover chunks [0, climit)
+  int my_ent = -1;         // entry whose span this lane has loaded into ra
+  u32x4 ra[RS_U] = {};
+  auto make_list = [&](int cl, bool preload) {
+    climit = cl;
+    const int ng = (cl + cpg - 1) / cpg;
+    uint32_t qual = 0;
+#pragma unroll
+    for (int g = 0; g < RS_NG; ++g) qual |= (uint32_t)((g < ng) & (from16(s_gm[g][tid]) >= th)) << g;
+    own_qual = qual;
+    own_q = wave_prefix(__builtin_popcount(qual), nlist);
+    int q = own_q;
+    while (qual) {
+      const int g = __builtin_ctz(qual);
+      qual &= qual - 1;
+      if (q < RS_WL) s_list[w][q] = (g << 8) | tid;
+      ++q;
+    }
+    // the wave reads back its own entries: LDS operations of one wave complete in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (preload && lane < nlist) {
+      my_ent = s_list[w][lane];
+      const int c = my_ent >> 8, ln = my_ent & 255;
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) ra[u] = bload(c, u, ln);
     }
   };
 
-  if (nfull > 0) {
-    u32x4 raw[RS_U], nxt[RS_U];
-    load_full(0, raw);
-    for (int c = 0; c < nfull - 1; ++c) {
-      load_full(c + 1, nxt);
-      if (c == cstar) checkpoint();
-      float x[E];
-      widen_full(raw, x);
-      consume(c, x);
+  // cA: chunks before it are re-read from memory, chunks from it on stay in registers
+  const int cA = fast ? nround - RS_D : nround;
+  u32x4 R[RS_D][RS_U];
+  if (fast) {
+    // ring of RS_D chunks in flight per wave; a chunk's slots are refilled (chunk c + RS_D)
+    // as soon as it is widened. One ring turn before the end a first bound lists the spans
+    // that may hold candidates and their loads are issued; the last turn keeps its raw
+    // chunks in the ring, so no memory round trip is left after the stream.
 #pragma unroll
-      for (int u = 0; u < RS_U; ++u) raw[u] = nxt[u];
-    }
-    const int c = nfull - 1;
-    if (c == cstar) checkpoint();
-    float x[E];
-    widen_full(raw, x);
-    consume(c, x);
-  }
-  for (int c = nfull; c < nchunks; ++c) {
-    if (c == cstar) checkpoint();
-    float x[E];
-    load_guarded(c, x);
-    consume(c, x);
-  }
-  if (cstar == nchunks) checkpoint();
-  // the in-flight re-reads, then every list entry not covered by one (multi-chunk groups,
-  // guarded chunks, entries beyond the threads), and on list overflow every group again
-  if (my_entry >= 0) {
-    float x[E];
-    widen_full(ra, x);
-    span_append(s_list[my_entry] >> 8, s_list[my_entry] & 255, x);
-  }
-  {
-    const int nq = s_nq;
-    const int nl = nq < RS_LIST ? nq : RS_LIST;
-    for (int i = tid; i < nl; i += RS_NT) {
-      const int g = s_list[i] >> 8, ln = s_list[i] & 255;
-      if (i == my_entry) continue;
-      const int ce = min(cstar, (g + 1) * cpg);
-      for (int c = g * cpg; c < ce; ++c) {
+    for (int j = 0; j < RS_D; ++j)
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) R[j][u] = bload(j, u, tid);
+    for (int c = 0; c < cA; c += RS_D) {
+#pragma unroll
+      for (int j = 0; j < RS_D; ++j) {
         float x[E];
-        if (c < nfull) {
-          u32x4 r[RS_U];
-          span_load(c, ln, r);
-          widen_full(r, x);
-        } else {
-          span_guarded(c, ln, x);
+#pragma unroll
+        for (int u = 0; u < RS_U; ++u) {
+          Vec<T>::widen(R[j][u], x + u * EPV);
+          R[j][u] = bload(c + j + RS_D, u, tid);
         }
-        span_append(c, ln, x);
+        if (c + j >= nfull) mask_span(x, c + j, tid, true);
+        consume(x);
       }
     }
-    if (nq > RS_LIST) {  // the list overflowed: this thread re-reads its own qualifying groups
-      for (int g = 0; g < ngroups; ++g) {
-        if (!(from16(s_gm[g][tid]) >= th)) continue;
-        bool listed = false;
-        for (int i = 0; i < RS_LIST && !listed; ++i) listed = s_list[i] == ((g << 8) | tid);
-        if (listed) continue;
-        const int ce = min(cstar, (g + 1) * cpg);
-        for (int c = g * cpg; c < ce; ++c) {
-          float x[E];
-          span_guarded(c, tid, x);
-          span_append(c, tid, x);
-        }
+    if (cA > 0) {
+      th = block_bound(0);
+      make_list(cA, cpg == 1);
+    }
+#pragma unroll
+    for (int j = 0; j < RS_D; ++j) {
+      float x[E];
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) Vec<T>::widen(R[j][u], x + u * EPV);
+      if (cA + j >= nfull) mask_span(x, cA + j, tid, true);
+      consume(x);
+    }
+  } else {
+    for (int c = 0; c < nround; ++c) {
+      float x[E];
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) gload(elem0(c, u, tid), x + u * EPV);
+      consume(x);
+    }
+  }
+  // final bound over every element (>= the first, so the first list still covers it)
+  th = block_bound(1);
+  if (!fast) make_list(nround, false);
+  // this thread's sum relative to 2^MH (the sums are exchanged with the next barrier).
+  // Its terms are exp2(x L - mh) = exp2((x - m) L + (m L - mh)) with L = fp32(log2 e); with
+  // exact log2 e each would carry 2^(m (log2 e - L)) more, the same for the whole thread, so
+  // the thread's factor is 2^(mh - MH + m (log2 e - L)) and then
+  // log2e * LSE = MH + log2(sum of the factored sums). The difference from L only ever
+  // multiplies x - m, not x itself.
+  {
+    double sc = 0.0;
+    if (m != -kInf) {
+      const double ex = ((double)mh - (double)MH) + (double)m * (kLog2ed - (double)kLog2e);
+      sc = s * (double)__builtin_amdgcn_exp2f((float)ex);
+    }
+    sc = wave_sum(sc);
+    if (lane == 0) s_ws[w] = sc;
+  }
+
+  // ---- candidates: the preloaded spans, the chunks kept in the ring
+  {
+    const int c = my_ent >> 8, ln = my_ent & 255;
+    float x[E];
+#pragma unroll
+    for (int u = 0; u < RS_U; ++u) Vec<T>::widen(ra[u], x + u * EPV);
+    mask_span(x, c, ln, my_ent >= 0);
+    append_span(x, c, ln);
+  }
+  if (fast) {
+#pragma unroll
+    for (int j = 0; j < RS_D; ++j) {
+      float x[E];
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) Vec<T>::widen(R[j][u], x + u * EPV);
+      mask_span(x, cA + j, tid, true);
+      append_span(x, cA + j, tid);
+    }
+  }
+
+  // ---- re-reads of the listed spans not preloaded (entries past the lanes, multi-chunk
+  // groups, the scalar path), then of groups that did not fit in the list (their own lane);
+  // only chunks before climit: later ones were kept in registers
+  auto reread_group = [&](int ent) {  // wave-uniform call; ent < 0: nothing for this lane
+    const int g = ent >> 8, ln = ent & 255;
+    for (int k = 0; k < cpg; ++k) {
+      const int c = g * cpg + k;
+      const bool act = ent >= 0 && c < climit;
+      float x[E];
+      if (fast) {
+        u32x4 r[RS_U];
+#pragma unroll
+        for (int u = 0; u < RS_U; ++u) r[u] = bload(act ? c : -1, u, ln);
+#pragma unroll
+        for (int u = 0; u < RS_U; ++u) Vec<T>::widen(r[u], x + u * EPV);
+        mask_span(x, c, ln, act);
+      } else {
+#pragma unroll
+        for (int u = 0; u < RS_U; ++u) gload(act ? elem0(c, u, ln) : v1, x + u * EPV);
+      }
+      append_span(x, c, ln);
+    }
+  };
+  {
+    const int nl = min(nlist, RS_WL);
+    // entries below 64 were preloaded when the first list was made with preloading
+    const bool preloaded = fast && cpg == 1 && cA > 0;
+    for (int i0 = preloaded ? 64 : 0; i0 < nl; i0 += 64) {
+      const int i = i0 + lane;
+      reread_group(i < nl ? s_list[w][i] : -1);
+    }
+    if (nlist > RS_WL) {
+      const int ng = (climit + cpg - 1) / cpg;
+      for (int g = 0; g < ng; ++g) {
+        const bool mine = (own_qual >> g) & 1u;
+        const int idx = own_q + __builtin_popcount(own_qual & ((1u << g) - 1u));
+        reread_group((mine && idx >= RS_WL) ? ((g << 8) | tid) : -1);
       }
     }
   }
-  // true sum: remove the 2^(m log2e - mh) factor (exact product in float64)
-  if (m != -kInf) s *= exp2(-((double)m * (double)kLog2e - (double)mh));
+
+  // pad this wave's region with zero keys (below every key) to a multiple of 16
+  {
+    const int pad = (16 - (wn & 15)) & 15;
+    if (lane < pad && wn + lane < RS_WBUF) wbuf[wn + lane] = 0ull;
+  }
+  if (lane == 0) s_rn[w] = wn;
   __syncthreads();
-  int n_total = s_cnt;
-  if (n_total > RS_BUF) {
-    // pathological: re-stream with the threshold at the K-th key of the full buffer
+  double St = 0.0;
+#pragma unroll
+  for (int i = 0; i < RS_NW; ++i) St += s_ws[i];
+  int rs[RS_NW], rn[RS_NW];
+  int n_total = 0;
+  bool over = false;
+#pragma unroll
+  for (int i = 0; i < RS_NW; ++i) {
+    rs[i] = i * RS_WBUF;
+    rn[i] = s_rn[i];
+    over |= rn[i] > RS_WBUF;
+    n_total += rn[i];
+  }
+  if (over) {
+    // pathological (a wave region overflowed): re-stream with the threshold at the K-th
+    // key of the full buffer until the candidates fit, then read them as four quarters
+    for (int i = tid; i < RS_BUF; i += RS_NT)
+      if (i % RS_WBUF >= rn[i / RS_WBUF]) buf[i] = 0ull;
+    __syncthreads();
     for (;;) {
       block_sort_desc_u64<RS_NT>(buf, RS_BUF);
       const uint64_t tk = buf[K - 1];
@@ -325,13 +443,64 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
       n_total = s_cnt;
       if (n_total <= RS_BUF) break;
     }
+    // quarters of 16-key multiples (zero keys past the end) when ranks will be counted
+    const int q = (n_total <= RS_NT) ? ((n_total + RS_NW * 16 - 1) / (RS_NW * 16)) * 16 : (n_total + RS_NW - 1) / RS_NW;
+    if (n_total <= RS_NT) {
+      for (int i = n_total + tid; i < RS_NW * q; i += RS_NT) buf[i] = 0ull;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < RS_NW; ++i) {
+      rs[i] = i * q;
+      rn[i] = max(0, min(q, n_total - i * q));
+    }
   }
-  // ---- top 64 of the candidates: each wave a quarter, then one wave merges
-  {
-    const int q = (n_total + RS_NW - 1) / RS_NW;
-    const int a = w * q;
-    const int nb = max(0, min(n_total, a + q) - a);
-    const uint64_t top = wave_top64(buf + a, nb);
+
+  // ---- top K of the candidates (keys are distinct; zero keys pad each region to a
+  // multiple of 16). Up to one per thread: the rank of a key is the number of keys above
+  // it, counted by two lanes (half of each region each) when every wave holds at most 32.
+  // More: each wave takes the top 64 of its region with register bitonic sorts and one
+  // wave merges the four lists.
+  if (n_total <= RS_NT) {
+    int pl[RS_NW], mx = 0;
+#pragma unroll
+    for (int i = 0; i < RS_NW; ++i) {
+      pl[i] = (rn[i] + 15) & ~15;
+      mx = max(mx, rn[i]);
+    }
+    auto count_above = [&](uint64_t mine, int half, int nhalf) {
+      int r = 0;
+#pragma unroll
+      for (int i = 0; i < RS_NW; ++i) {
+        const int len = pl[i] / nhalf;
+        const uint64_t *kb = buf + rs[i] + half * len;
+        for (int j = 0; j < len; j += 8) {
+          int rr = 0;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) rr += (int)(kb[j + t] > mine);
+          r += rr;
+        }
+      }
+      return r;
+    };
+    if (mx <= 32) {
+      const int l = lane & 31;
+      const bool has = l < rn[w];
+      const uint64_t mine = has ? buf[rs[w] + l] : 0ull;
+      int r = count_above(mine, lane >> 5, 2);
+      r += __shfl_xor(r, 32, 64);
+      if (lane < 32 && has && r < K) s_top[r] = mine;
+    } else {
+      for (int l0 = 0; l0 < rn[w]; l0 += 64) {
+        const int l = l0 + lane;
+        const bool has = l < rn[w];
+        const uint64_t mine = has ? buf[rs[w] + l] : 0ull;
+        const int r = count_above(mine, 0, 1);
+        if (has && r < K) s_top[r] = mine;
+      }
+    }
+  } else {
+    const uint64_t top = wave_top64(buf + rs[w], rn[w]);
     __syncthreads();
     buf[w * 64 + lane] = top;
     __syncthreads();
@@ -339,30 +508,14 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
       uint64_t t = buf[lane];
 #pragma unroll
       for (int i = 1; i < RS_NW; ++i) t = wave_merge_top64_u64(t, buf[i * 64 + lane]);
-      buf[RS_NW * 64 + lane] = t;
+      s_top[lane] = t;
     }
-    __syncthreads();
   }
-  const uint64_t *topk = buf + RS_NW * 64;
-
-  // ---- block reduction of (max, sum)
-  float wm = wave_max(m);
-  if (lane == 0) s_wm[w] = wm;
   __syncthreads();
-  float M = s_wm[0];
-#pragma unroll
-  for (int i = 1; i < RS_NW; ++i) M = fmaxf(M, s_wm[i]);
-  double sc = (m == -kInf) ? 0.0 : s * exp((double)m - (double)M);
-  sc = wave_sum(sc);
-  if (lane == 0) s_ws[w] = sc;
-  __syncthreads();
-  double St = 0.0;
-#pragma unroll
-  for (int i = 0; i < RS_NW; ++i) St += s_ws[i];
-
   const int have = n_total < K ? n_total : K;
+
   if (S == 1) {
-    const double lse = (double)M + log(St);
+    const double lse = kLn2d * ((double)MH + log2(St));
     if (tid == 0) {
       if (out.lse_d) out.lse_d[row] = lse;
       if (out.lse_f) out.lse_f[row] = (float)lse;
@@ -370,7 +523,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     for (int k = tid; k < K; k += RS_NT) {
       const size_t o = (size_t)row * K + k;
       if (k < have) {
-        const uint64_t key = topk[k];
+        const uint64_t key = s_top[k];
         const float zv = key_val(key);
         out.ids[o] = (int32_t)key_id(key);
         if (out.zk) out.zk[o] = zv;
@@ -384,10 +537,10 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   } else {
     const size_t g = (size_t)row * S + sp;
     if (tid == 0) {
-      part.m[g] = M;
+      part.m[g] = MH;
       part.s[g] = St;
     }
-    for (int k = tid; k < K; k += RS_NT) part.keys[g * K + k] = (k < have) ? topk[k] : 0ull;
+    for (int k = tid; k < K; k += RS_NT) part.keys[g * K + k] = (k < have) ? s_top[k] : 0ull;
   }
 }
 
@@ -401,14 +554,15 @@ __global__ __launch_bounds__(RS_NT) void k_rowsweep_merge(int K, int S, RowPart 
   const int np = next_pow2(n);
   for (int i = tid; i < np; i += RS_NT) buf[i] = (i < n) ? part.keys[(size_t)row * S * K + i] : 0ull;
   if (tid == 0) {
+    // partials: (MH, sum) with the sum relative to 2^MH, MH on the log2 scale
     float M = -kInf;
     for (int i = 0; i < S; ++i) M = fmaxf(M, part.m[(size_t)row * S + i]);
     double St = 0.0;
     for (int i = 0; i < S; ++i) {
       const float mi = part.m[(size_t)row * S + i];
-      if (mi != -kInf) St += part.s[(size_t)row * S + i] * exp((double)mi - (double)M);
+      if (mi != -kInf) St += part.s[(size_t)row * S + i] * exp2((double)mi - (double)M);
     }
-    s_lse = (double)M + log(St);
+    s_lse = kLn2d * ((double)M + log2(St));
   }
   __syncthreads();
   block_sort_desc_u64<RS_NT>(buf, np);

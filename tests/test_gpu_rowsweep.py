@@ -55,6 +55,9 @@ def test_rowsweep_constant_and_sorted_rows():
     rows = np.stack([np.zeros(V), np.arange(V), -np.arange(V), np.full(V, -7.5)]).astype(np.float32)
     run_and_compare(synth.bf16_from_f32(rows), "bf16", 64)
     run_and_compare(rows, "f32", 64)
+    # large magnitudes: the exponent's fp32 rounding of log2 e must only ever scale x - max(x)
+    big = np.stack([np.arange(V) * 0.5 + 1.0e5, 1.0e5 - np.arange(V) * 0.5, np.arange(V) * 0.5 - 1.0e5]).astype(np.float32)
+    run_and_compare(big, "f32", 64)
 
 
 def test_rowsweep_full_ddtree_shape_sampled():
