@@ -9,22 +9,29 @@
 // leaf) draw the extra token from p' by inverse CDF.
 //
 // Design (gfx950). Residuals are kept in closed form: after i rejections at a node,
-// p' = (p - t_i q)_+ / C_i with t_1 = 0, C_i = sum_v (p - t_i q)_+ and t_{i+1} = t_i + C_i,
-// so each rejection costs one streaming pass over the two rows and no row is ever
-// materialised. Every pass is one workgroup with a fixed thread->element map and a fixed
-// reduction tree, so a quantity computed twice is bit-identical. Two paths share these
-// passes: with one trial per round, one workgroup per round walks lazily (only the
-// visited nodes and the tried children cost passes); with many trials, a table kernel
-// precomputes per node the children's (q(c), p'(c)) and the block prefix sums of the
-// final residual (blocks of 64 tokens), and one thread per (trial, round) walks on the
-// tables, sampling by a binary search over blocks and a 64-element scan.
+// p' = (p - t_i q)_+ / C_i with t_1 = 0, C_1 = 1 (p is normalised), C_i = sum_v (p - t_i q)_+
+// and t_{i+1} = t_i + C_i, so each rejection costs one streaming pass over the two rows
+// and no row is ever materialised. Probabilities are taken on the log2 scale,
+// p = exp2(z s - LSE2) with s = fp32(log2 e / T) and LSE2 = log2 sum exp2(z s), which keeps
+// them normalised exactly as computed. A pass is one workgroup of 1024 threads streaming
+// both rows in units of 8 elements (16-byte buffer loads, a ring of units in flight per thread)
+// with a fixed thread->element map and a fixed reduction tree, so a quantity computed
+// twice is bit-identical. Every C pass also leaves the sums of its 64-token blocks in LDS,
+// which is all the final draw needs. Two paths share the passes: with one trial per round,
+// one workgroup per round walks lazily (only the visited nodes and the tried children
+// cost passes); with many trials, a table kernel precomputes per node the children's
+// (q(c), p'(c)) and the block prefix sums of the final residual, and one thread per
+// (trial, round) walks on the tables. Both draw the token inside the chosen block in the
+// same order: 8 lane sums of 8 tokens in float, accumulated lane by lane in float64.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dt {
 
-constexpr int AC_NT = 256;
-constexpr int AC_BLK = 64;  // tokens per sampling block (8 lanes x 8 elements)
+constexpr int AC_NT = 1024;        // threads per pass workgroup
+constexpr int AC_NW = AC_NT / 64;
+constexpr int AC_BLK = 64;         // tokens per sampling block (8 lanes x 8 elements)
+constexpr int AC_WT = 256;         // threads per workgroup of the table walk
 
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11).
@@ -47,141 +54,310 @@ DT_INLINE float philox_uniform(uint64_t seed, uint64_t trial, uint32_t rnd, uint
   return (float)(c0 >> 8) * (1.0f / 16777216.0f);
 }
 
-// ---------------------------------------------------------------- per-element residual
-struct RowPair {
-  const void *zt;   // target row
-  const void *zd;   // draft row
-  float invT;
-  float lt_hi, lt_lo;  // lse of target row / T, split hi + lo
-  float lq_hi, lq_lo;  // lse of draft row / T
+// ---------------------------------------------------------------- rows in units of 8
+// A row of V elements read in units of 8. A 16-byte aligned row is read with buffer loads
+// (reads past its end return zero; those elements are masked), any other element-wise.
+template <typename T>
+struct Row {
+  const T *p;
+  int V;
+  bool vec;
+  __amdgpu_buffer_rsrc_t rs;
+};
+template <typename T>
+DT_INLINE Row<T> make_row(const T *p, int V) {
+  Row<T> r;
+  r.p = p;
+  r.V = V;
+  r.vec = (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+  r.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(p), (short)0, r.vec ? V * (int)sizeof(T) : 0, 0x00020000);
+  return r;
+}
+template <typename T>
+struct Raw {
+  u32x4 v[8 / Vec<T>::N];
+};
+template <typename T>
+DT_INLINE Raw<T> raw_load(const Row<T> &r, int u) {
+  Raw<T> x;
+#pragma unroll
+  for (int i = 0; i < 8 / Vec<T>::N; ++i)
+    x.v[i] = (u32x4)__builtin_amdgcn_raw_buffer_load_b128(r.rs, u * 8 * (int)sizeof(T) + 16 * i, 0, 0);
+  return x;
+}
+template <typename T>
+DT_INLINE void raw_widen(const Raw<T> &x, float *f) {
+#pragma unroll
+  for (int i = 0; i < 8 / Vec<T>::N; ++i) Vec<T>::widen(x.v[i], f + i * Vec<T>::N);
+}
+template <typename T>
+DT_INLINE void unit_elems(const Row<T> &r, int u, float *f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int v = u * 8 + e;
+    f[e] = v < r.V ? load_elt(r.p, (size_t)v) : -kInf;
+  }
+}
+DT_INLINE void unit_mask(float *f, int u, int V) {
+  const int nv = V - u * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = e < nv ? f[e] : -kInf;
+}
+
+// Units in flight per thread and row (the ring depth): a pass is bound by the bytes one
+// workgroup keeps in flight, so bf16 rows use a deeper ring than fp32 rows (whose units
+// take twice the registers).
+template <typename T>
+struct Ring {
+  static constexpr int D = sizeof(T) == 2 ? 4 : 2;
 };
 
-template <typename T>
-DT_INLINE float softmax_elt(float z, float invT, float hi, float lo) {
-  return __builtin_amdgcn_exp2f(((z * invT - hi) - lo) * kLog2e);
+// f(u, a[8], b[8]) for every unit u of two rows of equal length (elements past the end are
+// -inf); unit u = threadIdx.x + k * AC_NT. Wave-uniform calls of f.
+template <typename T, typename F>
+DT_INLINE void stream2(const Row<T> &A, const Row<T> &B, F &&f) {
+  constexpr int D = Ring<T>::D;
+  const int V = A.V;
+  const int iters = ((V + 7) / 8 + AC_NT - 1) / AC_NT;
+  const int tid = threadIdx.x;
+  if (A.vec && B.vec) {
+    Raw<T> ra[D], rb[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      ra[j] = raw_load(A, tid + j * AC_NT);
+      rb[j] = raw_load(B, tid + j * AC_NT);
+    }
+    for (int k = 0; k < iters; k += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        if (k + j < iters) {
+          const int u = tid + (k + j) * AC_NT;
+          float xa[8], xb[8];
+          raw_widen(ra[j], xa);
+          raw_widen(rb[j], xb);
+          ra[j] = raw_load(A, u + D * AC_NT);
+          rb[j] = raw_load(B, u + D * AC_NT);
+          if (u * 8 + 8 > V) {
+            unit_mask(xa, u, V);
+            unit_mask(xb, u, V);
+          }
+          f(u, xa, xb);
+        }
+      }
+    }
+  } else {
+    for (int k = 0; k < iters; ++k) {
+      const int u = tid + k * AC_NT;
+      float xa[8], xb[8];
+      unit_elems(A, u, xa);
+      unit_elems(B, u, xb);
+      f(u, xa, xb);
+    }
+  }
 }
-template <typename T>
-DT_INLINE void pq_at(const RowPair &rp, int v, float &p, float &q) {
-  const float zt = load_elt(static_cast<const T *>(rp.zt), (size_t)v);
-  const float zd = load_elt(static_cast<const T *>(rp.zd), (size_t)v);
-  p = softmax_elt<T>(zt, rp.invT, rp.lt_hi, rp.lt_lo);
-  q = softmax_elt<T>(zd, rp.invT, rp.lq_hi, rp.lq_lo);
+// the same over one row
+template <typename T, typename F>
+DT_INLINE void stream1(const Row<T> &A, F &&f) {
+  constexpr int D = 2 * Ring<T>::D;
+  const int V = A.V;
+  const int iters = ((V + 7) / 8 + AC_NT - 1) / AC_NT;
+  const int tid = threadIdx.x;
+  if (A.vec) {
+    Raw<T> ra[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) ra[j] = raw_load(A, tid + j * AC_NT);
+    for (int k = 0; k < iters; k += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        if (k + j < iters) {
+          const int u = tid + (k + j) * AC_NT;
+          float xa[8];
+          raw_widen(ra[j], xa);
+          ra[j] = raw_load(A, u + D * AC_NT);
+          if (u * 8 + 8 > V) unit_mask(xa, u, V);
+          f(u, xa);
+        }
+      }
+    }
+  } else {
+    for (int k = 0; k < iters; ++k) {
+      const int u = tid + k * AC_NT;
+      float xa[8];
+      unit_elems(A, u, xa);
+      f(u, xa);
+    }
+  }
 }
-DT_INLINE float resid(float p, float q, float t) { return fmaxf(p - t * q, 0.f); }
 
-// ---------------------------------------------------------------- workgroup passes
-// Deterministic block sum of one double per thread.
-DT_INLINE double wg_sum(double v, double *red) {
+// ---------------------------------------------------------------- probabilities
+// p = exp2(z s - LSE2) as exp2(fma(z, s, -hi) - lo) with hi + lo = LSE2 (a float pair).
+struct Norm {
+  float s, hi, lo;
+};
+DT_INLINE float prob(float z, const Norm &n) { return __builtin_amdgcn_exp2f(__builtin_fmaf(z, n.s, -n.hi) - n.lo); }
+DT_INLINE float resid(float p, float q, float t) { return fmaxf(__builtin_fmaf(-t, q, p), 0.f); }
+DT_INLINE Norm make_norm(float s, double lse2) {
+  Norm n;
+  n.s = s;
+  n.hi = (float)lse2;
+  n.lo = __builtin_isfinite(lse2) ? (float)(lse2 - (double)n.hi) : 0.f;
+  return n;
+}
+
+// ---------------------------------------------------------------- workgroup reductions
+struct Red {
+  double d[AC_NW * 2];
+  float f[AC_NW * 2];
+  uint64_t k[AC_NW];
+};
+// Deterministic block sums of one or two doubles per thread.
+DT_INLINE double wg_sum(double v, Red &red) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
+  if ((threadIdx.x & 63) == 0) red.d[w] = v;
   __syncthreads();
   double s = 0.0;
 #pragma unroll
-  for (int i = 0; i < AC_NT / 64; ++i) s += red[i];
+  for (int i = 0; i < AC_NW; ++i) s += red.d[i];
   return s;
 }
 
-// ln sum_v exp(z_v * invT) over one row.
-template <typename T>
-DT_INLINE double wg_row_lse(const T *row, int V, float invT, float *redf, double *red) {
-  float m = -kInf;
-  double s = 0.0;
-  for (int v = threadIdx.x; v < V; v += AC_NT) {
-    const float x = load_elt(row, (size_t)v) * invT;
-    if (x > m) {
-      s = (m == -kInf) ? 0.0 : s * exp((double)m - (double)x);
-      m = x;
-    }
-    s += (double)__builtin_amdgcn_exp2f((x - m) * kLog2e);
-  }
-  float wm = wave_max(m);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) redf[threadIdx.x >> 6] = wm;
-  __syncthreads();
-  float M = redf[0];
+// Online log2-sum-exp2 of y = z s over one thread's elements: terms exp2(fma(z, s, -mh)) with
+// mh = fp32(m s) for the running maximum m; across threads the sums are scaled by
+// 2^(mh - MH), MH the largest mh, and LSE2 = MH + log2(total).
+struct L2Acc {
+  float m = -kInf, mh = 0.f;
+  double acc = 0.0;
+  DT_INLINE void add(const float *z, float s) {
+    float um = z[0];
 #pragma unroll
-  for (int i = 1; i < AC_NT / 64; ++i) M = fmaxf(M, redf[i]);
-  const double sc = (m == -kInf) ? 0.0 : s * exp((double)m - (double)M);
-  return (double)M + log(wg_sum(sc, red));
+    for (int e = 1; e < 8; ++e) um = fmaxf(um, z[e]);
+    if (um > m) {
+      const float nh = um * s;
+      acc = (m == -kInf) ? 0.0 : acc * (double)__builtin_amdgcn_exp2f(mh - nh);
+      m = um;
+      mh = nh;
+    }
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(z[e], s, -mh));
+      a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(z[e + 1], s, -mh));
+    }
+    acc += (double)(a0 + a1);
+  }
+};
+
+// LSE2 of both rows in one pass.
+template <typename T>
+DT_INLINE void wg_lse2(const Row<T> &A, const Row<T> &B, float s, Red &red, double &la, double &lb) {
+  L2Acc xa, xb;
+  stream2(A, B, [&](int, const float *za, const float *zb) {
+    xa.add(za, s);
+    xb.add(zb, s);
+  });
+  const float ma = wave_max(xa.m == -kInf ? -kInf : xa.mh), mb = wave_max(xb.m == -kInf ? -kInf : xb.mh);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    red.f[w] = ma;
+    red.f[AC_NW + w] = mb;
+  }
+  __syncthreads();
+  float MA = red.f[0], MB = red.f[AC_NW];
+#pragma unroll
+  for (int i = 1; i < AC_NW; ++i) {
+    MA = fmaxf(MA, red.f[i]);
+    MB = fmaxf(MB, red.f[AC_NW + i]);
+  }
+  double sa = (xa.m == -kInf) ? 0.0 : xa.acc * (double)__builtin_amdgcn_exp2f(xa.mh - MA);
+  double sb = (xb.m == -kInf) ? 0.0 : xb.acc * (double)__builtin_amdgcn_exp2f(xb.mh - MB);
+  sa = wave_sum(sa);
+  sb = wave_sum(sb);
+  if ((threadIdx.x & 63) == 0) {
+    red.d[w] = sa;
+    red.d[AC_NW + w] = sb;
+  }
+  __syncthreads();
+  double SA = 0.0, SB = 0.0;
+#pragma unroll
+  for (int i = 0; i < AC_NW; ++i) {
+    SA += red.d[i];
+    SB += red.d[AC_NW + i];
+  }
+  la = (double)MA + log2(SA);
+  lb = (double)MB + log2(SB);
 }
 
 // First index of the maximum of one row.
 template <typename T>
-DT_INLINE int wg_row_argmax(const T *row, int V, uint64_t *redk) {
+DT_INLINE int wg_row_argmax(const Row<T> &A, Red &red) {
   uint64_t best = 0;
-  for (int v = threadIdx.x; v < V; v += AC_NT) {
-    const uint64_t k = make_key(load_elt(row, (size_t)v), (uint32_t)v);
-    best = k > best ? k : best;
-  }
+  const int V = A.V;
+  stream1(A, [&](int u, const float *z) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int v = u * 8 + e;
+      const uint64_t k = v < V ? make_key(z[e], (uint32_t)v) : 0ull;
+      best = k > best ? k : best;
+    }
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const uint64_t x = __shfl_xor(best, o, 64);
     best = x > best ? x : best;
   }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) redk[threadIdx.x >> 6] = best;
+  if ((threadIdx.x & 63) == 0) red.k[threadIdx.x >> 6] = best;
   __syncthreads();
-  uint64_t b = redk[0];
+  uint64_t b = red.k[0];
 #pragma unroll
-  for (int i = 1; i < AC_NT / 64; ++i) b = redk[i] > b ? redk[i] : b;
+  for (int i = 1; i < AC_NW; ++i) b = red.k[i] > b ? red.k[i] : b;
   return (int)key_id(b);
 }
 
-// C(t) = sum_v max(p - t q, 0). Block b of 64 tokens is handled by 8 lanes x 8 elements;
-// when blk is non-null its per-block sums are written there (float, blocks in id order).
+// C(t) = sum_v (p - t q)_+; the float sums of the 64-token blocks go to blk[] (block b is
+// units 8b..8b+7: eight lanes, each summing its 8 tokens in order).
 template <typename T>
-DT_INLINE double wg_chain_pass(const RowPair &rp, int V, float t, float *blk, double *red) {
-  const int lane8 = threadIdx.x & 7;
-  const int nblk = (V + AC_BLK - 1) / AC_BLK;
+DT_INLINE double wg_chain_pass(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t, float *blk,
+                               int nblk, Red &red) {
   double acc = 0.0;
-  for (int b0 = 0; b0 < nblk; b0 += AC_NT / 8) {
-    const int b = b0 + (threadIdx.x >> 3);
+  stream2(A, B, [&](int u, const float *za, const float *zb) {
     float part = 0.f;
-    if (b < nblk) {
-      const int v0 = b * AC_BLK + lane8 * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = v0 + e;
-        if (v < V) {
-          float p, q;
-          pq_at<T>(rp, v, p, q);
-          part += resid(p, q, t);
-        }
-      }
-    }
+    for (int e = 0; e < 8; ++e) part += resid(prob(za[e], nt), prob(zb[e], nd), t);
     float bs = part;
     bs += __shfl_xor(bs, 1, 64);
     bs += __shfl_xor(bs, 2, 64);
     bs += __shfl_xor(bs, 4, 64);
-    if (blk && lane8 == 0 && b < nblk) blk[b] = bs;
+    if ((u & 7) == 0 && (u >> 3) < nblk) blk[u >> 3] = bs;
     acc += (double)part;
-  }
+  });
   return wg_sum(acc, red);
 }
 
-// Inclusive prefix sums (double) of n floats, in place into pre[]; one workgroup.
-DT_INLINE void wg_prefix(const float *blk, double *pre, int n, double *red) {
-  // each thread owns a contiguous span; serial within, scanned across threads
+// Inclusive prefix sums (float64) of the n block sums, into pre[]; one workgroup.
+DT_INLINE void wg_prefix(const float *blk, double *pre, int n, Red &red) {
   const int per = (n + AC_NT - 1) / AC_NT;
   const int a = threadIdx.x * per;
   const int e = min(n, a + per);
   double s = 0.0;
   for (int i = a; i < e; ++i) s += (double)blk[i];
-  __syncthreads();
-  red[threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double run = 0.0;
-    for (int i = 0; i < AC_NT; ++i) {
-      const double x = red[i];
-      red[i] = run;
-      run += x;
-    }
+  // exclusive scan over the threads: within the wave by lanes, then over wave totals
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  double incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double x = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += x;
   }
   __syncthreads();
-  double run = red[threadIdx.x];
+  if (lane == 63) red.d[w] = incl;
+  __syncthreads();
+  double run = 0.0;
+  for (int i = 0; i < w; ++i) run += red.d[i];
+  run += incl - s;
   for (int i = a; i < e; ++i) {
     run += (double)blk[i];
     pre[i] = run;
@@ -189,35 +365,90 @@ DT_INLINE void wg_prefix(const float *blk, double *pre, int n, double *red) {
   __syncthreads();
 }
 
-// Inverse CDF over the final residual: smallest v with cumsum > u * total.
-template <typename T>
-DT_INLINE int sample_from_blocks(const RowPair &rp, int V, float t, const double *pre, int nblk, float u) {
-  const double total = pre[nblk - 1];
-  const double target = (double)u * total;
-  int lo = 0, hi = nblk - 1;  // first block with pre[b] > target
+// First block b with pre[b] > target (the last when none).
+DT_INLINE int find_block(const double *pre, int nblk, double target) {
+  int lo = 0, hi = nblk - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (pre[mid] > target) hi = mid; else lo = mid + 1;
   }
-  const int b = lo;
-  double acc = (b > 0) ? pre[b - 1] : 0.0;
-  int last_pos = -1;
-  const int v0 = b * AC_BLK;
-  const int v1 = min(V, v0 + AC_BLK);
-  for (int v = v0; v < v1; ++v) {
-    float p, q;
-    pq_at<T>(rp, v, p, q);
-    const float r = resid(p, q, t);
-    if (r > 0.f) last_pos = v;
-    acc += (double)r;
-    if (acc > target && r > 0.f) return v;
-  }
-  return last_pos >= 0 ? last_pos : v0;
+  return lo;
 }
 
-DT_INLINE void split_lse(double lse, float &hi, float &lo) {
-  hi = (float)lse;
-  lo = (float)(lse - (double)hi);
+// Residuals of lane l of block b (tokens b*64 + 8l .. +7; 0 past the row end) and their
+// float sum in order.
+template <typename T>
+DT_INLINE float lane_resid(const T *zt, const T *zd, int V, const Norm &nt, const Norm &nd, float t, int b, int l,
+                           float *r) {
+  float part = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int v = b * AC_BLK + l * 8 + e;
+    r[e] = v < V ? resid(prob(load_elt(zt, (size_t)v), nt), prob(load_elt(zd, (size_t)v), nd), t) : 0.f;
+    part += r[e];
+  }
+  return part;
+}
+
+// Inverse CDF inside block b: with acc running from the block's base (pre[b-1]) lane by
+// lane (float64 sums of the lanes' float sums) and then token by token, the first token
+// with r > 0 whose acc exceeds target; else the last token with r > 0; else the block start.
+// Serial version (one thread).
+template <typename T>
+DT_INLINE int sample_in_block_serial(const T *zt, const T *zd, int V, const Norm &nt, const Norm &nd, float t,
+                                     const double *pre, int b, double target) {
+  double base = b > 0 ? pre[b - 1] : 0.0;
+  int last = -1;
+  for (int l = 0; l < 8; ++l) {
+    float r[8];
+    const float part = lane_resid(zt, zd, V, nt, nd, t, b, l, r);
+    double acc = base;
+    for (int e = 0; e < 8; ++e) {
+      acc += (double)r[e];
+      if (r[e] > 0.f) {
+        if (acc > target) return b * AC_BLK + l * 8 + e;
+        last = b * AC_BLK + l * 8 + e;
+      }
+    }
+    base += (double)part;
+  }
+  return last >= 0 ? last : b * AC_BLK;
+}
+// Wave version: lanes 0..7 of the calling wave take one lane of the block each.
+template <typename T>
+DT_INLINE int sample_in_block_wave(const T *zt, const T *zd, int V, const Norm &nt, const Norm &nd, float t,
+                                   const double *pre, int b, double target) {
+  const int lane = threadIdx.x & 63;
+  const int l = lane & 7;
+  float r[8];
+  const float part = lane_resid(zt, zd, V, nt, nd, t, b, l, r);
+  double base = b > 0 ? pre[b - 1] : 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float pi = __shfl(part, i, 64);
+    if (i < l) base += (double)pi;
+  }
+  double acc = base;
+  int hit = -1, last = -1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc += (double)r[e];
+    if (r[e] > 0.f) {
+      if (hit < 0 && acc > target) hit = e;
+      last = e;
+    }
+  }
+  const uint64_t hb = __ballot(lane < 8 && hit >= 0);
+  if (hb) {
+    const int L = __builtin_ctzll(hb);
+    return b * AC_BLK + L * 8 + __shfl(hit, L, 64);
+  }
+  const uint64_t lb = __ballot(lane < 8 && last >= 0);
+  if (lb) {
+    const int L = 63 - __builtin_clzll(lb);
+    return b * AC_BLK + L * 8 + __shfl(last, L, 64);
+  }
+  return b * AC_BLK;
 }
 
 // children of every slot: first child / next sibling in slot order. A slot whose parent
@@ -237,15 +468,14 @@ DT_INLINE void build_children(const int *par, const int *tok, int n, int V, int 
 
 DT_INLINE int clamp_nodes(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 DT_INLINE int draft_row(int depth, int L) { return depth < 0 ? 0 : (depth > L - 1 ? L - 1 : depth); }
+DT_INLINE float log2_scale(float T) { return (float)(1.4426950408889634 / (double)T); }
 
 // ---------------------------------------------------------------- lazy walk (one trial / T = 0)
 template <typename T>
 __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
   __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1];
-  __shared__ double red[AC_NT];
-  __shared__ float redf[AC_NT / 64];
-  __shared__ uint64_t redk[AC_NT / 64];
+  __shared__ Red red;
   extern __shared__ double dyn[];  // [nblk] prefix (double) then [nblk] block sums (float)
   const int r = blockIdx.x;
   const int cap = a.tree.cap;
@@ -262,7 +492,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
   int j = 0, out_tok = -1;
   if (a.T == 0.f) {
     for (;;) {
-      const int ts = wg_row_argmax<T>(target + (size_t)j * a.V, a.V, redk);
+      const int ts = wg_row_argmax(make_row(target + (size_t)j * a.V, a.V), red);
       int nxt = -1;
       for (int c = fc[j]; c >= 0; c = ns[c])
         if (tok[c] == ts) {
@@ -276,7 +506,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
       j = nxt;
     }
   } else {
-    const float invT = 1.0f / a.T;
+    const float s = log2_scale(a.T);
     const T *draft = static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V;
     const uint64_t trial = a.trial0;
     uint32_t step = 0;
@@ -284,40 +514,46 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
     double *pre = dyn;
     float *blk = reinterpret_cast<float *>(dyn + nblk);
     for (;;) {
-      RowPair rp;
-      rp.zt = target + (size_t)j * a.V;
-      rp.zd = draft + (size_t)draft_row(dep[j], a.L) * a.V;
-      rp.invT = invT;
-      split_lse(wg_row_lse<T>(static_cast<const T *>(rp.zt), a.V, invT, redf, red), rp.lt_hi, rp.lt_lo);
-      split_lse(wg_row_lse<T>(static_cast<const T *>(rp.zd), a.V, invT, redf, red), rp.lq_hi, rp.lq_lo);
+      const T *zt = target + (size_t)j * a.V;
+      const T *zd = draft + (size_t)draft_row(dep[j], a.L) * a.V;
+      const Row<T> A = make_row(zt, a.V), B = make_row(zd, a.V);
+      double la, lb;
+      wg_lse2(A, B, s, red, la, lb);
+      const Norm nt = make_norm(s, la), nd = make_norm(s, lb);
       float t = 0.f;
-      double C = wg_chain_pass<T>(rp, a.V, t, nullptr, red);
+      double C = 1.0;
+      bool blk_at_t = false;  // blk holds the block sums of the residual at t
       int nxt = -1;
       for (int c = fc[j]; c >= 0; c = ns[c]) {
-        float p, q;
-        pq_at<T>(rp, tok[c], p, q);
-        const float pc = resid(p, q, t) / (float)C;
+        const float z1 = load_elt(zt, (size_t)tok[c]), z2 = load_elt(zd, (size_t)tok[c]);
+        const float q = prob(z2, nd);
+        const float pc = resid(prob(z1, nt), q, t) / (float)C;
         const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
         if (u * q < pc) {
           nxt = c;
           break;
         }
         const float t2 = t + (float)C;
-        const double C2 = wg_chain_pass<T>(rp, a.V, t2, nullptr, red);
+        const double C2 = wg_chain_pass(A, B, nt, nd, t2, blk, nblk, red);
         if (C2 > 0.0) {
           t = t2;
           C = C2;
+          blk_at_t = true;
+        } else {
+          blk_at_t = false;
         }
       }
       if (nxt >= 0) {
         j = nxt;
         continue;
       }
-      (void)wg_chain_pass<T>(rp, a.V, t, blk, red);
+      if (!blk_at_t) (void)wg_chain_pass(A, B, nt, nd, t, blk, nblk, red);
       __syncthreads();
       wg_prefix(blk, pre, nblk, red);
       const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
-      out_tok = sample_from_blocks<T>(rp, a.V, t, pre, nblk, u);
+      const double target_mass = (double)u * pre[nblk - 1];
+      const int b = find_block(pre, nblk, target_mass);
+      out_tok = sample_in_block_wave(zt, zd, a.V, nt, nd, t, pre, b, target_mass);
       break;
     }
   }
@@ -333,7 +569,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
 struct AccTables {
   float *qc, *pc;                      // [R][cap+1], indexed by the child's slot
   float *tfin;                         // [R][cap+1]: t of the residual left at node j
-  float *lt_hi, *lt_lo, *lq_hi, *lq_lo;  // [R][cap+1]: row normalisers used at node j
+  float *lt_hi, *lt_lo, *lq_hi, *lq_lo;  // [R][cap+1]: LSE2 of the rows used at node j (float pairs)
   double *pre;                         // [R][cap+1][nblk]: block prefix sums of that residual
 };
 
@@ -341,8 +577,7 @@ template <typename T>
 __global__ __launch_bounds__(AC_NT) void k_accept_tables(AcceptArgs a, AccTables tb) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
   __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1];
-  __shared__ double red[AC_NT];
-  __shared__ float redf[AC_NT / 64];
+  __shared__ Red red;
   extern __shared__ double dyn[];  // [nblk] block sums (float)
   const int cap = a.tree.cap;
   const int r = blockIdx.x / (cap + 1);
@@ -357,50 +592,52 @@ __global__ __launch_bounds__(AC_NT) void k_accept_tables(AcceptArgs a, AccTables
   }
   __syncthreads();
   build_children(par, tok, n, a.V, fc, ns);
-  const float invT = 1.0f / a.T;
-  const T *target = static_cast<const T *>(a.target) + (size_t)r * (cap + 1) * a.V;
-  const T *draft = static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V;
+  const float s = log2_scale(a.T);
+  const T *zt = static_cast<const T *>(a.target) + ((size_t)r * (cap + 1) + j) * a.V;
+  const T *zd = static_cast<const T *>(a.draft) + ((size_t)r * a.L + draft_row(dep[j], a.L)) * a.V;
   const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
   float *blk = reinterpret_cast<float *>(dyn);
-  RowPair rp;
-  rp.zt = target + (size_t)j * a.V;
-  rp.zd = draft + (size_t)draft_row(dep[j], a.L) * a.V;
-  rp.invT = invT;
-  split_lse(wg_row_lse<T>(static_cast<const T *>(rp.zt), a.V, invT, redf, red), rp.lt_hi, rp.lt_lo);
-  split_lse(wg_row_lse<T>(static_cast<const T *>(rp.zd), a.V, invT, redf, red), rp.lq_hi, rp.lq_lo);
+  const Row<T> A = make_row(zt, a.V), B = make_row(zd, a.V);
+  double la, lb;
+  wg_lse2(A, B, s, red, la, lb);
+  const Norm nt = make_norm(s, la), nd = make_norm(s, lb);
   float t = 0.f;
-  double C = wg_chain_pass<T>(rp, a.V, t, nullptr, red);
+  double C = 1.0;
+  bool blk_at_t = false;
   for (int c = fc[j]; c >= 0; c = ns[c]) {
-    float p, q;
-    pq_at<T>(rp, tok[c], p, q);
+    const float z1 = load_elt(zt, (size_t)tok[c]), z2 = load_elt(zd, (size_t)tok[c]);
+    const float q = prob(z2, nd);
     if (threadIdx.x == 0) {
       tb.qc[base + c] = q;
-      tb.pc[base + c] = resid(p, q, t) / (float)C;
+      tb.pc[base + c] = resid(prob(z1, nt), q, t) / (float)C;
     }
     const float t2 = t + (float)C;
-    const double C2 = wg_chain_pass<T>(rp, a.V, t2, nullptr, red);
+    const double C2 = wg_chain_pass(A, B, nt, nd, t2, blk, nblk, red);
     if (C2 > 0.0) {
       t = t2;
       C = C2;
+      blk_at_t = true;
+    } else {
+      blk_at_t = false;
     }
   }
-  (void)wg_chain_pass<T>(rp, a.V, t, blk, red);
+  if (!blk_at_t) (void)wg_chain_pass(A, B, nt, nd, t, blk, nblk, red);
   __syncthreads();
   wg_prefix(blk, tb.pre + (base + j) * nblk, nblk, red);
   if (threadIdx.x == 0) {
     tb.tfin[base + j] = t;
-    tb.lt_hi[base + j] = rp.lt_hi;
-    tb.lt_lo[base + j] = rp.lt_lo;
-    tb.lq_hi[base + j] = rp.lq_hi;
-    tb.lq_lo[base + j] = rp.lq_lo;
+    tb.lt_hi[base + j] = nt.hi;
+    tb.lt_lo[base + j] = nt.lo;
+    tb.lq_hi[base + j] = nd.hi;
+    tb.lq_lo[base + j] = nd.lo;
   }
 }
 
-// One thread per (trial, round): the walk on the tables, then inverse-CDF sampling.
+// One thread per (trial, round): the walk on the tables, then the draw.
 template <typename T>
-__global__ __launch_bounds__(AC_NT) void k_accept_walk(AcceptArgs a, AccTables tb) {
+__global__ __launch_bounds__(AC_WT) void k_accept_walk(AcceptArgs a, AccTables tb) {
   const int cap = a.tree.cap;
-  const size_t gid = (size_t)blockIdx.x * AC_NT + threadIdx.x;
+  const size_t gid = (size_t)blockIdx.x * AC_WT + threadIdx.x;
   if (gid >= (size_t)a.n_trials * a.R) return;
   const int r = (int)(gid % a.R);
   const uint64_t trial = a.trial0 + gid / a.R;
@@ -424,19 +661,21 @@ __global__ __launch_bounds__(AC_NT) void k_accept_walk(AcceptArgs a, AccTables t
     j = nxt;
   }
   const int dj = a.tree.depth[base + j];
-  const T *target = static_cast<const T *>(a.target) + (size_t)r * (cap + 1) * a.V;
-  const T *draft = static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V;
-  RowPair rp;
-  rp.zt = target + (size_t)j * a.V;
-  rp.zd = draft + (size_t)draft_row(dj, a.L) * a.V;
-  rp.invT = 1.0f / a.T;
-  rp.lt_hi = tb.lt_hi[base + j];
-  rp.lt_lo = tb.lt_lo[base + j];
-  rp.lq_hi = tb.lq_hi[base + j];
-  rp.lq_lo = tb.lq_lo[base + j];
+  const T *zt = static_cast<const T *>(a.target) + ((size_t)r * (cap + 1) + j) * a.V;
+  const T *zd = static_cast<const T *>(a.draft) + ((size_t)r * a.L + draft_row(dj, a.L)) * a.V;
+  const float s = log2_scale(a.T);
+  Norm nt, nd;
+  nt.s = nd.s = s;
+  nt.hi = tb.lt_hi[base + j];
+  nt.lo = tb.lt_lo[base + j];
+  nd.hi = tb.lq_hi[base + j];
+  nd.lo = tb.lq_lo[base + j];
   const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
+  const double *pre = tb.pre + (base + j) * nblk;
   const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
-  const int v = sample_from_blocks<T>(rp, a.V, tb.tfin[base + j], tb.pre + (base + j) * nblk, nblk, u);
+  const double target_mass = (double)u * pre[nblk - 1];
+  const int b = find_block(pre, nblk, target_mass);
+  const int v = sample_in_block_serial(zt, zd, a.V, nt, nd, tb.tfin[base + j], pre, b, target_mass);
   a.accept_len[gid] = dj;
   a.accept_node[gid] = j;
   a.next_token[gid] = v;
@@ -489,11 +728,11 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t total = (size_t)a.n_trials * a.R;
-  const dim3 g2((unsigned)((total + AC_NT - 1) / AC_NT));
+  const dim3 g2((unsigned)((total + AC_WT - 1) / AC_WT));
   if (a.dtype == DTREE_BF16)
-    hipLaunchKernelGGL(k_accept_walk<uint16_t>, g2, dim3(AC_NT), 0, st, a, tb);
+    hipLaunchKernelGGL(k_accept_walk<uint16_t>, g2, dim3(AC_WT), 0, st, a, tb);
   else
-    hipLaunchKernelGGL(k_accept_walk<float>, g2, dim3(AC_NT), 0, st, a, tb);
+    hipLaunchKernelGGL(k_accept_walk<float>, g2, dim3(AC_WT), 0, st, a, tb);
   return hipGetLastError();
 }
 
