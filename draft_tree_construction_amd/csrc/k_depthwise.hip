@@ -110,25 +110,29 @@ __global__ __launch_bounds__(DW_NT) void k_dw_transpose_p(const uint16_t *__rest
 
 // ---------------------------------------------------------------- the correction sweep
 template <typename T>
-__global__ __launch_bounds__(DW_NT) void k_dw_corr(DwState s, const T *__restrict__ base, int d, int L, int V,
-                                                   int R, int NG) {
+__global__ __launch_bounds__(DW_NT, 4) void k_dw_corr(DwState s, const T *__restrict__ base, int d, int L, int V,
+                                                      int R, int NG) {
+  // P^T block (32 rows x 128 bytes) shared by the workgroup's four tiles, double buffered;
+  // 16-byte chunk k of row r is stored at chunk k ^ (r & 7), so the A-operand reads (16
+  // lanes on 16 rows) spread over the banks
+  __shared__ u32x4 sP[2][32 * 8];
   const int nct = R * NG;
   const int TG = (nct + 3) >> 2;
   const int i = blockIdx.x, xcd = i & 7, j = i >> 3;
   const int c = xcd + 8 * (j / TG);
   const int g = j - (j / TG) * TG;
   if (c >= DW_NC) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t = g * 4 + wave;
-  if (t >= nct) return;
-  const int r = t / NG;
+  const bool active = t < nct;  // inactive waves still load and synchronise
+  const int r = active ? t / NG : 0;
   const int col = lane & 31, half = lane >> 5;
 
-  const u32x4 *hrow = reinterpret_cast<const u32x4 *>(s.hx + ((size_t)t * 32 + col) * DW_HX);
+  const u32x4 *hrow = reinterpret_cast<const u32x4 *>(s.hx + ((size_t)(active ? t : 0) * 32 + col) * DW_HX);
   bf16x8 bfr[5];
 #pragma unroll
   for (int kb = 0; kb < 5; ++kb) bfr[kb] = as_bf16x8(hrow[2 * kb + half]);
-  const bool wide = s.wide[t] != 0;
+  const bool wide = active && s.wide[t] != 0;
   const T *brow = base + ((size_t)r * L + (d - 1)) * V;
   const int nb32 = (V + 31) >> 5;
   const int blk0 = (int)(((long long)nb32 * c) / DW_NC);
@@ -138,38 +142,50 @@ __global__ __launch_bounds__(DW_NT) void k_dw_corr(DwState s, const T *__restric
 
   double acc = 0.0;
   float m = wide ? -kInf : 0.f;
-  for (int blk = blk0; blk < blk1; ++blk) {
-    const int v = (blk << 5) + col;
-    bf16x8 a0 = zero8, a1 = zero8, a2 = zero8, a3 = zero8, a4 = zero8;
-    if (v < V) {
-      const u32x4 *pr = reinterpret_cast<const u32x4 *>(s.PT + (size_t)v * 64 + half * 32);
-      a0 = as_bf16x8(pr[0]);
-      a1 = as_bf16x8(pr[1]);
-      a2 = as_bf16x8(pr[2]);
-      a3 = as_bf16x8(pr[3]);
-      if (half == 0) {
-        uint32_t w0 = 0x3F80u;
-        if constexpr (kBf16) w0 |= ((uint32_t)reinterpret_cast<const uint16_t *>(brow)[v]) << 16;
-        a4 = as_bf16x8(u32x4{w0, 0u, 0u, 0u});
-      }
-    }
+  // P^T and the base row as buffers: rows past V read zero (masked below)
+  const __amdgpu_buffer_rsrc_t prs =
+      __builtin_amdgcn_make_buffer_rsrc(s.PT, (short)0, V * 64 * (int)sizeof(uint16_t), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(brow), (short)0, V * (int)sizeof(T), 0x00020000);
+  const int lrow = tid >> 3, lchk = tid & 7;  // this thread's 16 bytes of each block
+  auto gload = [&](int blk, u32x4 &gp, uint32_t &bw) {
+    const bool in = blk < blk1;
+    gp = (u32x4)__builtin_amdgcn_raw_buffer_load_b128(prs, in ? ((blk << 5) + lrow) * 128 + lchk * 16 : 0x7FFFFFF0, 0, 0);
+    if constexpr (kBf16)
+      bw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(brs, in ? ((blk << 5) + col) * 2 : 0x7FFFFFF0, 0, 0);
+    else
+      bw = 0u;
+  };
+  auto lstore = [&](int buf, const u32x4 &gp) { sP[buf][lrow * 8 + (lchk ^ (lrow & 7))] = gp; };
+  auto consume_blk = [&](int blk, int buf, uint32_t bw) {
+    u32x4 pa[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pa[q] = sP[buf][col * 8 + ((half * 4 + q) ^ (col & 7))];
+    const bf16x8 a4 = half == 0 ? as_bf16x8(u32x4{0x3F80u | (bw << 16), 0u, 0u, 0u}) : zero8;
     f32x16 z = {};
-    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfr[0], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfr[1], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, bfr[2], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, bfr[3], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[0]), bfr[0], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[1]), bfr[1], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[2]), bfr[2], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[3]), bfr[3], z, 0, 0, 0);
     z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a4, bfr[4], z, 0, 0, 0);
     // lane holds rows (blk*32 + 8*(q/4) + 4*half + q%4) of its branch column
     const int vbase = (blk << 5) + 4 * half;
     float x[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int vr = vbase + 8 * (q >> 2) + (q & 3);
-      float xv = z[q];
-      if constexpr (!kBf16) {
-        if (vr < V) xv += load_elt(brow, (size_t)vr);
+    for (int q = 0; q < 16; ++q) x[q] = z[q];
+    if constexpr (!kBf16) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int vr = vbase + 8 * (q >> 2) + (q & 3);
+        if (vr < V) x[q] += load_elt(brow, (size_t)vr);
       }
-      x[q] = (vr < V) ? xv : -kInf;
+    }
+    if ((blk << 5) + 32 > V) {  // the last block: rows past V do not exist
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int vr = vbase + 8 * (q >> 2) + (q & 3);
+        x[q] = vr < V ? x[q] : -kInf;
+      }
     }
     if (!wide) {
       float a = 0.f, b = 0.f;
@@ -194,6 +210,32 @@ __global__ __launch_bounds__(DW_NT) void k_dw_corr(DwState s, const T *__restric
         acc += (double)a;
       }
     }
+  };
+  // step blk: block blk is in LDS buffer blk & 1; block blk + 1 goes from registers to the
+  // other buffer, its register slot is refilled with block blk + 1 + PD; one barrier per step
+  constexpr int PD = 3;
+  u32x4 G[PD];
+  uint32_t BW[PD];
+#pragma unroll
+  for (int q = 0; q < PD; ++q) gload(blk0 + q, G[q], BW[q]);
+  lstore(0, G[0]);
+  uint32_t bw_cur = BW[0];
+  gload(blk0 + PD, G[0], BW[0]);
+  __syncthreads();
+  for (int b0 = blk0; b0 < blk1; b0 += PD) {
+#pragma unroll
+    for (int q = 0; q < PD; ++q) {
+      const int blk = b0 + q;
+      if (blk < blk1) {
+        const int nq = (q + 1) % PD;  // register slot holding block blk + 1
+        lstore((blk + 1 - blk0) & 1, G[nq]);
+        const uint32_t bw_next = BW[nq];
+        gload(blk + 1 + PD, G[nq], BW[nq]);
+        if (active) consume_blk(blk, (blk - blk0) & 1, bw_cur);
+        bw_cur = bw_next;
+        __syncthreads();
+      }
+    }
   }
   // merge the two row halves of this branch column (lanes l and l ^ 32)
   const float mo = __shfl_xor(m, 32, 64);
@@ -203,7 +245,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_corr(DwState s, const T *__restric
   if (mm != -kInf) {
     tot = ((m == -kInf) ? 0.0 : acc * exp((double)m - (double)mm)) + ((mo == -kInf) ? 0.0 : ao * exp((double)mo - (double)mm));
   }
-  if (half == 0) {
+  if (active && half == 0) {
     const size_t o = ((size_t)t * 32 + col) * DW_NC + c;
     s.part_s[o] = tot;
     s.part_m[o] = mm;
