@@ -70,7 +70,7 @@ def main():
     root = torch.from_numpy(root_h).to(dev)
 
     ws_m = torch.empty(dt.workspace_size(dt.OP_MARGINAL, R, L, V, 64, 64), dtype=torch.uint8, device=dev)
-    ws_d = torch.empty(dt.workspace_size(dt.OP_DEPTHWISE, R, L, V, 8, 128, 32, 64), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(dt.workspace_size(dt.OP_DEPTHWISE, R, L, V, 8, 128, 32, 64, 1024), dtype=torch.uint8, device=dev)
     ws_g = torch.empty(dt.workspace_size(dt.OP_GATED, R, L, V, 0, 60), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(dt.workspace_size(dt.OP_ACCEPT, R, L, V, 0, 64), dtype=torch.uint8, device=dev)
     t_m, t_d, t_g = dt.Tree.empty(R, 64, dev), dt.Tree.empty(R, 128, dev), dt.Tree.empty(R, 60, dev)

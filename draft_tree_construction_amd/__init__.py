@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     u64 = ctypes.c_uint64
     L.dtree_workspace_size.restype = sz
-    L.dtree_workspace_size.argtypes = [i32] * 8
+    L.dtree_workspace_size.argtypes = [i32] * 9
     L.dtree_topk_logsoftmax.restype = i32
     L.dtree_topk_logsoftmax.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.build_tree_marginal.restype = i32
@@ -109,8 +109,9 @@ def _require_device(*ts):
             raise ValueError("inputs must be contiguous device tensors")
 
 
-def workspace_size(op: int, R: int, L: int, V: int, K: int = 0, B_or_N: int = 0, W: int = 0, rank: int = 0) -> int:
-    return int(lib().dtree_workspace_size(op, R, L, V, K, B_or_N, W, rank))
+def workspace_size(op: int, R: int, L: int, V: int, K: int = 0, B_or_N: int = 0, W: int = 0, rank: int = 0,
+                   d_model: int = 0) -> int:
+    return int(lib().dtree_workspace_size(op, R, L, V, K, B_or_N, W, rank, d_model))
 
 
 def _workspace(nbytes: int, dev) -> torch.Tensor:
@@ -184,7 +185,7 @@ def build_tree_depthwise(logits: torch.Tensor, E: torch.Tensor, U: torch.Tensor,
     d_model, rank = U.shape[1], U.shape[2]
     dev = logits.device
     out = Tree.empty(R, B, dev) if out is None else out
-    ws = _workspace(workspace_size(OP_DEPTHWISE, R, L, V, K, B, W, rank), dev) if ws is None else ws
+    ws = _workspace(workspace_size(OP_DEPTHWISE, R, L, V, K, B, W, rank, d_model), dev) if ws is None else ws
     st = out.c_struct()
     _check(lib().build_tree_depthwise(_ptr(logits), _dtype(logits), R, L, V, _ptr(E), _ptr(U), _ptr(P), d_model, rank,
                                       _ptr(root_tok), K, W, B, float(beta), ctypes.byref(st), _ptr(ws), ws.numel(),

@@ -82,7 +82,7 @@ const char *dtree_status_string(int status) {
 
 const char *dtree_last_error(void) { return g_last_error.c_str(); }
 
-size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank) {
+size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank, int d_model) {
   if (R < 0 || L < 1 || V < 1) return 0;
   switch (op) {
     case DTREE_OP_TOPK:
@@ -96,8 +96,8 @@ size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int 
     case DTREE_OP_GATED:
       return a1_bytes(R * L, V, gated_k(V));
     case DTREE_OP_DEPTHWISE:
-      if (K < 1 || W < 1 || B_or_N < 1) return 0;
-      return a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B_or_N, rank);
+      if (K < 1 || W < 1 || B_or_N < 1 || d_model < 1) return 0;
+      return a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B_or_N, rank, d_model);
     case DTREE_OP_ACCEPT:
       if (B_or_N < 1) return 0;
       return dt::accept_ws_bytes(R, L, V, B_or_N);
@@ -187,7 +187,8 @@ int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, con
   if (rc) return rc;
   if (R == 0) return DTREE_OK;
   if (!logits || !E || !U || !P || !root_tok) return fail(DTREE_E_INVAL, "an input pointer is NULL");
-  const size_t need = a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B, rank);
+  if (((uintptr_t)E | (uintptr_t)U | (uintptr_t)P) & 15) return fail(DTREE_E_INVAL, "E, U and P must be 16-byte aligned");
+  const size_t need = a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B, rank, d_model);
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
   hipStream_t st = static_cast<hipStream_t>(s);
   A1Ws a1 = a1_carve(ws, R * L, K);

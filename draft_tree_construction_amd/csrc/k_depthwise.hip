@@ -55,6 +55,7 @@ DT_INLINE uint16_t f32_to_bf16_up(float x) {
 
 struct DwState {
   uint16_t *PT;     // [V][64]: row v holds P[k][v] at slot half*32 + kb*8 + e, k = 16kb + 8half + e
+  uint16_t *UT;     // [L][64][dm]: U transposed, row j of depth d holds U[d][k][j] over k
   float *pmax;      // [64]: max_v |P[j][v]|
   uint16_t *hx;     // [R][Wp][80]
   float *bref;      // [R][Wp]: ref of each branch (a bf16 value)
@@ -83,28 +84,70 @@ __global__ void k_dw_zero_f32(float *p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0.f;
 }
 
-// PT tile of 64 tokens; also max_v |P[k][v]| per k folded in with an integer atomic max
-// (non-negative floats order like their bit patterns).
+// PT tile of 256 tokens; also max_v |P[k][v]| per k, reduced over the tile and folded in
+// with an integer atomic max (non-negative floats order like their bit patterns). 16-byte
+// loads and stores when every row of P is 16-byte aligned (V % 8 == 0) and the tile is
+// whole, element-wise otherwise.
+constexpr int DW_TP = 256;
 __global__ __launch_bounds__(DW_NT) void k_dw_transpose_p(const uint16_t *__restrict__ P, int V, uint16_t *PT,
                                                           float *pmax) {
-  __shared__ uint16_t tile[64][66];
-  const int v0 = blockIdx.x * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += DW_NT) {
-    const int k = i >> 6, vv = i & 63;
-    tile[k][vv] = (v0 + vv < V) ? P[(size_t)k * V + v0 + vv] : (uint16_t)0;
+  __shared__ uint16_t tile[64][DW_TP + 8];
+  __shared__ float qmax[4][64];
+  const int v0 = blockIdx.x * DW_TP;
+  const bool vec = (V & 7) == 0 && v0 + DW_TP <= V;
+  if (vec) {
+    for (int i = threadIdx.x; i < 64 * (DW_TP / 8); i += DW_NT) {
+      const int k = i / (DW_TP / 8), q = i % (DW_TP / 8);
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(P + (size_t)k * V + v0 + q * 8);
+      *reinterpret_cast<u32x4 *>(&tile[k][q * 8]) = x;
+    }
+  } else {
+    for (int i = threadIdx.x; i < 64 * DW_TP; i += DW_NT) {
+      const int k = i / DW_TP, vv = i % DW_TP;
+      tile[k][vv] = (v0 + vv < V) ? P[(size_t)k * V + v0 + vv] : (uint16_t)0;
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += DW_NT) {
-    const int vv = i >> 6, slot = i & 63;
-    const int half = slot >> 5, kb = (slot >> 3) & 3, e = slot & 7;
-    const int k = 16 * kb + 8 * half + e;
-    if (v0 + vv < V) PT[(size_t)(v0 + vv) * 64 + slot] = tile[k][vv];
+  // PT row v, 16-byte piece q holds slots 8q..8q+7: k = 16 (q & 3) + 8 (q >> 2) + e
+  for (int i = threadIdx.x; i < DW_TP * 8; i += DW_NT) {
+    const int vv = i >> 3, q = i & 7;
+    if (v0 + vv >= V) continue;
+    const int kb = 16 * (q & 3) + 8 * (q >> 2);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[kb + 2 * e][vv] | ((uint32_t)tile[kb + 2 * e + 1][vv] << 16);
+    *reinterpret_cast<u32x4 *>(PT + (size_t)(v0 + vv) * 64 + q * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
+  {
+    const int k = threadIdx.x & 63, qq = threadIdx.x >> 6;
+    float m = 0.f;
+    for (int vv = qq * (DW_TP / 4); vv < (qq + 1) * (DW_TP / 4); ++vv) m = fmaxf(m, fabsf(bf16_to_f32(tile[k][vv])));
+    qmax[qq][k] = m;
+  }
+  __syncthreads();
   if (threadIdx.x < 64) {
     const int k = threadIdx.x;
-    float m = 0.f;
-    for (int vv = 0; vv < 64; ++vv) m = fmaxf(m, fabsf(bf16_to_f32(tile[k][vv])));
+    const float m = fmaxf(fmaxf(qmax[0][k], qmax[1][k]), fmaxf(qmax[2][k], qmax[3][k]));
     atomicMax(reinterpret_cast<unsigned int *>(pmax) + k, __float_as_uint(m));
+  }
+}
+
+// UT[d][j][k] = U[d][k][j]: tiles of 64 k-rows (d_model % 64 == 0), 16-byte loads and stores.
+__global__ __launch_bounds__(DW_NT) void k_dw_transpose_u(const uint16_t *__restrict__ U, int dm, uint16_t *UT) {
+  __shared__ uint16_t tile[64][72];
+  const int d = blockIdx.y, k0 = blockIdx.x * 64;
+  const uint16_t *Ud = U + (size_t)d * dm * 64;
+  for (int i = threadIdx.x; i < 64 * 8; i += DW_NT) {
+    const int k = i >> 3, q = i & 7;
+    *reinterpret_cast<u32x4 *>(&tile[k][q * 8]) = *reinterpret_cast<const u32x4 *>(Ud + (size_t)(k0 + k) * 64 + q * 8);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 8; i += DW_NT) {
+    const int j = i >> 3, q = i & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[q * 8 + 2 * e][j] | ((uint32_t)tile[q * 8 + 2 * e + 1][j] << 16);
+    *reinterpret_cast<u32x4 *>(UT + ((size_t)d * 64 + j) * dm + k0 + q * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -255,52 +298,88 @@ __global__ __launch_bounds__(DW_NT, 4) void k_dw_corr(DwState s, const T *__rest
 // ---------------------------------------------------------------- next-depth branch state
 // For the `keep` new branches of round r (tokens tok[]), h = bf16(E[tok] @ U[dn-1]) via MFMA,
 // the bf16 upper bound ref, and the hx rows / tile flags. Called by the whole block.
+// Wave (ct, kh) computes columns 32ct..32ct+31 over k in [kh dm/2, (kh+1) dm/2), ascending;
+// both operands are 16-byte loads (E rows, and the transposed U), four k-steps in flight.
+struct DwBranchLds {
+  float hacc[2][2][32][33];  // [column tile][k half][row][column within the tile]
+  float bnd[64];
+};
 DT_INLINE void dw_branch_state(const DwState &s, const DwDev &a, int r, int dn, int keep, const int *tok,
-                               const double *sc, float (*hacc)[32][65], float *bnd) {
+                               const double *sc, DwBranchLds &L) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   const int ct = wave & 1, kh = wave >> 1;
   const int kspan = a.dm >> 1;
-  const uint16_t *Ud = a.U + (size_t)(dn - 1) * a.dm * 64;
+  const int nsteps = kspan >> 4;
   const float mnext = a.zk[((size_t)r * a.L + (dn - 1)) * a.K];
-  const int nrt = (a.Wp + 31) >> 5;
-  for (int rt = 0; rt < nrt; ++rt) {
-    const int bi = rt * 32 + col;  // A row (branch) for this lane
-    const bool live = bi < keep;
-    const uint16_t *erow = live ? a.E + (size_t)tok[bi] * a.dm : nullptr;
-    f32x16 acc = {};
-    for (int k0 = kh * kspan; k0 < (kh + 1) * kspan; k0 += 16) {
-      bf16x8 av = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-      if (live) av = as_bf16x8(*reinterpret_cast<const u32x4 *>(erow + k0 + 8 * half));
-      uint16_t bb[8];
-      const int jc = 32 * ct + col;
+  const int nrt = (a.Wp + 31) >> 5;  // 1 or 2 row tiles
+  const uint16_t *brow = s.UT + ((size_t)(dn - 1) * 64 + 32 * ct + col) * a.dm + kh * kspan + 8 * half;
+  const uint16_t *erow[2];
+  bool live[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bb[e] = Ud[(size_t)(k0 + 8 * half + e) * 64 + jc];
-      bf16x8 bv;
-      __builtin_memcpy(&bv, bb, 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  for (int rt = 0; rt < 2; ++rt) {
+    const int bi = rt * 32 + col;
+    live[rt] = rt < nrt && bi < keep;
+    erow[rt] = (live[rt] ? a.E + (size_t)tok[bi] * a.dm : a.E) + kh * kspan + 8 * half;  // dead rows read row 0
+  }
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  constexpr int PF = 4;
+  u32x4 Bq[PF], A0q[PF], A1q[PF];
+  auto ld = [&](int st, int q) {
+    const int o = (st < nsteps ? st : 0) * 16;
+    Bq[q] = *reinterpret_cast<const u32x4 *>(brow + o);
+    A0q[q] = *reinterpret_cast<const u32x4 *>(erow[0] + o);
+    A1q[q] = *reinterpret_cast<const u32x4 *>(erow[1] + o);
+  };
+#pragma unroll
+  for (int q = 0; q < PF; ++q) ld(q, q);
+  f32x16 acc0 = {}, acc1 = {};
+  for (int st0 = 0; st0 < nsteps; st0 += PF) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int st = st0 + q;
+      if (st < nsteps) {
+        const bf16x8 bv = as_bf16x8(Bq[q]);
+        const bf16x8 a0 = as_bf16x8(live[0] ? A0q[q] : zero);
+        const bf16x8 a1 = as_bf16x8(live[1] ? A1q[q] : zero);
+        ld(st + PF, q);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv, acc0, 0, 0, 0);
+        if (nrt > 1) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, acc1, 0, 0, 0);
+      }
     }
+  }
+  for (int rt = 0; rt < nrt; ++rt) {
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = 8 * (q >> 2) + 4 * half + (q & 3);
-      hacc[kh][row][32 * ct + col] = acc[q];
+      L.hacc[ct][kh][row][col] = rt == 0 ? acc0[q] : acc1[q];
     }
     __syncthreads();
-    // h = bf16(sum of the two k halves); rows x 64 columns, 256 threads
+    // h = bf16(sum of the two k halves); 32 rows x 64 columns, 256 threads
+    float prod[32 * 64 / DW_NT];
+    int nprod = 0;
     for (int idx = threadIdx.x; idx < 32 * 64; idx += DW_NT) {
       const int row = idx >> 6, jj = idx & 63;
       const int b = rt * 32 + row;
-      const float hv = hacc[0][row][jj] + hacc[1][row][jj];
+      const float hv = L.hacc[jj >> 5][0][row][jj & 31] + L.hacc[jj >> 5][1][row][jj & 31];
       const uint16_t hb = (b < keep) ? f32_to_bf16_rne(hv) : (uint16_t)0;
       s.hx[((size_t)r * a.Wp + b) * DW_HX + jj] = hb;
-      hacc[0][row][jj] = fabsf(bf16_to_f32(hb)) * s.pmax[jj];
+      prod[nprod++] = fabsf(bf16_to_f32(hb)) * s.pmax[jj];
+    }
+    __syncthreads();
+    // bound per row: sum over j of |h_j| max|P_j.|, in column order
+    nprod = 0;
+    for (int idx = threadIdx.x; idx < 32 * 64; idx += DW_NT) {
+      const int row = idx >> 6, jj = idx & 63;
+      L.hacc[jj >> 5][0][row][jj & 31] = prod[nprod++];
     }
     __syncthreads();
     if (threadIdx.x < 32) {
       const int row = threadIdx.x;
       const int b = rt * 32 + row;
       float bound = 0.f;
-      for (int jj = 0; jj < 64; ++jj) bound += hacc[0][row][jj];
+      for (int jj = 0; jj < 64; ++jj) bound += L.hacc[jj >> 5][0][row][jj & 31];
       uint16_t *hr = s.hx + ((size_t)r * a.Wp + b) * DW_HX;
       if (b < keep) {
         const bool wide = bound > DW_WIDE;
@@ -309,27 +388,26 @@ DT_INLINE void dw_branch_state(const DwState &s, const DwDev &a, int r, int dn, 
         s.bs[(size_t)r * a.Wp + b] = sc[b];
         hr[64] = (uint16_t)(ru ^ 0x8000u);  // -ref
         hr[65] = 0x3F80u;                   // 1.0
-        bnd[b] = wide ? 1.f : 0.f;
+        L.bnd[b] = wide ? 1.f : 0.f;
       } else {
         hr[64] = 0;
         hr[65] = 0;
       }
       for (int e = 66; e < DW_HX; ++e) hr[e] = 0;
     }
-    __syncthreads();
   }
+  __syncthreads();
   if (threadIdx.x < a.NG) {
     int w = 0;
     for (int b = threadIdx.x * 32; b < (threadIdx.x + 1) * 32; ++b)
-      if (b < keep && bnd[b] != 0.f) w = 1;
+      if (b < keep && L.bnd[b] != 0.f) w = 1;
     s.wide[r * a.NG + threadIdx.x] = w;
   }
   if (threadIdx.x == 0) s.nb[r] = keep;
 }
 
 __global__ __launch_bounds__(DW_NT) void k_dw_init(DwState s, DwDev a) {
-  __shared__ float hacc[2][32][65];
-  __shared__ float bnd[64];
+  __shared__ DwBranchLds lb;
   __shared__ int tok[1];
   __shared__ double sc[1];
   const int r = blockIdx.x;
@@ -339,7 +417,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_init(DwState s, DwDev a) {
     sc[0] = 0.0;
   }
   __syncthreads();
-  dw_branch_state(s, a, r, 1, 1, tok, sc, hacc, bnd);
+  dw_branch_state(s, a, r, 1, 1, tok, sc, lb);
 }
 
 // ---------------------------------------------------------------- per-round selection
@@ -348,91 +426,92 @@ __global__ __launch_bounds__(DW_NT) void k_dw_select(DwState s, DwDev a, int d) 
   __shared__ double lse_b[64], s_b[64];
   __shared__ double cs[DW_CH];
   __shared__ int cpk[DW_CH];
-  __shared__ uint16_t cidx[DW_CH];
   __shared__ int ktok[64];
   __shared__ double ks[64];
-  __shared__ float hacc[2][32][65];
-  __shared__ float bnd[64];
+  __shared__ DwBranchLds lb;
   const int r = blockIdx.x;
   const int nbp = s.nb[r];
   const size_t rowl = (size_t)r * a.L + (d - 1);
-  // 1. LSE of every branch from the chunk partials; old branch state into LDS
-  if (threadIdx.x < nbp) {
-    const int b = threadIdx.x;
-    const size_t o = ((size_t)r * a.Wp + b) * DW_NC;
+  // 1. LSE of every branch from its DW_NC chunk partials: 8 lanes per branch, each folding
+  //    DW_NC/8 partials; the partial sums are relative to their own maxima
+  for (int b0 = 0; b0 < nbp; b0 += DW_NT / 8) {
+    const int b = b0 + (threadIdx.x >> 3), l8 = threadIdx.x & 7;
+    const bool ok = b < nbp;
+    const size_t o = ((size_t)r * a.Wp + (ok ? b : 0)) * DW_NC + l8 * (DW_NC / 8);
     float M = -kInf;
-    for (int c = 0; c < DW_NC; ++c) M = fmaxf(M, s.part_m[o + c]);
+#pragma unroll
+    for (int c = 0; c < DW_NC / 8; ++c) M = fmaxf(M, s.part_m[o + c]);
+#pragma unroll
+    for (int x = 1; x < 8; x <<= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
     double S = 0.0;
-    for (int c = 0; c < DW_NC; ++c) {
+#pragma unroll
+    for (int c = 0; c < DW_NC / 8; ++c) {
       const float mc = s.part_m[o + c];
-      if (mc != -kInf) S += s.part_s[o + c] * exp((double)mc - (double)M);
+      if (mc != -kInf) S += s.part_s[o + c] * (double)__builtin_amdgcn_exp2f((mc - M) * kLog2e);
     }
-    lse_b[b] = (double)s.bref[(size_t)r * a.Wp + b] + (double)M + log(S);
-    s_b[b] = s.bs[(size_t)r * a.Wp + b];
+#pragma unroll
+    for (int x = 1; x < 8; x <<= 1) S += __shfl_xor(S, x, 64);
+    if (ok && l8 == 0) {
+      lse_b[b] = (double)s.bref[(size_t)r * a.Wp + b] + (double)M + log(S);
+      s_b[b] = s.bs[(size_t)r * a.Wp + b];
+    }
   }
   for (int idx = threadIdx.x; idx < nbp * 64; idx += DW_NT) {
     const int b = idx >> 6, jj = idx & 63;
     hb[b][jj] = bf16_to_f32(s.hx[((size_t)r * a.Wp + b) * DW_HX + jj]);
   }
   __syncthreads();
-  // 2. score every child (b, k): z = base(c) + h_b . P[:, c]
+  // 2. score every child (b, k): z = base(c) + h_b . P[:, c] (slot order of the PT row)
   const int nc = nbp * a.K;
   for (int t = threadIdx.x; t < nc; t += DW_NT) {
     const int b = t / a.K, k = t - b * a.K;
     const int cid = a.ids[rowl * a.K + k];
-    const uint16_t *pr = s.PT + (size_t)cid * 64;
+    const u32x4 *pr = reinterpret_cast<const u32x4 *>(s.PT + (size_t)cid * 64);
     float corr = 0.f;
-#pragma unroll 8
-    for (int slot = 0; slot < 64; ++slot) {
-      const int half = slot >> 5, kb = (slot >> 3) & 3, e = slot & 7;
-      corr += hb[b][16 * kb + 8 * half + e] * bf16_to_f32(pr[slot]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 v = pr[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int slot = 8 * q + e;
+        const int half = slot >> 5, kb = (slot >> 3) & 3, ee = slot & 7;
+        const uint16_t bits = (uint16_t)(e & 1 ? w[e >> 1] >> 16 : w[e >> 1] & 0xFFFFu);
+        corr += hb[b][16 * kb + 8 * half + ee] * bf16_to_f32(bits);
+      }
     }
     const float z = a.zk[rowl * a.K + k] + corr;
     double sc = (s_b[b] + ((double)z - lse_b[b])) + (double)a.beta;
     cs[t] = fmin(sc, s_b[b]);
     cpk[t] = (b << 16) | k;
   }
-  const int npw = next_pow2(nc > 1 ? nc : 1);
-  for (int i = threadIdx.x; i < npw; i += DW_NT) cidx[i] = (uint16_t)i;
   __syncthreads();
-  // 3. order children by (s desc, parent position asc, rank asc)
-  for (int kk = 2; kk <= npw; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < npw; i += DW_NT) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int x = cidx[i], y = cidx[ixj];
-          bool x_first;
-          if (x >= nc) x_first = false;
-          else if (y >= nc) x_first = true;
-          else x_first = (cs[x] != cs[y]) ? (cs[x] > cs[y]) : (cpk[x] < cpk[y]);
-          const bool up = (i & kk) == 0;
-          if (up ? !x_first : x_first) {
-            cidx[i] = (uint16_t)y;
-            cidx[ixj] = (uint16_t)x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // 4. S_d = the first W children
+  // 3. S_d = the first W children by (s desc, parent position asc, rank asc): each child's
+  //    place is the number of children before it
   const int keep = nc < a.W ? nc : a.W;
-  for (int i = threadIdx.x; i < keep; i += DW_NT) {
-    const int x = cidx[i];
-    const size_t o = rowl * a.W + i;
-    const int k = cpk[x] & 0xFFFF;
-    const int tk = a.ids[rowl * a.K + k];
-    s.sup_s[o] = cs[x];
-    s.sup_pk[o] = cpk[x];
-    s.sup_tok[o] = tk;
-    ktok[i] = tk;
-    ks[i] = cs[x];
+  for (int t = threadIdx.x; t < nc; t += DW_NT) {
+    const double st = cs[t];
+    const int pt = cpk[t];
+    int before = 0;
+    for (int y = 0; y < nc; ++y) {
+      const double sy = cs[y];
+      before += (sy > st) || (sy == st && cpk[y] < pt);
+    }
+    if (before < keep) {
+      const size_t o = rowl * a.W + before;
+      const int k = pt & 0xFFFF;
+      const int tk = a.ids[rowl * a.K + k];
+      s.sup_s[o] = st;
+      s.sup_pk[o] = pt;
+      s.sup_tok[o] = tk;
+      ktok[before] = tk;
+      ks[before] = st;
+    }
   }
   if (threadIdx.x == 0) s.sup_n[rowl] = keep;
   __syncthreads();
-  // 5. state of the new branches for the next depth
-  if (d < a.L) dw_branch_state(s, a, r, d + 1, keep, ktok, ks, hacc, bnd);
+  // 4. state of the new branches for the next depth
+  if (d < a.L) dw_branch_state(s, a, r, d + 1, keep, ktok, ks, lb);
 }
 
 // ---------------------------------------------------------------- deferred Top-B + outputs
@@ -518,10 +597,10 @@ __global__ __launch_bounds__(DW_NT) void k_dw_final(DwState s, DwDev a, TreeOut 
 
 // ---------------------------------------------------------------- host side
 struct DwLayout {
-  size_t PT, pmax, hx, bref, bs, nb, wide, part_s, part_m, sup_s, sup_pk, sup_tok, sup_n, total;
+  size_t PT, UT, pmax, hx, bref, bs, nb, wide, part_s, part_m, sup_s, sup_pk, sup_tok, sup_n, total;
 };
 
-static DwLayout dw_layout(int R, int L, int V, int W) {
+static DwLayout dw_layout(int R, int L, int V, int W, int dm) {
   const int Wp = (W + 31) / 32 * 32, NG = Wp / 32;
   DwLayout l;
   size_t o = 0;
@@ -531,6 +610,7 @@ static DwLayout dw_layout(int R, int L, int V, int W) {
     return at;
   };
   l.PT = take((size_t)V * 64 * 2);
+  l.UT = take((size_t)L * 64 * dm * 2);
   l.pmax = take(64 * sizeof(float));
   l.hx = take((size_t)R * Wp * DW_HX * 2);
   l.bref = take((size_t)R * Wp * sizeof(float));
@@ -547,19 +627,20 @@ static DwLayout dw_layout(int R, int L, int V, int W) {
   return l;
 }
 
-size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank) {
+size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank, int dm) {
   (void)K;
   (void)B;
   (void)rank;
-  return dw_layout(R, L, V, W).total;
+  return dw_layout(R, L, V, W, dm).total;
 }
 
 hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
                             void *ws, hipStream_t st) {
-  const DwLayout l = dw_layout(a.R, a.L, a.V, a.W);
+  const DwLayout l = dw_layout(a.R, a.L, a.V, a.W, a.dm);
   char *w = static_cast<char *>(ws);
   DwState s;
   s.PT = reinterpret_cast<uint16_t *>(w + l.PT);
+  s.UT = reinterpret_cast<uint16_t *>(w + l.UT);
   s.pmax = reinterpret_cast<float *>(w + l.pmax);
   s.hx = reinterpret_cast<uint16_t *>(w + l.hx);
   s.bref = reinterpret_cast<float *>(w + l.bref);
@@ -590,7 +671,8 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   dv.beta = a.beta;
 
   hipLaunchKernelGGL(k_dw_zero_f32, dim3(1), dim3(64), 0, st, s.pmax, 64);
-  hipLaunchKernelGGL(k_dw_transpose_p, dim3((a.V + 63) / 64), dim3(DW_NT), 0, st, a.P, a.V, s.PT, s.pmax);
+  hipLaunchKernelGGL(k_dw_transpose_p, dim3((a.V + DW_TP - 1) / DW_TP), dim3(DW_NT), 0, st, a.P, a.V, s.PT, s.pmax);
+  hipLaunchKernelGGL(k_dw_transpose_u, dim3(a.dm / 64, a.L), dim3(DW_NT), 0, st, a.U, a.dm, s.UT);
   hipLaunchKernelGGL(k_dw_init, dim3(a.R), dim3(DW_NT), 0, st, s, dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -49,7 +49,7 @@ struct DepthwiseArgs {
   const uint16_t *E, *U, *P;
   const int32_t *root_tok;
 };
-size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank);
+size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank, int dm);
 hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
                             void *ws, hipStream_t st);
 

@@ -94,10 +94,10 @@ typedef struct {
 /*
  * Bytes of workspace an operation needs. `op` is a dtree_op; unused size arguments are
  * ignored: TOPK(rows = R*L, V, K), MARGINAL(R, L, V, K, B), DEPTHWISE(R, L, V, K, B, W,
- * rank), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap). Returns 0 for an
- * unknown op or invalid sizes.
+ * rank, d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap). Returns 0
+ * for an unknown op or invalid sizes.
  */
-size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank);
+size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank, int d_model);
 
 /*
  * Row log-softmax and top-K (DDTree blog 3.3: top-K tokens per position with their
@@ -127,8 +127,9 @@ int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int 
  * children are kept, then the B best of the whole super-tree by s_beta.
  * E [V][d_model], U [L][d_model][rank], P [rank][V] are bf16 bits; root_tok [R] int32.
  * Needs beta <= 0, rank == 64, d_model % 64 == 0, K <= DTREE_MAX_K, W <= 64, W*K <= 1024,
- * L*W <= 2048, B <= DTREE_MAX_CAP, out->cap == B. root_tok values must lie in [0, V) (an
- * out-of-range value is read as token 0).
+ * L*W <= 2048, B <= DTREE_MAX_CAP, out->cap == B. E, U and P must be 16-byte aligned
+ * (else DTREE_E_INVAL). root_tok values must lie in [0, V) (an out-of-range value is read
+ * as token 0).
  */
 int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, const uint16_t *E,
                          const uint16_t *U, const uint16_t *P, int d_model, int rank,

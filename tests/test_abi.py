@@ -38,7 +38,8 @@ def test_workspace_sizes():
     assert ws(dt.OP_MARGINAL, 64, 16, 151936, 64, 64) > 64 * 16 * 64 * 8
     assert ws(dt.OP_GATED, 64, 16, 151936, 0, 60) > 0
     assert ws(dt.OP_ACCEPT, 64, 16, 151936, 0, 64) > 64 * 65 * 2374 * 8
-    assert ws(dt.OP_DEPTHWISE, 64, 16, 151936, 8, 128, 32, 64) > 0
+    assert ws(dt.OP_DEPTHWISE, 64, 16, 151936, 8, 128, 32, 64, 1024) > 0
+    assert ws(dt.OP_DEPTHWISE, 64, 16, 151936, 8, 128, 32, 64, 0) == 0   # needs d_model
     assert ws(dt.OP_TOPK, 1024, 1, 151936, 64) == 0          # no split needed
     assert ws(dt.OP_TOPK, 2, 1, 151936, 64) > 0              # split rows need partials
     assert ws(99, 1, 1, 1) == 0
@@ -100,11 +101,12 @@ def test_gated_validation():
 
 def test_depthwise_validation():
     L = dt.lib()
-    def call(rank=64, dm=1024, K=8, W=32, B=128, beta=-0.5, cap=128):
+    def call(rank=64, dm=1024, K=8, W=32, B=128, beta=-0.5, cap=128, E=FAKE):
         t = tree(cap)
-        return L.build_tree_depthwise(FAKE, 0, 4, 16, 151936, FAKE, FAKE, FAKE, dm, rank, FAKE, K, W, B, beta,
+        return L.build_tree_depthwise(FAKE, 0, 4, 16, 151936, E, FAKE, FAKE, dm, rank, FAKE, K, W, B, beta,
                                       ctypes.byref(t), FAKE, 0, None)
     assert call(beta=0.1) == -2
+    assert call(E=ctypes.c_void_p(0x1002)) == -1   # E, U, P are read with 16-byte loads
     assert call(rank=32) == -4
     assert call(dm=1000) == -4
     assert call(W=65) == -4
