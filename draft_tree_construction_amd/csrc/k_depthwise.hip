@@ -7,25 +7,36 @@
 // W children (over all branches) form S_d, and finally the B best nodes of the super-tree
 // by s are kept (Lemma 1: a sort replaces the best-first heap).
 //
-// Design (gfx950), per depth two launches plus a final one:
-//  * k_dw_corr -- the only O(V) work and the only dense contraction. For a tile of 32
-//    branches of one round and a 32-token block, one v_mfma_f32_32x32x16_bf16 chain
+// Design (gfx950). The head is Markov: a branch's correction depends only on its last token,
+// and every branch at depth d >= 2 ends in a token of C_{d-1}. So each (round, depth) has at
+// most K distinct states -- the candidates of the previous depth (the root's token at depth
+// 1) -- all known once the row sweep has run, and their (h, logsumexp z) are computed once
+// for all depths in three launches, leaving the per-depth selection to table lookups:
+//  * k_dw_states -- h = bf16(E[tok] @ U_d) for every state by MFMA (32 states x 64 columns
+//    per workgroup), its bound ref and the B-operand row [h, -ref, one-hot base column, 1].
+//  * k_dw_corr -- the only O(V) work and the only dense contraction. For a tile of 32 states
+//    (one depth, up to 8 rounds) and a 32-token block, one v_mfma_f32_32x32x16_bf16 chain
 //    (K = 64 + 16) computes z - ref directly: the A operand is P^T (pre-transposed so each
-//    lane loads 64 contiguous bytes) with two extra columns [1, base(v)], the B operand is
-//    [h_b, -ref_b, 1] and stays in registers for the whole V range. ref_b is a bf16 upper
-//    bound of max_v z_b (max base + sum_j |h_j| max|P_j.|), so exp(z - ref) <= 1 needs no
-//    running max; each lane owns one branch column and 16 rows, so the sum of
-//    exponentials accumulates per lane with no cross-lane reduction until the end.
-//    Workgroups are mapped XCD-aware: all tiles of one V chunk run on one XCD, so that
-//    chunk of P^T is read from HBM once and then served from that XCD's L2.
-//    (If the bound is loose -- over 10 nats -- the tile switches to a running max.)
-//  * k_dw_select -- one workgroup per round: reduce the chunk partials to LSE_b, score the
-//    W*K children (candidate logits recomputed with the same h and P), sort in LDS, keep
-//    the top W as S_d, then compute the next depth's h = E[tok] @ U with MFMA.
-//  * k_dw_final -- one workgroup per round: Top-B over the super-tree, parent array, mask.
+//    lane loads 64 contiguous bytes) with extra columns [1, base of each round in the tile,
+//    mask], the B operand stays in registers for the whole V range; a state's one-hot row
+//    picks its round's base logits, and the mask column (0, or -inf past V) is matched by a
+//    row of ones. ref is a bf16 upper bound of max_v z (max base + sum_j |h_j| max|P_j.|),
+//    so exp(z - ref) <= 1 needs no running max; each lane owns one state column and 16 rows
+//    and accumulates with no cross-lane reduction until the end. A workgroup holds sixteen
+//    tiles that share each P^T block, staged through LDS (triple buffered) and mapped
+//    XCD-aware so a V chunk of P^T is read from HBM once per XCD. (If the bound is loose --
+//    over 10 nats -- the tile switches to a running max.)
+//  * k_dw_lq -- every state's logsumexp from the chunk partials and its log q~ row over the
+//    K candidates of its depth, z[c] = base(c) + h . P[:, c] (all depths in one launch).
+//  * k_dw_tree -- one workgroup per round walks the depths: the W * K children scored from
+//    their parents' log q~ rows and ranked, the top W kept as S_d; then the Top-B of the
+//    super-tree, parents and mask. Only this chain is sequential, and it reads no HBM but
+//    the next depth's log q~ rows, prefetched a depth ahead.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "treeio.hpp"
+
+#include <type_traits>
 
 namespace dt {
 
@@ -33,10 +44,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int DW_NT = 256;
-constexpr int DW_NC = 64;      // V chunks (partials per branch)
-constexpr int DW_HX = 80;      // branch row: h (64), -ref, 1, zero padding
+constexpr int DW_CNT = 1024;   // correction sweep workgroup: DW_CW tiles share each staged P^T block
+constexpr int DW_CW = DW_CNT / 64;
+constexpr int DW_NC = 64;      // V chunks (partials per state)
+constexpr int DW_HX = 80;      // state row: h (64), -ref, one-hot base (8), 1 (mask), zero padding
 constexpr int DW_SUP = 2048;   // super-tree nodes per round (L * W)
 constexpr int DW_CH = 1024;    // children per depth (W * K)
+constexpr int DW_MAXP = 8;     // rounds per tile (base columns)
 constexpr float DW_WIDE = 10.f;
 
 DT_INLINE bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
@@ -53,29 +67,49 @@ DT_INLINE uint16_t f32_to_bf16_up(float x) {
   return (uint16_t)((u >> 16) + 1);
 }
 
+// State slots: depth-major, then round, then candidate rank, Kp >= 4 slots per (depth,
+// round) (a power of two), rounds padded to Rp so a 32-slot tile never spans two depths
+// and holds np = 32 / Kp rounds (one round per two tiles when Kp = 64).
+struct DwDims {
+  int R, L, V, K, W, B, dm;
+  int Kp, np, Rp, S, ntile;
+};
+static DwDims dw_dims(int R, int L, int V, int K, int W, int B, int dm) {
+  DwDims g;
+  g.R = R;
+  g.L = L;
+  g.V = V;
+  g.K = K;
+  g.W = W;
+  g.B = B;
+  g.dm = dm;
+  g.Kp = 4;
+  while (g.Kp < K) g.Kp <<= 1;
+  g.np = g.Kp <= 32 ? 32 / g.Kp : 1;
+  g.Rp = (R + g.np - 1) / g.np * g.np;
+  g.S = L * g.Rp * g.Kp;
+  g.ntile = g.S / 32;
+  return g;
+}
+DT_INLINE int dw_slot(const DwDims &g, int d, int r, int k) { return ((d - 1) * g.Rp + r) * g.Kp + k; }
+
 struct DwState {
   uint16_t *PT;     // [V][64]: row v holds P[k][v] at slot half*32 + kb*8 + e, k = 16kb + 8half + e
   uint16_t *UT;     // [L][64][dm]: U transposed, row j of depth d holds U[d][k][j] over k
   float *pmax;      // [64]: max_v |P[j][v]|
-  uint16_t *hx;     // [R][Wp][80]
-  float *bref;      // [R][Wp]: ref of each branch (a bf16 value)
-  double *bs;       // [R][Wp]: branch scores
-  int *nb;          // [R]: branches at the current depth
-  int *wide;        // [R][NG]: tile uses a running max
-  double *part_s;   // [R*Wp][NC]
-  float *part_m;    // [R*Wp][NC]
-  double *sup_s;    // [R][L][W]
-  int *sup_pk;      // [R][L][W]: ppos << 16 | rank
-  int *sup_tok;     // [R][L][W]
-  int *sup_n;       // [R][L]
+  uint16_t *hx;     // [S][DW_HX]: B-operand rows of the states
+  float *bref;      // [S]: ref of each state (a bf16 value)
+  int *wide;        // [ntile]: tile uses a running max
+  double *part_s;   // [S][NC]
+  float *part_m;    // [S][NC]
+  double *lq;       // [S][K]: log q~ of each candidate of the state's depth
 };
 
 struct DwDev {
   const float *zk;     // [R*L][K] candidate base logits
   const int32_t *ids;  // [R*L][K]
-  const uint16_t *E, *U;
+  const uint16_t *E;
   const int32_t *root_tok;
-  int R, L, V, K, W, Wp, NG, B, dm;
   float beta;
 };
 
@@ -151,89 +185,245 @@ __global__ __launch_bounds__(DW_NT) void k_dw_transpose_u(const uint16_t *__rest
   }
 }
 
+// ---------------------------------------------------------------- state rows
+// One workgroup per tile of 32 slots (one depth d): token of each slot (the root's at depth
+// 1, else candidate k of row d - 1; dead slots have none), h = bf16(E[tok] @ U_d) by MFMA --
+// wave (ct, kh) computes columns 32ct..32ct+31 over k in [kh dm/2, (kh+1) dm/2), ascending,
+// operands by 16-byte loads four k-steps ahead -- then the bound and the B-operand row.
+__global__ __launch_bounds__(DW_NT) void k_dw_states(DwState s, DwDev a, DwDims g, int base_bf16) {
+  __shared__ float hacc[2][2][32][33];
+  __shared__ int stok[32];
+  const int t = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int ct = wave & 1, kh = wave >> 1;
+  const int per_d = g.Rp * g.Kp;
+  const int d = 1 + (t * 32) / per_d;
+  if (threadIdx.x < 32) {
+    const int sl = t * 32 + threadIdx.x;
+    const int rem = sl % per_d, r = rem / g.Kp, k = rem % g.Kp;
+    int tk = -1;
+    if (r < g.R) {
+      if (d == 1) {
+        if (k == 0) {
+          const int t0 = a.root_tok[r];
+          tk = (t0 >= 0 && t0 < g.V) ? t0 : 0;  // out-of-range root tokens are a precondition violation
+        }
+      } else if (k < g.K) {
+        tk = a.ids[((size_t)r * g.L + (d - 2)) * g.K + k];
+      }
+    }
+    stok[threadIdx.x] = tk;
+  }
+  __syncthreads();
+  const int kspan = g.dm >> 1;
+  const int nsteps = kspan >> 4;
+  const bool live = stok[col] >= 0;
+  const uint16_t *brow = s.UT + ((size_t)(d - 1) * 64 + 32 * ct + col) * g.dm + kh * kspan + 8 * half;
+  const uint16_t *erow = a.E + (size_t)(live ? stok[col] : 0) * g.dm + kh * kspan + 8 * half;  // dead rows read row 0
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  constexpr int PF = 4;
+  u32x4 Bq[PF], Aq[PF];
+  auto ld = [&](int st, int q) {
+    const int o = (st < nsteps ? st : 0) * 16;
+    Bq[q] = *reinterpret_cast<const u32x4 *>(brow + o);
+    Aq[q] = *reinterpret_cast<const u32x4 *>(erow + o);
+  };
+#pragma unroll
+  for (int q = 0; q < PF; ++q) ld(q, q);
+  f32x16 acc = {};
+  for (int st0 = 0; st0 < nsteps; st0 += PF) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int st = st0 + q;
+      if (st < nsteps) {
+        const bf16x8 bv = as_bf16x8(Bq[q]);
+        const bf16x8 av = as_bf16x8(live ? Aq[q] : zero);
+        ld(st + PF, q);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int row = 8 * (q >> 2) + 4 * half + (q & 3);
+    hacc[ct][kh][row][col] = acc[q];
+  }
+  __syncthreads();
+  // h = bf16(sum of the two k halves); 32 rows x 64 columns
+  float prod[32 * 64 / DW_NT];
+  int np = 0;
+  for (int idx = threadIdx.x; idx < 32 * 64; idx += DW_NT) {
+    const int row = idx >> 6, jj = idx & 63;
+    const float hv = hacc[jj >> 5][0][row][jj & 31] + hacc[jj >> 5][1][row][jj & 31];
+    const uint16_t hb = stok[row] >= 0 ? f32_to_bf16_rne(hv) : (uint16_t)0;
+    s.hx[((size_t)t * 32 + row) * DW_HX + jj] = hb;
+    prod[np++] = fabsf(bf16_to_f32(hb)) * s.pmax[jj];
+  }
+  __syncthreads();
+  np = 0;
+  for (int idx = threadIdx.x; idx < 32 * 64; idx += DW_NT) {
+    const int row = idx >> 6, jj = idx & 63;
+    hacc[jj >> 5][0][row][jj & 31] = prod[np++];
+  }
+  __syncthreads();
+  __shared__ int swide;
+  if (threadIdx.x == 0) swide = 0;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    const int row = threadIdx.x;
+    const int sl = t * 32 + row;
+    const int rem = sl % per_d, r = rem / g.Kp;
+    uint16_t *hr = s.hx + (size_t)sl * DW_HX;
+    for (int e = 64; e < DW_HX; ++e) hr[e] = 0;
+    hr[73] = 0x3F80u;  // matches the mask column of A (0, or -inf past V)
+    if (stok[row] >= 0) {
+      // bound per row: sum over j of |h_j| max|P_j.|, in column order
+      float bound = 0.f;
+      for (int jj = 0; jj < 64; ++jj) bound += hacc[jj >> 5][0][row][jj & 31];
+      const float mnext = a.zk[((size_t)r * g.L + (d - 1)) * g.K];
+      const bool wide = bound > DW_WIDE;
+      const uint16_t ru = f32_to_bf16_up(wide ? mnext : mnext + bound * 1.0001f + 1e-6f);
+      s.bref[sl] = bf16_to_f32(ru);
+      hr[64] = (uint16_t)(ru ^ 0x8000u);  // -ref
+      if (base_bf16) hr[65 + (g.Kp <= 32 ? (sl & 31) / g.Kp : 0)] = 0x3F80u;  // this round's base column
+      if (wide) atomicOr(&swide, 1);
+    } else {
+      s.bref[sl] = 0.f;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) s.wide[t] = swide;
+}
+
 // ---------------------------------------------------------------- the correction sweep
 template <typename T>
-__global__ __launch_bounds__(DW_NT, 4) void k_dw_corr(DwState s, const T *__restrict__ base, int d, int L, int V,
-                                                      int R, int NG) {
-  // P^T block (32 rows x 128 bytes) shared by the workgroup's four tiles, double buffered;
-  // 16-byte chunk k of row r is stored at chunk k ^ (r & 7), so the A-operand reads (16
-  // lanes on 16 rows) spread over the banks
-  __shared__ u32x4 sP[2][32 * 8];
-  const int nct = R * NG;
-  const int TG = (nct + 3) >> 2;
+__global__ __launch_bounds__(DW_CNT) void k_dw_corr(DwState s, const T *__restrict__ base, DwDims g) {
+  // P^T block (32 rows x 128 bytes) shared by the workgroup's sixteen tiles, triple
+  // buffered; rows are 144 bytes apart, so the A-operand reads (16 lanes on 16 rows) hit
+  // distinct banks and a lane's four chunks sit at fixed offsets
+  constexpr int SPR = 9;  // row pitch in 16-byte chunks
+  __shared__ u32x4 sP[3][32 * SPR];
+  __shared__ uint16_t sB[3][DW_CW][DW_MAXP][32];  // each tile's rounds' base logits of the block
+  const int V = g.V;
+  const int nct = g.ntile;
+  const int TG = (nct + DW_CW - 1) / DW_CW;
   const int i = blockIdx.x, xcd = i & 7, j = i >> 3;
   const int c = xcd + 8 * (j / TG);
-  const int g = j - (j / TG) * TG;
+  const int gi = j - (j / TG) * TG;
   if (c >= DW_NC) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t = g * 4 + wave;
+  // the wave index is uniform: tile and the quantities built from it live in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int t = gi * DW_CW + wave;
   const bool active = t < nct;  // inactive waves still load and synchronise
-  const int r = active ? t / NG : 0;
   const int col = lane & 31, half = lane >> 5;
+  const int per_d = g.Rp * g.Kp;
+  auto tile_d = [&](int tt) { return 1 + (tt * 32) / per_d; };
+  auto tile_r0 = [&](int tt) { return ((tt * 32) % per_d) / g.Kp; };
 
   const u32x4 *hrow = reinterpret_cast<const u32x4 *>(s.hx + ((size_t)(active ? t : 0) * 32 + col) * DW_HX);
   bf16x8 bfr[5];
 #pragma unroll
   for (int kb = 0; kb < 5; ++kb) bfr[kb] = as_bf16x8(hrow[2 * kb + half]);
   const bool wide = active && s.wide[t] != 0;
-  const T *brow = base + ((size_t)r * L + (d - 1)) * V;
   const int nb32 = (V + 31) >> 5;
   const int blk0 = (int)(((long long)nb32 * c) / DW_NC);
   const int blk1 = (int)(((long long)nb32 * (c + 1)) / DW_NC);
   constexpr bool kBf16 = sizeof(T) == 2;
-  const bf16x8 zero8 = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  const int np = g.np;
+  // fp32 bases are added after the MFMA: this lane's state column belongs to round r0 + col / Kp
+  const T *lane_base = base + ((size_t)min(active ? tile_r0(t) + (g.Kp <= 32 ? col / g.Kp : 0) : 0, g.R - 1) * g.L +
+                               (active ? tile_d(t) : 1) - 1) * V;
 
   double acc = 0.0;
   float m = wide ? -kInf : 0.f;
-  // P^T and the base row as buffers: rows past V read zero (masked below)
-  const __amdgpu_buffer_rsrc_t prs =
-      __builtin_amdgcn_make_buffer_rsrc(s.PT, (short)0, V * 64 * (int)sizeof(uint16_t), 0x00020000);
-  const __amdgpu_buffer_rsrc_t brs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(brow), (short)0, V * (int)sizeof(T), 0x00020000);
-  const int lrow = tid >> 3, lchk = tid & 7;  // this thread's 16 bytes of each block
-  auto gload = [&](int blk, u32x4 &gp, uint32_t &bw) {
-    const bool in = blk < blk1;
-    gp = (u32x4)__builtin_amdgcn_raw_buffer_load_b128(prs, in ? ((blk << 5) + lrow) * 128 + lchk * 16 : 0x7FFFFFF0, 0, 0);
-    if constexpr (kBf16)
-      bw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(brs, in ? ((blk << 5) + col) * 2 : 0x7FFFFFF0, 0, 0);
-    else
-      bw = 0u;
+  // threads 0..255 stage the P^T block (16 bytes each); for bf16 bases, threads 256..767
+  // stage the base logits of each tile's rounds (one 16-byte piece of 8 tokens each)
+  const bool stager = tid < 256;
+  const int lrow = (tid >> 3) & 31, lchk = tid & 7;
+  const int bi = tid - 256;
+  const int btile_w = (bi >> 5) & (DW_CW - 1), bpair = (bi >> 2) & 7, bp = bi & 3;
+  const bool bstager = kBf16 && tid >= 256 && bi < DW_CW * DW_MAXP * 4;
+  const int btile = gi * DW_CW + btile_w;
+  const int bround = btile < nct ? tile_r0(btile) + bpair : 0;
+  const bool bvalid_row = bstager && btile < nct && bpair < np && bround < g.R;
+  const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(base) +
+                         ((size_t)(bvalid_row ? bround : 0) * g.L + (bvalid_row ? tile_d(btile) : 1) - 1) * V;
+  const bool bvec = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0;
+  // one 16-byte load per thread and block (BVEC: whole 8-token pieces, V % 8 == 0 and
+  // 16-byte aligned rows),
+  // branch-free: rows and base pieces past V are clamped to valid memory (the mask column
+  // makes those rows -inf, so the values do not matter); threads that stage nothing re-read
+  // the first P^T row. Without BVEC the base pieces are read element-wise.
+  auto gload = [&](auto bvec_tag, int blk, u32x4 &gp) {
+    constexpr bool BVEC = decltype(bvec_tag)::value;
+    const int prow = min((blk << 5) + lrow, V - 1);
+    const int v = (blk << 5) + bp * 8;
+    if constexpr (BVEC || !kBf16) {
+      const uint16_t *addr = stager ? s.PT + (size_t)prow * 64 + lchk * 8
+                                    : (bstager ? bsrc + (v < V ? v : 0) : s.PT);
+      gp = *reinterpret_cast<const u32x4 *>(addr);
+    } else {
+      if (stager) {
+        gp = *reinterpret_cast<const u32x4 *>(s.PT + (size_t)prow * 64 + lchk * 8);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v0e = v + 2 * e;
+          const uint32_t lo = (bstager && v0e < V) ? bsrc[v0e] : 0u;
+          const uint32_t hi = (bstager && v0e + 1 < V) ? bsrc[v0e + 1] : 0u;
+          w[e] = lo | (hi << 16);
+        }
+        gp = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
   };
-  auto lstore = [&](int buf, const u32x4 &gp) { sP[buf][lrow * 8 + (lchk ^ (lrow & 7))] = gp; };
-  auto consume_blk = [&](int blk, int buf, uint32_t bw) {
+  auto lstore = [&](int buf, const u32x4 &gp) {
+    if (stager) sP[buf][lrow * SPR + lchk] = gp;
+    else if (bstager) *reinterpret_cast<u32x4 *>(&sB[buf][btile_w][bpair][bp * 8]) = gp;
+  };
+  auto mfma_blk = [&](int blk, int buf) {
+    // extra A columns 64..79: [1, base of the tile's rounds 0..7, mask, 0 ...]; a row past V
+    // gets -inf in the mask column (matched by a row of ones in every state's B), so
+    // z = -inf and its exponential is 0 with no per-element mask
+    const uint32_t mask = ((blk << 5) + col < V) ? 0u : 0xFF80u;
+    uint32_t b[DW_MAXP];
+#pragma unroll
+    for (int p = 0; p < DW_MAXP; ++p) b[p] = (kBf16 && p < np) ? (uint32_t)sB[buf][wave][p][col] : 0u;
+    u32x4 ext;
+    if (half == 0)
+      ext = u32x4{0x3F80u | (b[0] << 16), b[1] | (b[2] << 16), b[3] | (b[4] << 16), b[5] | (b[6] << 16)};
+    else
+      ext = u32x4{b[7] | (mask << 16), 0u, 0u, 0u};
     u32x4 pa[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) pa[q] = sP[buf][col * 8 + ((half * 4 + q) ^ (col & 7))];
-    const bf16x8 a4 = half == 0 ? as_bf16x8(u32x4{0x3F80u | (bw << 16), 0u, 0u, 0u}) : zero8;
+    for (int q = 0; q < 4; ++q) pa[q] = sP[buf][col * SPR + half * 4 + q];
     f32x16 z = {};
     z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[0]), bfr[0], z, 0, 0, 0);
     z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[1]), bfr[1], z, 0, 0, 0);
     z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[2]), bfr[2], z, 0, 0, 0);
     z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(pa[3]), bfr[3], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a4, bfr[4], z, 0, 0, 0);
-    // lane holds rows (blk*32 + 8*(q/4) + 4*half + q%4) of its branch column
+    z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ext), bfr[4], z, 0, 0, 0);
+    return z;
+  };
+  auto exps_blk = [&](int blk, const f32x16 &z) {
+    // lane holds rows (blk*32 + 8*(q/4) + 4*half + q%4) of its state column
     const int vbase = (blk << 5) + 4 * half;
     float x[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) x[q] = z[q];
-    if constexpr (!kBf16) {
+    if constexpr (!kBf16) {  // fp32 base rows are added here (rows past V are already -inf)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int vr = vbase + 8 * (q >> 2) + (q & 3);
-        if (vr < V) x[q] += load_elt(brow, (size_t)vr);
-      }
-    }
-    if ((blk << 5) + 32 > V) {  // the last block: rows past V do not exist
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int vr = vbase + 8 * (q >> 2) + (q & 3);
-        x[q] = vr < V ? x[q] : -kInf;
+        if (vr < V) x[q] += load_elt(lane_base, (size_t)vr);
       }
     }
     if (!wide) {
-      float a = 0.f, b = 0.f;
+      float a = __builtin_amdgcn_exp2f(x[0] * kLog2e), b = __builtin_amdgcn_exp2f(x[1] * kLog2e);
 #pragma unroll
-      for (int q = 0; q < 16; q += 2) {
+      for (int q = 2; q < 16; q += 2) {
         a += __builtin_amdgcn_exp2f(x[q] * kLog2e);
         b += __builtin_amdgcn_exp2f(x[q + 1] * kLog2e);
       }
@@ -254,33 +444,47 @@ __global__ __launch_bounds__(DW_NT, 4) void k_dw_corr(DwState s, const T *__rest
       }
     }
   };
-  // step blk: block blk is in LDS buffer blk & 1; block blk + 1 goes from registers to the
-  // other buffer, its register slot is refilled with block blk + 1 + PD; one barrier per step
+  // step blk: blocks blk and blk + 1 are in LDS buffers blk % 3 and (blk + 1) % 3; block
+  // blk + 2 goes from registers to the third buffer and its register slot is refilled with
+  // block blk + 2 + PD; the MFMA chain of block blk + 1 is issued before the exponentials
+  // of block blk, so the matrix cores run while the wave works on the vector units
   constexpr int PD = 3;
-  u32x4 G[PD];
-  uint32_t BW[PD];
+  auto pipeline = [&](auto bvec_tag) {
+    u32x4 G[PD];
 #pragma unroll
-  for (int q = 0; q < PD; ++q) gload(blk0 + q, G[q], BW[q]);
-  lstore(0, G[0]);
-  uint32_t bw_cur = BW[0];
-  gload(blk0 + PD, G[0], BW[0]);
-  __syncthreads();
-  for (int b0 = blk0; b0 < blk1; b0 += PD) {
+    for (int q = 0; q < PD; ++q) gload(bvec_tag, blk0 + q, G[q]);
+    lstore(0, G[0]);
+    lstore(1, G[1]);
+    gload(bvec_tag, blk0 + PD, G[0]);
+    gload(bvec_tag, blk0 + PD + 1, G[1]);
+    __syncthreads();
+    f32x16 zc = {};
+    if (active) zc = mfma_blk(blk0, 0);
+    for (int b0 = blk0; b0 < blk1; b0 += PD) {
 #pragma unroll
-    for (int q = 0; q < PD; ++q) {
-      const int blk = b0 + q;
-      if (blk < blk1) {
-        const int nq = (q + 1) % PD;  // register slot holding block blk + 1
-        lstore((blk + 1 - blk0) & 1, G[nq]);
-        const uint32_t bw_next = BW[nq];
-        gload(blk + 1 + PD, G[nq], BW[nq]);
-        if (active) consume_blk(blk, (blk - blk0) & 1, bw_cur);
-        bw_cur = bw_next;
-        __syncthreads();
+      for (int q = 0; q < PD; ++q) {
+        const int blk = b0 + q;
+        if (blk < blk1) {
+          const int k = blk - blk0;
+          const int nq = (q + 2) % PD;  // register slot holding block blk + 2
+          lstore((k + 2) % 3, G[nq]);
+          gload(bvec_tag, blk + 2 + PD, G[nq]);
+          if (active) {
+            // past the last block this reads a stale buffer; the result is never used
+            const f32x16 zn = mfma_blk(blk + 1, (k + 1) % 3);
+            exps_blk(blk, zc);
+            zc = zn;
+          }
+          __syncthreads();
+        }
       }
     }
-  }
-  // merge the two row halves of this branch column (lanes l and l ^ 32)
+  };
+  if (bvec)
+    pipeline(std::true_type{});
+  else
+    pipeline(std::false_type{});
+  // merge the two row halves of this state column (lanes l and l ^ 32)
   const float mo = __shfl_xor(m, 32, 64);
   const double ao = __shfl_xor(acc, 32, 64);
   const float mm = fmaxf(m, mo);
@@ -295,149 +499,24 @@ __global__ __launch_bounds__(DW_NT, 4) void k_dw_corr(DwState s, const T *__rest
   }
 }
 
-// ---------------------------------------------------------------- next-depth branch state
-// For the `keep` new branches of round r (tokens tok[]), h = bf16(E[tok] @ U[dn-1]) via MFMA,
-// the bf16 upper bound ref, and the hx rows / tile flags. Called by the whole block.
-// Wave (ct, kh) computes columns 32ct..32ct+31 over k in [kh dm/2, (kh+1) dm/2), ascending;
-// both operands are 16-byte loads (E rows, and the transposed U), four k-steps in flight.
-struct DwBranchLds {
-  float hacc[2][2][32][33];  // [column tile][k half][row][column within the tile]
-  float bnd[64];
-};
-DT_INLINE void dw_branch_state(const DwState &s, const DwDev &a, int r, int dn, int keep, const int *tok,
-                               const double *sc, DwBranchLds &L) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 31, half = lane >> 5;
-  const int ct = wave & 1, kh = wave >> 1;
-  const int kspan = a.dm >> 1;
-  const int nsteps = kspan >> 4;
-  const float mnext = a.zk[((size_t)r * a.L + (dn - 1)) * a.K];
-  const int nrt = (a.Wp + 31) >> 5;  // 1 or 2 row tiles
-  const uint16_t *brow = s.UT + ((size_t)(dn - 1) * 64 + 32 * ct + col) * a.dm + kh * kspan + 8 * half;
-  const uint16_t *erow[2];
-  bool live[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int bi = rt * 32 + col;
-    live[rt] = rt < nrt && bi < keep;
-    erow[rt] = (live[rt] ? a.E + (size_t)tok[bi] * a.dm : a.E) + kh * kspan + 8 * half;  // dead rows read row 0
-  }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  constexpr int PF = 4;
-  u32x4 Bq[PF], A0q[PF], A1q[PF];
-  auto ld = [&](int st, int q) {
-    const int o = (st < nsteps ? st : 0) * 16;
-    Bq[q] = *reinterpret_cast<const u32x4 *>(brow + o);
-    A0q[q] = *reinterpret_cast<const u32x4 *>(erow[0] + o);
-    A1q[q] = *reinterpret_cast<const u32x4 *>(erow[1] + o);
-  };
-#pragma unroll
-  for (int q = 0; q < PF; ++q) ld(q, q);
-  f32x16 acc0 = {}, acc1 = {};
-  for (int st0 = 0; st0 < nsteps; st0 += PF) {
-#pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      const int st = st0 + q;
-      if (st < nsteps) {
-        const bf16x8 bv = as_bf16x8(Bq[q]);
-        const bf16x8 a0 = as_bf16x8(live[0] ? A0q[q] : zero);
-        const bf16x8 a1 = as_bf16x8(live[1] ? A1q[q] : zero);
-        ld(st + PF, q);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv, acc0, 0, 0, 0);
-        if (nrt > 1) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, acc1, 0, 0, 0);
-      }
-    }
-  }
-  for (int rt = 0; rt < nrt; ++rt) {
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = 8 * (q >> 2) + 4 * half + (q & 3);
-      L.hacc[ct][kh][row][col] = rt == 0 ? acc0[q] : acc1[q];
-    }
-    __syncthreads();
-    // h = bf16(sum of the two k halves); 32 rows x 64 columns, 256 threads
-    float prod[32 * 64 / DW_NT];
-    int nprod = 0;
-    for (int idx = threadIdx.x; idx < 32 * 64; idx += DW_NT) {
-      const int row = idx >> 6, jj = idx & 63;
-      const int b = rt * 32 + row;
-      const float hv = L.hacc[jj >> 5][0][row][jj & 31] + L.hacc[jj >> 5][1][row][jj & 31];
-      const uint16_t hb = (b < keep) ? f32_to_bf16_rne(hv) : (uint16_t)0;
-      s.hx[((size_t)r * a.Wp + b) * DW_HX + jj] = hb;
-      prod[nprod++] = fabsf(bf16_to_f32(hb)) * s.pmax[jj];
-    }
-    __syncthreads();
-    // bound per row: sum over j of |h_j| max|P_j.|, in column order
-    nprod = 0;
-    for (int idx = threadIdx.x; idx < 32 * 64; idx += DW_NT) {
-      const int row = idx >> 6, jj = idx & 63;
-      L.hacc[jj >> 5][0][row][jj & 31] = prod[nprod++];
-    }
-    __syncthreads();
-    if (threadIdx.x < 32) {
-      const int row = threadIdx.x;
-      const int b = rt * 32 + row;
-      float bound = 0.f;
-      for (int jj = 0; jj < 64; ++jj) bound += L.hacc[jj >> 5][0][row][jj & 31];
-      uint16_t *hr = s.hx + ((size_t)r * a.Wp + b) * DW_HX;
-      if (b < keep) {
-        const bool wide = bound > DW_WIDE;
-        const uint16_t ru = f32_to_bf16_up(wide ? mnext : mnext + bound * 1.0001f + 1e-6f);
-        s.bref[(size_t)r * a.Wp + b] = bf16_to_f32(ru);
-        s.bs[(size_t)r * a.Wp + b] = sc[b];
-        hr[64] = (uint16_t)(ru ^ 0x8000u);  // -ref
-        hr[65] = 0x3F80u;                   // 1.0
-        L.bnd[b] = wide ? 1.f : 0.f;
-      } else {
-        hr[64] = 0;
-        hr[65] = 0;
-      }
-      for (int e = 66; e < DW_HX; ++e) hr[e] = 0;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < a.NG) {
-    int w = 0;
-    for (int b = threadIdx.x * 32; b < (threadIdx.x + 1) * 32; ++b)
-      if (b < keep && L.bnd[b] != 0.f) w = 1;
-    s.wide[r * a.NG + threadIdx.x] = w;
-  }
-  if (threadIdx.x == 0) s.nb[r] = keep;
-}
-
-__global__ __launch_bounds__(DW_NT) void k_dw_init(DwState s, DwDev a) {
-  __shared__ DwBranchLds lb;
-  __shared__ int tok[1];
-  __shared__ double sc[1];
-  const int r = blockIdx.x;
-  if (threadIdx.x == 0) {
-    const int t0 = a.root_tok[r];
-    tok[0] = (t0 >= 0 && t0 < a.V) ? t0 : 0;  // out-of-range root tokens are a precondition violation
-    sc[0] = 0.0;
-  }
-  __syncthreads();
-  dw_branch_state(s, a, r, 1, 1, tok, sc, lb);
-}
-
-// ---------------------------------------------------------------- per-round selection
-__global__ __launch_bounds__(DW_NT) void k_dw_select(DwState s, DwDev a, int d) {
-  __shared__ float hb[64][65];
-  __shared__ double lse_b[64], s_b[64];
-  __shared__ double cs[DW_CH];
-  __shared__ int cpk[DW_CH];
-  __shared__ int ktok[64];
-  __shared__ double ks[64];
-  __shared__ DwBranchLds lb;
-  const int r = blockIdx.x;
-  const int nbp = s.nb[r];
-  const size_t rowl = (size_t)r * a.L + (d - 1);
-  // 1. LSE of every branch from its DW_NC chunk partials: 8 lanes per branch, each folding
-  //    DW_NC/8 partials; the partial sums are relative to their own maxima
-  for (int b0 = 0; b0 < nbp; b0 += DW_NT / 8) {
-    const int b = b0 + (threadIdx.x >> 3), l8 = threadIdx.x & 7;
-    const bool ok = b < nbp;
-    const size_t o = ((size_t)r * a.Wp + (ok ? b : 0)) * DW_NC + l8 * (DW_NC / 8);
+// ---------------------------------------------------------------- log q~ of every state
+// One workgroup per tile of 32 slots: the state's logsumexp from its DW_NC chunk partials
+// (8 lanes per state, each folding DW_NC/8 partials relative to their own maxima), then
+// log q~(c | state) = z[c] - LSE for the K candidates c of the depth, with
+// z[c] = base(c) + h . P[:, c] summed in the slot order of the P^T row. None of this depends
+// on which branches get selected, so it runs for all depths at once.
+__global__ __launch_bounds__(DW_NT) void k_dw_lq(DwState s, DwDev a, DwDims g) {
+  __shared__ double lse[32];
+  __shared__ float hb[32][65];
+  __shared__ int stok_ok[32];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int per_d = g.Rp * g.Kp;
+  const int d = 1 + (t * 32) / per_d;
+  const int K = g.K;
+  {
+    const int row = tid >> 3, l8 = tid & 7;
+    const int sl = t * 32 + row;
+    const size_t o = (size_t)sl * DW_NC + l8 * (DW_NC / 8);
     float M = -kInf;
 #pragma unroll
     for (int c = 0; c < DW_NC / 8; ++c) M = fmaxf(M, s.part_m[o + c]);
@@ -451,21 +530,25 @@ __global__ __launch_bounds__(DW_NT) void k_dw_select(DwState s, DwDev a, int d) 
     }
 #pragma unroll
     for (int x = 1; x < 8; x <<= 1) S += __shfl_xor(S, x, 64);
-    if (ok && l8 == 0) {
-      lse_b[b] = (double)s.bref[(size_t)r * a.Wp + b] + (double)M + log(S);
-      s_b[b] = s.bs[(size_t)r * a.Wp + b];
+    if (l8 == 0) {
+      const int rem = sl % per_d, r = rem / g.Kp, k = rem % g.Kp;
+      const bool ok = r < g.R && (d == 1 ? k == 0 : k < K);
+      lse[row] = (double)s.bref[sl] + (double)M + log(S);
+      stok_ok[row] = ok;
     }
   }
-  for (int idx = threadIdx.x; idx < nbp * 64; idx += DW_NT) {
-    const int b = idx >> 6, jj = idx & 63;
-    hb[b][jj] = bf16_to_f32(s.hx[((size_t)r * a.Wp + b) * DW_HX + jj]);
+  for (int idx = tid; idx < 32 * 64; idx += DW_NT) {
+    const int row = idx >> 6, jj = idx & 63;
+    hb[row][jj] = bf16_to_f32(s.hx[((size_t)t * 32 + row) * DW_HX + jj]);
   }
   __syncthreads();
-  // 2. score every child (b, k): z = base(c) + h_b . P[:, c] (slot order of the PT row)
-  const int nc = nbp * a.K;
-  for (int t = threadIdx.x; t < nc; t += DW_NT) {
-    const int b = t / a.K, k = t - b * a.K;
-    const int cid = a.ids[rowl * a.K + k];
+  for (int it = tid; it < 32 * K; it += DW_NT) {
+    const int row = it / K, kc = it - row * K;
+    if (!stok_ok[row]) continue;
+    const int sl = t * 32 + row;
+    const int r = (sl % per_d) / g.Kp;
+    const size_t ci = ((size_t)r * g.L + (d - 1)) * K + kc;
+    const int cid = a.ids[ci];
     const u32x4 *pr = reinterpret_cast<const u32x4 *>(s.PT + (size_t)cid * 64);
     float corr = 0.f;
 #pragma unroll
@@ -475,133 +558,216 @@ __global__ __launch_bounds__(DW_NT) void k_dw_select(DwState s, DwDev a, int d) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int slot = 8 * q + e;
-        const int half = slot >> 5, kb = (slot >> 3) & 3, ee = slot & 7;
+        const int hf = slot >> 5, kb = (slot >> 3) & 3, ee = slot & 7;
         const uint16_t bits = (uint16_t)(e & 1 ? w[e >> 1] >> 16 : w[e >> 1] & 0xFFFFu);
-        corr += hb[b][16 * kb + 8 * half + ee] * bf16_to_f32(bits);
+        corr += hb[row][16 * kb + 8 * hf + ee] * bf16_to_f32(bits);
       }
     }
-    const float z = a.zk[rowl * a.K + k] + corr;
-    double sc = (s_b[b] + ((double)z - lse_b[b])) + (double)a.beta;
-    cs[t] = fmin(sc, s_b[b]);
-    cpk[t] = (b << 16) | k;
+    const float z = a.zk[ci] + corr;
+    s.lq[(size_t)sl * K + kc] = (double)z - lse[row];
   }
-  __syncthreads();
-  // 3. S_d = the first W children by (s desc, parent position asc, rank asc): each child's
-  //    place is the number of children before it
-  const int keep = nc < a.W ? nc : a.W;
-  for (int t = threadIdx.x; t < nc; t += DW_NT) {
-    const double st = cs[t];
-    const int pt = cpk[t];
-    int before = 0;
-    for (int y = 0; y < nc; ++y) {
-      const double sy = cs[y];
-      before += (sy > st) || (sy == st && cpk[y] < pt);
-    }
-    if (before < keep) {
-      const size_t o = rowl * a.W + before;
-      const int k = pt & 0xFFFF;
-      const int tk = a.ids[rowl * a.K + k];
-      s.sup_s[o] = st;
-      s.sup_pk[o] = pt;
-      s.sup_tok[o] = tk;
-      ktok[before] = tk;
-      ks[before] = st;
-    }
-  }
-  if (threadIdx.x == 0) s.sup_n[rowl] = keep;
-  __syncthreads();
-  // 4. state of the new branches for the next depth
-  if (d < a.L) dw_branch_state(s, a, r, d + 1, keep, ktok, ks, lb);
 }
 
-// ---------------------------------------------------------------- deferred Top-B + outputs
-__global__ __launch_bounds__(DW_NT) void k_dw_final(DwState s, DwDev a, TreeOut out) {
-  __shared__ double fs[DW_SUP];
-  __shared__ int fdp[DW_SUP];  // depth << 16 | pos
-  __shared__ uint16_t fidx[DW_SUP];
-  __shared__ int off[DTREE_MAX_L + 2], cnt[DTREE_MAX_L + 2];
-  __shared__ int opar[DTREE_MAX_CAP + 1], otok[DTREE_MAX_CAP + 1], odep[DTREE_MAX_CAP + 1];
-  __shared__ float osc[DTREE_MAX_CAP + 1];
+// ---------------------------------------------------------------- per-round tree
+// One workgroup per round: the depths in order (children scored from the log q~ rows of
+// their parents' states, the best W kept), then the deferred Top-B and the outputs.
+struct DwTreeLds {
+  double lqs[64 * 64];       // this depth's log q~ rows, [state][candidate]
+  double bs[64];             // current branches: score, state index
+  int bk[64];
+  double cs[DW_CH];          // children (padded to a multiple of 8)
+  int cpk[DW_CH];
+  double fs[DW_SUP];         // the super-tree, S_1 .. S_L: score, parent position << 16 | rank
+  int fpk[DW_SUP];
+  int off[DTREE_MAX_L + 2], cnt[DTREE_MAX_L + 2];
+  int opar[DTREE_MAX_CAP + 1], otok[DTREE_MAX_CAP + 1], odep[DTREE_MAX_CAP + 1];
+  float osc[DTREE_MAX_CAP + 1];
+};
+
+// place of each of this thread's children (t = tid + DW_NT i) among the nc children, by
+// (score desc, parent position asc, rank asc): the number of children before it
+template <int NOWN>
+DT_INLINE void dw_rank_children(DwTreeLds &Ls, int nc, int ncp, int keep, int o0) {
+  const int tid = threadIdx.x;
+  double ms[NOWN];
+  int mp[NOWN], before[NOWN];
+#pragma unroll
+  for (int i = 0; i < NOWN; ++i) {
+    const int t = tid + DW_NT * i;
+    ms[i] = Ls.cs[t < ncp ? t : 0];
+    mp[i] = Ls.cpk[t < ncp ? t : 0];
+    before[i] = 0;
+  }
+  for (int y = 0; y < ncp; y += 8) {
+    double sy[8];
+    int py[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sy[u] = Ls.cs[y + u];
+      py[u] = Ls.cpk[y + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < NOWN; ++i) before[i] += (sy[u] > ms[i]) || (sy[u] == ms[i] && py[u] < mp[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NOWN; ++i) {
+    const int t = tid + DW_NT * i;
+    if (t < nc && before[i] < keep) {
+      Ls.fs[o0 + before[i]] = ms[i];
+      Ls.fpk[o0 + before[i]] = mp[i];
+    }
+  }
+}
+
+__global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g, TreeOut out) {
+  __shared__ DwTreeLds Ls;
   const int r = blockIdx.x;
-  if (threadIdx.x == 0) {
-    int o = 0;
-    for (int d = 1; d <= a.L; ++d) {
-      off[d] = o;
-      o += s.sup_n[(size_t)r * a.L + d - 1];
+  const int tid = threadIdx.x;
+  const int K = g.K, W = g.W, L = g.L;
+  constexpr int PF = 64 * 64 / DW_NT;  // log q~ entries per thread and depth
+  auto slab = [&](int d) { return s.lq + (size_t)dw_slot(g, d, r, 0) * K; };
+  double pre[PF];
+  auto prefetch = [&](int d) {
+    const int n = (d == 1 ? 1 : K) * K;
+    const double *src = slab(d);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int x = tid + DW_NT * i;
+      if (x < n) pre[i] = src[x];
     }
-    off[a.L + 1] = o;
+  };
+  prefetch(1);
+  if (tid == 0) {
+    Ls.bs[0] = 0.0;
+    Ls.bk[0] = 0;
+    Ls.off[1] = 0;
   }
-  __syncthreads();
-  const int n = off[a.L + 1];
-  for (int d = 1; d <= a.L; ++d) {
-    const int nd = off[d + 1] - off[d];
-    for (int p = threadIdx.x; p < nd; p += DW_NT) {
-      fs[off[d] + p] = s.sup_s[((size_t)r * a.L + d - 1) * a.W + p];
-      fdp[off[d] + p] = (d << 16) | p;
+  int nb = 1;  // branches at the current depth (the root)
+  for (int d = 1; d <= L; ++d) {
+    {
+      const int n = (d == 1 ? 1 : K) * K;
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        const int x = tid + DW_NT * i;
+        if (x < n) Ls.lqs[x] = pre[i];
+      }
     }
+    if (d < L) prefetch(d + 1);
+    __syncthreads();
+    // score every child (b, kc) of the nb branches; pad to a multiple of 8
+    const int nc = nb * K, ncp = (nc + 7) & ~7;
+    for (int t = tid; t < ncp; t += DW_NT) {
+      if (t < nc) {
+        const int b = t / K, kc = t - b * K;
+        const double sb = Ls.bs[b];
+        const double sc = (sb + Ls.lqs[Ls.bk[b] * K + kc]) + (double)a.beta;
+        Ls.cs[t] = fmin(sc, sb);
+        Ls.cpk[t] = (b << 16) | kc;
+      } else {
+        Ls.cs[t] = -kInf;
+        Ls.cpk[t] = 0x7FFFFFFF;
+      }
+    }
+    __syncthreads();
+    const int keep = nc < W ? nc : W;
+    const int o0 = Ls.off[d];
+    const int nown = (nc + DW_NT - 1) / DW_NT;
+    if (nown <= 1)
+      dw_rank_children<1>(Ls, nc, ncp, keep, o0);
+    else if (nown == 2)
+      dw_rank_children<2>(Ls, nc, ncp, keep, o0);
+    else
+      dw_rank_children<4>(Ls, nc, ncp, keep, o0);
+    __syncthreads();
+    // the kept children become the next depth's branches (state = candidate rank)
+    for (int i = tid; i < keep; i += DW_NT) {
+      Ls.bs[i] = Ls.fs[o0 + i];
+      Ls.bk[i] = Ls.fpk[o0 + i] & 0xFFFF;
+    }
+    if (tid == 0) Ls.off[d + 1] = o0 + keep;
+    nb = keep;
+    __syncthreads();
   }
-  const int npw = next_pow2(n > 1 ? n : 1);
-  for (int i = threadIdx.x; i < npw; i += DW_NT) fidx[i] = (uint16_t)i;
-  if (threadIdx.x <= a.L + 1) cnt[threadIdx.x] = 0;
+  // ---- deferred Top-B over the super-tree by (s desc, depth asc, position asc). Each S_d
+  // is sorted, so a node's rank is its position plus, per other depth, the length of the
+  // prefix that comes before it (a branch-free binary search, four depths in lockstep); the
+  // kept nodes of a depth are a prefix of S_d.
+  const int n = Ls.off[L + 1];
+  const int keep = n < g.B ? n : g.B;
+  if (tid <= L + 1) Ls.cnt[tid] = 0;
   __syncthreads();
-  for (int kk = 2; kk <= npw; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < npw; i += DW_NT) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int x = fidx[i], y = fidx[ixj];
-          bool x_first;
-          if (x >= n) x_first = false;
-          else if (y >= n) x_first = true;
-          else x_first = (fs[x] != fs[y]) ? (fs[x] > fs[y]) : (fdp[x] < fdp[y]);
-          const bool up = (i & kk) == 0;
-          if (up ? !x_first : x_first) {
-            fidx[i] = (uint16_t)y;
-            fidx[ixj] = (uint16_t)x;
+  for (int x = tid; x < n; x += DW_NT) {
+    int d = 1;
+    while (Ls.off[d + 1] <= x) ++d;
+    const double sp = Ls.fs[x];
+    int rank = x - Ls.off[d];
+    for (int d0 = 1; d0 <= L; d0 += 4) {
+      int lo[4], base[4], size[4];
+      bool ge[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d2 = d0 + i;
+        const bool in = d2 <= L && d2 != d;
+        base[i] = in ? Ls.off[d2] : 0;
+        size[i] = in ? Ls.off[d2 + 1] - Ls.off[d2] : 0;
+        ge[i] = d2 < d;  // shallower depths win ties
+        lo[i] = 0;
+      }
+#pragma unroll
+      for (int step = 64; step >= 1; step >>= 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = lo[i] + step;
+          if (j <= size[i]) {
+            const double sq = Ls.fs[base[i] + j - 1];
+            if (ge[i] ? sq >= sp : sq > sp) lo[i] = j;
           }
         }
       }
-      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rank += lo[i];
     }
+    if (rank < keep) atomicAdd(&Ls.cnt[d], 1);
   }
-  const int keep = n < a.B ? n : a.B;
-  for (int i = threadIdx.x; i < keep; i += DW_NT) atomicAdd(&cnt[fdp[fidx[i]] >> 16], 1);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int o = 1;
-    for (int d = 1; d <= a.L; ++d) {
-      const int c = cnt[d];
-      cnt[d] = o;  // reuse as canonical offset of depth d
+    for (int d = 1; d <= L; ++d) {
+      const int c = Ls.cnt[d];
+      Ls.cnt[d] = o;  // canonical offset of depth d
       o += c;
     }
-    opar[0] = -1;
-    otok[0] = -1;
-    odep[0] = 0;
-    osc[0] = 0.f;
+    Ls.cnt[L + 1] = o;
+    Ls.opar[0] = -1;
+    Ls.otok[0] = -1;
+    Ls.odep[0] = 0;
+    Ls.osc[0] = 0.f;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < keep; i += DW_NT) {
-    const int x = fidx[i];
-    const int d = fdp[x] >> 16, p = fdp[x] & 0xFFFF;
-    const size_t o = ((size_t)r * a.L + d - 1) * a.W + p;
-    const int idx = cnt[d] + p;
-    const int ppos = s.sup_pk[o] >> 16;
-    opar[idx] = (d == 1) ? 0 : cnt[d - 1] + ppos;
-    otok[idx] = s.sup_tok[o];
-    odep[idx] = d;
-    osc[idx] = (float)fs[x];
+  for (int d = 1; d <= L; ++d) {
+    const int nd = Ls.cnt[d + 1] - Ls.cnt[d];
+    for (int p = tid; p < nd; p += DW_NT) {
+      const int x = Ls.off[d] + p;
+      const int idx = Ls.cnt[d] + p;
+      const int pk = Ls.fpk[x];
+      Ls.opar[idx] = (d == 1) ? 0 : Ls.cnt[d - 1] + (pk >> 16);
+      Ls.otok[idx] = a.ids[((size_t)r * L + (d - 1)) * K + (pk & 0xFFFF)];
+      Ls.odep[idx] = d;
+      Ls.osc[idx] = (float)Ls.fs[x];
+    }
   }
   __syncthreads();
-  write_tree(r, keep, opar, otok, odep, osc, out);
+  write_tree(r, keep, Ls.opar, Ls.otok, Ls.odep, Ls.osc, out);
 }
 
 // ---------------------------------------------------------------- host side
 struct DwLayout {
-  size_t PT, UT, pmax, hx, bref, bs, nb, wide, part_s, part_m, sup_s, sup_pk, sup_tok, sup_n, total;
+  size_t PT, UT, pmax, hx, bref, wide, part_s, part_m, lq, total;
 };
 
-static DwLayout dw_layout(int R, int L, int V, int W, int dm) {
-  const int Wp = (W + 31) / 32 * 32, NG = Wp / 32;
+static DwLayout dw_layout(const DwDims &g) {
   DwLayout l;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -609,34 +775,28 @@ static DwLayout dw_layout(int R, int L, int V, int W, int dm) {
     o += align256(bytes);
     return at;
   };
-  l.PT = take((size_t)V * 64 * 2);
-  l.UT = take((size_t)L * 64 * dm * 2);
+  l.PT = take((size_t)g.V * 64 * 2);
+  l.UT = take((size_t)g.L * 64 * g.dm * 2);
   l.pmax = take(64 * sizeof(float));
-  l.hx = take((size_t)R * Wp * DW_HX * 2);
-  l.bref = take((size_t)R * Wp * sizeof(float));
-  l.bs = take((size_t)R * Wp * sizeof(double));
-  l.nb = take((size_t)R * sizeof(int));
-  l.wide = take((size_t)R * NG * sizeof(int));
-  l.part_s = take((size_t)R * Wp * DW_NC * sizeof(double));
-  l.part_m = take((size_t)R * Wp * DW_NC * sizeof(float));
-  l.sup_s = take((size_t)R * L * W * sizeof(double));
-  l.sup_pk = take((size_t)R * L * W * sizeof(int));
-  l.sup_tok = take((size_t)R * L * W * sizeof(int));
-  l.sup_n = take((size_t)R * L * sizeof(int));
+  l.hx = take((size_t)g.S * DW_HX * 2);
+  l.bref = take((size_t)g.S * sizeof(float));
+  l.wide = take((size_t)g.ntile * sizeof(int));
+  l.part_s = take((size_t)g.S * DW_NC * sizeof(double));
+  l.part_m = take((size_t)g.S * DW_NC * sizeof(float));
+  l.lq = take((size_t)g.S * g.K * sizeof(double));
   l.total = o;
   return l;
 }
 
 size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank, int dm) {
-  (void)K;
-  (void)B;
   (void)rank;
-  return dw_layout(R, L, V, W, dm).total;
+  return dw_layout(dw_dims(R, L, V, K, W, B, dm)).total;
 }
 
 hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
                             void *ws, hipStream_t st) {
-  const DwLayout l = dw_layout(a.R, a.L, a.V, a.W, a.dm);
+  const DwDims g = dw_dims(a.R, a.L, a.V, a.K, a.W, a.B, a.dm);
+  const DwLayout l = dw_layout(g);
   char *w = static_cast<char *>(ws);
   DwState s;
   s.PT = reinterpret_cast<uint16_t *>(w + l.PT);
@@ -644,53 +804,33 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   s.pmax = reinterpret_cast<float *>(w + l.pmax);
   s.hx = reinterpret_cast<uint16_t *>(w + l.hx);
   s.bref = reinterpret_cast<float *>(w + l.bref);
-  s.bs = reinterpret_cast<double *>(w + l.bs);
-  s.nb = reinterpret_cast<int *>(w + l.nb);
   s.wide = reinterpret_cast<int *>(w + l.wide);
   s.part_s = reinterpret_cast<double *>(w + l.part_s);
   s.part_m = reinterpret_cast<float *>(w + l.part_m);
-  s.sup_s = reinterpret_cast<double *>(w + l.sup_s);
-  s.sup_pk = reinterpret_cast<int *>(w + l.sup_pk);
-  s.sup_tok = reinterpret_cast<int *>(w + l.sup_tok);
-  s.sup_n = reinterpret_cast<int *>(w + l.sup_n);
+  s.lq = reinterpret_cast<double *>(w + l.lq);
   DwDev dv;
   dv.zk = zk;
   dv.ids = ids;
   dv.E = a.E;
-  dv.U = a.U;
   dv.root_tok = a.root_tok;
-  dv.R = a.R;
-  dv.L = a.L;
-  dv.V = a.V;
-  dv.K = a.K;
-  dv.W = a.W;
-  dv.Wp = (a.W + 31) / 32 * 32;
-  dv.NG = dv.Wp / 32;
-  dv.B = a.B;
-  dv.dm = a.dm;
   dv.beta = a.beta;
 
   hipLaunchKernelGGL(k_dw_zero_f32, dim3(1), dim3(64), 0, st, s.pmax, 64);
   hipLaunchKernelGGL(k_dw_transpose_p, dim3((a.V + DW_TP - 1) / DW_TP), dim3(DW_NT), 0, st, a.P, a.V, s.PT, s.pmax);
   hipLaunchKernelGGL(k_dw_transpose_u, dim3(a.dm / 64, a.L), dim3(DW_NT), 0, st, a.U, a.dm, s.UT);
-  hipLaunchKernelGGL(k_dw_init, dim3(a.R), dim3(DW_NT), 0, st, s, dv);
+  hipLaunchKernelGGL(k_dw_states, dim3(g.ntile), dim3(DW_NT), 0, st, s, dv, g, a.dtype == DTREE_BF16 ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nct = a.R * dv.NG;
-  const int TG = (nct + 3) / 4;
+  const int TG = (g.ntile + DW_CW - 1) / DW_CW;
   const dim3 gcorr((unsigned)(8 * TG * (DW_NC / 8)));
-  for (int d = 1; d <= a.L; ++d) {
-    if (a.dtype == DTREE_BF16)
-      hipLaunchKernelGGL(k_dw_corr<uint16_t>, gcorr, dim3(DW_NT), 0, st, s, static_cast<const uint16_t *>(a.base),
-                         d, a.L, a.V, a.R, dv.NG);
-    else
-      hipLaunchKernelGGL(k_dw_corr<float>, gcorr, dim3(DW_NT), 0, st, s, static_cast<const float *>(a.base), d, a.L,
-                         a.V, a.R, dv.NG);
-    hipLaunchKernelGGL(k_dw_select, dim3(a.R), dim3(DW_NT), 0, st, s, dv, d);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(k_dw_final, dim3(a.R), dim3(DW_NT), 0, st, s, dv, out);
+  if (a.dtype == DTREE_BF16)
+    hipLaunchKernelGGL(k_dw_corr<uint16_t>, gcorr, dim3(DW_CNT), 0, st, s, static_cast<const uint16_t *>(a.base), g);
+  else
+    hipLaunchKernelGGL(k_dw_corr<float>, gcorr, dim3(DW_CNT), 0, st, s, static_cast<const float *>(a.base), g);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dw_lq, dim3(g.ntile), dim3(DW_NT), 0, st, s, dv, g);
+  hipLaunchKernelGGL(k_dw_tree, dim3(a.R), dim3(DW_NT), 0, st, s, dv, g, out);
   return hipGetLastError();
 }
 
