@@ -38,14 +38,24 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "rowsweep_traffic.json"))
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run 5 row sweeps and 5 plain copies of the same bytes (for rocprofv3 --pmc "
+                         "FETCH_SIZE / WRITE_SIZE runs: the copy calibrates the counters)")
     return ap.parse_args()
+
+
+def sweep_source_digest():
+    """Digest of the row sweep's source: the stored counter readings are used only while it matches."""
+    import hashlib
+    src = os.path.join(ROOT, "draft_tree_construction_amd", "csrc", "k_rowsweep.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(rounds shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(rounds shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -55,6 +65,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.traffic_probe:
+        traffic_probe(dt, synth, torch, np, dev)
+        return
 
     def bf(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -141,7 +154,9 @@ def main():
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
-            traffic = json.load(open(args.traffic_json)).get("bytes_per_launch")
+            rec = json.load(open(args.traffic_json))
+            if rec.get("source_digest") == sweep_source_digest():
+                traffic = rec.get("bytes_per_launch")
         except Exception:
             traffic = None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -168,9 +183,27 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(draft_h, talon_h, head):
-    """The oracle, as it stands, on a bounded sample: one round of the same step
-    (all five operations) on round 0's inputs, single-threaded numpy."""
+def traffic_probe(dt, synth, torch, np, dev):
+    """5 row sweeps over the [R*L, V] bf16 logits (K = 64), then 5 device-to-device copies of
+    a buffer of the same size: the copy reads and writes exactly R*L*V*2 bytes, which scales
+    the counters' readings to bytes."""
+    bits = synth.ddtree_logits(seed=2)
+    flat = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev).view(R * L, V)
+    K = 64
+    ws_t = torch.empty(max(dt.workspace_size(dt.OP_TOPK, R * L, 1, V, K), 1), dtype=torch.uint8, device=dev)
+    for _ in range(5):
+        dt.topk_logsoftmax(flat, K, ws=ws_t)
+    dst = torch.empty_like(flat)
+    for _ in range(5):
+        dst.copy_(flat)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "rowsweep+copy", "copy_bytes_each_way": R * L * V * 2,
+                      "source_digest": sweep_source_digest()}), flush=True)
+
+
+def cpu_baseline(draft_h, talon_h, head, n_rounds=16):
+    """The oracle, as it stands, on a bounded sample: the first `n_rounds` rounds of the same
+    step (all five operations, each round's own inputs), float64 numpy on one thread."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
@@ -181,33 +214,37 @@ def cpu_baseline(draft_h, talon_h, head):
 
     ctx = threadpool_limits(1) if threadpool_limits else None
     try:
-        r = 0
-        z = rowsweep.as_f64(draft_h[r], "bf16")
-        tal = rowsweep.as_f64(talon_h[r], "bf16")
         E_h, U_h, P_h, root_h = head
-        t0 = time.perf_counter()
-        tm = marginal.build_marginal(z, 64, 64, 0.0)
-        E64 = E_h  # rows are gathered on demand
         U64 = synth.f32_from_bf16(U_h).astype(np.float64)
         P64 = synth.f32_from_bf16(P_h).astype(np.float64)
 
-        class Rows:
+        class Rows:  # rows of E gathered on demand
             def __getitem__(self, idx):
-                return synth.f32_from_bf16(E64[idx]).astype(np.float64)
-        depthwise.build_depthwise(z, Rows(), U64, P64, int(root_h[r]), 8, 32, 128, -0.5)
-        gated.build_gated(tal, 10, float(np.float32(0.03)), 60, full_pool=False)
-        depth = np.array(tm.arrays(64)[2])[None, :]
-        tgt = rowsweep.as_f64(synth.verification_target(draft_h[:1], depth, seed=5)[0], "bf16")
-        accept.walk_greedy(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1])
-        tab = accept.ResidualTables(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1], z, 1.0)
-        accept.walk_sampled(tab, tm.depth, synth.PHILOX_SEED, 0, 0)
-        dt_s = time.perf_counter() - t0
+                return synth.f32_from_bf16(E_h[idx]).astype(np.float64)
+
+        elapsed = 0.0
+        for r in range(n_rounds):
+            z = rowsweep.as_f64(draft_h[r], "bf16")
+            tal = rowsweep.as_f64(talon_h[r], "bf16")
+            t0 = time.perf_counter()
+            tm = marginal.build_marginal(z, 64, 64, 0.0)
+            depthwise.build_depthwise(z, Rows(), U64, P64, int(root_h[r]), 8, 32, 128, -0.5)
+            gated.build_gated(tal, 10, float(np.float32(0.03)), 60, full_pool=False)
+            elapsed += time.perf_counter() - t0
+            # the target rows follow this round's marginal tree (input preparation, untimed)
+            depth = np.array(tm.arrays(64)[2])[None, :]
+            tgt = rowsweep.as_f64(synth.verification_target(draft_h[r:r + 1], depth, seed=5)[0], "bf16")
+            t0 = time.perf_counter()
+            accept.walk_greedy(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1])
+            tab = accept.ResidualTables(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1], z, 1.0)
+            accept.walk_sampled(tab, tm.depth, synth.PHILOX_SEED, 0, r)
+            elapsed += time.perf_counter() - t0
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
-    return {"value": round(1.0 / dt_s, 4), "unit": "rounds/s", "cores": 1, "kind": "oracle",
-            "sample": "1 round (round 0) of the full step: marginal + depthwise + gated + accept T=0 + T=1, "
-                      f"float64 numpy, 1 thread; {dt_s:.2f} s"}
+    return {"value": round(n_rounds / elapsed, 4), "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": f"rounds 0..{n_rounds - 1} of the full step (marginal + depthwise + gated + accept T=0 "
+                      f"+ T=1 per round), float64 numpy, 1 thread; {elapsed:.2f} s"}
 
 
 if __name__ == "__main__":
