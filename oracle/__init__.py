@@ -21,8 +21,7 @@ Pages cited by title and section:
 * "DDTree: from theory to practice" (CSDN blog): Top-B prefixes, the S_K
   restriction, the heap over rank descriptors, the debugging checklist.
 
-Modules: ``rowsweep`` (log-softmax + top-K), ``order`` (the total order on
-prefixes), ``marginal`` (DDTree Top-B), ``depthwise`` (DARTree Algorithm 1),
+Modules: ``rowsweep`` (log-softmax + top-K), ``marginal`` (DDTree Top-B), ``depthwise`` (DARTree Algorithm 1),
 ``gated`` (TALON), ``treeout`` (parent array and mask), ``accept`` (greedy and
 residual acceptance walks), ``philox`` (Philox4x32-10).
 """
