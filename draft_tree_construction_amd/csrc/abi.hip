@@ -115,6 +115,7 @@ int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K,
   if (!logits || !ids) return fail(DTREE_E_INVAL, "logits and ids must not be NULL");
   const size_t need = dt::rowsweep_ws_bytes(rows, V, K);
   if (need > 0 && (!ws || ws_bytes < need)) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(ws) & 255)) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   dt::RowOut o{nullptr, lse, ids, nullptr, lp};
   hipError_t e = dt::launch_rowsweep(logits, dtype, rows, V, K, o, ws, static_cast<hipStream_t>(s));
   if (e != hipSuccess) return hip_fail(e, "dtree_topk_logsoftmax");
@@ -137,6 +138,7 @@ int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int 
   if (!logits) return fail(DTREE_E_INVAL, "logits is NULL");
   const size_t need = a1_bytes(R * L, V, k);
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(s);
   A1Ws a = a1_carve(ws, R * L, k);
   dt::RowOut o{a.lse, nullptr, a.ids, a.zk, nullptr};
@@ -162,6 +164,7 @@ int build_tree_gated(const void *logits, int dtype, int R, int L, int V, int K_r
   if (!logits) return fail(DTREE_E_INVAL, "logits is NULL");
   const size_t need = a1_bytes(R * L, V, k);
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(s);
   A1Ws a = a1_carve(ws, R * L, k);
   dt::RowOut o{a.lse, nullptr, a.ids, a.zk, nullptr};
@@ -190,6 +193,7 @@ int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, con
   if (((uintptr_t)E | (uintptr_t)U | (uintptr_t)P) & 15) return fail(DTREE_E_INVAL, "E, U and P must be 16-byte aligned");
   const size_t need = a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B, rank, d_model);
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(s);
   A1Ws a1 = a1_carve(ws, R * L, K);
   dt::RowOut o{a1.lse, nullptr, a1.ids, a1.zk, nullptr};
@@ -219,6 +223,7 @@ int accept_tree(const dtree_tree *tree, const void *target_logits, const void *d
   if (temperature > 0.f && !draft_logits) return fail(DTREE_E_INVAL, "draft_logits is NULL with temperature > 0");
   const size_t need = dt::accept_ws_bytes(R, L, V, tree->cap);
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   dt::AcceptArgs a{tree_out(tree), target_logits, draft_logits, dtype, R, L, V, temperature, seed, trial0, n_trials,
                    accept_len, accept_node, next_token};
   hipError_t e = dt::launch_accept(a, ws, static_cast<hipStream_t>(s));

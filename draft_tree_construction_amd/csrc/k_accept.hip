@@ -114,9 +114,8 @@ struct Ring {
 
 // f(u, a[8], b[8]) for every unit u of two rows of equal length (elements past the end are
 // -inf); unit u = threadIdx.x + k * AC_NT. Wave-uniform calls of f.
-template <typename T, typename F>
+template <typename T, int D = Ring<T>::D, typename F>
 DT_INLINE void stream2(const Row<T> &A, const Row<T> &B, F &&f) {
-  constexpr int D = Ring<T>::D;
   const int V = A.V;
   const int iters = ((V + 7) / 8 + AC_NT - 1) / AC_NT;
   const int tid = threadIdx.x;
@@ -337,6 +336,101 @@ DT_INLINE double wg_chain_pass(const Row<T> &A, const Row<T> &B, const Norm &nt,
   return wg_sum(acc, red);
 }
 
+// Survivor lists. For t' >= t, (p - t' q)_+ is zero wherever (p - t q)_+ is (fma rounds an
+// exactly non-positive value to a non-positive one, and denormal results flush to zero
+// alike), so once a pass at t has run, the later passes of the same node only need the
+// elements whose residual at t was positive. Each thread keeps its own survivors, in the
+// order its units are streamed, as (p, q) float pairs in a column of global scratch
+// (element k of thread x at col[k * AC_NT], x = threadIdx.x); the last survivor of a unit
+// carries the unit end in q's sign bit. A pass over the list forms the same per-unit float
+// sums and the same float64 accumulation as the full pass -- the skipped terms are exact
+// zeros -- so C(t) is bit-identical to wg_chain_pass's (block sums are not formed).
+DT_INLINE float2 kept(float p, float q, bool unit_end) {
+  return make_float2(p, __uint_as_float(__float_as_uint(q) | (unit_end ? 0x80000000u : 0u)));
+}
+
+// wg_chain_pass at t that also writes the survivor list; nk = its length for this thread.
+template <typename T>
+DT_INLINE double wg_chain_pass_keep(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t,
+                                    float *blk, int nblk, Red &red, float2 *col, int &nk) {
+  double acc = 0.0;
+  int k = 0;
+  // a shallower ring than the plain pass: the list writes need the registers
+  stream2<T, (Ring<T>::D > 2 ? Ring<T>::D - 1 : Ring<T>::D)>(A, B, [&](int u, const float *za, const float *zb) {
+    float part = 0.f, lp = 0.f, lq = 0.f;
+    const int k0 = k;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = prob(za[e], nt), q = prob(zb[e], nd);
+      const float re = resid(p, q, t);
+      part += re;
+      if (re > 0.f) {
+        col[(size_t)(k++) * AC_NT] = kept(p, q, false);
+        lp = p;
+        lq = q;
+      }
+    }
+    if (k > k0) col[(size_t)(k - 1) * AC_NT] = kept(lp, lq, true);  // rewrite the unit's last with its end mark
+    float bs = part;
+    bs += __shfl_xor(bs, 1, 64);
+    bs += __shfl_xor(bs, 2, 64);
+    bs += __shfl_xor(bs, 4, 64);
+    if ((u & 7) == 0 && (u >> 3) < nblk) blk[u >> 3] = bs;
+    acc += (double)part;
+  });
+  nk = k;
+  return wg_sum(acc, red);
+}
+
+// C(t) over the survivor list, which is compacted in place to the survivors at t. The
+// list is read four entries ahead of the writes (a write never lands past the entry
+// being read, so the look-ahead reads are not overwritten).
+DT_INLINE double wg_list_pass(float2 *col, int &nk, float t, Red &red) {
+  constexpr int G = 4;
+  const int n = nk;
+  double acc = 0.0;
+  float part = 0.f;
+  int w = 0;
+  bool pend = false;
+  float pp = 0.f, pq = 0.f;
+  float2 cur[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) cur[i] = i < n ? col[(size_t)i * AC_NT] : make_float2(0.f, 0.f);
+  for (int k0 = 0; k0 < n; k0 += G) {
+    float2 nxt[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int k = k0 + G + i;
+      nxt[i] = k < n ? col[(size_t)k * AC_NT] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (k0 + i < n) {
+        const uint32_t qb = __float_as_uint(cur[i].y);
+        const float q = __uint_as_float(qb & 0x7FFFFFFFu);
+        const float rr = resid(cur[i].x, q, t);
+        part += rr;
+        if (rr > 0.f) {
+          if (pend) col[(size_t)(w++) * AC_NT] = kept(pp, pq, false);
+          pend = true;
+          pp = cur[i].x;
+          pq = q;
+        }
+        if (qb >> 31) {
+          acc += (double)part;
+          part = 0.f;
+          if (pend) col[(size_t)(w++) * AC_NT] = kept(pp, pq, true);
+          pend = false;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+  }
+  nk = w;
+  return wg_sum(acc, red);
+}
+
 // Inclusive prefix sums (float64) of the n block sums, into pre[]; one workgroup.
 DT_INLINE void wg_prefix(const float *blk, double *pre, int n, Red &red) {
   const int per = (n + AC_NT - 1) / AC_NT;
@@ -466,13 +560,15 @@ DT_INLINE void build_children(const int *par, const int *tok, int n, int V, int 
   __syncthreads();
 }
 
+// Survivor-list entries per thread: 8 per streamed unit.
+__host__ __device__ inline int accept_list_slots(int V) { return (((V + 7) / 8 + AC_NT - 1) / AC_NT) * 8; }
 DT_INLINE int clamp_nodes(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 DT_INLINE int draft_row(int depth, int L) { return depth < 0 ? 0 : (depth > L - 1 ? L - 1 : depth); }
 DT_INLINE float log2_scale(float T) { return (float)(1.4426950408889634 / (double)T); }
 
 // ---------------------------------------------------------------- lazy walk (one trial / T = 0)
 template <typename T>
-__global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
+__global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_keep) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
   __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1];
   __shared__ Red red;
@@ -513,6 +609,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
     const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
     double *pre = dyn;
     float *blk = reinterpret_cast<float *>(dyn + nblk);
+    float2 *col = a_keep + (size_t)r * accept_list_slots(a.V) * AC_NT + threadIdx.x;
     for (;;) {
       const T *zt = target + (size_t)j * a.V;
       const T *zd = draft + (size_t)draft_row(dep[j], a.L) * a.V;
@@ -523,6 +620,8 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
       float t = 0.f;
       double C = 1.0;
       bool blk_at_t = false;  // blk holds the block sums of the residual at t
+      bool listed = false;    // the survivor list covers the residual at t and beyond
+      int nk = 0;
       int nxt = -1;
       for (int c = fc[j]; c >= 0; c = ns[c]) {
         const float z1 = load_elt(zt, (size_t)tok[c]), z2 = load_elt(zd, (size_t)tok[c]);
@@ -534,11 +633,14 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a) {
           break;
         }
         const float t2 = t + (float)C;
-        const double C2 = wg_chain_pass(A, B, nt, nd, t2, blk, nblk, red);
+        const double C2 = listed ? wg_list_pass(col, nk, t2, red)
+                                 : wg_chain_pass_keep(A, B, nt, nd, t2, blk, nblk, red, col, nk);
+        const bool full = !listed;
+        listed = true;
         if (C2 > 0.0) {
           t = t2;
           C = C2;
-          blk_at_t = true;
+          blk_at_t = full;
         } else {
           blk_at_t = false;
         }
@@ -700,7 +802,9 @@ size_t accept_ws_bytes(int R, int L, int V, int cap) {
   (void)L;
   const size_t slots = (size_t)R * (cap + 1);
   const int nblk = (V + AC_BLK - 1) / AC_BLK;
-  return 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
+  const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
+  const size_t lists = (size_t)R * accept_list_slots(V) * AC_NT * sizeof(float2);  // the lazy walk's
+  return tables > lists ? tables : lists;
 }
 
 size_t accept_lds_bytes(int V) {
@@ -713,9 +817,9 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
   if (a.T == 0.f || a.n_trials == 1) {
     const size_t shm = accept_lds_bytes(a.V);
     if (a.dtype == DTREE_BF16)
-      hipLaunchKernelGGL(k_accept_lazy<uint16_t>, dim3(a.R), dim3(AC_NT), shm, st, a);
+      hipLaunchKernelGGL(k_accept_lazy<uint16_t>, dim3(a.R), dim3(AC_NT), shm, st, a, static_cast<float2 *>(ws));
     else
-      hipLaunchKernelGGL(k_accept_lazy<float>, dim3(a.R), dim3(AC_NT), shm, st, a);
+      hipLaunchKernelGGL(k_accept_lazy<float>, dim3(a.R), dim3(AC_NT), shm, st, a, static_cast<float2 *>(ws));
     return hipGetLastError();
   }
   AccTables tb = carve_tables(ws, a.R, a.V, a.tree.cap);

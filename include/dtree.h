@@ -19,7 +19,8 @@
  *   - All array arguments are DEVICE pointers (memory of the current HIP device), except
  *     the dtree_tree struct itself and scalar arguments, which live on the host.
  *   - The caller owns every buffer, including the workspace `ws` of at least
- *     dtree_workspace_size(...) bytes. The library never allocates or frees memory, keeps
+ *     dtree_workspace_size(...) bytes, 256-byte aligned (as hipMalloc and torch allocations
+ *     are; else DTREE_E_INVAL). The library never allocates or frees memory, keeps
  *     no state between calls and holds no pointer after it returns.
  *   - Every call only enqueues kernels on stream `s` (a hipStream_t; NULL = null stream)
  *     and returns; results are valid once the stream reaches that point. Calls are

@@ -75,6 +75,7 @@ def marg(**kw):
     (dict(logits=None), -1),
     (dict(ws=None), -3),
     (dict(nbytes=10), -3),
+    (dict(ws=ctypes.c_void_p(0x1010), nbytes=1 << 40), -1),   # ws must be 256-byte aligned
 ])
 def test_marginal_validation(kw, code):
     assert marg(**kw) == code
@@ -126,6 +127,8 @@ def test_accept_validation():
     assert call(draft=None) == -1
     assert call(V=300000) == -4
     assert call() == -3
+    assert L.accept_tree(ctypes.byref(t), FAKE, FAKE, 0, 4, 16, 151936, 1.0, 1, 0, 1, FAKE, FAKE, FAKE,
+                         ctypes.c_void_p(0x1008), 1 << 40, None) == -1   # misaligned workspace
     assert L.accept_tree(None, FAKE, FAKE, 0, 4, 16, 100, 1.0, 1, 0, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
 
 
