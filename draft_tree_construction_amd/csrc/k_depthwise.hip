@@ -44,6 +44,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int DW_NT = 256;
+constexpr int DW_TT = 1024;  // per-round tree workgroup
 constexpr int DW_CNT = 1024;   // correction sweep workgroup: DW_CW tiles share each staged P^T block
 constexpr int DW_CW = DW_CNT / 64;
 constexpr int DW_NC = 64;      // V chunks (partials per state)
@@ -584,49 +585,43 @@ struct DwTreeLds {
   float osc[DTREE_MAX_CAP + 1];
 };
 
-// place of each of this thread's children (t = tid + DW_NT i) among the nc children, by
-// (score desc, parent position asc, rank asc): the number of children before it
-template <int NOWN>
+// Place of every child among the nc children by (score desc, parent position asc, rank
+// asc): the number of children before it. G lanes share a child (G = 1024 / ncp, at most
+// 8), each counting over every G-th group of 8, and combine their counts by shuffles.
+template <int G>
 DT_INLINE void dw_rank_children(DwTreeLds &Ls, int nc, int ncp, int keep, int o0) {
   const int tid = threadIdx.x;
-  double ms[NOWN];
-  int mp[NOWN], before[NOWN];
+  const int part = tid & (G - 1);
+  for (int t = tid / G; t < ncp; t += DW_TT / G) {
+    const double ms = Ls.cs[t];
+    const int mp = Ls.cpk[t];
+    int before = 0;
+    for (int y = 8 * part; y < ncp; y += 8 * G) {
+      double sy[8];
+      int py[8];
 #pragma unroll
-  for (int i = 0; i < NOWN; ++i) {
-    const int t = tid + DW_NT * i;
-    ms[i] = Ls.cs[t < ncp ? t : 0];
-    mp[i] = Ls.cpk[t < ncp ? t : 0];
-    before[i] = 0;
-  }
-  for (int y = 0; y < ncp; y += 8) {
-    double sy[8];
-    int py[8];
+      for (int u = 0; u < 8; ++u) {
+        sy[u] = Ls.cs[y + u];
+        py[u] = Ls.cpk[y + u];
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      sy[u] = Ls.cs[y + u];
-      py[u] = Ls.cpk[y + u];
+      for (int u = 0; u < 8; ++u) before += (sy[u] > ms) || (sy[u] == ms && py[u] < mp);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int i = 0; i < NOWN; ++i) before[i] += (sy[u] > ms[i]) || (sy[u] == ms[i] && py[u] < mp[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < NOWN; ++i) {
-    const int t = tid + DW_NT * i;
-    if (t < nc && before[i] < keep) {
-      Ls.fs[o0 + before[i]] = ms[i];
-      Ls.fpk[o0 + before[i]] = mp[i];
+    for (int o = 1; o < G; o <<= 1) before += __shfl_xor(before, o, 64);
+    if (part == 0 && t < nc && before < keep) {
+      Ls.fs[o0 + before] = ms;
+      Ls.fpk[o0 + before] = mp;
     }
   }
 }
 
-__global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g, TreeOut out) {
+__global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g, TreeOut out) {
   __shared__ DwTreeLds Ls;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int K = g.K, W = g.W, L = g.L;
-  constexpr int PF = 64 * 64 / DW_NT;  // log q~ entries per thread and depth
+  constexpr int PF = 64 * 64 / DW_TT;  // log q~ entries per thread and depth
   auto slab = [&](int d) { return s.lq + (size_t)dw_slot(g, d, r, 0) * K; };
   double pre[PF];
   auto prefetch = [&](int d) {
@@ -634,7 +629,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g,
     const double *src = slab(d);
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const int x = tid + DW_NT * i;
+      const int x = tid + DW_TT * i;
       if (x < n) pre[i] = src[x];
     }
   };
@@ -650,7 +645,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g,
       const int n = (d == 1 ? 1 : K) * K;
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
-        const int x = tid + DW_NT * i;
+        const int x = tid + DW_TT * i;
         if (x < n) Ls.lqs[x] = pre[i];
       }
     }
@@ -658,7 +653,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g,
     __syncthreads();
     // score every child (b, kc) of the nb branches; pad to a multiple of 8
     const int nc = nb * K, ncp = (nc + 7) & ~7;
-    for (int t = tid; t < ncp; t += DW_NT) {
+    for (int t = tid; t < ncp; t += DW_TT) {
       if (t < nc) {
         const int b = t / K, kc = t - b * K;
         const double sb = Ls.bs[b];
@@ -673,16 +668,17 @@ __global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g,
     __syncthreads();
     const int keep = nc < W ? nc : W;
     const int o0 = Ls.off[d];
-    const int nown = (nc + DW_NT - 1) / DW_NT;
-    if (nown <= 1)
-      dw_rank_children<1>(Ls, nc, ncp, keep, o0);
-    else if (nown == 2)
+    if (ncp <= DW_TT / 8)
+      dw_rank_children<8>(Ls, nc, ncp, keep, o0);
+    else if (ncp <= DW_TT / 4)
+      dw_rank_children<4>(Ls, nc, ncp, keep, o0);
+    else if (ncp <= DW_TT / 2)
       dw_rank_children<2>(Ls, nc, ncp, keep, o0);
     else
-      dw_rank_children<4>(Ls, nc, ncp, keep, o0);
+      dw_rank_children<1>(Ls, nc, ncp, keep, o0);
     __syncthreads();
     // the kept children become the next depth's branches (state = candidate rank)
-    for (int i = tid; i < keep; i += DW_NT) {
+    for (int i = tid; i < keep; i += DW_TT) {
       Ls.bs[i] = Ls.fs[o0 + i];
       Ls.bk[i] = Ls.fpk[o0 + i] & 0xFFFF;
     }
@@ -698,12 +694,15 @@ __global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g,
   const int keep = n < g.B ? n : g.B;
   if (tid <= L + 1) Ls.cnt[tid] = 0;
   __syncthreads();
-  for (int x = tid; x < n; x += DW_NT) {
+  // GF lanes per node, each searching every GF-th group of four depths
+  const int GF = n <= DW_TT / 8 ? 8 : n <= DW_TT / 4 ? 4 : n <= DW_TT / 2 ? 2 : 1;
+  const int part = tid & (GF - 1);
+  for (int x = tid / GF; x < n; x += DW_TT / GF) {
     int d = 1;
     while (Ls.off[d + 1] <= x) ++d;
     const double sp = Ls.fs[x];
-    int rank = x - Ls.off[d];
-    for (int d0 = 1; d0 <= L; d0 += 4) {
+    int rank = 0;
+    for (int d0 = 1 + 4 * part; d0 <= L; d0 += 4 * GF) {
       int lo[4], base[4], size[4];
       bool ge[4];
 #pragma unroll
@@ -729,7 +728,9 @@ __global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g,
 #pragma unroll
       for (int i = 0; i < 4; ++i) rank += lo[i];
     }
-    if (rank < keep) atomicAdd(&Ls.cnt[d], 1);
+    for (int o = 1; o < GF; o <<= 1) rank += __shfl_xor(rank, o, 64);
+    rank += x - Ls.off[d];
+    if (part == 0 && rank < keep) atomicAdd(&Ls.cnt[d], 1);
   }
   __syncthreads();
   if (tid == 0) {
@@ -748,7 +749,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_tree(DwState s, DwDev a, DwDims g,
   __syncthreads();
   for (int d = 1; d <= L; ++d) {
     const int nd = Ls.cnt[d + 1] - Ls.cnt[d];
-    for (int p = tid; p < nd; p += DW_NT) {
+    for (int p = tid; p < nd; p += DW_TT) {
       const int x = Ls.off[d] + p;
       const int idx = Ls.cnt[d] + p;
       const int pk = Ls.fpk[x];
@@ -830,7 +831,7 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dw_lq, dim3(g.ntile), dim3(DW_NT), 0, st, s, dv, g);
-  hipLaunchKernelGGL(k_dw_tree, dim3(a.R), dim3(DW_NT), 0, st, s, dv, g, out);
+  hipLaunchKernelGGL(k_dw_tree, dim3(a.R), dim3(DW_TT), 0, st, s, dv, g, out);
   return hipGetLastError();
 }
 
