@@ -32,6 +32,8 @@ constexpr int AC_NT = 1024;        // threads per pass workgroup
 constexpr int AC_NW = AC_NT / 64;
 constexpr int AC_BLK = 64;         // tokens per sampling block (8 lanes x 8 elements)
 constexpr int AC_WT = 256;         // threads per workgroup of the table walk
+constexpr int AC_NB = 2048;        // p/q bins of a node's residual support
+constexpr int AC_BSH = 16;         // bin width: 2^(23 - AC_BSH) = 128 bins per octave of p/q
 
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11).
@@ -208,6 +210,8 @@ struct Red {
   double d[AC_NW * 2];
   float f[AC_NW * 2];
   uint64_t k[AC_NW];
+  uint64_t u[AC_NW * 4];
+  int i[AC_NW];
 };
 // Deterministic block sums of one or two doubles per thread.
 DT_INLINE double wg_sum(double v, Red &red) {
@@ -336,99 +340,221 @@ DT_INLINE double wg_chain_pass(const Row<T> &A, const Row<T> &B, const Norm &nt,
   return wg_sum(acc, red);
 }
 
-// Survivor lists. For t' >= t, (p - t' q)_+ is zero wherever (p - t q)_+ is (fma rounds an
-// exactly non-positive value to a non-positive one, and denormal results flush to zero
-// alike), so once a pass at t has run, the later passes of the same node only need the
-// elements whose residual at t was positive. Each thread keeps its own survivors, in the
-// order its units are streamed, as (p, q) float pairs in a column of global scratch
-// (element k of thread x at col[k * AC_NT], x = threadIdx.x); the last survivor of a unit
-// carries the unit end in q's sign bit. A pass over the list forms the same per-unit float
-// sums and the same float64 accumulation as the full pass -- the skipped terms are exact
-// zeros -- so C(t) is bit-identical to wg_chain_pass's (block sums are not formed).
-DT_INLINE float2 kept(float p, float q, bool unit_end) {
-  return make_float2(p, __uint_as_float(__float_as_uint(q) | (unit_end ? 0x80000000u : 0u)));
+// ---------------------------------------------------------------- exact C(t)
+// C(t) = sum over S(t) = {v : p_v > t q_v} of (p_v - t q_v), the mass of the residual
+// (p - t q)_+, for 1 <= t < 2^10 (every C pass has t >= t_2 = 1, and t grows by at most 1
+// per child). The sums of p and q over S(t) are exact integer sums of floor(x 2^60), so they
+// do not depend on the order of the terms, and C = P - t Q in float64. A term with
+// p < 2^-60 adds nothing to either sum (a member also has q < p / t), and for p >= 2^-60 a
+// nonzero p - t q is a multiple of at least 2^-116, so the float fma has its exact sign
+// even with denormals flushed: membership by the float fma decides every term that counts.
+DT_INLINE bool in_s(float p, float q, float t) { return __builtin_fmaf(-t, q, p) > 0.f; }
+// floor(x 2^60) for 0 <= x < 8, from the float's bits
+DT_INLINE uint64_t fx60(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const int e = (int)(u >> 23);
+  const uint64_t m = (u & 0x7FFFFFu) | 0x800000u;
+  const int sh = e - 90;  // x = m 2^(e - 150)
+  return e == 0 ? 0ull : sh >= 0 ? (m << sh) : sh > -24 ? (m >> -sh) : 0ull;
+}
+DT_INLINE double fx_to_d(uint64_t v) {
+  return (double)(uint32_t)(v >> 32) * 0x1p-28 + (double)(uint32_t)v * 0x1p-60;
+}
+DT_INLINE double c_from(uint64_t P, uint64_t Q, float t) { return fx_to_d(P) - (double)t * fx_to_d(Q); }
+// Values equal in every lane, moved to scalar registers.
+DT_INLINE uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+DT_INLINE int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+DT_INLINE uint64_t uni(uint64_t x) { return ((uint64_t)uni((uint32_t)(x >> 32)) << 32) | uni((uint32_t)x); }
+DT_INLINE float uni(float x) { return __uint_as_float(uni(__float_as_uint(x))); }
+DT_INLINE double uni(double x) { return __longlong_as_double((long long)uni((uint64_t)__double_as_longlong(x))); }
+
+// Wave sum of an unsigned 64-bit value (exact): xor swizzles within each half of the wave
+// (the lane pattern is an immediate), then the two halves' sums from lanes 0 and 32.
+template <int M>
+DT_INLINE uint64_t swz_xor(uint64_t v) {
+  constexpr int pat = 0x1F | (M << 10);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)v, pat);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(v >> 32), pat);
+  return ((uint64_t)hi << 32) | lo;
+}
+DT_INLINE uint64_t wave_sum_u64(uint64_t v) {
+  v += swz_xor<1>(v);
+  v += swz_xor<2>(v);
+  v += swz_xor<4>(v);
+  v += swz_xor<8>(v);
+  v += swz_xor<16>(v);
+  const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 0) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 0);
+  const uint64_t b = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 32) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 32);
+  return a + b;
 }
 
-// wg_chain_pass at t that also writes the survivor list; nk = its length for this thread.
+// Block sums of N unsigned 64-bit values per thread (exact, so any order): wave sums, then
+// lane x of every wave reads wave x's sum and the wave sums those again.
+template <int N>
+DT_INLINE void wg_sum_u64(uint64_t *v, Red &red) {
+  static_assert(N * AC_NW <= sizeof(red.u) / sizeof(red.u[0]), "red.u too small");
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum_u64(v[i]);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < N; ++i) red.u[i * AC_NW + w] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum_u64(lane < AC_NW ? red.u[i * AC_NW + lane] : 0ull);
+}
+
+// C(t) by a pass over both rows; also the float block sums of the residual for the draw
+// (as wg_chain_pass forms them).
 template <typename T>
-DT_INLINE double wg_chain_pass_keep(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t,
-                                    float *blk, int nblk, Red &red, float2 *col, int &nk) {
-  double acc = 0.0;
-  int k = 0;
-  // a shallower ring than the plain pass: the list writes need the registers
-  stream2<T, (Ring<T>::D > 2 ? Ring<T>::D - 1 : Ring<T>::D)>(A, B, [&](int u, const float *za, const float *zb) {
-    float part = 0.f, lp = 0.f, lq = 0.f;
-    const int k0 = k;
+DT_INLINE double wg_c_pass(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t, float *blk,
+                           int nblk, Red &red) {
+  uint64_t v[2] = {0, 0};
+  stream2(A, B, [&](int u, const float *za, const float *zb) {
+    float part = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = prob(za[e], nt), q = prob(zb[e], nd);
-      const float re = resid(p, q, t);
-      part += re;
-      if (re > 0.f) {
-        col[(size_t)(k++) * AC_NT] = kept(p, q, false);
-        lp = p;
-        lq = q;
-      }
+      part += resid(p, q, t);
+      const bool m = in_s(p, q, t);
+      v[0] += m ? fx60(p) : 0ull;
+      v[1] += m ? fx60(q) : 0ull;
     }
-    if (k > k0) col[(size_t)(k - 1) * AC_NT] = kept(lp, lq, true);  // rewrite the unit's last with its end mark
     float bs = part;
     bs += __shfl_xor(bs, 1, 64);
     bs += __shfl_xor(bs, 2, 64);
     bs += __shfl_xor(bs, 4, 64);
     if ((u & 7) == 0 && (u >> 3) < nblk) blk[u >> 3] = bs;
-    acc += (double)part;
   });
-  nk = k;
-  return wg_sum(acc, red);
+  wg_sum_u64<2>(v, red);
+  return c_from(v[0], v[1], t);
 }
 
-// C(t) over the survivor list, which is compacted in place to the survivors at t. The
-// list is read four entries ahead of the writes (a write never lands past the entry
-// being read, so the look-ahead reads are not overwritten).
-DT_INLINE double wg_list_pass(float2 *col, int &nk, float t, Red &red) {
-  constexpr int G = 4;
-  const int n = nk;
-  double acc = 0.0;
-  float part = 0.f;
-  int w = 0;
-  bool pend = false;
-  float pp = 0.f, pq = 0.f;
-  float2 cur[G];
+// Ratio bins. Once a node's first rejection has fixed t0, every later t is >= t0, so S(t) is
+// a subset of S(t0). S(t0) is sorted into AC_NB bins by the exact ratio p / q: bin b holds
+// the ratios in [e_b, e_{b+1}) with e_b the float whose bits are bits(t0) + b 2^AC_BSH (the
+// last bin open-ended); a float t lies in bin (bits(t) - bits(t0)) >> AC_BSH. For a query t
+// in bin bt, every member of a lower bin has p < t q and every member of a higher bin has
+// p > t q, so only bin bt needs the exact test. With the bins' members listed contiguously,
+// a query removes the bins it has passed (each member once per node) and tests its own bin.
+DT_INLINE float bin_edge(uint32_t tbb, int b) { return __uint_as_float(tbb + ((uint32_t)b << AC_BSH)); }
+// p >= e q, exact for the terms that count (as in_s; the edges stay below 2^17)
+DT_INLINE bool ge_edge(float p, float q, float e) { return __builtin_fmaf(-e, q, p) >= 0.f; }
+// A guess from an approximate ratio (within a few ulp of p / q, a bin being 2^AC_BSH ulp
+// wide), then one exact step to the bin whose edges bracket p / q. Where the guess can be
+// further off -- q = 0 or a reciprocal out of range -- either the ratio is beyond the last
+// edge or p < 2^-60, whose terms add nothing.
+DT_INLINE int ratio_bin(float p, float q, uint32_t tbb) {
+  const float rho = q > 0.f ? p * __builtin_amdgcn_rcpf(q) : kInf;
+  const int d = (int)(__float_as_uint(rho) - tbb);
+  const int b = d < 0 ? 0 : min(d >> AC_BSH, AC_NB - 1);
+  const bool dn = b > 0 && !ge_edge(p, q, bin_edge(tbb, b));
+  const bool up = b < AC_NB - 1 && ge_edge(p, q, bin_edge(tbb, b + 1));
+  return b + (up ? 1 : 0) - (dn ? 1 : 0);
+}
+DT_INLINE int t_bin(float t, uint32_t tbb) { return min((int)(__float_as_uint(t) - tbb) >> AC_BSH, AC_NB - 1); }
+
+// Exclusive prefix of n ints (n a multiple of AC_NT) into out[0..n], out[n] = total.
+DT_INLINE void wg_scan_int(const int *in, int *out, int n, Red &red) {
+  const int per = n / AC_NT;
+  const int a = threadIdx.x * per;
+  int s = 0;
+  for (int i = 0; i < per; ++i) s += in[a + i];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = s;
 #pragma unroll
-  for (int i = 0; i < G; ++i) cur[i] = i < n ? col[(size_t)i * AC_NT] : make_float2(0.f, 0.f);
-  for (int k0 = 0; k0 < n; k0 += G) {
-    float2 nxt[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int k = k0 + G + i;
-      nxt[i] = k < n ? col[(size_t)k * AC_NT] : make_float2(0.f, 0.f);
-    }
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      if (k0 + i < n) {
-        const uint32_t qb = __float_as_uint(cur[i].y);
-        const float q = __uint_as_float(qb & 0x7FFFFFFFu);
-        const float rr = resid(cur[i].x, q, t);
-        part += rr;
-        if (rr > 0.f) {
-          if (pend) col[(size_t)(w++) * AC_NT] = kept(pp, pq, false);
-          pend = true;
-          pp = cur[i].x;
-          pq = q;
-        }
-        if (qb >> 31) {
-          acc += (double)part;
-          part = 0.f;
-          if (pend) col[(size_t)(w++) * AC_NT] = kept(pp, pq, true);
-          pend = false;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += x;
   }
-  nk = w;
-  return wg_sum(acc, red);
+  __syncthreads();
+  if (lane == 63) red.i[w] = incl;
+  __syncthreads();
+  int run = 0;
+  for (int i = 0; i < w; ++i) run += red.i[i];
+  run += incl - s;
+  for (int i = 0; i < per; ++i) {
+    out[a + i] = run;
+    run += in[a + i];
+  }
+  if (threadIdx.x == AC_NT - 1) out[n] = run;
+  __syncthreads();
+}
+
+struct Bins {
+  int *cnt, *off;  // LDS: [AC_NB] counts / cursors, [AC_NB + 1] offsets
+  float2 *list;    // global: this round's members of S(t0), (p, q), grouped by bin
+  uint32_t tbb;    // bits of t0
+  int lo;          // bins below lo have been removed from (P, Q)
+  uint64_t P, Q;   // sums over the members of bins >= lo
+};
+
+// Sort S(t0) into the bins (two passes over the rows: counts, then placement) and sum p and q
+// over the list; returns C(t0).
+template <typename T>
+DT_INLINE double wg_bins_build(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t0, Bins &bn,
+                               Red &red) {
+  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) bn.cnt[i] = 0;
+  bn.tbb = uni(__float_as_uint(t0));
+  __syncthreads();
+  stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = prob(za[e], nt), q = prob(zb[e], nd);
+      const int b = ratio_bin(p, q, bn.tbb);
+      if (in_s(p, q, t0)) atomicAdd(&bn.cnt[b], 1);
+    }
+  });
+  __syncthreads();
+  wg_scan_int(bn.cnt, bn.off, AC_NB, red);
+  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) bn.cnt[i] = bn.off[i];
+  __syncthreads();
+  stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = prob(za[e], nt), q = prob(zb[e], nd);
+      const int b = ratio_bin(p, q, bn.tbb);
+      if (in_s(p, q, t0)) bn.list[atomicAdd(&bn.cnt[b], 1)] = make_float2(p, q);
+    }
+  });
+  __syncthreads();
+  // the sums over S(t0), from the list
+  uint64_t v[2] = {0, 0};
+  const int total = bn.off[AC_NB];
+  for (int i = threadIdx.x; i < total; i += AC_NT) {
+    const float2 x = bn.list[i];
+    v[0] += fx60(x.x);
+    v[1] += fx60(x.y);
+  }
+  wg_sum_u64<2>(v, red);
+  bn.lo = 0;
+  bn.P = uni(v[0]);
+  bn.Q = uni(v[1]);
+  return uni(c_from(bn.P, bn.Q, t0));
+}
+
+// C(t) for t >= the last query's t (>= t0) from the bins.
+DT_INLINE double wg_bins_query(Bins &bn, float t, Red &red) {
+  const int bt = t_bin(t, bn.tbb);
+  const int a0 = bn.off[bn.lo], a1 = bn.off[bt], b1 = bn.off[bt + 1];
+  uint64_t v[4] = {0, 0, 0, 0};  // removed bins (p, q); members of bin bt outside S(t) (p, q)
+  for (int i = a0 + threadIdx.x; i < b1; i += AC_NT) {
+    const float2 x = bn.list[i];
+    const bool below = i < a1, out = !below && !in_s(x.x, x.y, t);
+    const uint64_t fp = fx60(x.x), fq = fx60(x.y);
+    v[0] += below ? fp : 0ull;
+    v[1] += below ? fq : 0ull;
+    v[2] += out ? fp : 0ull;
+    v[3] += out ? fq : 0ull;
+  }
+  wg_sum_u64<4>(v, red);
+  bn.P = uni(bn.P - v[0]);
+  bn.Q = uni(bn.Q - v[1]);
+  bn.lo = uni(bt);
+  return uni(c_from(bn.P - uni(v[2]), bn.Q - uni(v[3]), t));
 }
 
 // Inclusive prefix sums (float64) of the n block sums, into pre[]; one workgroup.
@@ -560,18 +686,18 @@ DT_INLINE void build_children(const int *par, const int *tok, int n, int V, int 
   __syncthreads();
 }
 
-// Survivor-list entries per thread: 8 per streamed unit.
-__host__ __device__ inline int accept_list_slots(int V) { return (((V + 7) / 8 + AC_NT - 1) / AC_NT) * 8; }
 DT_INLINE int clamp_nodes(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 DT_INLINE int draft_row(int depth, int L) { return depth < 0 ? 0 : (depth > L - 1 ? L - 1 : depth); }
 DT_INLINE float log2_scale(float T) { return (float)(1.4426950408889634 / (double)T); }
 
 // ---------------------------------------------------------------- lazy walk (one trial / T = 0)
 template <typename T>
-__global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_keep) {
+__global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_list) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
   __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1];
   __shared__ Red red;
+  __shared__ float cz1[DTREE_MAX_CAP + 1], cz2[DTREE_MAX_CAP + 1], cu[DTREE_MAX_CAP + 1];
+  __shared__ int bcnt[AC_NB], boff[AC_NB + 1];
   extern __shared__ double dyn[];  // [nblk] prefix (double) then [nblk] block sums (float)
   const int r = blockIdx.x;
   const int cap = a.tree.cap;
@@ -609,47 +735,54 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_k
     const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
     double *pre = dyn;
     float *blk = reinterpret_cast<float *>(dyn + nblk);
-    float2 *col = a_keep + (size_t)r * accept_list_slots(a.V) * AC_NT + threadIdx.x;
+    Bins bn;
+    bn.cnt = bcnt;
+    bn.off = boff;
+    bn.list = a_list + (size_t)r * a.V;
     for (;;) {
       const T *zt = target + (size_t)j * a.V;
       const T *zd = draft + (size_t)draft_row(dep[j], a.L) * a.V;
       const Row<T> A = make_row(zt, a.V), B = make_row(zd, a.V);
+      // the children's logits and uniforms (the k-th child in slot order takes draw
+      // step + k), prepared once for the whole node
+      for (int i = threadIdx.x; i <= n; i += AC_NT)
+        if (i > j && par[i] == j && tok[i] >= 0 && tok[i] < a.V) {
+          cz1[i] = load_elt(zt, (size_t)tok[i]);
+          cz2[i] = load_elt(zd, (size_t)tok[i]);
+          int k = 0;
+          for (int c = j + 1; c < i; ++c) k += par[c] == j && tok[c] >= 0 && tok[c] < a.V;
+          cu[i] = philox_uniform(a.seed, trial, (uint32_t)r, step + (uint32_t)k);
+        }
       double la, lb;
-      wg_lse2(A, B, s, red, la, lb);
+      wg_lse2(A, B, s, red, la, lb);  // ends with a barrier
       const Norm nt = make_norm(s, la), nd = make_norm(s, lb);
       float t = 0.f;
       double C = 1.0;
-      bool blk_at_t = false;  // blk holds the block sums of the residual at t
-      bool listed = false;    // the survivor list covers the residual at t and beyond
-      int nk = 0;
+      bool built = false;  // the bins hold this node's residual support
       int nxt = -1;
       for (int c = fc[j]; c >= 0; c = ns[c]) {
-        const float z1 = load_elt(zt, (size_t)tok[c]), z2 = load_elt(zd, (size_t)tok[c]);
+        const float z1 = cz1[c], z2 = cz2[c];
         const float q = prob(z2, nd);
         const float pc = resid(prob(z1, nt), q, t) / (float)C;
-        const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
+        const float u = cu[c];
+        ++step;
         if (u * q < pc) {
           nxt = c;
           break;
         }
         const float t2 = t + (float)C;
-        const double C2 = listed ? wg_list_pass(col, nk, t2, red)
-                                 : wg_chain_pass_keep(A, B, nt, nd, t2, blk, nblk, red, col, nk);
-        const bool full = !listed;
-        listed = true;
+        const double C2 = built ? wg_bins_query(bn, t2, red) : wg_bins_build(A, B, nt, nd, t2, bn, red);
+        built = true;
         if (C2 > 0.0) {
-          t = t2;
-          C = C2;
-          blk_at_t = full;
-        } else {
-          blk_at_t = false;
+          t = uni(t2);
+          C = uni(C2);
         }
       }
       if (nxt >= 0) {
         j = nxt;
         continue;
       }
-      if (!blk_at_t) (void)wg_chain_pass(A, B, nt, nd, t, blk, nblk, red);
+      (void)wg_chain_pass(A, B, nt, nd, t, blk, nblk, red);
       __syncthreads();
       wg_prefix(blk, pre, nblk, red);
       const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
@@ -714,7 +847,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_tables(AcceptArgs a, AccTables
       tb.pc[base + c] = resid(prob(z1, nt), q, t) / (float)C;
     }
     const float t2 = t + (float)C;
-    const double C2 = wg_chain_pass(A, B, nt, nd, t2, blk, nblk, red);
+    const double C2 = wg_c_pass(A, B, nt, nd, t2, blk, nblk, red);
     if (C2 > 0.0) {
       t = t2;
       C = C2;
@@ -803,7 +936,7 @@ size_t accept_ws_bytes(int R, int L, int V, int cap) {
   const size_t slots = (size_t)R * (cap + 1);
   const int nblk = (V + AC_BLK - 1) / AC_BLK;
   const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
-  const size_t lists = (size_t)R * accept_list_slots(V) * AC_NT * sizeof(float2);  // the lazy walk's
+  const size_t lists = (size_t)R * V * sizeof(float2);  // the lazy walk's binned supports
   return tables > lists ? tables : lists;
 }
 
