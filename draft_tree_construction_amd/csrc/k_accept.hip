@@ -434,26 +434,21 @@ DT_INLINE double wg_c_pass(const Row<T> &A, const Row<T> &B, const Norm &nt, con
 }
 
 // Ratio bins. Once a node's first rejection has fixed t0, every later t is >= t0, so S(t) is
-// a subset of S(t0). S(t0) is sorted into AC_NB bins by the exact ratio p / q: bin b holds
-// the ratios in [e_b, e_{b+1}) with e_b the float whose bits are bits(t0) + b 2^AC_BSH (the
-// last bin open-ended); a float t lies in bin (bits(t) - bits(t0)) >> AC_BSH. For a query t
-// in bin bt, every member of a lower bin has p < t q and every member of a higher bin has
-// p > t q, so only bin bt needs the exact test. With the bins' members listed contiguously,
-// a query removes the bins it has passed (each member once per node) and tests its own bin.
-DT_INLINE float bin_edge(uint32_t tbb, int b) { return __uint_as_float(tbb + ((uint32_t)b << AC_BSH)); }
-// p >= e q, exact for the terms that count (as in_s; the edges stay below 2^17)
-DT_INLINE bool ge_edge(float p, float q, float e) { return __builtin_fmaf(-e, q, p) >= 0.f; }
-// A guess from an approximate ratio (within a few ulp of p / q, a bin being 2^AC_BSH ulp
-// wide), then one exact step to the bin whose edges bracket p / q. Where the guess can be
-// further off -- q = 0 or a reciprocal out of range -- either the ratio is beyond the last
-// edge or p < 2^-60, whose terms add nothing.
+// a subset of S(t0). The members of S(t0) are sorted into AC_NB bins by their ratio: with
+// e_b the float whose bits are bits(t0) + b 2^AC_BSH, bin b covers [e_b, e_{b+1}) (the last
+// one open-ended), and a float t lies in bin (bits(t) - bits(t0)) >> AC_BSH. A member is
+// placed by an approximate ratio p rcp(q), within a few ulp of p / q while a bin is 2^AC_BSH
+// ulp wide, so it sits at most one bin away from the bin of its exact ratio. (Where the
+// approximation can be further off -- q = 0, or a reciprocal out of range -- the exact ratio
+// is beyond the last edge, or p < 2^-60 and the term adds nothing.) For a query t in bin bt,
+// a member placed in bin bt - 2 or lower has p < t q, one placed in bin bt + 2 or higher has
+// p > t q, and only bins bt - 1 .. bt + 1 need the exact test. With the bins' members listed
+// contiguously, a query removes the bins it has left behind (each member once per node) and
+// tests the three bins around t.
 DT_INLINE int ratio_bin(float p, float q, uint32_t tbb) {
   const float rho = q > 0.f ? p * __builtin_amdgcn_rcpf(q) : kInf;
   const int d = (int)(__float_as_uint(rho) - tbb);
-  const int b = d < 0 ? 0 : min(d >> AC_BSH, AC_NB - 1);
-  const bool dn = b > 0 && !ge_edge(p, q, bin_edge(tbb, b));
-  const bool up = b < AC_NB - 1 && ge_edge(p, q, bin_edge(tbb, b + 1));
-  return b + (up ? 1 : 0) - (dn ? 1 : 0);
+  return d < 0 ? 0 : min(d >> AC_BSH, AC_NB - 1);
 }
 DT_INLINE int t_bin(float t, uint32_t tbb) { return min((int)(__float_as_uint(t) - tbb) >> AC_BSH, AC_NB - 1); }
 
@@ -539,7 +534,8 @@ DT_INLINE double wg_bins_build(const Row<T> &A, const Row<T> &B, const Norm &nt,
 // C(t) for t >= the last query's t (>= t0) from the bins.
 DT_INLINE double wg_bins_query(Bins &bn, float t, Red &red) {
   const int bt = t_bin(t, bn.tbb);
-  const int a0 = bn.off[bn.lo], a1 = bn.off[bt], b1 = bn.off[bt + 1];
+  const int lo = max(bn.lo, bt - 1);  // bins below lo are left behind
+  const int a0 = bn.off[bn.lo], a1 = bn.off[lo], b1 = bn.off[min(bt + 2, AC_NB)];
   uint64_t v[4] = {0, 0, 0, 0};  // removed bins (p, q); members of bin bt outside S(t) (p, q)
   for (int i = a0 + threadIdx.x; i < b1; i += AC_NT) {
     const float2 x = bn.list[i];
@@ -553,7 +549,7 @@ DT_INLINE double wg_bins_query(Bins &bn, float t, Red &red) {
   wg_sum_u64<4>(v, red);
   bn.P = uni(bn.P - v[0]);
   bn.Q = uni(bn.Q - v[1]);
-  bn.lo = uni(bt);
+  bn.lo = uni(lo);
   return uni(c_from(bn.P - uni(v[2]), bn.Q - uni(v[3]), t));
 }
 
