@@ -98,6 +98,7 @@ struct DwState {
   uint16_t *PT;     // [V][64]: row v holds P[k][v] at slot half*32 + kb*8 + e, k = 16kb + 8half + e
   uint16_t *UT;     // [L][64][dm]: U transposed, row j of depth d holds U[d][k][j] over k
   float *pmax;      // [64]: max_v |P[j][v]|
+  float *pm_part;   // [ceil(V / DW_TP)][64]: the P tiles' maxima
   uint16_t *hx;     // [S][DW_HX]: B-operand rows of the states
   float *bref;      // [S]: ref of each state (a bf16 value)
   int *wide;        // [ntile]: tile uses a running max
@@ -115,62 +116,95 @@ struct DwDev {
 };
 
 // ---------------------------------------------------------------- prep: P^T and column maxima
-__global__ void k_dw_zero_f32(float *p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0.f;
-}
-
-// PT tile of 256 tokens; also max_v |P[k][v]| per k, reduced over the tile and folded in
-// with an integer atomic max (non-negative floats order like their bit patterns). 16-byte
-// loads and stores when every row of P is 16-byte aligned (V % 8 == 0) and the tile is
-// whole, element-wise otherwise.
+// PT tile of 256 tokens, thread t writing the 128-byte row of token v0 + t (its reads of the
+// LDS tile run along a row, consecutive lanes on consecutive tokens: no bank conflicts).
+// Also max_v |P[k][v]| per k: each workgroup leaves its tile's maxima in part[blockIdx.x]
+// (folded by an extra block of the next launch). 16-byte loads when every row of P is 16-byte aligned
+// (V % 8 == 0) and the tile is whole, element-wise otherwise.
 constexpr int DW_TP = 256;
+constexpr int DW_TPP = DW_TP + 2;  // tile pitch: an odd number of 4-byte words
 __global__ __launch_bounds__(DW_NT) void k_dw_transpose_p(const uint16_t *__restrict__ P, int V, uint16_t *PT,
-                                                          float *pmax) {
-  __shared__ uint16_t tile[64][DW_TP + 8];
-  __shared__ float qmax[4][64];
-  const int v0 = blockIdx.x * DW_TP;
+                                                          float *part) {
+  __shared__ uint16_t tile[64 * DW_TPP];
+  __shared__ unsigned int qmax[64];
+  const int v0 = blockIdx.x * DW_TP, t = threadIdx.x;
+  if (t < 64) qmax[t] = 0u;
+  __syncthreads();
   const bool vec = (V & 7) == 0 && v0 + DW_TP <= V;
-  if (vec) {
-    for (int i = threadIdx.x; i < 64 * (DW_TP / 8); i += DW_NT) {
-      const int k = i / (DW_TP / 8), q = i % (DW_TP / 8);
-      const u32x4 x = *reinterpret_cast<const u32x4 *>(P + (size_t)k * V + v0 + q * 8);
-      *reinterpret_cast<u32x4 *>(&tile[k][q * 8]) = x;
+  // tile[k][vv] = P[k][v0 + vv]; chunk i = 8 tokens of row i / 32
+  for (int i = t; i < 64 * (DW_TP / 8); i += DW_NT) {
+    const int k = i / (DW_TP / 8), c = i % (DW_TP / 8);
+    uint32_t w[4];
+    if (vec) {
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(P + (size_t)k * V + v0 + c * 8);
+      w[0] = x.x;
+      w[1] = x.y;
+      w[2] = x.z;
+      w[3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = v0 + c * 8 + 2 * e;
+        const uint32_t lo = v < V ? P[(size_t)k * V + v] : 0u, hi = v + 1 < V ? P[(size_t)k * V + v + 1] : 0u;
+        w[e] = lo | (hi << 16);
+      }
     }
-  } else {
-    for (int i = threadIdx.x; i < 64 * DW_TP; i += DW_NT) {
-      const int k = i / DW_TP, vv = i % DW_TP;
-      tile[k][vv] = (v0 + vv < V) ? P[(size_t)k * V + v0 + vv] : (uint16_t)0;
+    uint32_t m = 0u;  // bits of max |x| (non-negative floats order like their bit patterns)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *reinterpret_cast<uint32_t *>(&tile[k * DW_TPP + c * 8 + 2 * e]) = w[e];
+      m = max(m, max((w[e] & 0x7FFFu) << 16, (w[e] >> 16 & 0x7FFFu) << 16));
     }
+    atomicMax(&qmax[k], m);
   }
   __syncthreads();
   // PT row v, 16-byte piece q holds slots 8q..8q+7: k = 16 (q & 3) + 8 (q >> 2) + e
-  for (int i = threadIdx.x; i < DW_TP * 8; i += DW_NT) {
-    const int vv = i >> 3, q = i & 7;
-    if (v0 + vv >= V) continue;
-    const int kb = 16 * (q & 3) + 8 * (q >> 2);
-    uint32_t w[4];
+  if (v0 + t < V) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[kb + 2 * e][vv] | ((uint32_t)tile[kb + 2 * e + 1][vv] << 16);
-    *reinterpret_cast<u32x4 *>(PT + (size_t)(v0 + vv) * 64 + q * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    for (int q = 0; q < 8; ++q) {
+      const int kb = 16 * (q & 3) + 8 * (q >> 2);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)tile[(kb + 2 * e) * DW_TPP + t] | ((uint32_t)tile[(kb + 2 * e + 1) * DW_TPP + t] << 16);
+      *reinterpret_cast<u32x4 *>(PT + (size_t)(v0 + t) * 64 + q * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
   }
-  {
-    const int k = threadIdx.x & 63, qq = threadIdx.x >> 6;
-    float m = 0.f;
-    for (int vv = qq * (DW_TP / 4); vv < (qq + 1) * (DW_TP / 4); ++vv) m = fmaxf(m, fabsf(bf16_to_f32(tile[k][vv])));
-    qmax[qq][k] = m;
-  }
+  if (t < 64) part[(size_t)blockIdx.x * 64 + t] = __uint_as_float(qmax[t]);
+}
+
+// pmax[k] = max over the tiles' maxima (part has ntp rows of 64), eight loads in flight.
+DT_INLINE void dw_fold_pmax(const float *__restrict__ part, int ntp, float *pmax) {
+  __shared__ unsigned int qm[64];
+  const int t = threadIdx.x;
+  if (t < 64) qm[t] = 0u;
   __syncthreads();
-  if (threadIdx.x < 64) {
-    const int k = threadIdx.x;
-    const float m = fmaxf(fmaxf(qmax[0][k], qmax[1][k]), fmaxf(qmax[2][k], qmax[3][k]));
-    atomicMax(reinterpret_cast<unsigned int *>(pmax) + k, __float_as_uint(m));
+  const int n = ntp * 64;  // entry i belongs to k = i % 64 = t % 64
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i0 = t; i0 < n; i0 += 8 * DW_NT) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * DW_NT;
+      m[u] = fmaxf(m[u], i < n ? part[i] : 0.f);
+    }
   }
+#pragma unroll
+  for (int u = 1; u < 8; ++u) m[0] = fmaxf(m[0], m[u]);
+  atomicMax(&qm[t & 63], __float_as_uint(m[0]));
+  __syncthreads();
+  if (t < 64) pmax[t] = __uint_as_float(qm[t]);
 }
 
 // UT[d][j][k] = U[d][k][j]: tiles of 64 k-rows (d_model % 64 == 0), 16-byte loads and stores.
-__global__ __launch_bounds__(DW_NT) void k_dw_transpose_u(const uint16_t *__restrict__ U, int dm, uint16_t *UT) {
+// The extra block (0, L) folds the P tiles' maxima into pmax.
+__global__ __launch_bounds__(DW_NT) void k_dw_transpose_u(const uint16_t *__restrict__ U, int dm, int L, uint16_t *UT,
+                                                          const float *__restrict__ part, int ntp, float *pmax) {
   __shared__ uint16_t tile[64][72];
   const int d = blockIdx.y, k0 = blockIdx.x * 64;
+  if (d == L) {
+    if (blockIdx.x == 0) dw_fold_pmax(part, ntp, pmax);
+    return;
+  }
   const uint16_t *Ud = U + (size_t)d * dm * 64;
   for (int i = threadIdx.x; i < 64 * 8; i += DW_NT) {
     const int k = i >> 3, q = i & 7;
@@ -765,7 +799,7 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
 
 // ---------------------------------------------------------------- host side
 struct DwLayout {
-  size_t PT, UT, pmax, hx, bref, wide, part_s, part_m, lq, total;
+  size_t PT, UT, pmax, pm_part, hx, bref, wide, part_s, part_m, lq, total;
 };
 
 static DwLayout dw_layout(const DwDims &g) {
@@ -779,6 +813,7 @@ static DwLayout dw_layout(const DwDims &g) {
   l.PT = take((size_t)g.V * 64 * 2);
   l.UT = take((size_t)g.L * 64 * g.dm * 2);
   l.pmax = take(64 * sizeof(float));
+  l.pm_part = take((size_t)((g.V + DW_TP - 1) / DW_TP) * 64 * sizeof(float));
   l.hx = take((size_t)g.S * DW_HX * 2);
   l.bref = take((size_t)g.S * sizeof(float));
   l.wide = take((size_t)g.ntile * sizeof(int));
@@ -803,6 +838,7 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   s.PT = reinterpret_cast<uint16_t *>(w + l.PT);
   s.UT = reinterpret_cast<uint16_t *>(w + l.UT);
   s.pmax = reinterpret_cast<float *>(w + l.pmax);
+  s.pm_part = reinterpret_cast<float *>(w + l.pm_part);
   s.hx = reinterpret_cast<uint16_t *>(w + l.hx);
   s.bref = reinterpret_cast<float *>(w + l.bref);
   s.wide = reinterpret_cast<int *>(w + l.wide);
@@ -816,9 +852,10 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   dv.root_tok = a.root_tok;
   dv.beta = a.beta;
 
-  hipLaunchKernelGGL(k_dw_zero_f32, dim3(1), dim3(64), 0, st, s.pmax, 64);
-  hipLaunchKernelGGL(k_dw_transpose_p, dim3((a.V + DW_TP - 1) / DW_TP), dim3(DW_NT), 0, st, a.P, a.V, s.PT, s.pmax);
-  hipLaunchKernelGGL(k_dw_transpose_u, dim3(a.dm / 64, a.L), dim3(DW_NT), 0, st, a.U, a.dm, s.UT);
+  const int ntp = (a.V + DW_TP - 1) / DW_TP;
+  hipLaunchKernelGGL(k_dw_transpose_p, dim3(ntp), dim3(DW_NT), 0, st, a.P, a.V, s.PT, s.pm_part);
+  hipLaunchKernelGGL(k_dw_transpose_u, dim3(a.dm / 64, a.L + 1), dim3(DW_NT), 0, st, a.U, a.dm, a.L, s.UT, s.pm_part,
+                     ntp, s.pmax);
   hipLaunchKernelGGL(k_dw_states, dim3(g.ntile), dim3(DW_NT), 0, st, s, dv, g, a.dtype == DTREE_BF16 ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
