@@ -4,24 +4,29 @@
 // tokens ranked first by (logit desc, id asc) with their log-probs z - LSE (DDTree blog
 // 3.3; DARTree Algorithm 1 step 4).
 //
-// Design (gfx950). A workgroup of 256 threads streams a row segment in chunks of
-// 256 x 4 sixteen-byte vectors (coalesced, branch-free, the next chunk prefetched into
-// registers); each thread keeps an online (max, sum-exp) pair -- exp2 of one FMA per
-// element, fp32 terms, float64 accumulation -- and records each chunk's maximum in LDS
-// (as bf16 rounded up, which can only over-select). One or two chunks before the end
-// (checkpoint c*), each wave finds the ceil(K/4)-th largest of its 64 running lane
-// maxima with ballots; the smallest over the four waves has at least K distinct elements at or
-// above it, so it bounds the K-th value from below. Only lane-chunks whose maximum
-// reaches the bound can hold top-K elements (about K of them): each wave lists its own in
-// LDS and its lane j issues the loads of the j-th 64-byte span right away, consuming them
-// after the last chunks are streamed, so the re-read is one round hidden behind the stream.
-// Elements >= bound are keyed (value desc, id asc) into LDS, their slots reserved once
-// per wave; with at most one candidate per thread each thread's rank is the number of
-// keys above its own, else each wave takes the top 64 of a quarter with register
-// bitonic sorts and one wave merges the four lists. Pathological rows whose candidates overflow the
-// buffer are re-streamed with the threshold raised to the K-th key of the full buffer
-// until a pass fits. Rows too short to fill the GPU are split over several workgroups
-// whose partial (max, sum, top-K) are merged by a second kernel.
+// Design (gfx950). A workgroup of 256 threads streams a row segment in chunks of 256 x 2
+// sixteen-byte vectors; the 64 lanes of a wave read 1 KiB contiguous per load (fully
+// coalesced), two chunks in flight per thread through a register ring. Each thread keeps an
+// online (max, sum-exp) pair -- exp2 of one FMA per element, fp32 terms, float64
+// accumulation -- and records each chunk's maximum (its "span" of 16 or 8 elements) in LDS
+// as a 16-bit code rounded up, so the record can only over-select. Nothing else happens
+// per element: the top-K is found from the record.
+// Four chunks before the end the workgroup takes a bound on the row's K-th largest value
+// -- each wave the ceil(K/4)-th largest of its lanes' running maxima (ballots on the top 16
+// bits of the order-preserving code, rounded down), the smallest over the four waves (each
+// certifies ceil(K/4) distinct elements, so together K). It lists the recorded spans that
+// reach the bound and issues their loads at once (lane j of a wave the wave's j-th span),
+// hidden behind the last chunks; those last chunks are checked against the bound while in
+// registers and the spans that reach it are kept in LDS. The candidates -- elements at or
+// above the bound in the listed and kept spans -- are keyed (value desc, id asc), and each
+// one's rank is the number of keys above it. Rows with more listed spans or candidates than
+// LDS holds (long runs of ties, sorted rows) are re-streamed with the threshold raised to
+// the K-th key found until a pass fits. Rows too short to fill the GPU are split over
+// several workgroups whose partial (max, sum, top-K) are merged by a second kernel.
+// The four workgroups that share a CU start together; served oldest first, the last would
+// finish its stream long after the first. Each wave therefore rotates its priority with
+// the global clock (shifted by its dispatch position), so every workgroup holds each
+// priority equally often and the streams end together.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,12 +34,15 @@ namespace dt {
 
 constexpr int RS_NT = 256;
 constexpr int RS_NW = RS_NT / 64;
-constexpr int RS_U = 4;        // 16-byte vectors per thread per chunk
-constexpr int RS_BUF = 2048;   // LDS candidate keys
-constexpr int RS_NG = 32;      // recorded chunk(-group) maxima per thread
-constexpr int RS_WL = 128;     // listed re-read spans per wave
-constexpr int RS_WBUF = RS_BUF / RS_NW;  // candidate keys per wave region
-constexpr int RS_D = 2;        // chunks in flight per wave ahead of the one being consumed
+constexpr int RS_U = 2;                 // 16-byte vectors per thread per chunk
+constexpr int RS_NG = 48;               // recorded chunk(-group) maxima per thread
+constexpr int RS_WL = 128;              // listed spans per wave
+constexpr int RS_PRE = 4;               // chunks streamed after the bound (even)
+constexpr int RS_WSP = 32;              // spans of those chunks kept per wave
+constexpr int RS_KEYS = 512;            // candidate keys
+constexpr int RS_WK = RS_KEYS / RS_NW;  // candidate keys per wave region
+constexpr int RS_FB = 2048;             // keys the re-stream fallback holds (in the record)
+constexpr int RS_MBUF = 2048;           // merge kernel: split partial keys per row
 
 struct RowPart {
   uint64_t *keys;  // [rows*S][K]
@@ -43,17 +51,30 @@ struct RowPart {
 };
 constexpr double kLn2d = 0.6931471805599453;
 constexpr double kLog2ed = 1.4426950408889634;
+constexpr float kFltLowest = -3.402823466e38f;
 
-// Top 64 keys (sorted descending across the lanes) of keys[0..n).
-DT_INLINE uint64_t wave_top64(const uint64_t *keys, int n) {
-  const int lane = threadIdx.x & 63;
-  uint64_t top = 0;
-  for (int g = 0; g < n; g += 64) {
-    const uint64_t v = (g + lane < n) ? keys[g + lane] : 0ull;
-    const uint64_t srt = wave_sort64_desc_u64(v);
-    top = (g == 0) ? srt : wave_merge_top64_u64(top, srt);
+// The kw-th largest (1 <= kw <= 64) of the lanes' 16-bit prefixes of the order-preserving
+// code, found bit by bit with ballots (wave-uniform; no LDS traffic). Every value whose
+// prefix is >= it is >= bound16(prefix).
+DT_INLINE uint32_t wave_kth_prefix16(float v, int kw) {
+  const uint32_t key = ord_f32(v) >> 16;
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    if (__popcll(__ballot(key >= c)) >= kw) t = c;
   }
-  return top;
+  return t;
+}
+// Smallest float whose 16-bit code prefix is t; prefixes at or below -inf's give the lowest
+// finite float, so padding (-inf) never reaches a bound.
+DT_INLINE float bound16(uint32_t t) { return t < 0x0080u ? kFltLowest : unord_f32(t << 16); }
+// Top 16 bits of the order-preserving code of a finite (or -inf) x, rounded up: the record
+// r of a maximum x satisfies r << 16 >= ord_f32(x), so comparing r << 16 with a bound's code
+// never drops a span that reaches the bound.
+DT_INLINE uint16_t up_prefix16(float x) {
+  const uint32_t o = ord_f32(x);
+  return (uint16_t)((o >> 16) + ((o & 0xFFFFu) != 0u));
 }
 
 // Exclusive prefix over the wave's lanes of cnt (0 <= cnt < 64) and the wave total, from
@@ -69,54 +90,44 @@ DT_INLINE int wave_prefix(int cnt, int &total) {
   total = tot;
   return pre;
 }
-// Slots for cnt items per lane from an LDS counter with one atomic per wave: returns this
-// lane's first slot (the lanes' items are consecutive, in lane order). Wave-uniform call.
-DT_INLINE int wave_reserve(int *ctr, int cnt) {
-  int total;
-  const int pre = wave_prefix(cnt, total);
-  int base = 0;
-  if (total > 0) {
-    if ((threadIdx.x & 63) == 0) base = atomicAdd(ctr, total);
-    base = __builtin_amdgcn_readlane(base, 0);
-  }
-  return base + pre;
-}
-// The kw-th largest value (1 <= kw <= 64) among the wave's lanes, found bit by bit on the
-// order-preserving code with ballots (exact; no LDS traffic).
-DT_INLINE float wave_kth_largest(float v, int kw) {
-  const uint32_t key = ord_f32(v);
-  uint32_t t = 0;
+
+// Raw 16-byte vector of T built from single elements (ids outside [0, v1) read as -inf).
+DT_INLINE u32x4 gather_vec(const uint16_t *p, int b, int v1) {
+  uint32_t w[4];
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = t | (1u << b);
-    if (__popcll(__ballot(key >= c)) >= kw) t = c;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (b + 2 * i < v1) ? (uint32_t)p[b + 2 * i] : 0xFF80u;
+    const uint32_t hi = (b + 2 * i + 1 < v1) ? (uint32_t)p[b + 2 * i + 1] : 0xFF80u;
+    w[i] = lo | (hi << 16);
   }
-  return unord_f32(t);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+DT_INLINE u32x4 gather_vec(const float *p, int b, int v1) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (b + i < v1) ? __float_as_uint(p[b + i]) : 0xFF800000u;
+  return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// bf16 rounded toward +inf (as an ordered 16-bit code) and back; -inf stays -inf.
-DT_INLINE uint16_t up16(float x) {
-  const uint32_t u = __float_as_uint(x);
-  uint32_t h = u >> 16;
-  if ((u & 0xFFFFu) != 0 && !(u & 0x80000000u)) h += 1;  // positive: bump; negative: truncate
-  return (uint16_t)h;
-}
-DT_INLINE float from16(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
-
-template <typename T>
+// FAST: every segment starts 16-byte aligned and holds whole vectors (V a multiple of the
+// vector width, logits 16-byte aligned); otherwise elements are gathered one by one.
+template <typename T, bool FAST>
 __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ logits, int V, int K, int S,
                                                        int seg, RowPart part, RowOut out) {
   constexpr int EPV = Vec<T>::N;
-  constexpr int E = RS_U * EPV;           // elements per thread per chunk
-  constexpr int CH = RS_NT * E;           // elements per chunk
-  __shared__ uint64_t buf[RS_BUF];        // candidate keys: one region of RS_WBUF per wave
-  __shared__ uint16_t s_gm[RS_NG][RS_NT];
-  __shared__ int s_list[RS_NW][RS_WL];
+  constexpr int E = RS_U * EPV;  // elements per thread per chunk
+  constexpr int CH = RS_NT * E;  // elements per chunk
+  __shared__ uint64_t s_rec[RS_NG * RS_NT / 4];  // recorded maxima (16-bit codes); fallback keys
+  __shared__ int s_list[RS_NW][RS_WL];           // listed spans: (group << 8) | lane
+  __shared__ u32x4 s_span[RS_U][RS_NW * RS_WSP];  // spans of the last chunks that reach the bound
+  __shared__ int s_spid[RS_NW * RS_WSP];          // (chunk << 8) | lane of each stored span
+  __shared__ uint64_t keys[RS_KEYS];
   __shared__ uint64_t s_top[64];
-  __shared__ float s_wb[2][RS_NW], s_wm[RS_NW];
+  __shared__ float s_wb[RS_NW], s_wm[RS_NW];
   __shared__ double s_ws[RS_NW];
-  __shared__ int s_rn[RS_NW];
-  __shared__ int s_cnt;
+  __shared__ int s_kn[RS_NW], s_over[RS_NW];
+  __shared__ int s_nkey;  // re-stream fallback counter
+  uint16_t(*s_gm)[RS_NT] = reinterpret_cast<uint16_t(*)[RS_NT]>(s_rec);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = blockIdx.x / S;
@@ -125,71 +136,53 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   const int v1 = min(V, v0 + seg);
   const int len = max(0, v1 - v0);
   const T *p = logits + (size_t)row * (size_t)V;
-  // vector path: 16-byte aligned segment of whole vectors
-  const bool fast = ((reinterpret_cast<uintptr_t>(p + v0) & 15) == 0) && (len % EPV == 0) && len >= EPV;
-  const int nchunks = (len + CH - 1) / CH;
-  const int nfull = len / CH;  // chunks entirely inside the segment
-  const int nround = (nchunks + RS_D - 1) / RS_D * RS_D;  // whole ring turns (tail chunks masked)
-  const int cpg = (nround + RS_NG - 1) / RS_NG;           // chunks per recorded group
-  const int ngroups = cpg > 0 ? (nround + cpg - 1) / cpg : 0;
+  const int nchunks = max(1, (len + CH - 1) / CH);
+  const int nround = (nchunks + 1) & ~1;        // whole ring turns (tail chunks masked)
+  const int nfull = len / CH;                   // chunks entirely inside the segment
+  const int cB = max(0, nround - RS_PRE);       // chunks [0, cB) are recorded and re-read
+  const int cpg = max(1, (cB + RS_NG - 1) / RS_NG);  // chunks per recorded group
+  const int ng = (cB + cpg - 1) / cpg;
+  const int kw = (K + RS_NW - 1) / RS_NW;
+
+  // element layout: vector u of chunk c on lane ln starts at element c*CH + (u*256 + ln)*EPV
+  auto elem0 = [&](int c, int u, int ln) { return v0 + c * CH + (u * RS_NT + ln) * EPV; };
+  // vectors of chunk c of lane ln (ln = tid in the stream)
+  auto load_span = [&](int c, int ln, u32x4 *r) {
+    if constexpr (FAST) {
+      // buffer view of the segment: reads past its end return zero and touch no memory
+      // (those elements are masked when widened)
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<T *>(p + v0), (short)0, len * (int)sizeof(T), 0x00020000);
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u)
+        r[u] = (u32x4)__builtin_amdgcn_raw_buffer_load_b128(rs, (c * CH + (u * RS_NT + ln) * EPV) * (int)sizeof(T),
+                                                            0, 0);
+    } else {
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) r[u] = gather_vec(p, elem0(c, u, ln), v1);
+    }
+  };
+  // widen a span; elements at or past the segment's end, or all of them when !valid, become -inf
+  auto widen_span = [&](const u32x4 *r, int c, int ln, bool valid, float *x) {
+#pragma unroll
+    for (int u = 0; u < RS_U; ++u) Vec<T>::widen(r[u], x + u * EPV);
+    if (!valid || c >= nfull) {
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) {
+        const int b = elem0(c, u, ln);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) x[u * EPV + e] = (valid && b + e < v1) ? x[u * EPV + e] : -kInf;
+      }
+    }
+  };
 
   float m = -kInf, mh = 0.f;  // running max; mh = fp32(m log2 e) once m is finite
   double s = 0.0;             // sum of exp2(x log2e - mh): the true sum times 2^(m log2e - mh)
   float gm = -kInf;           // maximum of the current recorded group
   int gi = 0, gk = 0;         // recorded group and position in it (wave-uniform)
-  float th = kInf;            // bound once known (elements >= th are candidates)
-  int wn = 0;                 // keys in this wave's region (wave-uniform)
-  uint64_t *const wbuf = buf + w * RS_WBUF;
-
-  // element layout: lane ln holds E consecutive elements of each chunk (one 64-byte span)
-  auto elem0 = [&](int c, int u, int ln) { return v0 + c * CH + ln * E + u * EPV; };
-  // buffer view of the segment (vector path): reads past its end return zero and touch no
-  // memory, so the ring and the re-reads need no address clamping
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T *>(p + v0), (short)0, fast ? len * (int)sizeof(T) : 0, 0x00020000);
-  auto bload = [&](int c, int u, int ln) -> u32x4 {
-    return (u32x4)__builtin_amdgcn_raw_buffer_load_b128(rsrc, (c * CH + ln * E + u * EPV) * (int)sizeof(T), 0, 0);
-  };
-  auto gload = [&](int b, float *x) {
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) x[e] = (b + e >= 0 && b + e < v1) ? load_elt(p, (size_t)(b + e)) : -kInf;
-  };
-  // vectors of a span (chunk c, lane ln) at or past the segment's end, or all of it when
-  // !valid, become -inf
-  auto mask_span = [&](float *x, int c, int ln, bool valid) {
-#pragma unroll
-    for (int u = 0; u < RS_U; ++u) {
-      const bool ok = valid && elem0(c, u, ln) < v1;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) x[u * EPV + e] = ok ? x[u * EPV + e] : -kInf;
-    }
-  };
-  // key the elements >= th of a span (chunk c, lane ln) into the wave's region (wave-uniform)
-  auto append_span = [&](const float *x, int c, int ln) {
-    int hits = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) hits += x[e] >= th;
-    if (__ballot(hits > 0)) {
-      int total;
-      int slot = wn + wave_prefix(hits, total);
-#pragma unroll
-      for (int u = 0; u < RS_U; ++u) {
-        const int b = elem0(c, u, ln);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float xv = x[u * EPV + e];
-          if (xv >= th) {
-            if (slot < RS_WBUF) wbuf[slot] = make_key(xv, (uint32_t)(b + e));
-            ++slot;
-          }
-        }
-      }
-      wn += total;
-    }
-  };
-  // online (max, sum-exp) over this thread's span of a chunk; the running maximum of the
-  // chunk group is stored every chunk (no branch in the streaming loop)
-  auto consume = [&](const float *x) {
+  // online (max, sum-exp) over this thread's span of a chunk; returns the span's maximum.
+  // Chunks before cB are recorded.
+  auto consume = [&](const float *x, int c) {
     float cm = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) cm = fmaxf(cm, x[e]);
@@ -209,57 +202,90 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
       a3 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 3], kLog2e, -mh));
     }
     s += (double)((a0 + a1) + (a2 + a3));
-    gm = (gk == 0) ? cm : fmaxf(gm, cm);
-    s_gm[gi][tid] = up16(gm);
-    if (++gk == cpg) {
-      gk = 0;
-      ++gi;
+    if (c < cB) {
+      gm = (gk == 0) ? cm : fmaxf(gm, cm);
+      s_gm[gi][tid] = up_prefix16(gm);
+      if (++gk == cpg) {
+        gk = 0;
+        ++gi;
+      }
     }
+    return cm;
+  };
+  // Fair share of the CU: the four workgroups on a CU start together and would otherwise be
+  // served oldest first (the last one finishing long after the first). Every ring turn a
+  // wave takes the priority given by the global clock, shifted by its dispatch position, so
+  // over time each workgroup holds each priority equally often.
+  const int prio_shift = (int)((blockIdx.x >> 8) & 3);
+  auto rotate_priority = [&]() {
+    const int ph = (int)((wall_clock64() >> 9) + prio_shift) & 3;
+    if (ph == 0)
+      __builtin_amdgcn_s_setprio(0);
+    else if (ph == 1)
+      __builtin_amdgcn_s_setprio(1);
+    else if (ph == 2)
+      __builtin_amdgcn_s_setprio(2);
+    else
+      __builtin_amdgcn_s_setprio(3);
   };
 
-  // ---- bound: the ceil(K/4)-th largest lane maximum of each wave, the smallest over the
-  // waves (every wave has that many distinct elements at or above it). The final one also
-  // exchanges the waves' largest scaled maxima (mh of the lanes that saw data).
-  float MH = -kInf;  // block maximum of mh (final bound only)
-  auto block_bound = [&](int slot) {
-    const int kw = (K + RS_NW - 1) / RS_NW;
-    const float b = (kw <= 64) ? wave_kth_largest(m, kw) : -kInf;
-    const float wmh = slot ? wave_max(m == -kInf ? -kInf : mh) : 0.f;
-    if (lane == 0) {
-      s_wb[slot][w] = b;
-      if (slot) s_wm[w] = wmh;
+  // ---- stream, part 1: chunk c sits in ring slot c & 1 and is refilled with chunk c + 2 as
+  // soon as it is widened; chunks before cB are recorded
+  u32x4 R0[RS_U], R1[RS_U];
+  load_span(0, tid, R0);
+  load_span(1, tid, R1);
+  for (int c = 0; c < cB; c += 2) {
+    rotate_priority();
+    {
+      float x[E];
+      widen_span(R0, c, tid, true, x);
+      load_span(c + 2, tid, R0);
+      consume(x, c);
     }
+    {
+      float x[E];
+      widen_span(R1, c + 1, tid, true, x);
+      load_span(c + 3, tid, R1);
+      consume(x, c + 1);
+    }
+  }
+
+  // ---- bound: chunks cB and cB + 1 are taken in first; then each wave's ceil(K/4)-th
+  // largest running lane maximum, the smallest over the waves (each certifies ceil(K/4)
+  // distinct elements, so together K). Every later bound would be higher, so th holds for
+  // the rest of the row.
+  float cm0, cm1;
+  {
+    float x[E];
+    widen_span(R0, cB, tid, true, x);
+    cm0 = consume(x, cB);
+    widen_span(R1, cB + 1, tid, true, x);
+    cm1 = consume(x, cB + 1);
+  }
+  float th;
+  {
+    const float b = bound16(wave_kth_prefix16(m, kw));
+    if (lane == 0) s_wb[w] = b;
     __syncthreads();
-    float t = s_wb[slot][0];
+    th = s_wb[0];
 #pragma unroll
-    for (int i = 1; i < RS_NW; ++i) t = fminf(t, s_wb[slot][i]);
-    if (slot) {
-      MH = s_wm[0];
-#pragma unroll
-      for (int i = 1; i < RS_NW; ++i) MH = fmaxf(MH, s_wm[i]);
-    }
-    return fmaxf(t, -3.402823466e38f);  // padding (-inf) never qualifies
-  };
-  // ---- per-wave list of the (group, lane) spans whose recorded maximum reaches th, over
-  // the groups of chunks [0, climit); lane j may then load its wave's j-th span at once
-  int nlist = 0;           // entries in this wave's list (wave-uniform)
-  int own_q = 0;           // list index of this lane's first qualifying group
-  uint32_t own_qual = 0;   // this lane's qualifying groups
-  int climit = 0;          // listed spans cover chunks [0, climit)
-  int my_ent = -1;         // entry whose span this lane has loaded into ra
+    for (int i = 1; i < RS_NW; ++i) th = fminf(th, s_wb[i]);
+  }
+  // ---- the recorded groups (chunks before cB) that reach th: listed per wave, lane j of a
+  // wave loads the wave's j-th listed span at once (consumed after the last chunks)
+  int nlist = 0;       // entries in this wave's list (wave-uniform)
+  int own_q = 0;       // list index of this lane's first listed group
+  uint64_t own = 0;    // this lane's listed groups
+  int my_ent = -1;     // entry whose (first) chunk this lane has preloaded into ra
   u32x4 ra[RS_U] = {};
-  auto make_list = [&](int cl, bool preload) {
-    climit = cl;
-    const int ng = (cl + cpg - 1) / cpg;
-    uint32_t qual = 0;
-#pragma unroll
-    for (int g = 0; g < RS_NG; ++g) qual |= (uint32_t)((g < ng) & (from16(s_gm[g][tid]) >= th)) << g;
-    own_qual = qual;
-    own_q = wave_prefix(__builtin_popcount(qual), nlist);
+  if (cB > 0) {
+    const uint32_t o1 = ord_f32(th);
+#pragma unroll 4
+    for (int g = 0; g < ng; ++g) own |= (uint64_t)(((uint32_t)s_gm[g][tid] << 16) >= o1) << g;
+    own_q = wave_prefix(__popcll(own), nlist);
     int q = own_q;
-    while (qual) {
-      const int g = __builtin_ctz(qual);
-      qual &= qual - 1;
+    for (uint64_t b = own; b; b &= b - 1) {
+      const int g = __builtin_ctzll(b);
       if (q < RS_WL) s_list[w][q] = (g << 8) | tid;
       ++q;
     }
@@ -267,68 +293,63 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (preload && lane < nlist) {
+    if (lane < min(nlist, RS_WL)) {
       my_ent = s_list[w][lane];
-      const int c = my_ent >> 8, ln = my_ent & 255;
-#pragma unroll
-      for (int u = 0; u < RS_U; ++u) ra[u] = bload(c, u, ln);
-    }
-  };
-
-  // cA: chunks before it are re-read from memory, chunks from it on stay in registers
-  const int cA = fast ? nround - RS_D : nround;
-  u32x4 R[RS_D][RS_U];
-  if (fast) {
-    // ring of RS_D chunks in flight per wave; a chunk's slots are refilled (chunk c + RS_D)
-    // as soon as it is widened. One ring turn before the end a first bound lists the spans
-    // that may hold candidates and their loads are issued; the last turn keeps its raw
-    // chunks in the ring, so no memory round trip is left after the stream.
-#pragma unroll
-    for (int j = 0; j < RS_D; ++j)
-#pragma unroll
-      for (int u = 0; u < RS_U; ++u) R[j][u] = bload(j, u, tid);
-    for (int c = 0; c < cA; c += RS_D) {
-#pragma unroll
-      for (int j = 0; j < RS_D; ++j) {
-        float x[E];
-#pragma unroll
-        for (int u = 0; u < RS_U; ++u) {
-          Vec<T>::widen(R[j][u], x + u * EPV);
-          R[j][u] = bload(c + j + RS_D, u, tid);
-        }
-        if (c + j >= nfull) mask_span(x, c + j, tid, true);
-        consume(x);
-      }
-    }
-    if (cA > 0) {
-      th = block_bound(0);
-      make_list(cA, cpg == 1);
-    }
-#pragma unroll
-    for (int j = 0; j < RS_D; ++j) {
-      float x[E];
-#pragma unroll
-      for (int u = 0; u < RS_U; ++u) Vec<T>::widen(R[j][u], x + u * EPV);
-      if (cA + j >= nfull) mask_span(x, cA + j, tid, true);
-      consume(x);
-    }
-  } else {
-    for (int c = 0; c < nround; ++c) {
-      float x[E];
-#pragma unroll
-      for (int u = 0; u < RS_U; ++u) gload(elem0(c, u, tid), x + u * EPV);
-      consume(x);
+      load_span((my_ent >> 8) * cpg, my_ent & 255, ra);
     }
   }
-  // final bound over every element (>= the first, so the first list still covers it)
-  th = block_bound(1);
-  if (!fast) make_list(nround, false);
-  // this thread's sum relative to 2^MH (the sums are exchanged with the next barrier).
-  // Its terms are exp2(x L - mh) = exp2((x - m) L + (m L - mh)) with L = fp32(log2 e); with
-  // exact log2 e each would carry 2^(m (log2 e - L)) more, the same for the whole thread, so
-  // the thread's factor is 2^(mh - MH + m (log2 e - L)) and then
+  // ---- stream, part 2: the chunks from cB on are checked against th while in registers;
+  // spans that reach it are kept in the wave's LDS span region
+  int wn = 0;  // spans this wave wanted to keep (wave-uniform)
+  auto keep_span = [&](const u32x4 *r, float cm, int c) {
+    const bool hit = cm >= th;
+    const uint64_t bal = __ballot(hit);
+    if (bal) {
+      const int j = wn + lane_prefix(bal);
+      if (hit && j < RS_WSP) {
+#pragma unroll
+        for (int u = 0; u < RS_U; ++u) s_span[u][w * RS_WSP + j] = r[u];
+        s_spid[w * RS_WSP + j] = (c << 8) | tid;
+      }
+      wn += (int)__popcll(bal);
+    }
+  };
+  keep_span(R0, cm0, cB);
+  load_span(cB + 2, tid, R0);
+  keep_span(R1, cm1, cB + 1);
+  load_span(cB + 3, tid, R1);
+  for (int c = cB + 2; c < nround; c += 2) {
+    {
+      float x[E];
+      widen_span(R0, c, tid, true, x);
+      const float cm = consume(x, c);
+      keep_span(R0, cm, c);
+      load_span(c + 2, tid, R0);
+    }
+    {
+      float x[E];
+      widen_span(R1, c + 1, tid, true, x);
+      const float cm = consume(x, c + 1);
+      keep_span(R1, cm, c + 1);
+      load_span(c + 3, tid, R1);
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+
+  // ---- block maximum of mh; this thread's sum relative to 2^MH (exchanged at the next
+  // barrier). Its terms are exp2(x L - mh) = exp2((x - m) L + (m L - mh)) with
+  // L = fp32(log2 e); with exact log2 e each would carry 2^(m (log2 e - L)) more, the same
+  // for the whole thread, so the thread's factor is 2^(mh - MH + m (log2 e - L)) and
   // log2e * LSE = MH + log2(sum of the factored sums). The difference from L only ever
   // multiplies x - m, not x itself.
+  {
+    const float wmh = wave_max(m == -kInf ? -kInf : mh);
+    if (lane == 0) s_wm[w] = wmh;
+  }
+  __syncthreads();
+  float MH = s_wm[0];
+#pragma unroll
+  for (int i = 1; i < RS_NW; ++i) MH = fmaxf(MH, s_wm[i]);
   {
     double sc = 0.0;
     if (m != -kInf) {
@@ -339,177 +360,151 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     if (lane == 0) s_ws[w] = sc;
   }
 
-  // ---- candidates: the preloaded spans, the chunks kept in the ring
-  {
-    const int c = my_ent >> 8, ln = my_ent & 255;
-    float x[E];
+  // ---- candidates: elements >= th, keyed (value desc, id asc) into the wave's key region
+  uint64_t *const wkey = keys + w * RS_WK;
+  int kn = 0;
+  auto append = [&](float *x, int c, int ln) {  // wave-uniform call
+    int hits = 0;
 #pragma unroll
-    for (int u = 0; u < RS_U; ++u) Vec<T>::widen(ra[u], x + u * EPV);
-    mask_span(x, c, ln, my_ent >= 0);
-    append_span(x, c, ln);
-  }
-  if (fast) {
-#pragma unroll
-    for (int j = 0; j < RS_D; ++j) {
-      float x[E];
-#pragma unroll
-      for (int u = 0; u < RS_U; ++u) Vec<T>::widen(R[j][u], x + u * EPV);
-      mask_span(x, cA + j, tid, true);
-      append_span(x, cA + j, tid);
+    for (int e = 0; e < E; ++e) {
+      x[e] = x[e] >= th ? x[e] : -kInf;
+      hits += x[e] != -kInf;
     }
-  }
-
-  // ---- re-reads of the listed spans not preloaded (entries past the lanes, multi-chunk
-  // groups, the scalar path), then of groups that did not fit in the list (their own lane);
-  // only chunks before climit: later ones were kept in registers
-  auto reread_group = [&](int ent) {  // wave-uniform call; ent < 0: nothing for this lane
-    const int g = ent >> 8, ln = ent & 255;
-    for (int k = 0; k < cpg; ++k) {
-      const int c = g * cpg + k;
-      const bool act = ent >= 0 && c < climit;
-      float x[E];
-      if (fast) {
-        u32x4 r[RS_U];
+    int total;
+    int slot = kn + wave_prefix(hits, total);
+    if (hits) {
 #pragma unroll
-        for (int u = 0; u < RS_U; ++u) r[u] = bload(act ? c : -1, u, ln);
+      for (int u = 0; u < RS_U; ++u) {
+        const int b = elem0(c, u, ln);
 #pragma unroll
-        for (int u = 0; u < RS_U; ++u) Vec<T>::widen(r[u], x + u * EPV);
-        mask_span(x, c, ln, act);
-      } else {
-#pragma unroll
-        for (int u = 0; u < RS_U; ++u) gload(act ? elem0(c, u, ln) : v1, x + u * EPV);
+        for (int e = 0; e < EPV; ++e) {
+          if (x[u * EPV + e] != -kInf) {
+            if (slot < RS_WK) wkey[slot] = make_key(x[u * EPV + e], (uint32_t)(b + e));
+            ++slot;
+          }
+        }
       }
-      append_span(x, c, ln);
+    }
+    kn += total;
+  };
+  // the preloaded spans (the first chunk of each listed group)
+  {
+    float x[E];
+    widen_span(ra, (my_ent >> 8) * cpg, my_ent & 255, my_ent >= 0, x);
+    append(x, (my_ent >> 8) * cpg, my_ent & 255);
+  }
+  // the kept spans of the chunks from cB on
+  for (int i0 = 0; i0 < min(wn, RS_WSP); i0 += 64) {
+    const int i = i0 + lane;
+    const bool valid = i < min(wn, RS_WSP);
+    u32x4 r[RS_U];
+    int id = 0;
+    if (valid) {
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) r[u] = s_span[u][w * RS_WSP + i];
+      id = s_spid[w * RS_WSP + i];
+    }
+    float x[E];
+    widen_span(r, id >> 8, id & 255, valid, x);
+    append(x, id >> 8, id & 255);
+  }
+  // re-reads: further chunks of multi-chunk groups, entries past the lanes, then groups that
+  // did not fit in the list (their own lane)
+  auto reread_group = [&](int ent, int k0) {  // wave-uniform call; ent < 0: nothing for this lane
+    const int g = ent >> 8, ln = ent & 255;
+    for (int k = k0; k < cpg; ++k) {
+      const int c = g * cpg + k;
+      const bool act = ent >= 0 && c < cB;
+      u32x4 r[RS_U];
+      load_span(act ? c : 0, ln, r);
+      float x[E];
+      widen_span(r, c, ln, act, x);
+      append(x, c, ln);
     }
   };
-  {
+  if (cB > 0) {
+    if (cpg > 1) reread_group(my_ent, 1);
     const int nl = min(nlist, RS_WL);
-    // entries below 64 were preloaded when the first list was made with preloading
-    const bool preloaded = fast && cpg == 1 && cA > 0;
-    for (int i0 = preloaded ? 64 : 0; i0 < nl; i0 += 64) {
+    for (int i0 = 64; i0 < nl; i0 += 64) {
       const int i = i0 + lane;
-      reread_group(i < nl ? s_list[w][i] : -1);
+      reread_group(i < nl ? s_list[w][i] : -1, 0);
     }
     if (nlist > RS_WL) {
-      const int ng = (climit + cpg - 1) / cpg;
       for (int g = 0; g < ng; ++g) {
-        const bool mine = (own_qual >> g) & 1u;
-        const int idx = own_q + __builtin_popcount(own_qual & ((1u << g) - 1u));
-        reread_group((mine && idx >= RS_WL) ? ((g << 8) | tid) : -1);
+        const bool mine = (own >> g) & 1ull;
+        const int idx = own_q + __popcll(own & ((1ull << g) - 1ull));
+        reread_group((mine && idx >= RS_WL) ? ((g << 8) | tid) : -1, 0);
       }
     }
   }
-
-  // pad this wave's region with zero keys (below every key) to a multiple of 16
-  {
-    const int pad = (16 - (wn & 15)) & 15;
-    if (lane < pad && wn + lane < RS_WBUF) wbuf[wn + lane] = 0ull;
+  const int kpad = (kn + 7) & ~7;
+  if (kn + lane < kpad && kn + lane < RS_WK) wkey[kn + lane] = 0ull;
+  if (lane == 0) {
+    s_kn[w] = kn;
+    s_over[w] = kn > RS_WK || wn > RS_WSP;
   }
-  if (lane == 0) s_rn[w] = wn;
   __syncthreads();
   double St = 0.0;
 #pragma unroll
   for (int i = 0; i < RS_NW; ++i) St += s_ws[i];
-  int rs[RS_NW], rn[RS_NW];
   int n_total = 0;
   bool over = false;
+  int kn_[RS_NW];
 #pragma unroll
   for (int i = 0; i < RS_NW; ++i) {
-    rs[i] = i * RS_WBUF;
-    rn[i] = s_rn[i];
-    over |= rn[i] > RS_WBUF;
-    n_total += rn[i];
+    kn_[i] = s_kn[i];
+    over |= s_over[i] != 0;
+    n_total += kn_[i];
   }
-  if (over) {
-    // pathological (a wave region overflowed): re-stream with the threshold at the K-th
-    // key of the full buffer until the candidates fit, then read them as four quarters
-    for (int i = tid; i < RS_BUF; i += RS_NT)
-      if (i % RS_WBUF >= rn[i / RS_WBUF]) buf[i] = 0ull;
-    __syncthreads();
+
+  if (!over) {
+    // ---- top K by rank: the number of (distinct) keys above each candidate, over the four
+    // regions (zero keys pad each to a multiple of 8); each wave ranks its own region's keys
+    for (int i0 = 0; i0 < kn_[w]; i0 += 64) {
+      const int i = i0 + lane;
+      if (i < kn_[w]) {
+        const uint64_t mine = wkey[i];
+        int r = 0;
+#pragma unroll
+        for (int q = 0; q < RS_NW; ++q) {
+          const uint64_t *kq = keys + q * RS_WK;
+          const int np = (kn_[q] + 7) & ~7;
+          for (int j = 0; j < np; j += 8) {
+            int rr = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) rr += (int)(kq[j + t] > mine);
+            r += rr;
+          }
+        }
+        if (r < K) s_top[r] = mine;
+      }
+    }
+  } else {
+    // ---- pathological row: re-stream keeping keys >= tk, raising tk to the K-th key of a
+    // full buffer until a pass fits, then sort what is kept
+    uint64_t *fb = s_rec;
+    uint64_t tk = (uint64_t)ord_f32(th) << 32;
     for (;;) {
-      block_sort_desc_u64<RS_NT>(buf, RS_BUF);
-      const uint64_t tk = buf[K - 1];
-      __syncthreads();
-      if (tid == 0) s_cnt = 0;
+      if (tid == 0) s_nkey = 0;
       __syncthreads();
       for (int v = v0 + tid; v < v1; v += RS_NT) {
         const uint64_t key = make_key(load_elt(p, (size_t)v), (uint32_t)v);
         if (key >= tk) {
-          const int slot = atomicAdd(&s_cnt, 1);
-          if (slot < RS_BUF) buf[slot] = key;
+          const int slot = atomicAdd(&s_nkey, 1);
+          if (slot < RS_FB) fb[slot] = key;
         }
       }
       __syncthreads();
-      n_total = s_cnt;
-      if (n_total <= RS_BUF) break;
+      n_total = s_nkey;
+      if (n_total <= RS_FB) break;
+      block_sort_desc_u64<RS_NT>(fb, RS_FB);
+      tk = fb[K - 1];
     }
-    // quarters of 16-key multiples (zero keys past the end) when ranks will be counted
-    const int q = (n_total <= RS_NT) ? ((n_total + RS_NW * 16 - 1) / (RS_NW * 16)) * 16 : (n_total + RS_NW - 1) / RS_NW;
-    if (n_total <= RS_NT) {
-      for (int i = n_total + tid; i < RS_NW * q; i += RS_NT) buf[i] = 0ull;
-      __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < RS_NW; ++i) {
-      rs[i] = i * q;
-      rn[i] = max(0, min(q, n_total - i * q));
-    }
-  }
-
-  // ---- top K of the candidates (keys are distinct; zero keys pad each region to a
-  // multiple of 16). Up to one per thread: the rank of a key is the number of keys above
-  // it, counted by two lanes (half of each region each) when every wave holds at most 32.
-  // More: each wave takes the top 64 of its region with register bitonic sorts and one
-  // wave merges the four lists.
-  if (n_total <= RS_NT) {
-    int pl[RS_NW], mx = 0;
-#pragma unroll
-    for (int i = 0; i < RS_NW; ++i) {
-      pl[i] = (rn[i] + 15) & ~15;
-      mx = max(mx, rn[i]);
-    }
-    auto count_above = [&](uint64_t mine, int half, int nhalf) {
-      int r = 0;
-#pragma unroll
-      for (int i = 0; i < RS_NW; ++i) {
-        const int len = pl[i] / nhalf;
-        const uint64_t *kb = buf + rs[i] + half * len;
-        for (int j = 0; j < len; j += 8) {
-          int rr = 0;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) rr += (int)(kb[j + t] > mine);
-          r += rr;
-        }
-      }
-      return r;
-    };
-    if (mx <= 32) {
-      const int l = lane & 31;
-      const bool has = l < rn[w];
-      const uint64_t mine = has ? buf[rs[w] + l] : 0ull;
-      int r = count_above(mine, lane >> 5, 2);
-      r += __shfl_xor(r, 32, 64);
-      if (lane < 32 && has && r < K) s_top[r] = mine;
-    } else {
-      for (int l0 = 0; l0 < rn[w]; l0 += 64) {
-        const int l = l0 + lane;
-        const bool has = l < rn[w];
-        const uint64_t mine = has ? buf[rs[w] + l] : 0ull;
-        const int r = count_above(mine, 0, 1);
-        if (has && r < K) s_top[r] = mine;
-      }
-    }
-  } else {
-    const uint64_t top = wave_top64(buf + rs[w], rn[w]);
+    const int np = next_pow2(max(n_total, 1));
+    for (int i = n_total + tid; i < np; i += RS_NT) fb[i] = 0ull;
     __syncthreads();
-    buf[w * 64 + lane] = top;
-    __syncthreads();
-    if (w == 0) {
-      uint64_t t = buf[lane];
-#pragma unroll
-      for (int i = 1; i < RS_NW; ++i) t = wave_merge_top64_u64(t, buf[i * 64 + lane]);
-      s_top[lane] = t;
-    }
+    block_sort_desc_u64<RS_NT>(fb, np);
+    for (int k = tid; k < K; k += RS_NT) s_top[k] = fb[k];
   }
   __syncthreads();
   const int have = n_total < K ? n_total : K;
@@ -546,7 +541,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
 
 // Merge the S partials of each row.
 __global__ __launch_bounds__(RS_NT) void k_rowsweep_merge(int K, int S, RowPart part, RowOut out) {
-  __shared__ uint64_t buf[RS_BUF];
+  __shared__ uint64_t buf[RS_MBUF];
   __shared__ double s_lse;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -601,7 +596,7 @@ int rowsweep_splits(int rows, int V, int K) {
   const int min_seg = 4 * RS_NT * 32;
   int smax = (V + min_seg - 1) / min_seg;
   if (S > smax) S = smax;
-  if (S > RS_BUF / (K > 0 ? K : 1)) S = RS_BUF / (K > 0 ? K : 1);
+  if (S > RS_MBUF / (K > 0 ? K : 1)) S = RS_MBUF / (K > 0 ? K : 1);
   if (S < 1) S = 1;
   // no empty splits
   const int seg = seg_len(V, S, 8);
@@ -631,12 +626,22 @@ hipError_t launch_rowsweep(const void *logits, int dtype, int rows, int V, int K
     part.s = reinterpret_cast<double *>(w);
   }
   const dim3 grid((unsigned)rows * S);
-  if (dtype == DTREE_BF16)
-    hipLaunchKernelGGL(k_rowsweep<uint16_t>, grid, dim3(RS_NT), 0, st, static_cast<const uint16_t *>(logits),
-                       V, K, S, seg, part, out);
-  else
-    hipLaunchKernelGGL(k_rowsweep<float>, grid, dim3(RS_NT), 0, st, static_cast<const float *>(logits), V, K,
-                       S, seg, part, out);
+  // whole 16-byte vectors in every segment: V a multiple of the vector width (segment
+  // lengths are multiples of 8 elements) and an aligned base
+  const bool aligned = (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  if (dtype == DTREE_BF16) {
+    const uint16_t *x = static_cast<const uint16_t *>(logits);
+    if (aligned && V % 8 == 0)
+      hipLaunchKernelGGL((k_rowsweep<uint16_t, true>), grid, dim3(RS_NT), 0, st, x, V, K, S, seg, part, out);
+    else
+      hipLaunchKernelGGL((k_rowsweep<uint16_t, false>), grid, dim3(RS_NT), 0, st, x, V, K, S, seg, part, out);
+  } else {
+    const float *x = static_cast<const float *>(logits);
+    if (aligned && V % 4 == 0)
+      hipLaunchKernelGGL((k_rowsweep<float, true>), grid, dim3(RS_NT), 0, st, x, V, K, S, seg, part, out);
+    else
+      hipLaunchKernelGGL((k_rowsweep<float, false>), grid, dim3(RS_NT), 0, st, x, V, K, S, seg, part, out);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   hipLaunchKernelGGL(k_rowsweep_merge, dim3(rows), dim3(RS_NT), 0, st, K, S, part, out);
