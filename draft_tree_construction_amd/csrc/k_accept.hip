@@ -293,19 +293,22 @@ DT_INLINE void wg_lse2(const Row<T> &A, const Row<T> &B, float s, Red &red, doub
   lb = (double)MB + log2(SB);
 }
 
-// First index of the maximum of one row.
+// First index of the maximum of one row. Each thread sees its elements in increasing index
+// order and keeps the first of its largest (compare and select); the threads' results are
+// combined as (value desc, id asc) keys.
 template <typename T>
 DT_INLINE int wg_row_argmax(const Row<T> &A, Red &red) {
-  uint64_t best = 0;
-  const int V = A.V;
+  float bm = -kInf;
+  int bi = -1;
   stream1(A, [&](int u, const float *z) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int v = u * 8 + e;
-      const uint64_t k = v < V ? make_key(z[e], (uint32_t)v) : 0ull;
-      best = k > best ? k : best;
+      const bool gt = z[e] > bm;  // elements past the row end are -inf
+      bm = gt ? z[e] : bm;
+      bi = gt ? u * 8 + e : bi;
     }
   });
+  uint64_t best = bi >= 0 ? make_key(bm, (uint32_t)bi) : 0ull;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const uint64_t x = __shfl_xor(best, o, 64);
@@ -667,17 +670,27 @@ DT_INLINE int sample_in_block_wave(const T *zt, const T *zd, int V, const Norm &
   return b * AC_BLK;
 }
 
-// children of every slot: first child / next sibling in slot order. A slot whose parent
-// is not an earlier slot, or whose token is outside the vocabulary, is ignored (never indexed).
-DT_INLINE void build_children(const int *par, const int *tok, int n, int V, int *fc, int *ns) {
-  if (threadIdx.x == 0) {
-    for (int i = 0; i <= n; ++i) fc[i] = -1;
-    for (int i = n; i >= 1; --i) {
-      const int p = par[i];
-      if (p < 0 || p >= i || tok[i] < 0 || tok[i] >= V) continue;
-      ns[i] = fc[p];
-      fc[p] = i;
+// children of every slot: first child / next sibling in slot order, and each slot's rank
+// among its siblings (its draw offset at its parent). A slot whose parent is not an earlier
+// slot, or whose token is outside the vocabulary, is ignored (never indexed). One thread
+// per slot scans every slot's parent (branch-free, one broadcast LDS read per slot).
+DT_INLINE void build_children(const int *par, const int *tok, int n, int V, int *fc, int *ns, int *sr, int *pv) {
+  for (int i = threadIdx.x; i <= n; i += blockDim.x)
+    pv[i] = (i >= 1 && par[i] >= 0 && par[i] < i && tok[i] >= 0 && tok[i] < V) ? par[i] : -2;
+  __syncthreads();
+  for (int i = threadIdx.x; i <= n; i += blockDim.x) {
+    const int p = pv[i];  // -2: not a valid slot (its next sibling and rank are never read)
+    int first = 0x7FFFFFFF, next = 0x7FFFFFFF, rank = 0;
+#pragma unroll 8
+    for (int c = 1; c <= n; ++c) {
+      const int pc = pv[c];
+      first = pc == i ? min(first, c) : first;  // a valid child is always after its parent
+      next = (pc == p && c > i) ? min(next, c) : next;
+      rank += (pc == p && c < i);
     }
+    fc[i] = first == 0x7FFFFFFF ? -1 : first;
+    ns[i] = next == 0x7FFFFFFF ? -1 : next;
+    sr[i] = rank;
   }
   __syncthreads();
 }
@@ -690,7 +703,7 @@ DT_INLINE float log2_scale(float T) { return (float)(1.4426950408889634 / (doubl
 template <typename T>
 __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_list) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
-  __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1];
+  __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1], sr[DTREE_MAX_CAP + 1], pv[DTREE_MAX_CAP + 1];
   __shared__ Red red;
   __shared__ float cz1[DTREE_MAX_CAP + 1], cz2[DTREE_MAX_CAP + 1], cu[DTREE_MAX_CAP + 1];
   __shared__ int bcnt[AC_NB], boff[AC_NB + 1];
@@ -699,18 +712,24 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
   const int cap = a.tree.cap;
   const int n = clamp_nodes(a.tree.n_nodes[r], cap);
   const size_t tb = (size_t)r * (cap + 1);
-  for (int i = threadIdx.x; i <= n; i += AC_NT) {
+  // the whole slot range is loaded (its loads do not wait for n) and the child lists are
+  // built after the root's first pass, which needs none of them (the pass's barriers make
+  // the loaded slots visible)
+  for (int i = threadIdx.x; i <= cap; i += AC_NT) {
     par[i] = a.tree.parent[tb + i];
     tok[i] = a.tree.token[tb + i];
     dep[i] = a.tree.depth[tb + i];
   }
-  __syncthreads();
-  build_children(par, tok, n, a.V, fc, ns);
   const T *target = static_cast<const T *>(a.target) + (size_t)r * (cap + 1) * a.V;
   int j = 0, out_tok = -1;
   if (a.T == 0.f) {
+    bool lists = false;
     for (;;) {
       const int ts = wg_row_argmax(make_row(target + (size_t)j * a.V, a.V), red);
+      if (!lists) {
+        build_children(par, tok, n, a.V, fc, ns, sr, pv);
+        lists = true;
+      }
       int nxt = -1;
       for (int c = fc[j]; c >= 0; c = ns[c])
         if (tok[c] == ts) {
@@ -735,22 +754,26 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
     bn.cnt = bcnt;
     bn.off = boff;
     bn.list = a_list + (size_t)r * a.V;
+    bool lists = false;
     for (;;) {
       const T *zt = target + (size_t)j * a.V;
-      const T *zd = draft + (size_t)draft_row(dep[j], a.L) * a.V;
+      const T *zd = draft + (size_t)draft_row(j == 0 ? a.tree.depth[tb] : dep[j], a.L) * a.V;
       const Row<T> A = make_row(zt, a.V), B = make_row(zd, a.V);
+      double la, lb;
+      wg_lse2(A, B, s, red, la, lb);  // ends with a barrier
+      if (!lists) {
+        build_children(par, tok, n, a.V, fc, ns, sr, pv);
+        lists = true;
+      }
       // the children's logits and uniforms (the k-th child in slot order takes draw
       // step + k), prepared once for the whole node
       for (int i = threadIdx.x; i <= n; i += AC_NT)
-        if (i > j && par[i] == j && tok[i] >= 0 && tok[i] < a.V) {
+        if (pv[i] == j) {
           cz1[i] = load_elt(zt, (size_t)tok[i]);
           cz2[i] = load_elt(zd, (size_t)tok[i]);
-          int k = 0;
-          for (int c = j + 1; c < i; ++c) k += par[c] == j && tok[c] >= 0 && tok[c] < a.V;
-          cu[i] = philox_uniform(a.seed, trial, (uint32_t)r, step + (uint32_t)k);
+          cu[i] = philox_uniform(a.seed, trial, (uint32_t)r, step + (uint32_t)sr[i]);
         }
-      double la, lb;
-      wg_lse2(A, B, s, red, la, lb);  // ends with a barrier
+      __syncthreads();
       const Norm nt = make_norm(s, la), nd = make_norm(s, lb);
       float t = 0.f;
       double C = 1.0;
@@ -807,7 +830,7 @@ struct AccTables {
 template <typename T>
 __global__ __launch_bounds__(AC_NT) void k_accept_tables(AcceptArgs a, AccTables tb) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
-  __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1];
+  __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1], sr[DTREE_MAX_CAP + 1], pv[DTREE_MAX_CAP + 1];
   __shared__ Red red;
   extern __shared__ double dyn[];  // [nblk] block sums (float)
   const int cap = a.tree.cap;
@@ -822,7 +845,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_tables(AcceptArgs a, AccTables
     dep[i] = a.tree.depth[base + i];
   }
   __syncthreads();
-  build_children(par, tok, n, a.V, fc, ns);
+  build_children(par, tok, n, a.V, fc, ns, sr, pv);
   const float s = log2_scale(a.T);
   const T *zt = static_cast<const T *>(a.target) + ((size_t)r * (cap + 1) + j) * a.V;
   const T *zd = static_cast<const T *>(a.draft) + ((size_t)r * a.L + draft_row(dep[j], a.L)) * a.V;
