@@ -51,7 +51,6 @@ constexpr int DW_NC = 64;      // V chunks (partials per state)
 constexpr int DW_HX = 80;      // state row: h (64), -ref, one-hot base (8), 1 (mask), zero padding
 constexpr int DW_SUP = 2048;   // super-tree nodes per round (L * W)
 constexpr int DW_CH = 1024;    // children per depth (W * K)
-constexpr int DW_MAXP = 8;     // rounds per tile (base columns)
 constexpr float DW_WIDE = 10.f;
 
 DT_INLINE bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
@@ -311,7 +310,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_states(DwState s, DwDev a, DwDims 
     const int rem = sl % per_d, r = rem / g.Kp;
     uint16_t *hr = s.hx + (size_t)sl * DW_HX;
     for (int e = 64; e < DW_HX; ++e) hr[e] = 0;
-    hr[73] = 0x3F80u;  // matches the mask column of A (0, or -inf past V)
+    hr[base_bf16 && g.np == 8 ? 73 : 71] = 0x3F80u;  // matches the mask column of A (0, or -inf past V)
     if (stok[row] >= 0) {
       // bound per row: sum over j of |h_j| max|P_j.|, in column order
       float bound = 0.f;
@@ -332,14 +331,24 @@ __global__ __launch_bounds__(DW_NT) void k_dw_states(DwState s, DwDev a, DwDims 
 }
 
 // ---------------------------------------------------------------- the correction sweep
-template <typename T>
+// A workgroup covers sixteen tiles (one per wave) over one V chunk of whole six-block groups;
+// the sweep past V is masked by the A operand's mask column. Roles are fixed per wave, and
+// each role (and the running-max variant) runs its own copy of the loop, so that its loads
+// are unconditional (the compiler's wait counts stay exact) and a step is one stretch of
+// straight code for the scheduler: waves 0-3 stage the P^T block (256 pieces of 16
+// bytes), waves 4 .. 4 + NP - 1 stage base round p of the sixteen tiles (bf16 bases; 64
+// pieces each). NP is the number of rounds a tile holds; BVEC says that base rows are whole
+// 16-byte pieces (V % 8 == 0, aligned).
+template <typename T, int NP, bool BVEC>
 __global__ __launch_bounds__(DW_CNT) void k_dw_corr(DwState s, const T *__restrict__ base, DwDims g) {
   // P^T block (32 rows x 128 bytes) shared by the workgroup's sixteen tiles, triple
   // buffered; rows are 144 bytes apart, so the A-operand reads (16 lanes on 16 rows) hit
   // distinct banks and a lane's four chunks sit at fixed offsets
   constexpr int SPR = 9;  // row pitch in 16-byte chunks
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int NB = kBf16 ? NP : 1;
   __shared__ u32x4 sP[3][32 * SPR];
-  __shared__ uint16_t sB[3][DW_CW][DW_MAXP][32];  // each tile's rounds' base logits of the block
+  __shared__ uint16_t sB[3][NB][DW_CW][32];  // base round p of each tile, 32 tokens
   const int V = g.V;
   const int nct = g.ntile;
   const int TG = (nct + DW_CW - 1) / DW_CW;
@@ -350,87 +359,103 @@ __global__ __launch_bounds__(DW_CNT) void k_dw_corr(DwState s, const T *__restri
   // the wave index is uniform: tile and the quantities built from it live in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int t = gi * DW_CW + wave;
-  const bool active = t < nct;  // inactive waves still load and synchronise
+  const bool active = t < nct;  // an inactive wave computes tile 0 again and writes nothing
+  const int tc = active ? t : 0;
   const int col = lane & 31, half = lane >> 5;
   const int per_d = g.Rp * g.Kp;
   auto tile_d = [&](int tt) { return 1 + (tt * 32) / per_d; };
   auto tile_r0 = [&](int tt) { return ((tt * 32) % per_d) / g.Kp; };
 
-  const u32x4 *hrow = reinterpret_cast<const u32x4 *>(s.hx + ((size_t)(active ? t : 0) * 32 + col) * DW_HX);
+  const u32x4 *hrow = reinterpret_cast<const u32x4 *>(s.hx + ((size_t)tc * 32 + col) * DW_HX);
   bf16x8 bfr[5];
 #pragma unroll
   for (int kb = 0; kb < 5; ++kb) bfr[kb] = as_bf16x8(hrow[2 * kb + half]);
-  const bool wide = active && s.wide[t] != 0;
-  const int nb32 = (V + 31) >> 5;
-  const int blk0 = (int)(((long long)nb32 * c) / DW_NC);
-  const int blk1 = (int)(((long long)nb32 * (c + 1)) / DW_NC);
-  constexpr bool kBf16 = sizeof(T) == 2;
-  const int np = g.np;
+  const bool wide = s.wide[tc] != 0;
+  const int ng = ((V + 31) / 32 + 5) / 6;  // six-block groups over the row
+  const int blk0 = 6 * (int)(((long long)ng * c) / DW_NC);
+  const int nblk = 6 * (int)(((long long)ng * (c + 1)) / DW_NC) - blk0;
+  const int blast = blk0 + nblk - 1;
   // fp32 bases are added after the MFMA: this lane's state column belongs to round r0 + col / Kp
-  const T *lane_base = base + ((size_t)min(active ? tile_r0(t) + (g.Kp <= 32 ? col / g.Kp : 0) : 0, g.R - 1) * g.L +
-                               (active ? tile_d(t) : 1) - 1) * V;
+  const T *lane_base = base + ((size_t)min(tile_r0(tc) + (g.Kp <= 32 ? col / g.Kp : 0), g.R - 1) * g.L +
+                               tile_d(tc) - 1) * V;
+  // mask column of the A operand: -inf on rows past V (in the half whose B rows carry it),
+  // i.e. from block mblk on
+  const int mblk = (NP == 8 || half == 0) ? (V - col + 31) >> 5 : 0x7FFFFFFF;
 
-  double acc = 0.0;
-  float m = wide ? -kInf : 0.f;
-  // threads 0..255 stage the P^T block (16 bytes each); for bf16 bases, threads 256..767
-  // stage the base logits of each tile's rounds (one 16-byte piece of 8 tokens each)
-  const bool stager = tid < 256;
-  const int lrow = (tid >> 3) & 31, lchk = tid & 7;
-  const int bi = tid - 256;
-  const int btile_w = (bi >> 5) & (DW_CW - 1), bpair = (bi >> 2) & 7, bp = bi & 3;
-  const bool bstager = kBf16 && tid >= 256 && bi < DW_CW * DW_MAXP * 4;
-  const int btile = gi * DW_CW + btile_w;
-  const int bround = btile < nct ? tile_r0(btile) + bpair : 0;
-  const bool bvalid_row = bstager && btile < nct && bpair < np && bround < g.R;
+  // stagers: P^T row tid / 8 of the block, 16-byte chunk tid % 8; base piece lane % 4 (8
+  // tokens) of round bp of tile lane / 4. A base row past the tiles or rounds reads a valid
+  // row: no live state's one-hot column selects it.
+  const int prl = (tid >> 3) & 31, pch = tid & 7;
+  const int bp = wave - 4;
+  const int btw = lane >> 2, bpc = lane & 3;
+  const int btile = gi * DW_CW + btw;
+  const int bround = (bp >= 0 && bp < NB && btile < nct) ? tile_r0(btile) + bp : g.R;
+  const bool bvalid = bround < g.R;
   const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(base) +
-                         ((size_t)(bvalid_row ? bround : 0) * g.L + (bvalid_row ? tile_d(btile) : 1) - 1) * V;
-  const bool bvec = (V & 7) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0;
-  // one 16-byte load per thread and block (BVEC: whole 8-token pieces, V % 8 == 0 and
-  // 16-byte aligned rows),
-  // branch-free: rows and base pieces past V are clamped to valid memory (the mask column
-  // makes those rows -inf, so the values do not matter); threads that stage nothing re-read
-  // the first P^T row. Without BVEC the base pieces are read element-wise.
-  auto gload = [&](auto bvec_tag, int blk, u32x4 &gp) {
-    constexpr bool BVEC = decltype(bvec_tag)::value;
-    const int prow = min((blk << 5) + lrow, V - 1);
-    const int v = (blk << 5) + bp * 8;
-    if constexpr (BVEC || !kBf16) {
-      const uint16_t *addr = stager ? s.PT + (size_t)prow * 64 + lchk * 8
-                                    : (bstager ? bsrc + (v < V ? v : 0) : s.PT);
-      gp = *reinterpret_cast<const u32x4 *>(addr);
-    } else {
-      if (stager) {
-        gp = *reinterpret_cast<const u32x4 *>(s.PT + (size_t)prow * 64 + lchk * 8);
+                         ((size_t)(bvalid ? bround : 0) * g.L + (bvalid ? tile_d(btile) : 1) - 1) * V;
+  auto gload = [&](auto role, int blk, u32x4 &gp) {
+    constexpr int ROLE = decltype(role)::value;
+    if constexpr (ROLE == 0) {
+      const int prow = min((blk << 5) + prl, V - 1);
+      gp = *reinterpret_cast<const u32x4 *>(s.PT + (size_t)prow * 64 + pch * 8);
+    } else if constexpr (ROLE == 1) {
+      const int v = (blk << 5) + bpc * 8;
+      if constexpr (BVEC) {
+        gp = *reinterpret_cast<const u32x4 *>(bsrc + (v < V ? v : 0));
       } else {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v0e = v + 2 * e;
-          const uint32_t lo = (bstager && v0e < V) ? bsrc[v0e] : 0u;
-          const uint32_t hi = (bstager && v0e + 1 < V) ? bsrc[v0e + 1] : 0u;
+          const uint32_t lo = bsrc[v0e < V ? v0e : 0];
+          const uint32_t hi = bsrc[v0e + 1 < V ? v0e + 1 : 0];
           w[e] = lo | (hi << 16);
         }
         gp = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
   };
-  auto lstore = [&](int buf, const u32x4 &gp) {
-    if (stager) sP[buf][lrow * SPR + lchk] = gp;
-    else if (bstager) *reinterpret_cast<u32x4 *>(&sB[buf][btile_w][bpair][bp * 8]) = gp;
-  };
-  auto mfma_blk = [&](int blk, int buf) {
-    // extra A columns 64..79: [1, base of the tile's rounds 0..7, mask, 0 ...]; a row past V
-    // gets -inf in the mask column (matched by a row of ones in every state's B), so
-    // z = -inf and its exponential is 0 with no per-element mask
-    const uint32_t mask = ((blk << 5) + col < V) ? 0u : 0xFF80u;
-    uint32_t b[DW_MAXP];
+  // logits must be finite; should a -inf arrive anyway it becomes the lowest finite bf16
+  // (its exponential is still 0), so a zero of another round's one-hot column never meets
+  // an infinity in the MFMA and turns a whole state column into NaN
+  auto lstore = [&](auto role, int buf, const u32x4 &gp) {
+    constexpr int ROLE = decltype(role)::value;
+    if constexpr (ROLE == 0) {
+      sP[buf][prl * SPR + pch] = gp;
+    } else if constexpr (ROLE == 1) {
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      const u16x2 lim = {0xFF7Fu, 0xFF7Fu};
+      u32x4 q;
 #pragma unroll
-    for (int p = 0; p < DW_MAXP; ++p) b[p] = (kBf16 && p < np) ? (uint32_t)sB[buf][wave][p][col] : 0u;
+      for (int e = 0; e < 4; ++e) {
+        // copy the element out first: a bit_cast of the subscript expression itself reads
+        // element 0 for every e with this compiler
+        const uint32_t w = gp[e];
+        q[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, w), lim));
+      }
+      *reinterpret_cast<u32x4 *>(&sB[buf][bp][btw][bpc * 8]) = q;
+    }
+  };
+  // A operand: P^T rows of the block, then the extra columns 64..79: [1, base of the tile's
+  // rounds 0..NP-1, 0 ..., mask at 71] for NP <= 4 (both halves hold the same values, the
+  // mask only in half 0: the B rows 72..79 are 0 there); [1, base 0..6 | base 7, mask, 0 ...]
+  // for NP = 8
+  auto mfma_blk = [&](int buf, int blk) {
+    const uint32_t mk = blk >= mblk ? 0xFF800000u : 0u;
     u32x4 ext;
-    if (half == 0)
-      ext = u32x4{0x3F80u | (b[0] << 16), b[1] | (b[2] << 16), b[3] | (b[4] << 16), b[5] | (b[6] << 16)};
-    else
-      ext = u32x4{b[7] | (mask << 16), 0u, 0u, 0u};
+    if constexpr (kBf16) {
+      uint32_t b[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) b[p] = sB[buf][p][wave][col];
+      if constexpr (NP == 8) {
+        ext = half == 0 ? u32x4{0x3F80u | (b[0] << 16), b[1] | (b[2] << 16), b[3] | (b[4] << 16), b[5] | (b[6] << 16)}
+                        : u32x4{b[7] | mk, 0u, 0u, 0u};
+      } else {
+        ext = u32x4{0x3F80u | (b[0] << 16), NP > 1 ? (b[1] | (NP > 2 ? b[2] << 16 : 0u)) : 0u, NP > 3 ? b[3] : 0u, mk};
+      }
+    } else {
+      ext = u32x4{0x3F80u, 0u, 0u, mk};
+    }
     u32x4 pa[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) pa[q] = sP[buf][col * SPR + half * 4 + q];
@@ -442,20 +467,17 @@ __global__ __launch_bounds__(DW_CNT) void k_dw_corr(DwState s, const T *__restri
     z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ext), bfr[4], z, 0, 0, 0);
     return z;
   };
-  auto exps_blk = [&](int blk, const f32x16 &z) {
+  double acc = 0.0;
+  float m = wide ? -kInf : 0.f;
+  auto exps_blk = [&](auto wide_tag, int blk, f32x16 x) {
+    constexpr bool WIDE = decltype(wide_tag)::value;
     // lane holds rows (blk*32 + 8*(q/4) + 4*half + q%4) of its state column
-    const int vbase = (blk << 5) + 4 * half;
-    float x[16];
+    if constexpr (!kBf16) {  // fp32 base rows are added here (rows past V are -inf already)
+      const int vbase = (blk << 5) + 4 * half;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) x[q] = z[q];
-    if constexpr (!kBf16) {  // fp32 base rows are added here (rows past V are already -inf)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int vr = vbase + 8 * (q >> 2) + (q & 3);
-        if (vr < V) x[q] += load_elt(lane_base, (size_t)vr);
-      }
+      for (int q = 0; q < 16; ++q) x[q] += load_elt(lane_base, (size_t)min(vbase + 8 * (q >> 2) + (q & 3), V - 1));
     }
-    if (!wide) {
+    if constexpr (!WIDE) {
       float a = __builtin_amdgcn_exp2f(x[0] * kLog2e), b = __builtin_amdgcn_exp2f(x[1] * kLog2e);
 #pragma unroll
       for (int q = 2; q < 16; q += 2) {
@@ -479,46 +501,62 @@ __global__ __launch_bounds__(DW_CNT) void k_dw_corr(DwState s, const T *__restri
       }
     }
   };
-  // step blk: blocks blk and blk + 1 are in LDS buffers blk % 3 and (blk + 1) % 3; block
-  // blk + 2 goes from registers to the third buffer and its register slot is refilled with
-  // block blk + 2 + PD; the MFMA chain of block blk + 1 is issued before the exponentials
-  // of block blk, so the matrix cores run while the wave works on the vector units
-  constexpr int PD = 3;
-  auto pipeline = [&](auto bvec_tag) {
-    u32x4 G[PD];
-#pragma unroll
-    for (int q = 0; q < PD; ++q) gload(bvec_tag, blk0 + q, G[q]);
-    lstore(0, G[0]);
-    lstore(1, G[1]);
-    gload(bvec_tag, blk0 + PD, G[0]);
-    gload(bvec_tag, blk0 + PD + 1, G[1]);
+  // Step k (block blk0 + k): blocks k and k + 1 are in LDS buffers k % 3 and (k + 1) % 3,
+  // block k + 2 goes from registers (slot (k + 2) % 3) to the third buffer and its slot is
+  // refilled with block k + 5 (clamped to the chunk: re-reads of the last block hit the
+  // cache); the MFMA chain of block k + 1 is issued before the exponentials of block k, so
+  // the matrix cores run while the wave works on the vector units. Unrolled by six, every
+  // buffer, register slot and accumulator index is static.
+  auto pipeline = [&](auto role, auto wide_tag) {
+    u32x4 G[3];
+    gload(role, blk0, G[0]);
+    gload(role, blk0 + 1, G[1]);
+    lstore(role, 0, G[0]);
+    lstore(role, 1, G[1]);
+    gload(role, blk0 + 2, G[2]);
+    gload(role, blk0 + 3, G[0]);
+    gload(role, blk0 + 4, G[1]);
     __syncthreads();
-    f32x16 zc = {};
-    if (active) zc = mfma_blk(blk0, 0);
-    for (int b0 = blk0; b0 < blk1; b0 += PD) {
+    f32x16 zz[2];
+    zz[0] = mfma_blk(0, blk0);
+    for (int k0 = 0; k0 < nblk; k0 += 6) {
 #pragma unroll
-      for (int q = 0; q < PD; ++q) {
-        const int blk = b0 + q;
-        if (blk < blk1) {
-          const int k = blk - blk0;
-          const int nq = (q + 2) % PD;  // register slot holding block blk + 2
-          lstore((k + 2) % 3, G[nq]);
-          gload(bvec_tag, blk + 2 + PD, G[nq]);
-          if (active) {
-            // past the last block this reads a stale buffer; the result is never used
-            const f32x16 zn = mfma_blk(blk + 1, (k + 1) % 3);
-            exps_blk(blk, zc);
-            zc = zn;
-          }
-          __syncthreads();
-        }
+      for (int q = 0; q < 6; ++q) {
+        const int blk = blk0 + k0 + q;
+        lstore(role, (q + 2) % 3, G[(q + 2) % 3]);
+        gload(role, min(blk + 5, blast), G[(q + 2) % 3]);
+        // past the last block this reads a stale buffer; the result is never used
+        zz[(q + 1) & 1] = mfma_blk((q + 1) % 3, blk + 1);
+        exps_blk(wide_tag, blk, zz[q & 1]);
+        // order: the LDS reads of block k + 1 first, then half of the exponentials of
+        // block k (time for the reads to land), the MFMA chain of block k + 1, and the rest
+        // of the exponentials while the chain runs; nothing moves across the barrier
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write (stagers)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load (stagers)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 26, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 60, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  if (bvec)
-    pipeline(std::true_type{});
-  else
-    pipeline(std::false_type{});
+  auto run = [&](auto role) {
+    if (wide)
+      pipeline(role, std::true_type{});
+    else
+      pipeline(role, std::false_type{});
+  };
+  if (nblk > 0) {
+    if (wave < 4)
+      run(std::integral_constant<int, 0>{});
+    else if (kBf16 && wave < 4 + NB)
+      run(std::integral_constant<int, 1>{});
+    else
+      run(std::integral_constant<int, 2>{});
+  }
   // merge the two row halves of this state column (lanes l and l ^ 32)
   const float mo = __shfl_xor(m, 32, 64);
   const double ao = __shfl_xor(acc, 32, 64);
@@ -861,10 +899,25 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   if (e != hipSuccess) return e;
   const int TG = (g.ntile + DW_CW - 1) / DW_CW;
   const dim3 gcorr((unsigned)(8 * TG * (DW_NC / 8)));
-  if (a.dtype == DTREE_BF16)
-    hipLaunchKernelGGL(k_dw_corr<uint16_t>, gcorr, dim3(DW_CNT), 0, st, s, static_cast<const uint16_t *>(a.base), g);
-  else
-    hipLaunchKernelGGL(k_dw_corr<float>, gcorr, dim3(DW_CNT), 0, st, s, static_cast<const float *>(a.base), g);
+  if (a.dtype == DTREE_BF16) {
+    const uint16_t *b16 = static_cast<const uint16_t *>(a.base);
+    const bool bvec = (a.V & 7) == 0 && (reinterpret_cast<uintptr_t>(b16) & 15) == 0;
+    auto corr = [&](auto np_tag) {
+      constexpr int NP = decltype(np_tag)::value;
+      if (bvec)
+        hipLaunchKernelGGL((k_dw_corr<uint16_t, NP, true>), gcorr, dim3(DW_CNT), 0, st, s, b16, g);
+      else
+        hipLaunchKernelGGL((k_dw_corr<uint16_t, NP, false>), gcorr, dim3(DW_CNT), 0, st, s, b16, g);
+    };
+    switch (g.np) {
+      case 1: corr(std::integral_constant<int, 1>{}); break;
+      case 2: corr(std::integral_constant<int, 2>{}); break;
+      case 4: corr(std::integral_constant<int, 4>{}); break;
+      default: corr(std::integral_constant<int, 8>{}); break;
+    }
+  } else {
+    hipLaunchKernelGGL((k_dw_corr<float, 1, false>), gcorr, dim3(DW_CNT), 0, st, s, static_cast<const float *>(a.base), g);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_dw_lq, dim3(g.ntile), dim3(DW_NT), 0, st, s, dv, g);

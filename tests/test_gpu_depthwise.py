@@ -92,3 +92,13 @@ def test_depthwise_full_dartree_config_sampled():
     E, U, P, root = synth.correction_head(seed=3)
     exact, n = check(base, "bf16", E, U, P, root, 8, 32, 128, -0.5, rounds=(0, 31, 63))
     assert exact >= n - 1
+
+
+def test_depthwise_one_round_over_two_tiles():
+    """K = 40 pads a round to 64 state slots: each tile holds 32 states of one round."""
+    R, L, V, dm = 2, 5, 900, 64
+    base = synth.ddtree_logits(seed=13, R=R, L=L, V=V)
+    E, U, P, root = synth.correction_head(seed=113, R=R, L=L, V=V, d_model=dm, rank=64)
+    exact, n = check(base, "bf16", E, U, P, root, 40, 16, 60, -0.3)
+    assert exact >= n - 1
+
