@@ -18,8 +18,12 @@
 // reach the bound and issues their loads at once (lane j of a wave the wave's j-th span),
 // hidden behind the last chunks; those last chunks are checked against the bound while in
 // registers and the spans that reach it are kept in LDS. The candidates -- elements at or
-// above the bound in the listed and kept spans -- are keyed (value desc, id asc), and each
-// one's rank is the number of keys above it. Rows with more listed spans or candidates than
+// above the bound in the listed and kept spans, gathered with one hit mask per lane -- are
+// keyed (value desc, id asc), and each one's rank is the number of keys above it: each wave
+// counts the keys of its own region above every candidate and adds that into the
+// candidate's rank, and a candidate ranked below K writes its output entry itself. The
+// finishing work runs on all workgroups at once after their streams, so it is kept to few
+// instructions and barriers. Rows with more listed spans or candidates than
 // LDS holds (long runs of ties, sorted rows) are re-streamed with the threshold raised to
 // the K-th key found until a pass fits. Rows too short to fill the GPU are split over
 // several workgroups whose partial (max, sum, top-K) are merged by a second kernel.
@@ -122,12 +126,12 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   __shared__ u32x4 s_span[RS_U][RS_NW * RS_WSP];  // spans of the last chunks that reach the bound
   __shared__ int s_spid[RS_NW * RS_WSP];          // (chunk << 8) | lane of each stored span
   __shared__ uint64_t keys[RS_KEYS];
-  __shared__ uint64_t s_top[64];
   __shared__ float s_wb[RS_NW], s_wm[RS_NW];
   __shared__ double s_ws[RS_NW];
   __shared__ int s_kn[RS_NW], s_over[RS_NW];
   __shared__ int s_nkey;  // re-stream fallback counter
   uint16_t(*s_gm)[RS_NT] = reinterpret_cast<uint16_t(*)[RS_NT]>(s_rec);
+  static_assert(RS_NG * RS_NT / 4 * 2 >= RS_KEYS, "the record holds the candidates' ranks");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = blockIdx.x / S;
@@ -314,25 +318,18 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
       wn += (int)__popcll(bal);
     }
   };
+  // (straight code, no loads past the row: the compiler then waits for each slot alone)
   keep_span(R0, cm0, cB);
-  load_span(cB + 2, tid, R0);
   keep_span(R1, cm1, cB + 1);
-  load_span(cB + 3, tid, R1);
-  for (int c = cB + 2; c < nround; c += 2) {
-    {
-      float x[E];
-      widen_span(R0, c, tid, true, x);
-      const float cm = consume(x, c);
-      keep_span(R0, cm, c);
-      load_span(c + 2, tid, R0);
-    }
-    {
-      float x[E];
-      widen_span(R1, c + 1, tid, true, x);
-      const float cm = consume(x, c + 1);
-      keep_span(R1, cm, c + 1);
-      load_span(c + 3, tid, R1);
-    }
+  if (nround - cB == RS_PRE) {
+    static_assert(RS_PRE == 4, "part 2 streams two more chunks");
+    load_span(cB + 2, tid, R0);
+    load_span(cB + 3, tid, R1);
+    float x[E];
+    widen_span(R0, cB + 2, tid, true, x);
+    keep_span(R0, consume(x, cB + 2), cB + 2);
+    widen_span(R1, cB + 3, tid, true, x);
+    keep_span(R1, consume(x, cB + 3), cB + 3);
   }
   __builtin_amdgcn_s_setprio(0);
 
@@ -350,6 +347,8 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   float MH = s_wm[0];
 #pragma unroll
   for (int i = 1; i < RS_NW; ++i) MH = fmaxf(MH, s_wm[i]);
+  // the record has been read (listing): its space now holds the candidates' ranks
+  for (int i = tid; i < RS_KEYS; i += RS_NT) reinterpret_cast<int *>(s_rec)[i] = 0;
   {
     double sc = 0.0;
     if (m != -kInf) {
@@ -360,53 +359,76 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     if (lane == 0) s_ws[w] = sc;
   }
 
-  // ---- candidates: elements >= th, keyed (value desc, id asc) into the wave's key region
+  // ---- candidates: elements >= th, keyed (value desc, id asc) into the wave's key region.
+  // One call takes one span per lane: a 16-bit hit mask per lane, slots from a wave prefix
+  // of the hit counts, then one store per hit in as many rounds as the busiest lane has
+  // hits (no branch per element).
   uint64_t *const wkey = keys + w * RS_WK;
   int kn = 0;
-  auto append = [&](float *x, int c, int ln) {  // wave-uniform call
-    int hits = 0;
+  auto append = [&](const u32x4 *r, bool valid, int c, int ln) {  // wave-uniform call
+    float x[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      x[e] = x[e] >= th ? x[e] : -kInf;
-      hits += x[e] != -kInf;
+    for (int u = 0; u < RS_U; ++u) Vec<T>::widen(r[u], x + u * EPV);
+    uint32_t hm = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) hm |= (x[e] >= th ? 1u : 0u) << e;
+    // elements at or past the segment's end (partial chunks) hold no candidates
+#pragma unroll
+    for (int u = 0; u < RS_U; ++u) {
+      const int cnt = min(max(v1 - elem0(c, u, ln), 0), EPV);
+      hm &= ~(((1u << EPV) - 1u) << (u * EPV)) | (((1u << cnt) - 1u) << (u * EPV));
     }
+    if (!valid) hm = 0;
     int total;
-    int slot = kn + wave_prefix(hits, total);
-    if (hits) {
+    const int slot0 = kn + wave_prefix(__popc(hm), total);
+    for (int j = 0; __ballot(hm != 0); ++j) {
+      if (hm) {
+        const int e = __builtin_ctz(hm);
+        hm &= hm - 1;
+        float a[E];
 #pragma unroll
-      for (int u = 0; u < RS_U; ++u) {
-        const int b = elem0(c, u, ln);
+        for (int i = 0; i < E; ++i) a[i] = x[i];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          if (x[u * EPV + e] != -kInf) {
-            if (slot < RS_WK) wkey[slot] = make_key(x[u * EPV + e], (uint32_t)(b + e));
-            ++slot;
-          }
+        for (int bit = 1; bit < E; bit <<= 1) {
+#pragma unroll
+          for (int i = 0; i < E; i += 2 * bit) a[i] = (e & bit) ? a[i + bit] : a[i];
         }
+        const int id = elem0(c, e / EPV, ln) + e % EPV;
+        if (slot0 + j < RS_WK) wkey[slot0 + j] = make_key(a[0], (uint32_t)id);
       }
     }
     kn += total;
   };
-  // the preloaded spans (the first chunk of each listed group)
+  // the preloaded spans (the first chunk of each listed group, lanes below npre) and the
+  // kept spans of the chunks from cB on (the next lanes, then further calls)
   {
-    float x[E];
-    widen_span(ra, (my_ent >> 8) * cpg, my_ent & 255, my_ent >= 0, x);
-    append(x, (my_ent >> 8) * cpg, my_ent & 255);
-  }
-  // the kept spans of the chunks from cB on
-  for (int i0 = 0; i0 < min(wn, RS_WSP); i0 += 64) {
-    const int i = i0 + lane;
-    const bool valid = i < min(wn, RS_WSP);
-    u32x4 r[RS_U];
+    const int npre = min(nlist, 64), nk = min(wn, RS_WSP);
+    const int i = lane - npre;
+    u32x4 r[RS_U] = {};
     int id = 0;
-    if (valid) {
+    const bool kept = i >= 0 && i < nk;
+    if (kept) {
 #pragma unroll
       for (int u = 0; u < RS_U; ++u) r[u] = s_span[u][w * RS_WSP + i];
       id = s_spid[w * RS_WSP + i];
     }
-    float x[E];
-    widen_span(r, id >> 8, id & 255, valid, x);
-    append(x, id >> 8, id & 255);
+    if (my_ent >= 0) {
+#pragma unroll
+      for (int u = 0; u < RS_U; ++u) r[u] = ra[u];
+      id = ((my_ent >> 8) * cpg << 8) | (my_ent & 255);
+    }
+    append(r, kept || my_ent >= 0, id >> 8, id & 255);
+    for (int i0 = 64 - npre; i0 < nk; i0 += 64) {
+      const int ik = i0 + lane;
+      const bool valid = ik < nk;
+      int idk = 0;
+      if (valid) {
+#pragma unroll
+        for (int u = 0; u < RS_U; ++u) r[u] = s_span[u][w * RS_WSP + ik];
+        idk = s_spid[w * RS_WSP + ik];
+      }
+      append(r, valid, idk >> 8, idk & 255);
+    }
   }
   // re-reads: further chunks of multi-chunk groups, entries past the lanes, then groups that
   // did not fit in the list (their own lane)
@@ -417,9 +439,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
       const bool act = ent >= 0 && c < cB;
       u32x4 r[RS_U];
       load_span(act ? c : 0, ln, r);
-      float x[E];
-      widen_span(r, c, ln, act, x);
-      append(x, c, ln);
+      append(r, act, c, ln);
     }
   };
   if (cB > 0) {
@@ -457,28 +477,75 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     n_total += kn_[i];
   }
 
+  // ---- output: entry k of the row's top K (k >= the candidates found: empty)
+  const double lse = kLn2d * ((double)MH + log2(St));
+  const size_t g = (size_t)row * S + sp;
+  auto emit = [&](int k, uint64_t key, bool have) {
+    if (S == 1) {
+      const size_t o = (size_t)row * K + k;
+      if (have) {
+        const float zv = key_val(key);
+        out.ids[o] = (int32_t)key_id(key);
+        if (out.zk) out.zk[o] = zv;
+        if (out.lp) out.lp[o] = (float)((double)zv - lse);
+      } else {
+        out.ids[o] = -1;
+        if (out.zk) out.zk[o] = -kInf;
+        if (out.lp) out.lp[o] = -kInf;
+      }
+    } else {
+      part.keys[g * K + k] = have ? key : 0ull;
+    }
+  };
+  if (tid == 0) {
+    if (S == 1) {
+      if (out.lse_d) out.lse_d[row] = lse;
+      if (out.lse_f) out.lse_f[row] = (float)lse;
+    } else {
+      part.m[g] = MH;
+      part.s[g] = St;
+    }
+  }
   if (!over) {
-    // ---- top K by rank: the number of (distinct) keys above each candidate, over the four
-    // regions (zero keys pad each to a multiple of 8); each wave ranks its own region's keys
-    for (int i0 = 0; i0 < kn_[w]; i0 += 64) {
-      const int i = i0 + lane;
-      if (i < kn_[w]) {
-        const uint64_t mine = wkey[i];
+    // ---- top K by rank: the rank of a candidate is the number of (distinct) keys above it.
+    // Wave w counts, for every candidate, the keys of its own region above it (zero keys pad
+    // the region to a multiple of 8) and adds that into the candidate's rank; then each
+    // candidate whose rank is below K takes its place.
+    int *const s_rank = reinterpret_cast<int *>(s_rec);
+    int kb[RS_NW + 1];
+    kb[0] = 0;
+#pragma unroll
+    for (int q = 0; q < RS_NW; ++q) kb[q + 1] = kb[q] + kn_[q];
+    auto cand = [&](int ci) {  // candidate ci of the four regions laid end to end
+      int q = 0;
+#pragma unroll
+      for (int i = 1; i < RS_NW; ++i) q += ci >= kb[i];
+      int b = kb[0];
+#pragma unroll
+      for (int i = 1; i < RS_NW; ++i) b = q == i ? kb[i] : b;
+      return keys[q * RS_WK + ci - b];
+    };
+    const int npw = (kn_[w] + 7) & ~7;
+    for (int c0 = 0; c0 < n_total; c0 += 64) {
+      const int ci = c0 + lane;
+      if (ci < n_total) {
+        const uint64_t mine = cand(ci);
         int r = 0;
+        for (int j = 0; j < npw; j += 8) {
+          int rr = 0;
 #pragma unroll
-        for (int q = 0; q < RS_NW; ++q) {
-          const uint64_t *kq = keys + q * RS_WK;
-          const int np = (kn_[q] + 7) & ~7;
-          for (int j = 0; j < np; j += 8) {
-            int rr = 0;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) rr += (int)(kq[j + t] > mine);
-            r += rr;
-          }
+          for (int t = 0; t < 8; ++t) rr += (int)(wkey[j + t] > mine);
+          r += rr;
         }
-        if (r < K) s_top[r] = mine;
+        if (r) atomicAdd(&s_rank[ci], r);
       }
     }
+    __syncthreads();
+    for (int ci = tid; ci < n_total; ci += RS_NT) {
+      const int r = s_rank[ci];
+      if (r < K) emit(r, cand(ci), true);
+    }
+    for (int k = n_total + tid; k < K; k += RS_NT) emit(k, 0ull, false);
   } else {
     // ---- pathological row: re-stream keeping keys >= tk, raising tk to the K-th key of a
     // full buffer until a pass fits, then sort what is kept
@@ -504,38 +571,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     for (int i = n_total + tid; i < np; i += RS_NT) fb[i] = 0ull;
     __syncthreads();
     block_sort_desc_u64<RS_NT>(fb, np);
-    for (int k = tid; k < K; k += RS_NT) s_top[k] = fb[k];
-  }
-  __syncthreads();
-  const int have = n_total < K ? n_total : K;
-
-  if (S == 1) {
-    const double lse = kLn2d * ((double)MH + log2(St));
-    if (tid == 0) {
-      if (out.lse_d) out.lse_d[row] = lse;
-      if (out.lse_f) out.lse_f[row] = (float)lse;
-    }
-    for (int k = tid; k < K; k += RS_NT) {
-      const size_t o = (size_t)row * K + k;
-      if (k < have) {
-        const uint64_t key = s_top[k];
-        const float zv = key_val(key);
-        out.ids[o] = (int32_t)key_id(key);
-        if (out.zk) out.zk[o] = zv;
-        if (out.lp) out.lp[o] = (float)((double)zv - lse);
-      } else {
-        out.ids[o] = -1;
-        if (out.zk) out.zk[o] = -kInf;
-        if (out.lp) out.lp[o] = -kInf;
-      }
-    }
-  } else {
-    const size_t g = (size_t)row * S + sp;
-    if (tid == 0) {
-      part.m[g] = MH;
-      part.s[g] = St;
-    }
-    for (int k = tid; k < K; k += RS_NT) part.keys[g * K + k] = (k < have) ? s_top[k] : 0ull;
+    for (int k = tid; k < K; k += RS_NT) emit(k, fb[k], k < n_total);
   }
 }
 
