@@ -17,7 +17,9 @@
 // both rows in units of 8 elements (16-byte buffer loads, a ring of units in flight per thread)
 // with a fixed thread->element map and a fixed reduction tree, so a quantity computed
 // twice is bit-identical. Every C pass also leaves the sums of its 64-token blocks in LDS,
-// which is all the final draw needs. Two paths share the passes: with one trial per round,
+// which is all the final draw needs. A node with several children still to try after a
+// rejection sorts its residual support into ratio bins once (then each further C(t) is a
+// small query); with fewer left, each rejection is one direct C pass. Two paths share the passes: with one trial per round,
 // one workgroup per round walks lazily (only the visited nodes and the tried children
 // cost passes); with many trials, a table kernel precomputes per node the children's
 // (q(c), p'(c)) and the block prefix sums of the final residual, and one thread per
@@ -34,6 +36,7 @@ constexpr int AC_BLK = 64;         // tokens per sampling block (8 lanes x 8 ele
 constexpr int AC_WT = 256;         // threads per workgroup of the table walk
 constexpr int AC_NB = 2048;        // p/q bins of a node's residual support
 constexpr int AC_BSH = 16;         // bin width: 2^(23 - AC_BSH) = 128 bins per octave of p/q
+constexpr int AC_BINS_MIN = 3;     // children left to try that make a node build its bins
 
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11).
@@ -490,8 +493,8 @@ struct Bins {
   uint64_t P, Q;   // sums over the members of bins >= lo
 };
 
-// Sort S(t0) into the bins (two passes over the rows: counts, then placement) and sum p and q
-// over the list; returns C(t0).
+// Sort S(t0) into the bins (two passes over the rows: counts, then placement, which also
+// sums p and q over S(t0)); returns C(t0).
 template <typename T>
 DT_INLINE double wg_bins_build(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t0, Bins &bn,
                                Red &red) {
@@ -510,23 +513,20 @@ DT_INLINE double wg_bins_build(const Row<T> &A, const Row<T> &B, const Norm &nt,
   wg_scan_int(bn.cnt, bn.off, AC_NB, red);
   for (int i = threadIdx.x; i < AC_NB; i += AC_NT) bn.cnt[i] = bn.off[i];
   __syncthreads();
+  // placement, with the sums over S(t0) (exact, so in any order)
+  uint64_t v[2] = {0, 0};
   stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = prob(za[e], nt), q = prob(zb[e], nd);
       const int b = ratio_bin(p, q, bn.tbb);
-      if (in_s(p, q, t0)) bn.list[atomicAdd(&bn.cnt[b], 1)] = make_float2(p, q);
+      if (in_s(p, q, t0)) {
+        bn.list[atomicAdd(&bn.cnt[b], 1)] = make_float2(p, q);
+        v[0] += fx60(p);
+        v[1] += fx60(q);
+      }
     }
   });
-  __syncthreads();
-  // the sums over S(t0), from the list
-  uint64_t v[2] = {0, 0};
-  const int total = bn.off[AC_NB];
-  for (int i = threadIdx.x; i < total; i += AC_NT) {
-    const float2 x = bn.list[i];
-    v[0] += fx60(x.x);
-    v[1] += fx60(x.y);
-  }
   wg_sum_u64<2>(v, red);
   bn.lo = 0;
   bn.P = uni(v[0]);
@@ -777,7 +777,8 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
       const Norm nt = make_norm(s, la), nd = make_norm(s, lb);
       float t = 0.f;
       double C = 1.0;
-      bool built = false;  // the bins hold this node's residual support
+      bool built = false;     // the bins hold this node's residual support
+      bool blk_at_t = false;  // blk[] holds the block sums of the residual at t
       int nxt = -1;
       for (int c = fc[j]; c >= 0; c = ns[c]) {
         const float z1 = cz1[c], z2 = cz2[c];
@@ -789,9 +790,24 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
           nxt = c;
           break;
         }
+        // C(t2): from the bins when at least AC_BINS_MIN children are left to try (one
+        // build, then cheap queries), else by a direct pass, which also leaves the block
+        // sums at t2 (all that is needed after the last child)
         const float t2 = t + (float)C;
-        const double C2 = built ? wg_bins_query(bn, t2, red) : wg_bins_build(A, B, nt, nd, t2, bn, red);
-        built = true;
+        int left = 0;
+        for (int k = ns[c]; k >= 0 && left < AC_BINS_MIN; k = ns[k]) ++left;
+        double C2;
+        if (built) {
+          C2 = wg_bins_query(bn, t2, red);
+          blk_at_t = false;
+        } else if (left >= AC_BINS_MIN) {
+          C2 = wg_bins_build(A, B, nt, nd, t2, bn, red);
+          built = true;
+          blk_at_t = false;
+        } else {
+          C2 = wg_c_pass(A, B, nt, nd, t2, blk, nblk, red);
+          blk_at_t = C2 > 0.0;
+        }
         if (C2 > 0.0) {
           t = uni(t2);
           C = uni(C2);
@@ -801,7 +817,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
         j = nxt;
         continue;
       }
-      (void)wg_chain_pass(A, B, nt, nd, t, blk, nblk, red);
+      if (!blk_at_t) (void)wg_chain_pass(A, B, nt, nd, t, blk, nblk, red);
       __syncthreads();
       wg_prefix(blk, pre, nblk, red);
       const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
