@@ -17,6 +17,13 @@ each against the current residual with q fixed; when every child is rejected,
 or at a leaf, one token is drawn from the current residual -- the bonus token
 after a fully accepted path, the correction token otherwise.
 
+Exact target-sample matching (DARTree summary, same section: DFlash checks
+drafts by matching exact samples of the target): at node j draw x from
+p = softmax(target[j] / T) by inverse CDF with the walk's next uniform; descend to
+the child carrying x (the first in canonical order) or, with none, stop and emit
+x. Every committed token is then a sample of the target's own distribution, for
+any tree. At T = 0 the draw is the argmax and the rule is the greedy walk.
+
 p = softmax(target[j] / T) for node j; q = softmax(draft[depth(j)] / T), the
 position its children were drafted from. Acceptance is tested without a
 division as u * q(c) < p'(c); sampling is by inverse CDF in id order: the
@@ -127,3 +134,49 @@ def exact_outcomes(tab: ResidualTables):
             r = r * (1.0 - a)
         stop[j] = r
     return stop, reach
+
+
+def walk_match(parent, token, depth, target_rows: np.ndarray, T: float, seed: int, trial: int, rnd: int):
+    """Target-sample matching for one (trial, round): one Philox uniform per visited node
+    (step 0, 1, ...). Returns (accept_len, accept_node, next_token)."""
+    kids = children_lists(parent)
+    j = 0
+    step = 0
+    while True:
+        u = uniform(seed, trial, rnd, step)
+        step += 1
+        x = sample_inverse_cdf(softmax_row(target_rows[j], T), u)
+        nxt = -1
+        for c in kids[j]:
+            if token[c] == x:
+                nxt = c
+                break
+        if nxt < 0:
+            return depth[j], j, x
+        j = nxt
+
+
+def match_outcomes(parent, token, target_rows: np.ndarray, T: float):
+    """Exact law of target-sample matching: reach[c] = reach[j] p_j(token c) for the first
+    child of j carrying that token; stop[j] = reach[j] times the p_j-mass of the tokens no
+    child of j carries, and the emitted token then follows p_j restricted to those tokens.
+    Returns (stop, reach, emit) with emit[j] that restricted, renormalised law (None when
+    the restricted mass is 0)."""
+    kids = children_lists(parent)
+    n1 = len(parent)
+    reach = np.zeros(n1)
+    stop = np.zeros(n1)
+    emit = [None] * n1
+    reach[0] = 1.0
+    for j in range(n1):
+        p = softmax_row(target_rows[j], T)
+        free = p.copy()
+        for c in kids[j]:
+            x = token[c]
+            if free[x] > 0.0:  # the first child carrying x takes the draws of x
+                reach[c] = reach[j] * p[x]
+                free[x] = 0.0
+        m = float(np.sum(free))
+        stop[j] = reach[j] * m
+        emit[j] = free / m if m > 0.0 else None
+    return stop, reach, emit

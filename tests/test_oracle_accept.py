@@ -118,3 +118,63 @@ def test_yield_bounds_and_total_probability():
         assert 0 <= nxt < V
         # committed tokens per round: accepted drafts plus one extra token
         assert 1 <= alen + 1 <= L + 1
+
+
+def match_case(seed=21, L=4, V=12, B=14):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((L, V)) * 1.5
+    t = marginal.build_marginal(z, 0, B, 0.0)
+    target = np.stack([z[min(t.depth[j], L - 1)] + rng.standard_normal(V) for j in range(t.n + 1)])
+    return t, target
+
+
+def test_match_law_is_lossless():
+    """Target-sample matching commits exact target samples: whatever the tree, the first
+    committed token (a depth-1 child's token, or the token emitted at the root) has the law
+    p_root, and after a child c it continues with p_c, which is what the law's reach/stop
+    split must reproduce token by token."""
+    t, target = match_case()
+    for T in (1.0, 0.7):
+        stop, reach, emit = accept.match_outcomes(t.parent, t.token, target, T)
+        assert abs(stop.sum() - 1.0) < 1e-12
+        kids = accept.children_lists(t.parent)
+        for j in range(t.n + 1):
+            if reach[j] == 0.0:
+                continue
+            p = accept.softmax_row(target[j], T)
+            law = np.zeros_like(p)       # next committed token, given the walk reached j
+            if emit[j] is not None:
+                law += stop[j] / reach[j] * emit[j]
+            for c in kids[j]:
+                law[t.token[c]] += reach[c] / reach[j]
+            np.testing.assert_allclose(law, p, atol=1e-12)
+
+
+def test_match_walk_frequencies():
+    t, target = match_case(seed=22)
+    stop, _, emit = accept.match_outcomes(t.parent, t.token, target, 1.0)
+    n = 20000
+    res = [accept.walk_match(t.parent, t.token, t.depth, target, 1.0, 0x5EED5EED, tr, 3) for tr in range(n)]
+    nodes = np.bincount([r[1] for r in res], minlength=t.n + 1)
+    for j in range(t.n + 1):
+        assert abs(nodes[j] - n * stop[j]) <= 3.5 * math.sqrt(n * stop[j] * (1 - stop[j])) + 1
+    j = int(np.argmax(stop))
+    toks = np.array([r[2] for r in res if r[1] == j])
+    m = toks.shape[0]
+    for v in range(target.shape[1]):
+        f = emit[j][v]
+        assert abs(np.sum(toks == v) - m * f) <= 3.5 * math.sqrt(m * f * (1 - f)) + 1
+    for alen, node, nxt in res[:200]:
+        assert t.depth[node] == alen and nxt not in [t.token[c] for c in accept.children_lists(t.parent)[node]]
+
+
+def test_match_walk_sharp_target_is_greedy():
+    """A target row with one dominant logit draws that token with probability ~1: the walk
+    then follows the greedy walk exactly."""
+    t, target = match_case(seed=23)
+    sharp = target.copy()
+    for j in range(sharp.shape[0]):
+        sharp[j, int(np.argmax(sharp[j]))] += 80.0
+    g = accept.walk_greedy(t.parent, t.token, t.depth, sharp)
+    for tr in range(50):
+        assert accept.walk_match(t.parent, t.token, t.depth, sharp, 1.0, 9, tr, 0) == g
