@@ -164,6 +164,21 @@ def main():
                 "kernel": "k_rowsweep<bf16> (dtree_topk_logsoftmax, R*L=1024 rows, K=64)",
                 "us_per_launch": round(sweep_us, 2), "alg_bytes_per_launch": alg_bytes}
 
+    # ---- outside the step: exact target-sample matching (T = 1, one trial per round) on the
+    # same trees and target rows, timed per call with events on this stream
+    ws_x = torch.empty(dt.workspace_size(dt.OP_ACCEPT, R, 1, V, 0, 64), dtype=torch.uint8, device=dev)
+    for i in range(3):
+        dt.accept_tree_match(t_m, target, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_x, outs=o1)
+    torch.cuda.synchronize()
+    n_match = max(args.steps, 10)
+    ex = [torch.cuda.Event(enable_timing=True) for _ in range(n_match + 1)]
+    ex[0].record(stream)
+    for i in range(n_match):
+        dt.accept_tree_match(t_m, target, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_x, outs=o1)
+        ex[i + 1].record(stream)
+    torch.cuda.synchronize()
+    match_ms = float(np.mean([ex[i].elapsed_time(ex[i + 1]) for i in range(n_match)]))
+
     out = {
         "metric": "tree-build rounds/sec + us/round at V=151936,L=16,B=128; HBM GB/s vs peak",
         "value": round(value, 1), "unit": "rounds/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -177,6 +192,7 @@ def main():
         "breakdown_ms": {n: round(float(per[:, k].mean()), 4) for k, n in enumerate(names)},
         "event_ms_per_step": round(step_ms, 4),
         "roofline": roofline,
+        "extra_ms": {"accept_match_t1": round(match_ms, 4)},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(draft_h, talon_h, head)

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
     build_tree_gated(logits, K_root, mu, N)             -> Tree
     accept_tree(tree, target, draft, temperature, seed, trial0, n_trials)
         -> (accept_len, accept_node, next_token), each [n_trials, R]
+    accept_tree_match(tree, target, temperature, seed, trial0, n_trials)   (same outputs)
 Logits are torch.bfloat16 or torch.float32 device tensors ([R, L, V] for the builders).
 """
 from __future__ import annotations
@@ -32,7 +33,7 @@ STATUS = {0: "DTREE_OK", -1: "DTREE_E_INVAL", -2: "DTREE_E_BETA", -3: "DTREE_E_W
 
 # every symbol include/dtree.h declares
 SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_depthwise",
-           "build_tree_gated", "accept_tree", "dtree_status_string", "dtree_last_error")
+           "build_tree_gated", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
 
 
 class DTreeError(RuntimeError):
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
     L.accept_tree.restype = i32
     L.accept_tree.argtypes = [ctypes.POINTER(CTree), vp, vp, i32, i32, i32, i32, f32, u64, u64, i32, vp, vp, vp,
                               vp, sz, vp]
+    L.accept_tree_match.restype = i32
+    L.accept_tree_match.argtypes = [ctypes.POINTER(CTree), vp, i32, i32, i32, f32, u64, u64, i32, vp, vp, vp, vp, sz,
+                                    vp]
     L.dtree_status_string.restype = ctypes.c_char_p
     L.dtree_status_string.argtypes = [i32]
     L.dtree_last_error.restype = ctypes.c_char_p
@@ -222,4 +226,22 @@ def accept_tree(tree: Tree, target: torch.Tensor, draft: torch.Tensor | None, te
     _check(lib().accept_tree(ctypes.byref(st), _ptr(target), _ptr(draft), _dtype(target), R, L, V, float(temperature),
                              int(seed), int(trial0), int(n_trials), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
                              _ptr(ws), ws.numel(), _stream(dev)))
+    return outs
+
+
+def accept_tree_match(tree: Tree, target: torch.Tensor, temperature: float, seed: int, trial0: int = 0,
+                      n_trials: int = 1, ws: torch.Tensor | None = None, outs=None):
+    """Exact target-sample matching; target [R, cap+1, V]."""
+    _require_device(target)
+    R, rows, V = target.shape
+    if rows != tree.cap + 1:
+        raise ValueError("target must have cap+1 rows per round")
+    dev = target.device
+    if outs is None:
+        outs = tuple(torch.empty(n_trials, R, dtype=torch.int32, device=dev) for _ in range(3))
+    ws = _workspace(workspace_size(OP_ACCEPT, R, 1, V, 0, tree.cap), dev) if ws is None else ws
+    st = tree.c_struct()
+    _check(lib().accept_tree_match(ctypes.byref(st), _ptr(target), _dtype(target), R, V, float(temperature), int(seed),
+                                   int(trial0), int(n_trials), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(ws),
+                                   ws.numel(), _stream(dev)))
     return outs

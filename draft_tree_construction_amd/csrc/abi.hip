@@ -225,9 +225,35 @@ int accept_tree(const dtree_tree *tree, const void *target_logits, const void *d
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   dt::AcceptArgs a{tree_out(tree), target_logits, draft_logits, dtype, R, L, V, temperature, seed, trial0, n_trials,
-                   accept_len, accept_node, next_token};
+                   accept_len, accept_node, next_token, 0};
   hipError_t e = dt::launch_accept(a, ws, static_cast<hipStream_t>(s));
   if (e != hipSuccess) return hip_fail(e, "accept_tree");
+  return DTREE_OK;
+}
+
+int accept_tree_match(const dtree_tree *tree, const void *target_logits, int dtype, int R, int V, float temperature,
+                      uint64_t seed, uint64_t trial0, int n_trials, int32_t *accept_len, int32_t *accept_node,
+                      int32_t *next_token, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (!tree) return fail(DTREE_E_INVAL, "tree struct is NULL");
+  if (R < 0 || V < 1 || n_trials < 1) return fail(DTREE_E_INVAL, "need R >= 0, V, n_trials >= 1");
+  if (!(temperature >= 0.f) || isinf(temperature)) return fail(DTREE_E_INVAL, "need finite temperature >= 0");
+  if (tree->cap < 1) return fail(DTREE_E_INVAL, "tree cap < 1");
+  if (tree->cap > DTREE_MAX_CAP || V > DTREE_MAX_ACCEPT_V)
+    return fail(DTREE_E_UNSUPPORTED, "cap or V beyond the compiled envelope");
+  int rc = check_tree(tree, tree->cap);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!target_logits || !accept_len || !accept_node || !next_token)
+    return fail(DTREE_E_INVAL, "target_logits or an output is NULL");
+  const size_t need = dt::accept_ws_bytes(R, 1, V, tree->cap);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
+  // at T = 0 the target's draw is its argmax: the greedy walk
+  dt::AcceptArgs a{tree_out(tree), target_logits, nullptr, dtype, R, 1, V, temperature, seed, trial0, n_trials,
+                   accept_len, accept_node, next_token, temperature > 0.f ? 1 : 0};
+  hipError_t e = dt::launch_accept(a, ws, static_cast<hipStream_t>(s));
+  if (e != hipSuccess) return hip_fail(e, "accept_tree_match");
   return DTREE_OK;
 }
 

@@ -3,6 +3,9 @@
 // What it computes (DARTree background "speculative sampling"; course notes unit 11):
 // T = 0: from the root, descend to the child carrying the target's argmax (smallest id on
 // ties); where no child matches, stop and emit that argmax.
+// Target-sample matching (T > 0; the DARTree summary's note on DFlash): at node j draw x from
+// p = softmax(target[j] / T) by inverse CDF; descend to the first child carrying x, else stop
+// and emit x. Each visited node costs an LSE pass and a block-sum pass over its target row.
 // T > 0: at node j with p = softmax(target[j] / T) and q = softmax(draft[depth j] / T),
 // try the children in slot order: accept child c iff u * q(c) < p'(c); a rejection sets
 // p' <- (p' - q)_+ / sum (unchanged when the sum is 0). With no child accepted (or at a
@@ -296,6 +299,29 @@ DT_INLINE void wg_lse2(const Row<T> &A, const Row<T> &B, float s, Red &red, doub
   lb = (double)MB + log2(SB);
 }
 
+// LSE2 of one row (the same online accumulation as wg_lse2, one row).
+template <typename T>
+DT_INLINE double wg_lse2_1(const Row<T> &A, float s, Red &red) {
+  L2Acc xa;
+  stream1(A, [&](int, const float *za) { xa.add(za, s); });
+  const float ma = wave_max(xa.m == -kInf ? -kInf : xa.mh);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red.f[w] = ma;
+  __syncthreads();
+  float MA = red.f[0];
+#pragma unroll
+  for (int i = 1; i < AC_NW; ++i) MA = fmaxf(MA, red.f[i]);
+  double sa = (xa.m == -kInf) ? 0.0 : xa.acc * (double)__builtin_amdgcn_exp2f(xa.mh - MA);
+  sa = wave_sum(sa);
+  if ((threadIdx.x & 63) == 0) red.d[w] = sa;
+  __syncthreads();
+  double SA = 0.0;
+#pragma unroll
+  for (int i = 0; i < AC_NW; ++i) SA += red.d[i];
+  return (double)MA + log2(SA);
+}
+
 // First index of the maximum of one row. Each thread sees its elements in increasing index
 // order and keeps the first of its largest (compare and select); the threads' results are
 // combined as (value desc, id asc) keys.
@@ -344,6 +370,22 @@ DT_INLINE double wg_chain_pass(const Row<T> &A, const Row<T> &B, const Norm &nt,
     acc += (double)part;
   });
   return wg_sum(acc, red);
+}
+
+// The float sums of p over the 64-token blocks, formed as wg_chain_pass forms them at t = 0
+// (there the residual is p itself, bit for bit).
+template <typename T>
+DT_INLINE void wg_p_blocks(const Row<T> &A, const Norm &nt, float *blk, int nblk) {
+  stream1(A, [&](int u, const float *za) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part += prob(za[e], nt);
+    float bs = part;
+    bs += __shfl_xor(bs, 1, 64);
+    bs += __shfl_xor(bs, 2, 64);
+    bs += __shfl_xor(bs, 4, 64);
+    if ((u & 7) == 0 && (u >> 3) < nblk) blk[u >> 3] = bs;
+  });
 }
 
 // ---------------------------------------------------------------- exact C(t)
@@ -742,6 +784,40 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
       }
       j = nxt;
     }
+  } else if (a.match) {
+    const float s = log2_scale(a.T);
+    const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
+    double *pre = dyn;
+    float *blk = reinterpret_cast<float *>(dyn + nblk);
+    uint32_t step = 0;
+    bool lists = false;
+    for (;;) {
+      const T *zt = target + (size_t)j * a.V;
+      const Row<T> A = make_row(zt, a.V);
+      const Norm nt = make_norm(s, wg_lse2_1(A, s, red));  // ends with a barrier
+      if (!lists) {
+        build_children(par, tok, n, a.V, fc, ns, sr, pv);
+        lists = true;
+      }
+      wg_p_blocks(A, nt, blk, nblk);
+      __syncthreads();
+      wg_prefix(blk, pre, nblk, red);
+      const float u = philox_uniform(a.seed, a.trial0, (uint32_t)r, step++);
+      const double target_mass = (double)u * pre[nblk - 1];
+      const int b = find_block(pre, nblk, target_mass);
+      const int x = sample_in_block_wave(zt, zt, a.V, nt, nt, 0.f, pre, b, target_mass);
+      int nxt = -1;
+      for (int c = fc[j]; c >= 0; c = ns[c])
+        if (tok[c] == x) {
+          nxt = c;
+          break;
+        }
+      if (nxt < 0) {
+        out_tok = x;
+        break;
+      }
+      j = nxt;
+    }
   } else {
     const float s = log2_scale(a.T);
     const T *draft = static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V;
@@ -864,9 +940,22 @@ __global__ __launch_bounds__(AC_NT) void k_accept_tables(AcceptArgs a, AccTables
   build_children(par, tok, n, a.V, fc, ns, sr, pv);
   const float s = log2_scale(a.T);
   const T *zt = static_cast<const T *>(a.target) + ((size_t)r * (cap + 1) + j) * a.V;
-  const T *zd = static_cast<const T *>(a.draft) + ((size_t)r * a.L + draft_row(dep[j], a.L)) * a.V;
   const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
   float *blk = reinterpret_cast<float *>(dyn);
+  if (a.match) {  // the node's own target distribution and its block prefix sums
+    const Row<T> A = make_row(zt, a.V);
+    const Norm nt = make_norm(s, wg_lse2_1(A, s, red));
+    wg_p_blocks(A, nt, blk, nblk);
+    __syncthreads();
+    wg_prefix(blk, tb.pre + (base + j) * nblk, nblk, red);
+    if (threadIdx.x == 0) {
+      tb.tfin[base + j] = 0.f;
+      tb.lt_hi[base + j] = tb.lq_hi[base + j] = nt.hi;
+      tb.lt_lo[base + j] = tb.lq_lo[base + j] = nt.lo;
+    }
+    return;
+  }
+  const T *zd = static_cast<const T *>(a.draft) + ((size_t)r * a.L + draft_row(dep[j], a.L)) * a.V;
   const Row<T> A = make_row(zt, a.V), B = make_row(zd, a.V);
   double la, lb;
   wg_lse2(A, B, s, red, la, lb);
@@ -916,6 +1005,33 @@ __global__ __launch_bounds__(AC_WT) void k_accept_walk(AcceptArgs a, AccTables t
   const int32_t *par = a.tree.parent + base;
   int j = 0;
   uint32_t step = 0;
+  const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
+  if (a.match) {
+    Norm nt;
+    nt.s = log2_scale(a.T);
+    for (;;) {
+      nt.hi = tb.lt_hi[base + j];
+      nt.lo = tb.lt_lo[base + j];
+      const T *zt = static_cast<const T *>(a.target) + ((size_t)r * (cap + 1) + j) * a.V;
+      const double *pre = tb.pre + (base + j) * nblk;
+      const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
+      const double target_mass = (double)u * pre[nblk - 1];
+      const int x = sample_in_block_serial(zt, zt, a.V, nt, nt, 0.f, pre, find_block(pre, nblk, target_mass), target_mass);
+      int nxt = -1;
+      for (int c = j + 1; c <= n; ++c)
+        if (par[c] == j && a.tree.token[base + c] == x) {
+          nxt = c;
+          break;
+        }
+      if (nxt < 0) {
+        a.accept_len[gid] = a.tree.depth[base + j];
+        a.accept_node[gid] = j;
+        a.next_token[gid] = x;
+        return;
+      }
+      j = nxt;
+    }
+  }
   for (;;) {
     int nxt = -1;
     for (int c = j + 1; c <= n; ++c) {
@@ -940,7 +1056,6 @@ __global__ __launch_bounds__(AC_WT) void k_accept_walk(AcceptArgs a, AccTables t
   nt.lo = tb.lt_lo[base + j];
   nd.hi = tb.lq_hi[base + j];
   nd.lo = tb.lq_lo[base + j];
-  const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
   const double *pre = tb.pre + (base + j) * nblk;
   const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
   const double target_mass = (double)u * pre[nblk - 1];

@@ -173,6 +173,23 @@ int accept_tree(const dtree_tree *tree, const void *target_logits, const void *d
                 int32_t *accept_len, int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes,
                 dtree_stream_t s);
 
+/*
+ * Exact target-sample matching (DARTree background "speculative sampling": DFlash verifies
+ * by matching exact samples of the target), for any tree.
+ * At node j draw x from p = softmax(target[r][j] / T) by inverse CDF (smallest v with
+ * cumsum p(v) > u * sum p) with the walk's next uniform (one per visited node, step 0, 1,
+ * ..., same Philox stream as accept_tree); descend to the first child in slot order that
+ * carries x, else stop and emit x. Every committed token is then a sample of the target's
+ * distribution. temperature == 0 is the greedy walk of accept_tree.
+ * tree, target_logits [R][cap+1][V], outputs [n_trials][R] and workspace
+ * (dtree_workspace_size(DTREE_OP_ACCEPT, R, 1, V, 0, cap, ...)) as for accept_tree; no
+ * draft logits. Needs cap <= DTREE_MAX_CAP, V <= DTREE_MAX_ACCEPT_V, n_trials >= 1,
+ * temperature >= 0.
+ */
+int accept_tree_match(const dtree_tree *tree, const void *target_logits, int dtype, int R, int V,
+                      float temperature, uint64_t seed, uint64_t trial0, int n_trials, int32_t *accept_len,
+                      int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes, dtree_stream_t s);
+
 /* Static string for a dtree_status code. */
 const char *dtree_status_string(int status);
 

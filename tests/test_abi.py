@@ -132,6 +132,21 @@ def test_accept_validation():
     assert L.accept_tree(None, FAKE, FAKE, 0, 4, 16, 100, 1.0, 1, 0, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
 
 
+def test_accept_match_validation():
+    L = dt.lib()
+    t = tree(64)
+    def call(T=1.0, n=1, V=151936, ws=FAKE, nbytes=0):
+        o = FAKE
+        return L.accept_tree_match(ctypes.byref(t), FAKE, 0, 4, V, T, 1, 0, n, o, o, o, ws, nbytes, None)
+    assert call(T=-1.0) == -1
+    assert call(T=float("nan")) == -1
+    assert call(n=0) == -1
+    assert call(V=300000) == -4
+    assert call() == -3
+    assert call(ws=ctypes.c_void_p(0x1008), nbytes=1 << 40) == -1   # misaligned workspace
+    assert L.accept_tree_match(None, FAKE, 0, 4, 100, 1.0, 1, 0, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == -1
+
+
 def test_topk_validation():
     L = dt.lib()
     def call(K=8, V=32, rows=4, dtype=0):

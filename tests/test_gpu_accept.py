@@ -154,3 +154,84 @@ def test_worked_example_on_gpu():
         toks = np.where(alen[:, x] == 1, x, nxt[:, x])
         out += q[x] * np.bincount(toks, minlength=3) / n
     assert np.all(np.abs(out - p) <= 3 * np.sqrt(p * (1 - p) / n) * 2)
+
+
+@pytest.mark.parametrize("R,L,V,B,n", [(4, 16, 2000, 64, 300), (5, 6, 777, 20, 200)])
+def test_match_walk_trial_by_trial_against_oracle(R, L, V, B, n):
+    """Target-sample matching on the table path (many trials) against the oracle's walk."""
+    draft, trees, target = verification_case(R, L, V, B)
+    alen, anode, nxt = host_outs(dt.accept_tree_match(oracle_to_device(trees, B), dev_bf16(target), 1.0, SEED, 0, n))
+    bad = 0
+    for r in range(R):
+        rows = rowsweep.as_f64(target[r, :trees[r].n + 1], "bf16")
+        for t in range(n):
+            ref = accept.walk_match(trees[r].parent, trees[r].token, trees[r].depth, rows, 1.0, SEED, t, r)
+            bad += ref != (alen[t, r], anode[t, r], nxt[t, r])
+    assert bad <= 2, bad   # draws within float rounding of a block or token boundary may differ
+
+
+def test_match_walk_lazy_equals_tables():
+    R, L, V, B = 6, 16, 4000, 64
+    draft, trees, target = verification_case(R, L, V, B)
+    dtree, tg = oracle_to_device(trees, B), dev_bf16(target)
+    many = host_outs(dt.accept_tree_match(dtree, tg, 0.8, SEED, 0, 64))
+    for t in (0, 5, 63):
+        one = host_outs(dt.accept_tree_match(dtree, tg, 0.8, SEED, t, 1))
+        for k in range(3):
+            np.testing.assert_array_equal(one[k][0], many[k][t])
+
+
+def test_match_walk_frequencies_within_3_sigma():
+    """Stop-node frequencies over 10^6 trials per round against the oracle's exact law, and
+    the emitted token's law at the most frequent stop node."""
+    R, L, V, B = 4, 16, 3000, 64
+    n = 1_000_000
+    draft, trees, target = verification_case(R, L, V, B, seed=13)
+    alen, anode, nxt = host_outs(dt.accept_tree_match(oracle_to_device(trees, B), dev_bf16(target), 1.0, SEED, 0, n))
+    bins = beyond = 0
+    for r in range(R):
+        rows = rowsweep.as_f64(target[r, :trees[r].n + 1], "bf16")
+        stop, _, emit = accept.match_outcomes(trees[r].parent, trees[r].token, rows, 1.0)
+        counts = np.bincount(anode[:, r], minlength=len(stop))
+        for j, p in enumerate(stop):
+            if p * n < 5:
+                assert counts[j] <= max(10, 10 * p * n)
+                continue
+            bins += 1
+            beyond += abs(counts[j] - n * p) > 3 * math.sqrt(n * p * (1 - p))
+        j = int(np.argmax(stop))
+        sel = nxt[anode[:, r] == j, r]
+        m = sel.shape[0]
+        for v in np.argsort(-emit[j])[:5]:
+            f = emit[j][v]
+            if f * m < 5:
+                continue
+            bins += 1
+            beyond += abs(np.sum(sel == v) - m * f) > 3 * math.sqrt(m * f * (1 - f))
+    assert beyond <= 0.01 * bins + 2, (beyond, bins)
+
+
+def test_match_walk_full_vocabulary_sampled_rounds():
+    """Verification config at full vocabulary (V = 151,936, B = 64): the one-trial walk
+    (one workgroup per round) on three rounds, several trials, against the oracle."""
+    R, L, V, B = 3, 16, 151936, 64
+    draft, trees, target = verification_case(R, L, V, B)
+    dtree, tg = oracle_to_device(trees, B), dev_bf16(target)
+    rows = [rowsweep.as_f64(target[r, :trees[r].n + 1], "bf16") for r in range(R)]
+    bad = 0
+    for t in range(4):
+        alen, anode, nxt = host_outs(dt.accept_tree_match(dtree, tg, 1.0, SEED, t, 1))
+        for r in range(R):
+            ref = accept.walk_match(trees[r].parent, trees[r].token, trees[r].depth, rows[r], 1.0, SEED, t, r)
+            bad += ref != (alen[0, r], anode[0, r], nxt[0, r])
+    assert bad <= 1, bad
+
+
+def test_match_walk_zero_temperature_is_greedy():
+    R, L, V, B = 4, 16, 3000, 64
+    draft, trees, target = verification_case(R, L, V, B)
+    dtree, tg = oracle_to_device(trees, B), dev_bf16(target)
+    g = host_outs(dt.accept_tree(dtree, tg, None, 0.0, SEED, 0, 2))
+    m = host_outs(dt.accept_tree_match(dtree, tg, 0.0, SEED, 0, 2))
+    for k in range(3):
+        np.testing.assert_array_equal(g[k], m[k])
