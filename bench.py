@@ -179,6 +179,33 @@ def main():
     torch.cuda.synchronize()
     match_ms = float(np.mean([ex[i].elapsed_time(ex[i + 1]) for i in range(n_match)]))
 
+    # ---- outside the step: DARTree's other widths on the same inputs, W = B (the exact
+    # best-first tree) and W = B / L (the fixed variant), beta = 0; and each tree's covered
+    # draft mass, sum over nodes of exp(s_0(u)) (s_0 the score without the depth bonus; the
+    # expected accepted length under the corrected draft, DDTree's Proposition 1)
+    def covered(t, beta):
+        sc, dp = t.score.cpu().numpy().astype(np.float64), t.depth.cpu().numpy()
+        nn = t.n_nodes.cpu().numpy()
+        return float(np.mean([np.exp(sc[r, 1:nn[r] + 1] - beta * dp[r, 1:nn[r] + 1]).sum() for r in range(R)]))
+
+    ws_w = torch.empty(dt.workspace_size(dt.OP_DEPTHWISE, R, L, V, 8, 128, 128, 64, 1024), dtype=torch.uint8,
+                       device=dev)
+    t_w = dt.Tree.empty(R, 128, dev)
+    extra_ms = {"accept_match_t1": round(match_ms, 4)}
+    mass = {"pruned_w32_beta-0.5": round(covered(t_d, -0.5), 4)}
+    for name, W in (("exact_w128", 128), ("fixed_w8", 8)):
+        for _ in range(2):
+            dt.build_tree_depthwise(draft, E, U, P, root, 8, W, 128, 0.0, ws=ws_w, out=t_w)
+        torch.cuda.synchronize()
+        ew = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ew[0].record(stream)
+        for i in range(5):
+            dt.build_tree_depthwise(draft, E, U, P, root, 8, W, 128, 0.0, ws=ws_w, out=t_w)
+            ew[i + 1].record(stream)
+        torch.cuda.synchronize()
+        extra_ms["depthwise_" + name] = round(float(np.mean([ew[i].elapsed_time(ew[i + 1]) for i in range(5)])), 4)
+        mass[name] = round(covered(t_w, 0.0), 4)
+
     out = {
         "metric": "tree-build rounds/sec + us/round at V=151936,L=16,B=128; HBM GB/s vs peak",
         "value": round(value, 1), "unit": "rounds/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -192,7 +219,8 @@ def main():
         "breakdown_ms": {n: round(float(per[:, k].mean()), 4) for k, n in enumerate(names)},
         "event_ms_per_step": round(step_ms, 4),
         "roofline": roofline,
-        "extra_ms": {"accept_match_t1": round(match_ms, 4)},
+        "extra_ms": extra_ms,
+        "covered_draft_mass": mass,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(draft_h, talon_h, head)

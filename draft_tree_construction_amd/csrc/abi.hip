@@ -183,7 +183,7 @@ int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, con
     return fail(DTREE_E_INVAL, "need R >= 0, L, V, W, B, d_model, rank >= 1, 1 <= K <= V");
   if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
   if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
-  if (rank != 64 || d_model % 64 != 0 || K > DTREE_MAX_K || W > 64 || W * K > 1024 || L * W > 2048 ||
+  if (rank != 64 || d_model % 64 != 0 || K > DTREE_MAX_K || W > 128 || W * K > 1024 || L * W > 2048 ||
       B > DTREE_MAX_CAP || L > DTREE_MAX_L)
     return fail(DTREE_E_UNSUPPORTED, "rank, d_model, K, W, B or L beyond the compiled envelope");
   int rc = check_tree(out, B);

@@ -51,6 +51,7 @@ constexpr int DW_NC = 64;      // V chunks (partials per state)
 constexpr int DW_HX = 80;      // state row: h (64), -ref, one-hot base (8), 1 (mask), zero padding
 constexpr int DW_SUP = 2048;   // super-tree nodes per round (L * W)
 constexpr int DW_CH = 1024;    // children per depth (W * K)
+constexpr int DW_WMAX = 128;   // kept branches per depth (W)
 constexpr float DW_WIDE = 10.f;
 
 DT_INLINE bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
@@ -646,8 +647,8 @@ __global__ __launch_bounds__(DW_NT) void k_dw_lq(DwState s, DwDev a, DwDims g) {
 // their parents' states, the best W kept), then the deferred Top-B and the outputs.
 struct DwTreeLds {
   double lqs[64 * 64];       // this depth's log q~ rows, [state][candidate]
-  double bs[64];             // current branches: score, state index
-  int bk[64];
+  double bs[DW_WMAX];        // current branches: score, state index
+  int bk[DW_WMAX];
   double cs[DW_CH];          // children (padded to a multiple of 8)
   int cpk[DW_CH];
   double fs[DW_SUP];         // the super-tree, S_1 .. S_L: score, parent position << 16 | rank
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
         lo[i] = 0;
       }
 #pragma unroll
-      for (int step = 64; step >= 1; step >>= 1) {
+      for (int step = DW_WMAX; step >= 1; step >>= 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = lo[i] + step;

@@ -125,9 +125,11 @@ int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int 
  * correction head: branch state = its last token (root: root_tok[r]);
  *   h = bf16(E[tok] @ U_d),  z = base_d + h @ P,  log q~_d(c | b) = z[c] - logsumexp(z)
  * for c in C_d = top-K of base_d (shared by all branches); per depth the global top-W
- * children are kept, then the B best of the whole super-tree by s_beta.
+ * children are kept, then the B best of the whole super-tree by s_beta. W = B gives the
+ * exact best-first tree over the corrected path scores (the summary's sequential
+ * correction with a heap); B = L*W keeps every kept branch (DARTree's fixed variant).
  * E [V][d_model], U [L][d_model][rank], P [rank][V] are bf16 bits; root_tok [R] int32.
- * Needs beta <= 0, rank == 64, d_model % 64 == 0, K <= DTREE_MAX_K, W <= 64, W*K <= 1024,
+ * Needs beta <= 0, rank == 64, d_model % 64 == 0, K <= DTREE_MAX_K, W <= 128, W*K <= 1024,
  * L*W <= 2048, B <= DTREE_MAX_CAP, out->cap == B. E, U and P must be 16-byte aligned
  * (else DTREE_E_INVAL). root_tok values must lie in [0, V) (an out-of-range value is read
  * as token 0).

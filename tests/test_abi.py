@@ -110,7 +110,7 @@ def test_depthwise_validation():
     assert call(E=ctypes.c_void_p(0x1002)) == -1   # E, U, P are read with 16-byte loads
     assert call(rank=32) == -4
     assert call(dm=1000) == -4
-    assert call(W=65) == -4
+    assert call(W=129, K=4) == -4
     assert call(K=9, W=64*2) == -4
     assert call() == -3
 

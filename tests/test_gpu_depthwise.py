@@ -102,3 +102,29 @@ def test_depthwise_one_round_over_two_tiles():
     exact, n = check(base, "bf16", E, U, P, root, 40, 16, 60, -0.3)
     assert exact >= n - 1
 
+
+
+def test_depthwise_width_b_exact_best_first():
+    """W = B = 128 (K = 8, W*K = 1024 children per depth): the exact corrected best-first tree."""
+    R, L, V, dm = 3, 6, 900, 64
+    base = synth.ddtree_logits(seed=16, R=R, L=L, V=V)
+    E, U, P, root = synth.correction_head(seed=116, R=R, L=L, V=V, d_model=dm, rank=64)
+    exact, n = check(base, "bf16", E, U, P, root, 8, 128, 128, 0.0)
+    assert exact >= n - 1
+
+
+def test_depthwise_fixed_width_keeps_every_branch():
+    """DARTree (fixed): W = B / L, B = L * W, no depth bonus."""
+    R, L, V, dm = 3, 16, 1200, 64
+    base = synth.ddtree_logits(seed=17, R=R, L=L, V=V)
+    E, U, P, root = synth.correction_head(seed=117, R=R, L=L, V=V, d_model=dm, rank=64)
+    exact, n = check(base, "bf16", E, U, P, root, 8, 8, 128, 0.0)
+    assert exact >= n - 1
+
+
+def test_depthwise_full_config_exact_best_first_sampled():
+    """Full DARTree shapes with W = B = 128 (exact best-first), two rounds against the oracle."""
+    base = synth.ddtree_logits(seed=2)
+    E, U, P, root = synth.correction_head(seed=3)
+    exact, n = check(base, "bf16", E, U, P, root, 8, 128, 128, 0.0, rounds=(0, 63))
+    assert exact >= n - 1

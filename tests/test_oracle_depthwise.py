@@ -83,6 +83,23 @@ def test_no_pruning_equals_exact_corrected_best_first(seed):
     treeout.check_invariants(t, B, L)
 
 
+@pytest.mark.parametrize("seed", [5, 6])
+def test_width_b_equals_exact_corrected_best_first(seed):
+    """W = B already gives the exact best-first tree (the DARTree summary's sequential
+    correction with a heap): a prefix in the global Top-B has fewer than B prefixes above
+    it, so it is among the B best of its depth, whose parents are among the B best of theirs."""
+    rng = np.random.default_rng(seed)
+    L, V, K, B = 4, 24, 3, 10
+    base = rng.standard_normal((L, V)) * 1.5
+    E, U, P = small_head(rng, V, 8, 4, L, 0.8)
+    t = depthwise.build_depthwise(base, E, U, P, root_tok=2, K=K, W=B, B=B, beta=0.0)
+    ref = corrected_brute_force(base, E, U, P, 2, K, B, 0.0)
+    got = {p: s for p, s in zip(t.paths()[1:], t.score[1:])}
+    assert set(got) == set(ref)
+    for p in got:
+        assert abs(got[p] - ref[p]) < 1e-12
+
+
 def test_width_one_is_greedy_corrected_chain():
     rng = np.random.default_rng(4)
     L, V, K = 5, 30, 4
