@@ -649,8 +649,10 @@ struct DwTreeLds {
   double lqs[64 * 64];       // this depth's log q~ rows, [state][candidate]
   double bs[DW_WMAX];        // current branches: score, state index
   int bk[DW_WMAX];
-  double cs[DW_CH];          // children (padded to a multiple of 8)
+  double cs[DW_CH];          // children, [branch][candidate rank]
   int cpk[DW_CH];
+  double ss[DW_CH];          // children of each branch in order
+  int spk[DW_CH];
   double fs[DW_SUP];         // the super-tree, S_1 .. S_L: score, parent position << 16 | rank
   int fpk[DW_SUP];
   int off[DTREE_MAX_L + 2], cnt[DTREE_MAX_L + 2];
@@ -658,36 +660,8 @@ struct DwTreeLds {
   float osc[DTREE_MAX_CAP + 1];
 };
 
-// Place of every child among the nc children by (score desc, parent position asc, rank
-// asc): the number of children before it. G lanes share a child (G = 1024 / ncp, at most
-// 8), each counting over every G-th group of 8, and combine their counts by shuffles.
-template <int G>
-DT_INLINE void dw_rank_children(DwTreeLds &Ls, int nc, int ncp, int keep, int o0) {
-  const int tid = threadIdx.x;
-  const int part = tid & (G - 1);
-  for (int t = tid / G; t < ncp; t += DW_TT / G) {
-    const double ms = Ls.cs[t];
-    const int mp = Ls.cpk[t];
-    int before = 0;
-    for (int y = 8 * part; y < ncp; y += 8 * G) {
-      double sy[8];
-      int py[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        sy[u] = Ls.cs[y + u];
-        py[u] = Ls.cpk[y + u];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) before += (sy[u] > ms) || (sy[u] == ms && py[u] < mp);
-    }
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) before += __shfl_xor(before, o, 64);
-    if (part == 0 && t < nc && before < keep) {
-      Ls.fs[o0 + before] = ms;
-      Ls.fpk[o0 + before] = mp;
-    }
-  }
-}
+// y comes before x in the order (score desc, parent position asc, rank asc)
+DT_INLINE bool dw_before(double sy, int py, double sx, int px) { return (sy > sx) | ((sy == sx) & (py < px)); }
 
 __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g, TreeOut out) {
   __shared__ DwTreeLds Ls;
@@ -724,31 +698,74 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
     }
     if (d < L) prefetch(d + 1);
     __syncthreads();
-    // score every child (b, kc) of the nb branches; pad to a multiple of 8
-    const int nc = nb * K, ncp = (nc + 7) & ~7;
-    for (int t = tid; t < ncp; t += DW_TT) {
-      if (t < nc) {
-        const int b = t / K, kc = t - b * K;
-        const double sb = Ls.bs[b];
-        const double sc = (sb + Ls.lqs[Ls.bk[b] * K + kc]) + (double)a.beta;
-        Ls.cs[t] = fmin(sc, sb);
-        Ls.cpk[t] = (b << 16) | kc;
-      } else {
-        Ls.cs[t] = -kInf;
-        Ls.cpk[t] = 0x7FFFFFFF;
-      }
+    // score every child (b, kc) of the nb branches
+    const int nc = nb * K;
+    for (int t = tid; t < nc; t += DW_TT) {
+      const int b = t / K, kc = t - b * K;
+      const double sb = Ls.bs[b];
+      const double sc = (sb + Ls.lqs[Ls.bk[b] * K + kc]) + (double)a.beta;
+      Ls.cs[t] = fmin(sc, sb);
+      Ls.cpk[t] = (b << 16) | kc;
     }
     __syncthreads();
+    // each branch's K children in order: its own place among them
+    for (int t = tid; t < nc; t += DW_TT) {
+      const int b0 = t - t % K;
+      const double ms = Ls.cs[t];
+      const int mp = Ls.cpk[t];
+      int i = 0;
+      for (int y0 = 0; y0 < K; y0 += 8) {  // eight reads in flight (clamped to the branch)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int y = b0 + min(y0 + u, K - 1);
+          i += (y0 + u < K) & dw_before(Ls.cs[y], Ls.cpk[y], ms, mp);
+        }
+      }
+      Ls.ss[b0 + i] = ms;
+      Ls.spk[b0 + i] = mp;
+    }
+    __syncthreads();
+    // place among all children = place in its branch + for every other branch the length of
+    // the prefix of that branch's ordered children that comes before it (a binary search);
+    // G lanes share a child, each over every G-th branch (eight in lockstep), and stop once
+    // their count alone reaches `keep` (the child is then not kept)
     const int keep = nc < W ? nc : W;
     const int o0 = Ls.off[d];
-    if (ncp <= DW_TT / 8)
-      dw_rank_children<8>(Ls, nc, ncp, keep, o0);
-    else if (ncp <= DW_TT / 4)
-      dw_rank_children<4>(Ls, nc, ncp, keep, o0);
-    else if (ncp <= DW_TT / 2)
-      dw_rank_children<2>(Ls, nc, ncp, keep, o0);
-    else
-      dw_rank_children<1>(Ls, nc, ncp, keep, o0);
+    {
+      const int G = nc <= DW_TT / 8 ? 8 : nc <= DW_TT / 4 ? 4 : nc <= DW_TT / 2 ? 2 : 1;
+      const int part = tid & (G - 1);
+      int kp = 1;
+      while (kp * 2 <= K) kp *= 2;
+      for (int x = tid / G; x < nc; x += DW_TT / G) {
+        const double ms = Ls.ss[x];
+        const int mp = Ls.spk[x];
+        const int b = x / K;
+        int rank = 0;
+        // eight branches searched in lockstep (independent LDS reads)
+        for (int c0 = part; c0 < nb && rank < keep; c0 += 8 * G) {
+          int lo[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) lo[i] = 0;
+          for (int step = kp; step >= 1; step >>= 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {  // unconditional clamped reads, branch-free update
+              const int b2 = c0 + i * G, j = lo[i] + step;
+              const int e = min(b2, nb - 1) * K + min(j, K) - 1;
+              const bool ok = (b2 < nb) & (b2 != b) & (j <= K) & dw_before(Ls.ss[e], Ls.spk[e], ms, mp);
+              lo[i] = ok ? j : lo[i];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) rank += lo[i];
+        }
+        for (int o = 1; o < G; o <<= 1) rank += __shfl_xor(rank, o, 64);
+        rank += x - b * K;
+        if (part == 0 && rank < keep) {
+          Ls.fs[o0 + rank] = ms;
+          Ls.fpk[o0 + rank] = mp;
+        }
+      }
+    }
     __syncthreads();
     // the kept children become the next depth's branches (state = candidate rank)
     for (int i = tid; i < keep; i += DW_TT) {
