@@ -20,7 +20,8 @@
 // both rows in units of 8 elements (16-byte buffer loads, a ring of units in flight per thread)
 // with a fixed thread->element map and a fixed reduction tree, so a quantity computed
 // twice is bit-identical. Every C pass also leaves the sums of its 64-token blocks in LDS,
-// which is all the final draw needs. A node with several children still to try after a
+// which is all the final draw needs. With one trial at T > 0 four workgroups share each
+// round (k_accept_coop, below). A node with several children still to try after a
 // rejection sorts its residual support into ratio bins once (then each further C(t) is a
 // small query); with fewer left, each rejection is one direct C pass. Two paths share the passes: with one trial per round,
 // one workgroup per round walks lazily (only the visited nodes and the tried children
@@ -260,6 +261,52 @@ struct L2Acc {
 
 // LSE2 of both rows in one pass.
 template <typename T>
+DT_INLINE void wg_lse2(const Row<T> &A, const Row<T> &B, float s, Red &red, double &la, double &lb);
+// The workgroup's part of both rows' LSE2: the largest fp32 y = z s (mx) and the sum of
+// exp2(y - mx) (sm); parts combine as M = max mx, LSE2 = M + log2(sum sm 2^(mx - M)).
+template <typename T>
+DT_INLINE void wg_lse2_part(const Row<T> &A, const Row<T> &B, float s, Red &red, float &ma, double &sa, float &mb,
+                            double &sb) {
+  L2Acc xa, xb;
+  stream2(A, B, [&](int, const float *za, const float *zb) {
+    xa.add(za, s);
+    xb.add(zb, s);
+  });
+  const float wa = wave_max(xa.m == -kInf ? -kInf : xa.mh), wb = wave_max(xb.m == -kInf ? -kInf : xb.mh);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    red.f[w] = wa;
+    red.f[AC_NW + w] = wb;
+  }
+  __syncthreads();
+  float MA = red.f[0], MB = red.f[AC_NW];
+#pragma unroll
+  for (int i = 1; i < AC_NW; ++i) {
+    MA = fmaxf(MA, red.f[i]);
+    MB = fmaxf(MB, red.f[AC_NW + i]);
+  }
+  double va = (xa.m == -kInf) ? 0.0 : xa.acc * (double)__builtin_amdgcn_exp2f(xa.mh - MA);
+  double vb = (xb.m == -kInf) ? 0.0 : xb.acc * (double)__builtin_amdgcn_exp2f(xb.mh - MB);
+  va = wave_sum(va);
+  vb = wave_sum(vb);
+  if ((threadIdx.x & 63) == 0) {
+    red.d[w] = va;
+    red.d[AC_NW + w] = vb;
+  }
+  __syncthreads();
+  double SA = 0.0, SB = 0.0;
+#pragma unroll
+  for (int i = 0; i < AC_NW; ++i) {
+    SA += red.d[i];
+    SB += red.d[AC_NW + i];
+  }
+  ma = MA;
+  mb = MB;
+  sa = SA;
+  sb = SB;
+}
+template <typename T>
 DT_INLINE void wg_lse2(const Row<T> &A, const Row<T> &B, float s, Red &red, double &la, double &lb) {
   L2Acc xa, xb;
   stream2(A, B, [&](int, const float *za, const float *zb) {
@@ -455,11 +502,23 @@ DT_INLINE void wg_sum_u64(uint64_t *v, Red &red) {
   for (int i = 0; i < N; ++i) v[i] = wave_sum_u64(lane < AC_NW ? red.u[i * AC_NW + lane] : 0ull);
 }
 
+// The exact sums of p and q over S(t) by a pass over both rows (fixed point, see fx60), and
+// the float block sums of the residual for the draw (as wg_chain_pass forms them).
+template <typename T>
+DT_INLINE void wg_c_sums(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t, float *blk,
+                         int nblk, Red &red, uint64_t &P, uint64_t &Q);
 // C(t) by a pass over both rows; also the float block sums of the residual for the draw
 // (as wg_chain_pass forms them).
 template <typename T>
 DT_INLINE double wg_c_pass(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t, float *blk,
                            int nblk, Red &red) {
+  uint64_t P, Q;
+  wg_c_sums(A, B, nt, nd, t, blk, nblk, red, P, Q);
+  return c_from(P, Q, t);
+}
+template <typename T>
+DT_INLINE void wg_c_sums(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t, float *blk,
+                         int nblk, Red &red, uint64_t &P, uint64_t &Q) {
   uint64_t v[2] = {0, 0};
   stream2(A, B, [&](int u, const float *za, const float *zb) {
     float part = 0.f;
@@ -478,7 +537,8 @@ DT_INLINE double wg_c_pass(const Row<T> &A, const Row<T> &B, const Norm &nt, con
     if ((u & 7) == 0 && (u >> 3) < nblk) blk[u >> 3] = bs;
   });
   wg_sum_u64<2>(v, red);
-  return c_from(v[0], v[1], t);
+  P = v[0];
+  Q = v[1];
 }
 
 // Ratio bins. Once a node's first rejection has fixed t0, every later t is >= t0, so S(t) is
@@ -533,6 +593,7 @@ struct Bins {
   uint32_t tbb;    // bits of t0
   int lo;          // bins below lo have been removed from (P, Q)
   uint64_t P, Q;   // sums over the members of bins >= lo
+  uint64_t Pt, Qt; // sums over S(t) for the last t asked (build or query)
 };
 
 // Sort S(t0) into the bins (two passes over the rows: counts, then placement, which also
@@ -571,8 +632,8 @@ DT_INLINE double wg_bins_build(const Row<T> &A, const Row<T> &B, const Norm &nt,
   });
   wg_sum_u64<2>(v, red);
   bn.lo = 0;
-  bn.P = uni(v[0]);
-  bn.Q = uni(v[1]);
+  bn.P = bn.Pt = uni(v[0]);
+  bn.Q = bn.Qt = uni(v[1]);
   return uni(c_from(bn.P, bn.Q, t0));
 }
 
@@ -595,7 +656,9 @@ DT_INLINE double wg_bins_query(Bins &bn, float t, Red &red) {
   bn.P = uni(bn.P - v[0]);
   bn.Q = uni(bn.Q - v[1]);
   bn.lo = uni(lo);
-  return uni(c_from(bn.P - uni(v[2]), bn.Q - uni(v[3]), t));
+  bn.Pt = uni(bn.P - uni(v[2]));
+  bn.Qt = uni(bn.Q - uni(v[3]));
+  return uni(c_from(bn.Pt, bn.Qt, t));
 }
 
 // Inclusive prefix sums (float64) of the n block sums, into pre[]; one workgroup.
@@ -911,6 +974,231 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
   }
 }
 
+// ---------------------------------------------------------------- cooperative walk (one trial, T > 0)
+// AC_NS workgroups per round, one per CU, each streaming its own contiguous range of whole
+// 64-token blocks of the two rows, so every pass takes a quarter of the time. After each
+// pass they exchange their partials through slots that are written and polled with
+// agent-scope atomic stores and loads: a slot starts at a sentinel and is written once, so
+// a reader that sees a value sees that pass's value and no fence is needed. All workgroups
+// combine the partials in the same order and so take identical decisions. C(t) is exact
+// (integer sums), so it equals the one-workgroup value; the LSE and the final draw's block
+// prefix are summed in another order, within float rounding of the one-workgroup walk.
+// Every wait is bounded: past the bound the walk records an error and finishes.
+constexpr int AC_NS = 4;          // workgroups per round
+constexpr int AC_XK = 4;          // exchanged values per workgroup and pass
+constexpr int AC_MAXPASS = 512;   // passes per round the exchange area holds
+constexpr uint64_t AC_SENT = ~0ull;
+
+struct Xch {
+  uint64_t *slot;  // [R][AC_MAXPASS][AC_NS][AC_XK], AC_SENT before the walk
+  int *err;        // set when a wait ran out or the passes overflowed
+};
+DT_INLINE void xch_put(uint64_t *p, uint64_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DT_INLINE uint64_t xch_wait(uint64_t *p, int *err) {
+  for (int it = 0;; ++it) {
+    const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v != AC_SENT) return v;
+    if (it > (1 << 22)) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return 0ull;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+DT_INLINE uint64_t dbits(double x) { return (uint64_t)__double_as_longlong(x); }
+DT_INLINE double bitsd(uint64_t x) { return __longlong_as_double((long long)x); }
+
+__global__ void k_accept_xch_init(uint64_t *slot, size_t n, int *err) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    slot[i] = AC_SENT;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
+}
+
+template <typename T>
+__global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, float2 *a_list) {
+  __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
+  __shared__ int bcnt[AC_NB], boff[AC_NB + 1];
+  __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1], sr[DTREE_MAX_CAP + 1], pv[DTREE_MAX_CAP + 1];
+  __shared__ Red red;
+  __shared__ float cz1[DTREE_MAX_CAP + 1], cz2[DTREE_MAX_CAP + 1], cu[DTREE_MAX_CAP + 1];
+  __shared__ uint64_t got[AC_NS][AC_XK];
+  extern __shared__ double dyn[];  // [nblk] prefix (double) then [nblk] block sums (float)
+  const int r = blockIdx.x / AC_NS, q = blockIdx.x - r * AC_NS;
+  const int cap = a.tree.cap;
+  const int n = clamp_nodes(a.tree.n_nodes[r], cap);
+  const size_t tb = (size_t)r * (cap + 1);
+  for (int i = threadIdx.x; i <= cap; i += AC_NT) {
+    par[i] = a.tree.parent[tb + i];
+    tok[i] = a.tree.token[tb + i];
+    dep[i] = a.tree.depth[tb + i];
+  }
+  // this workgroup's blocks [b0, b1) and elements [e0, e1)
+  const int nblk_all = (a.V + AC_BLK - 1) / AC_BLK;
+  const int b0 = (int)((long long)nblk_all * q / AC_NS), b1 = (int)((long long)nblk_all * (q + 1) / AC_NS);
+  const int e0 = b0 * AC_BLK, len = max(0, min(a.V, b1 * AC_BLK) - e0);
+  const int nblk = b1 - b0;
+  double *pre = dyn;
+  float *blk = reinterpret_cast<float *>(dyn + nblk_all);
+  int pass = 0;
+  bool bad = false;
+  // publish k values, then gather every workgroup's k values into got[][] (all threads)
+  auto exchange = [&](const uint64_t *v, int k) {
+    uint64_t *S = x.slot + ((size_t)r * AC_MAXPASS + (size_t)min(pass, AC_MAXPASS - 1)) * (AC_NS * AC_XK);
+    if (pass >= AC_MAXPASS) bad = true;
+    __syncthreads();
+    // lanes 0 .. AC_NS * AC_XK - 1 of the first wave: each publishes (its own workgroup's
+    // slots) and polls one slot, all at once
+    if (threadIdx.x < AC_NS * AC_XK) {
+      const int w = threadIdx.x / AC_XK, i = threadIdx.x % AC_XK;
+      if (i < k) {
+        if (w == q) xch_put(S + q * AC_XK + i, i == 0 ? v[0] : i == 1 ? v[k > 1 ? 1 : 0] : i == 2 ? v[k > 2 ? 2 : 0] : v[k > 3 ? 3 : 0]);
+        got[w][i] = xch_wait(S + w * AC_XK + i, x.err);
+      }
+    }
+    __syncthreads();
+    ++pass;
+  };
+  const T *target = static_cast<const T *>(a.target) + (size_t)r * (cap + 1) * a.V;
+  const T *draft = static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V;
+  const float s = log2_scale(a.T);
+  const uint64_t trial = a.trial0;
+  uint32_t step = 0;
+  int j = 0, out_tok = -1;
+  bool lists = false;
+  // each workgroup bins the residual support of its own range (its own list slice); the
+  // exchanged partials are the sums over S(t), exact, so the totals do not depend on it
+  Bins bn;
+  bn.cnt = bcnt;
+  bn.off = boff;
+  bn.list = a_list + (size_t)r * a.V + e0;
+  for (;;) {
+    const T *zt = target + (size_t)j * a.V;
+    const T *zd = draft + (size_t)draft_row(j == 0 ? a.tree.depth[tb] : dep[j], a.L) * a.V;
+    const Row<T> A = make_row(zt + e0, len), B = make_row(zd + e0, len);
+    double la, lb;
+    {
+      float ma, mb;
+      double sa, sb;
+      wg_lse2_part(A, B, s, red, ma, sa, mb, sb);
+      const uint64_t v[4] = {(uint64_t)__float_as_uint(ma), dbits(sa), (uint64_t)__float_as_uint(mb), dbits(sb)};
+      exchange(v, 4);
+      float MA = -kInf, MB = -kInf;
+      for (int w = 0; w < AC_NS; ++w) {
+        MA = fmaxf(MA, __uint_as_float((uint32_t)got[w][0]));
+        MB = fmaxf(MB, __uint_as_float((uint32_t)got[w][2]));
+      }
+      double SA = 0.0, SB = 0.0;
+      for (int w = 0; w < AC_NS; ++w) {
+        const float mw = __uint_as_float((uint32_t)got[w][0]), mv = __uint_as_float((uint32_t)got[w][2]);
+        if (mw != -kInf) SA += bitsd(got[w][1]) * (double)__builtin_amdgcn_exp2f(mw - MA);
+        if (mv != -kInf) SB += bitsd(got[w][3]) * (double)__builtin_amdgcn_exp2f(mv - MB);
+      }
+      la = (double)MA + log2(SA);
+      lb = (double)MB + log2(SB);
+    }
+    if (!lists) {
+      build_children(par, tok, n, a.V, fc, ns, sr, pv);
+      lists = true;
+    }
+    for (int i = threadIdx.x; i <= n; i += AC_NT)
+      if (pv[i] == j) {
+        cz1[i] = load_elt(zt, (size_t)tok[i]);
+        cz2[i] = load_elt(zd, (size_t)tok[i]);
+        cu[i] = philox_uniform(a.seed, trial, (uint32_t)r, step + (uint32_t)sr[i]);
+      }
+    __syncthreads();
+    const Norm nt = make_norm(s, la), nd = make_norm(s, lb);
+    float t = 0.f;
+    double C = 1.0;
+    bool built = false, blk_at_t = false;
+    int nxt = -1;
+    for (int c = fc[j]; c >= 0; c = ns[c]) {
+      const float qv = prob(cz2[c], nd);
+      const float pc = resid(prob(cz1[c], nt), qv, t) / (float)C;
+      ++step;
+      if (cu[c] * qv < pc) {
+        nxt = c;
+        break;
+      }
+      const float t2 = t + (float)C;
+      int left = 0;
+      for (int k = ns[c]; k >= 0 && left < AC_BINS_MIN; k = ns[k]) ++left;
+      uint64_t v[2];
+      if (built) {
+        (void)wg_bins_query(bn, t2, red);
+        v[0] = bn.Pt;
+        v[1] = bn.Qt;
+      } else if (left >= AC_BINS_MIN) {
+        (void)wg_bins_build(A, B, nt, nd, t2, bn, red);
+        built = true;
+        v[0] = bn.Pt;
+        v[1] = bn.Qt;
+      } else {
+        wg_c_sums(A, B, nt, nd, t2, blk, nblk, red, v[0], v[1]);
+      }
+      const bool direct = !built;
+      exchange(v, 2);
+      uint64_t P = 0, Q = 0;
+      for (int w = 0; w < AC_NS; ++w) {
+        P += got[w][0];
+        Q += got[w][1];
+      }
+      const double C2 = c_from(P, Q, t2);
+      blk_at_t = direct && C2 > 0.0;
+      if (C2 > 0.0) {
+        t = t2;
+        C = C2;
+      }
+    }
+    if (nxt >= 0) {
+      j = nxt;
+      continue;
+    }
+    if (!blk_at_t) (void)wg_chain_pass(A, B, nt, nd, t, blk, nblk, red);
+    __syncthreads();
+    // the draw: every workgroup's block total, then the owner of the target mass samples
+    // inside its own blocks and sends the token
+    if (nblk > 0) wg_prefix(blk, pre, nblk, red);
+    const double tot_q = nblk > 0 ? pre[nblk - 1] : 0.0;
+    {
+      const uint64_t v[1] = {dbits(tot_q)};
+      exchange(v, 1);
+    }
+    double off[AC_NS + 1];
+    off[0] = 0.0;
+    for (int w = 0; w < AC_NS; ++w) off[w + 1] = off[w] + bitsd(got[w][0]);
+    const float u = philox_uniform(a.seed, trial, (uint32_t)r, step++);
+    const double target_mass = (double)u * off[AC_NS];
+    int owner = -1, last = 0;
+    for (int w = 0; w < AC_NS; ++w) {
+      if (bitsd(got[w][0]) > 0.0) last = w;
+      if (owner < 0 && target_mass < off[w + 1]) owner = w;
+    }
+    if (owner < 0) owner = last;
+    uint64_t mine = AC_SENT - 1;
+    if (q == owner && nblk > 0) {
+      const double tl = target_mass - off[q];
+      const int b = find_block(pre, nblk, tl);
+      mine = (uint64_t)(uint32_t)(e0 + sample_in_block_wave(zt + e0, zd + e0, len, nt, nd, t, pre, b, tl));
+    }
+    {
+      const uint64_t v[1] = {mine};
+      exchange(v, 1);
+    }
+    out_tok = (int)(uint32_t)got[owner][0];
+    break;
+  }
+  if (q == 0) {
+    const bool err = bad || __hip_atomic_load(x.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    for (int i = threadIdx.x; i < a.n_trials; i += AC_NT) {
+      const size_t o = (size_t)i * a.R + r;
+      a.accept_len[o] = err ? -1 : dep[j];
+      a.accept_node[o] = err ? -1 : j;
+      a.next_token[o] = err ? -1 : out_tok;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- tables for many trials
 struct AccTables {
   float *qc, *pc;                      // [R][cap+1], indexed by the child's slot
@@ -1081,13 +1369,16 @@ static AccTables carve_tables(void *ws, int R, int V, int cap) {
   return t;
 }
 
+static size_t xch_slots(int R) { return (size_t)R * AC_MAXPASS * AC_NS * AC_XK; }
+
 size_t accept_ws_bytes(int R, int L, int V, int cap) {
   (void)L;
   const size_t slots = (size_t)R * (cap + 1);
   const int nblk = (V + AC_BLK - 1) / AC_BLK;
   const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
   const size_t lists = (size_t)R * V * sizeof(float2);  // the lazy walk's binned supports
-  return tables > lists ? tables : lists;
+  // then the cooperative walk's exchange slots and error flag
+  return align256(tables > lists ? tables : lists) + align256(xch_slots(R) * sizeof(uint64_t)) + 256;
 }
 
 size_t accept_lds_bytes(int V) {
@@ -1099,6 +1390,31 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
   const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
   if (a.T == 0.f || a.n_trials == 1) {
     const size_t shm = accept_lds_bytes(a.V);
+    if (a.T > 0.f && !a.match) {
+      // residual walk with one trial: AC_NS workgroups per round when the whole grid fits on
+      // the device at once (a cooperative launch checks that), else one workgroup per round
+      const size_t slots = (size_t)a.R * (a.tree.cap + 1);
+      const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
+      const size_t lists = (size_t)a.R * a.V * sizeof(float2);
+      char *w = static_cast<char *>(ws) + align256(tables > lists ? tables : lists);
+      Xch x;
+      x.slot = reinterpret_cast<uint64_t *>(w);
+      x.err = reinterpret_cast<int *>(w + align256(xch_slots(a.R) * sizeof(uint64_t)));
+      hipLaunchKernelGGL(k_accept_xch_init, dim3(256), dim3(256), 0, st, x.slot, xch_slots(a.R), x.err);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      AcceptArgs ac = a;
+      float2 *lists_p = static_cast<float2 *>(ws);
+      void *args[3] = {&ac, &x, &lists_p};
+      const dim3 grid((unsigned)(a.R * AC_NS)), block(AC_NT);
+      e = a.dtype == DTREE_BF16
+              ? hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_accept_coop<uint16_t>), grid, block, args,
+                                           (unsigned)shm, st)
+              : hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_accept_coop<float>), grid, block, args,
+                                           (unsigned)shm, st);
+      if (e == hipSuccess) return hipSuccess;
+      (void)hipGetLastError();  // too large for one wave of workgroups: the one-workgroup walk
+    }
     if (a.dtype == DTREE_BF16)
       hipLaunchKernelGGL(k_accept_lazy<uint16_t>, dim3(a.R), dim3(AC_NT), shm, st, a, static_cast<float2 *>(ws));
     else
