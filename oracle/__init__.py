@@ -14,7 +14,8 @@ Pages cited by title and section:
   DDTree.
 * "TALON: Confidence-Aware Speculative Decoding with Adaptive Token Trees"
   (papernotes, NeurIPS 2026): key designs 1-2 (root Top-K, gating against the
-  per-depth anchor m_d, global budget N).
+  per-depth anchor m_d, global budget N), and its research background (the static
+  D x K grid expansion it compares against).
 * Course notes "Sampling, speculative decoding and multi-token prediction"
   (unit 11): the accept / residual rule, the three-token worked example, the
   degenerate cases, the bonus token and the per-round yield.
@@ -22,6 +23,6 @@ Pages cited by title and section:
   restriction, the heap over rank descriptors, the debugging checklist.
 
 Modules: ``rowsweep`` (log-softmax + top-K), ``marginal`` (DDTree Top-B), ``depthwise`` (DARTree Algorithm 1),
-``gated`` (TALON), ``treeout`` (parent array and mask), ``accept`` (greedy and
+``gated`` (TALON), ``static`` (the static D x K grid), ``treeout`` (parent array and mask), ``accept`` (greedy and
 residual acceptance walks), ``philox`` (Philox4x32-10).
 """
