@@ -8,6 +8,8 @@ One step = one pass of the whole hot path over a batch of R = 64 rounds
   3. build_tree_gated      TALON-shape logits, K_root = 10, mu = 0.03, N = 60
   4. accept_tree T = 0     the step's marginal trees against draft-correlated target logits
   5. accept_tree T = 1     same, one Philox-seeded trial per round (trial index = step)
+Timed outside the step and reported under extra_ms: the matching walk, DARTree's exact
+(W = B) and fixed (W = B / L) widths, and the static D x K grid (K = 10, D = 6).
 value = rounds per second of that whole step (R / step time). Inputs are resident in
 HBM before timing. Prints one JSON line.
 
@@ -205,6 +207,24 @@ def main():
         torch.cuda.synchronize()
         extra_ms["depthwise_" + name] = round(float(np.mean([ew[i].elapsed_time(ew[i + 1]) for i in range(5)])), 4)
         mass[name] = round(covered(t_w, 0.0), 4)
+
+    # ---- outside the step: the static D x K grid, K = 10, D = 6 (60 nodes, TALON's budget N),
+    # on the TALON-shape logits: the fixed-shape builder of TALON's tree-build comparison,
+    # next to the step's gated tree (its time is breakdown_ms["gated"])
+    t_s = dt.Tree.empty(R, 60, dev)
+    ws_s = torch.empty(dt.workspace_size(dt.OP_STATIC, R, L, V, 10), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        dt.build_tree_static(talon, 10, 6, ws=ws_s, out=t_s)
+    torch.cuda.synchronize()
+    es = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    es[0].record(stream)
+    for i in range(5):
+        dt.build_tree_static(talon, 10, 6, ws=ws_s, out=t_s)
+        es[i + 1].record(stream)
+    torch.cuda.synchronize()
+    extra_ms["static_k10_d6"] = round(float(np.mean([es[i].elapsed_time(es[i + 1]) for i in range(5)])), 4)
+    mass["talon_gated_n60"] = round(covered(t_g, 0.0), 4)
+    mass["static_k10_d6"] = round(covered(t_s, 0.0), 4)
 
     out = {
         "metric": "tree-build rounds/sec + us/round at V=151936,L=16,B=128; HBM GB/s vs peak",

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     build_tree_marginal(logits, K, B, beta)             -> Tree
     build_tree_depthwise(logits, E, U, P, root_tok, K, W, B, beta) -> Tree
     build_tree_gated(logits, K_root, mu, N)             -> Tree
+    build_tree_static(logits, K, D)                     -> Tree  (K*D nodes)
     accept_tree(tree, target, draft, temperature, seed, trial0, n_trials)
         -> (accept_len, accept_node, next_token), each [n_trials, R]
     accept_tree_match(tree, target, temperature, seed, trial0, n_trials)   (same outputs)
@@ -27,13 +28,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdtree.so")
 
 DTREE_BF16, DTREE_F32 = 0, 1
-OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT = range(5)
+OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT, OP_STATIC = range(6)
 STATUS = {0: "DTREE_OK", -1: "DTREE_E_INVAL", -2: "DTREE_E_BETA", -3: "DTREE_E_WORKSPACE",
           -4: "DTREE_E_UNSUPPORTED", -5: "DTREE_E_HIP"}
 
 # every symbol include/dtree.h declares
 SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_depthwise",
-           "build_tree_gated", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
+           "build_tree_gated", "build_tree_static", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
 
 
 class DTreeError(RuntimeError):
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(CTree), vp, sz, vp]
     L.build_tree_gated.restype = i32
     L.build_tree_gated.argtypes = [vp, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(CTree), vp, sz, vp]
+    L.build_tree_static.restype = i32
+    L.build_tree_static.argtypes = [vp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(CTree), vp, sz, vp]
     L.accept_tree.restype = i32
     L.accept_tree.argtypes = [ctypes.POINTER(CTree), vp, vp, i32, i32, i32, i32, f32, u64, u64, i32, vp, vp, vp,
                               vp, sz, vp]
@@ -207,6 +210,20 @@ def build_tree_gated(logits: torch.Tensor, K_root: int, mu: float, N: int, ws: t
     st = out.c_struct()
     _check(lib().build_tree_gated(_ptr(logits), _dtype(logits), R, L, V, K_root, float(mu), N, ctypes.byref(st),
                                   _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def build_tree_static(logits: torch.Tensor, K: int, D: int, ws: torch.Tensor | None = None,
+                      out: Tree | None = None) -> Tree:
+    """Static D x K grid: K nodes per depth to depth D (cap = K*D)."""
+    _require_device(logits)
+    R, L, V = logits.shape
+    dev = logits.device
+    out = Tree.empty(R, K * D, dev) if out is None else out
+    ws = _workspace(workspace_size(OP_STATIC, R, L, V, K), dev) if ws is None else ws
+    st = out.c_struct()
+    _check(lib().build_tree_static(_ptr(logits), _dtype(logits), R, L, V, K, D, ctypes.byref(st), _ptr(ws),
+                                   ws.numel(), _stream(dev)))
     return out
 
 

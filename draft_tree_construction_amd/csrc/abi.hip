@@ -98,6 +98,9 @@ size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int 
     case DTREE_OP_DEPTHWISE:
       if (K < 1 || W < 1 || B_or_N < 1 || d_model < 1) return 0;
       return a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B_or_N, rank, d_model);
+    case DTREE_OP_STATIC:
+      if (K < 1) return 0;
+      return a1_bytes(R * L, V, K);
     case DTREE_OP_ACCEPT:
       if (B_or_N < 1) return 0;
       return dt::accept_ws_bytes(R, L, V, B_or_N);
@@ -172,6 +175,30 @@ int build_tree_gated(const void *logits, int dtype, int R, int L, int V, int K_r
   if (e != hipSuccess) return hip_fail(e, "build_tree_gated (row sweep)");
   e = dt::launch_gated(a.zk, a.ids, a.lse, R, L, k, K_root, log((double)mu), N, tree_out(out), st);
   if (e != hipSuccess) return hip_fail(e, "build_tree_gated (gate)");
+  return DTREE_OK;
+}
+
+int build_tree_static(const void *logits, int dtype, int R, int L, int V, int K, int D, const dtree_tree *out, void *ws,
+                      size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || K < 1 || K > V || D < 1 || D > L)
+    return fail(DTREE_E_INVAL, "need R >= 0, L, V >= 1, 1 <= K <= V, 1 <= D <= L");
+  if (K > DTREE_MAX_K || K * D > DTREE_MAX_CAP || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "K, K*D or L beyond the compiled envelope");
+  int rc = check_tree(out, K * D);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits) return fail(DTREE_E_INVAL, "logits is NULL");
+  const size_t need = a1_bytes(R * L, V, K);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(s);
+  A1Ws a = a1_carve(ws, R * L, K);
+  dt::RowOut o{a.lse, nullptr, a.ids, a.zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, K, o, a.rest, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_static (row sweep)");
+  e = dt::launch_static(a.zk, a.ids, a.lse, R, L, K, K, D, tree_out(out), st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_static (grid)");
   return DTREE_OK;
 }
 

@@ -40,6 +40,10 @@ hipError_t launch_marginal(const float *zk, const int32_t *ids, const double *ls
 hipError_t launch_gated(const float *zk, const int32_t *ids, const double *lse, int R, int L, int K,
                         int K_root, double ln_mu, int N, const TreeOut &out, hipStream_t st);
 
+// ---- static D x K grid expansion (the fixed-shape baseline of TALON's comparison) ---------------
+hipError_t launch_static(const float *zk, const int32_t *ids, const double *lse, int R, int L, int Kc, int K, int D,
+                         const TreeOut &out, hipStream_t st);
+
 // ---- a3 + a4 + a6: DARTree depth-wise ---------------------------------------------------------
 struct DepthwiseArgs {
   const void *base;  // [R][L][V]

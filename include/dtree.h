@@ -73,7 +73,8 @@ enum dtree_op {
   DTREE_OP_MARGINAL = 1,
   DTREE_OP_DEPTHWISE = 2,
   DTREE_OP_GATED = 3,
-  DTREE_OP_ACCEPT = 4
+  DTREE_OP_ACCEPT = 4,
+  DTREE_OP_STATIC = 5
 };
 
 /* Compiled envelope (DTREE_E_UNSUPPORTED beyond it). */
@@ -95,7 +96,7 @@ typedef struct {
 /*
  * Bytes of workspace an operation needs. `op` is a dtree_op; unused size arguments are
  * ignored: TOPK(rows = R*L, V, K), MARGINAL(R, L, V, K, B), DEPTHWISE(R, L, V, K, B, W,
- * rank, d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap). Returns 0
+ * rank, d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap), STATIC(R, L, V, K). Returns 0
  * for an unknown op or invalid sizes.
  */
 size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank, int d_model);
@@ -149,6 +150,19 @@ int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, con
  */
 int build_tree_gated(const void *logits, int dtype, int R, int L, int V, int K_root, float mu, int N,
                      const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * Static D x K grid expansion (TALON research background: the fixed-shape tree of Eagle-3,
+ * the baseline of TALON's tree-build comparison): depth 1 holds the top K tokens of
+ * position 1; each further depth keeps the best K of the K x K grid (each kept node of the
+ * depth above times its position's top K tokens) by path log-probability, ties broken by
+ * the parent's slot, then the token's rank (logit descending, id ascending). The tree is
+ * every kept node: n_nodes = K*D, depth d in slots 1 + (d-1)K .. dK, each depth in score
+ * order. Rows of all L positions are swept; positions >= D are not used.
+ * Needs 1 <= K <= min(V, DTREE_MAX_K), 1 <= D <= L, K*D <= DTREE_MAX_CAP, out->cap == K*D.
+ */
+int build_tree_static(const void *logits, int dtype, int R, int L, int V, int K, int D,
+                      const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
 
 /*
  * Tree verification walk (DARTree background "speculative sampling"; course notes unit 11).

@@ -100,6 +100,24 @@ def test_gated_validation():
     assert call() == -3
 
 
+def test_static_validation():
+    L = dt.lib()
+    def call(K=10, D=6, Lp=16, V=151936, cap_t=None):
+        ct = tree(K * D) if cap_t is None else cap_t
+        return L.build_tree_static(FAKE, 0, 4, Lp, V, K, D, ctypes.byref(ct), FAKE, 0, None)
+    assert call(K=0) == -1
+    assert call(D=0) == -1
+    assert call(D=17) == -1
+    assert call(K=20, V=10) == -1
+    assert call(K=65, D=1) == -4
+    assert call(K=16, D=9) == -4
+    assert call(cap_t=tree(59)) == -1
+    assert call() == -3
+    assert dt.workspace_size(dt.OP_STATIC, 4, 16, 151936, 10) >= dt.workspace_size(dt.OP_TOPK, 64, 1, 151936, 10)
+    assert dt.workspace_size(dt.OP_STATIC, 4, 16, 151936, 0) == 0
+    assert L.build_tree_static(None, 0, 0, 16, 100, 10, 6, ctypes.byref(tree(60)), None, 0, None) == 0
+
+
 def test_depthwise_validation():
     L = dt.lib()
     def call(rank=64, dm=1024, K=8, W=32, B=128, beta=-0.5, cap=128, E=FAKE):
