@@ -19,10 +19,13 @@ Pages cited by title and section:
 * Course notes "Sampling, speculative decoding and multi-token prediction"
   (unit 11): the accept / residual rule, the three-token worked example, the
   degenerate cases, the bonus token and the per-round yield.
+* "GRAFT: adaptive DLM draft-tree construction with target-distilled edge scoring"
+  (paper page): method sections on target-distilled edge scoring (the edge MLP),
+  inference (best-first by summed edge scores) and state-aware budget allocation.
 * "DDTree: from theory to practice" (CSDN blog): Top-B prefixes, the S_K
   restriction, the heap over rank descriptors, the debugging checklist.
 
 Modules: ``rowsweep`` (log-softmax + top-K), ``marginal`` (DDTree Top-B), ``depthwise`` (DARTree Algorithm 1),
-``gated`` (TALON), ``static`` (the static D x K grid), ``treeout`` (parent array and mask), ``accept`` (greedy and
+``gated`` (TALON), ``static`` (the static D x K grid), ``tdes`` (GRAFT edge scores, best-first, budget), ``treeout`` (parent array and mask), ``accept`` (greedy and
 residual acceptance walks), ``philox`` (Philox4x32-10).
 """
