@@ -9,7 +9,8 @@ One step = one pass of the whole hot path over a batch of R = 64 rounds
   4. accept_tree T = 0     the step's marginal trees against draft-correlated target logits
   5. accept_tree T = 1     same, one Philox-seeded trial per round (trial index = step)
 Timed outside the step and reported under extra_ms: the matching walk, DARTree's exact
-(W = B) and fixed (W = B / L) widths, and the static D x K grid (K = 10, D = 6).
+(W = B) and fixed (W = B / L) widths, the static D x K grid (K = 10, D = 6) and GRAFT's
+edge-scored best-first tree (K = 32, B = 128).
 value = rounds per second of that whole step (R / step time). Inputs are resident in
 HBM before timing. Prints one JSON line.
 
@@ -225,6 +226,26 @@ def main():
     extra_ms["static_k10_d6"] = round(float(np.mean([es[i].elapsed_time(es[i + 1]) for i in range(5)])), 4)
     mass["talon_gated_n60"] = round(covered(t_g, 0.0), 4)
     mass["static_k10_d6"] = round(covered(t_s, 0.0), 4)
+
+    # ---- outside the step: GRAFT's edge-scored best-first tree on the DDTree-shape logits,
+    # K = 32 candidates per position, B = 128, random-init edge MLP (hp = hc = 64, hd = 16,
+    # H = 128)
+    prm, root_g = synth.edge_mlp(seed=6)
+    mlp = {k: torch.from_numpy(prm[k]).to(dev) for k in ("Gp", "Gc", "Ed", "W", "b", "w")}
+    mlp["b0"], mlp["s"] = prm["b0"], prm["s"]
+    root_g = torch.from_numpy(root_g).to(dev)
+    t_t = dt.Tree.empty(R, 128, dev)
+    ws_e = torch.empty(dt.workspace_size(dt.OP_TDES, R, L, V, 32), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        dt.build_tree_tdes(draft, root_g, mlp, 32, 128, ws=ws_e, out=t_t)
+    torch.cuda.synchronize()
+    es = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    es[0].record(stream)
+    for i in range(5):
+        dt.build_tree_tdes(draft, root_g, mlp, 32, 128, ws=ws_e, out=t_t)
+        es[i + 1].record(stream)
+    torch.cuda.synchronize()
+    extra_ms["tdes_k32_b128"] = round(float(np.mean([es[i].elapsed_time(es[i + 1]) for i in range(5)])), 4)
 
     out = {
         "metric": "tree-build rounds/sec + us/round at V=151936,L=16,B=128; HBM GB/s vs peak",

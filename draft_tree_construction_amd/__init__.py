@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
     build_tree_depthwise(logits, E, U, P, root_tok, K, W, B, beta) -> Tree
     build_tree_gated(logits, K_root, mu, N)             -> Tree
     build_tree_static(logits, K, D)                     -> Tree  (K*D nodes)
+    build_tree_tdes(logits, root_tok, mlp, K, B, budget=None) -> Tree
+    saba_budget(a, beta, c_verify, c_fixed, B_max)      -> int   (host only)
     accept_tree(tree, target, draft, temperature, seed, trial0, n_trials)
         -> (accept_len, accept_node, next_token), each [n_trials, R]
     accept_tree_match(tree, target, temperature, seed, trial0, n_trials)   (same outputs)
@@ -28,13 +30,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdtree.so")
 
 DTREE_BF16, DTREE_F32 = 0, 1
-OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT, OP_STATIC = range(6)
+OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT, OP_STATIC, OP_TDES = range(7)
 STATUS = {0: "DTREE_OK", -1: "DTREE_E_INVAL", -2: "DTREE_E_BETA", -3: "DTREE_E_WORKSPACE",
           -4: "DTREE_E_UNSUPPORTED", -5: "DTREE_E_HIP"}
 
 # every symbol include/dtree.h declares
 SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_depthwise",
-           "build_tree_gated", "build_tree_static", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
+           "build_tree_gated", "build_tree_static", "build_tree_tdes", "dtree_saba_budget", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
 
 
 class DTreeError(RuntimeError):
@@ -75,6 +77,11 @@ def lib() -> ctypes.CDLL:
     L.build_tree_gated.argtypes = [vp, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(CTree), vp, sz, vp]
     L.build_tree_static.restype = i32
     L.build_tree_static.argtypes = [vp, i32, i32, i32, i32, i32, i32, ctypes.POINTER(CTree), vp, sz, vp]
+    L.build_tree_tdes.restype = i32
+    L.build_tree_tdes.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, f32, i32, i32, i32, i32,
+                                  i32, i32, vp, ctypes.POINTER(CTree), vp, sz, vp]
+    L.dtree_saba_budget.restype = i32
+    L.dtree_saba_budget.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double, i32]
     L.accept_tree.restype = i32
     L.accept_tree.argtypes = [ctypes.POINTER(CTree), vp, vp, i32, i32, i32, i32, f32, u64, u64, i32, vp, vp, vp,
                               vp, sz, vp]
@@ -225,6 +232,39 @@ def build_tree_static(logits: torch.Tensor, K: int, D: int, ws: torch.Tensor | N
     _check(lib().build_tree_static(_ptr(logits), _dtype(logits), R, L, V, K, D, ctypes.byref(st), _ptr(ws),
                                    ws.numel(), _stream(dev)))
     return out
+
+
+def build_tree_tdes(logits: torch.Tensor, root_tok: torch.Tensor, mlp: dict, K: int, B: int,
+                    budget: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                    out: Tree | None = None) -> Tree:
+    """GRAFT edge-scored best-first tree. mlp: float32 device tensors Gp [V, hp], Gc [V, hc],
+    Ed [L, hd], W [H, hp+hc+hd], b [H], w [H] and floats b0, s. budget: int32 [R] or None."""
+    names = ("Gp", "Gc", "Ed", "W", "b", "w")
+    _require_device(logits, root_tok, *(mlp[k] for k in names))
+    for k in names:
+        if mlp[k].dtype != torch.float32 or not mlp[k].is_contiguous():
+            raise TypeError(f"{k} must be a contiguous float32 tensor")
+    if root_tok.dtype != torch.int32 or (budget is not None and budget.dtype != torch.int32):
+        raise TypeError("root_tok and budget must be int32")
+    R, L, V = logits.shape
+    hp, hc, hd = mlp["Gp"].shape[1], mlp["Gc"].shape[1], mlp["Ed"].shape[1]
+    H = mlp["W"].shape[0]
+    dev = logits.device
+    out = Tree.empty(R, B, dev) if out is None else out
+    ws = _workspace(workspace_size(OP_TDES, R, L, V, K), dev) if ws is None else ws
+    st = out.c_struct()
+    _check(lib().build_tree_tdes(_ptr(logits), _dtype(logits), R, L, V, _ptr(root_tok), *(_ptr(mlp[k]) for k in names),
+                                 float(mlp["b0"]), float(mlp["s"]), hp, hc, hd, H, K, B,
+                                 None if budget is None else _ptr(budget), ctypes.byref(st), _ptr(ws), ws.numel(),
+                                 _stream(dev)))
+    return out
+
+
+def saba_budget(a: float, beta: float, c_verify: float, c_fixed: float, B_max: int) -> int:
+    """GRAFT's budget: argmax over B in [1, B_max] of a B^beta / (B c_verify + c_fixed) (host)."""
+    rc = lib().dtree_saba_budget(float(a), float(beta), float(c_verify), float(c_fixed), int(B_max))
+    _check(rc if rc < 0 else 0)
+    return rc
 
 
 def accept_tree(tree: Tree, target: torch.Tensor, draft: torch.Tensor | None, temperature: float, seed: int,

@@ -62,6 +62,11 @@ dt::TreeOut tree_out(const dtree_tree *t) {
 }
 
 int marginal_k(int K, int B, int V) { return K == 0 ? (B < V ? B : V) : K; }
+size_t tdes_table_bytes(int R, int L, int K) {
+  const size_t n = (size_t)R * L * K * K;
+  return dt::align256(n * sizeof(float)) + dt::align256(n);
+}
+
 int gated_k(int V) { return V < DTREE_MAX_K ? V : DTREE_MAX_K; }
 
 }  // namespace
@@ -101,6 +106,9 @@ size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int 
     case DTREE_OP_STATIC:
       if (K < 1) return 0;
       return a1_bytes(R * L, V, K);
+    case DTREE_OP_TDES:
+      if (K < 1) return 0;
+      return a1_bytes(R * L, V, K) + tdes_table_bytes(R, L, K);
     case DTREE_OP_ACCEPT:
       if (B_or_N < 1) return 0;
       return dt::accept_ws_bytes(R, L, V, B_or_N);
@@ -200,6 +208,54 @@ int build_tree_static(const void *logits, int dtype, int R, int L, int V, int K,
   e = dt::launch_static(a.zk, a.ids, a.lse, R, L, K, K, D, tree_out(out), st);
   if (e != hipSuccess) return hip_fail(e, "build_tree_static (grid)");
   return DTREE_OK;
+}
+
+int build_tree_tdes(const void *logits, int dtype, int R, int L, int V, const int32_t *root_tok, const float *Gp,
+                    const float *Gc, const float *Ed, const float *W, const float *b, const float *w, float b0, float s,
+                    int hp, int hc, int hd, int H, int K, int B, const int32_t *budget, const dtree_tree *out,
+                    void *ws, size_t ws_bytes, dtree_stream_t st_) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || K < 1 || K > V || B < 0 || hp < 1 || hc < 1 || hd < 1 || H < 1)
+    return fail(DTREE_E_INVAL, "need R >= 0, L, V, hp, hc, hd, H >= 1, 1 <= K <= V, B >= 0");
+  if (!isfinite(b0) || !isfinite(s) || !(s > 0.f)) return fail(DTREE_E_INVAL, "need finite b0 and s > 0");
+  if (K > DTREE_MAX_K || B > DTREE_MAX_CAP || L > DTREE_MAX_L || hp > 64 || hc > 64 || hd > 64 || H > 128 ||
+      (hp | hc | hd) & 3)
+    return fail(DTREE_E_UNSUPPORTED, "K, B, L, hp, hc, hd or H beyond the compiled envelope");
+  int rc = check_tree(out, B);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits || !root_tok || !Gp || !Gc || !Ed || !W || !b || !w)
+    return fail(DTREE_E_INVAL, "an input pointer is NULL");
+  if (((uintptr_t)Gp | (uintptr_t)Gc | (uintptr_t)W) & 15) return fail(DTREE_E_INVAL, "Gp, Gc and W must be 16-byte aligned");
+  const size_t need = a1_bytes(R * L, V, K) + tdes_table_bytes(R, L, K);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(st_);
+  A1Ws a = a1_carve(ws, R * L, K);
+  dt::RowOut o{a.lse, nullptr, a.ids, a.zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, K, o, a.rest, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_tdes (row sweep)");
+  char *tw = static_cast<char *>(ws) + a1_bytes(R * L, V, K);
+  float *TS = reinterpret_cast<float *>(tw);
+  uint8_t *TO = reinterpret_cast<uint8_t *>(tw + dt::align256((size_t)R * L * K * K * sizeof(float)));
+  dt::TdesParams p{Gp, Gc, Ed, W, b, w, b0, s, hp, hc, hd, H};
+  e = dt::launch_tdes(a.zk, a.ids, a.lse, root_tok, p, R, L, V, K, B, budget, TS, TO, tree_out(out), st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_tdes");
+  return DTREE_OK;
+}
+
+int dtree_saba_budget(double a, double beta, double c_verify, double c_fixed, int B_max) {
+  if (!(a > 0.0) || !(beta > 0.0 && beta < 1.0) || !(c_verify > 0.0) || !(c_fixed >= 0.0) || B_max < 1 ||
+      !isfinite(a) || !isfinite(c_verify) || !isfinite(c_fixed))
+    return fail(DTREE_E_INVAL, "need a > 0, 0 < beta < 1, c_verify > 0, c_fixed >= 0, B_max >= 1");
+  // G/C = a B^beta / (B c_verify + c_fixed) rises up to B* = beta c_fixed / ((1 - beta) c_verify)
+  // and falls after it, so the integer maximiser is floor(B*) or ceil(B*) within [1, B_max]
+  double bs = beta * c_fixed / ((1.0 - beta) * c_verify);
+  if (!(bs <= (double)B_max)) bs = (double)B_max;
+  if (bs < 1.0) bs = 1.0;
+  const int lo = (int)floor(bs), hi = (int)ceil(bs);
+  auto u = [&](int B) { return a * pow((double)B, beta) / ((double)B * c_verify + c_fixed); };
+  return u(hi) > u(lo) ? hi : lo;
 }
 
 int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, const uint16_t *E, const uint16_t *U,

@@ -44,6 +44,17 @@ hipError_t launch_gated(const float *zk, const int32_t *ids, const double *lse, 
 hipError_t launch_static(const float *zk, const int32_t *ids, const double *lse, int R, int L, int Kc, int K, int D,
                          const TreeOut &out, hipStream_t st);
 
+// ---- GRAFT edge scores + best-first tree ----------------------------------------------------
+struct TdesParams {
+  const float *Gp, *Gc, *Ed, *W, *b, *w;  // [V][hp], [V][hc], [L][hd], [H][hp+hc+hd], [H], [H]
+  float b0, s;
+  int hp, hc, hd, H;
+};
+// Edge tables: TS [R*L][K][K] float (each parent row sorted), TO [R*L][K][K] child index.
+hipError_t launch_tdes(const float *zk, const int32_t *ids, const double *lse, const int32_t *root_tok,
+                       const TdesParams &p, int R, int L, int V, int K, int B, const int32_t *budget, float *TS,
+                       uint8_t *TO, const TreeOut &out, hipStream_t st);
+
 // ---- a3 + a4 + a6: DARTree depth-wise ---------------------------------------------------------
 struct DepthwiseArgs {
   const void *base;  // [R][L][V]

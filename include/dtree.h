@@ -74,7 +74,8 @@ enum dtree_op {
   DTREE_OP_DEPTHWISE = 2,
   DTREE_OP_GATED = 3,
   DTREE_OP_ACCEPT = 4,
-  DTREE_OP_STATIC = 5
+  DTREE_OP_STATIC = 5,
+  DTREE_OP_TDES = 6
 };
 
 /* Compiled envelope (DTREE_E_UNSUPPORTED beyond it). */
@@ -96,7 +97,7 @@ typedef struct {
 /*
  * Bytes of workspace an operation needs. `op` is a dtree_op; unused size arguments are
  * ignored: TOPK(rows = R*L, V, K), MARGINAL(R, L, V, K, B), DEPTHWISE(R, L, V, K, B, W,
- * rank, d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap), STATIC(R, L, V, K). Returns 0
+ * rank, d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap), STATIC(R, L, V, K), TDES(R, L, V, K). Returns 0
  * for an unknown op or invalid sizes.
  */
 size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank, int d_model);
@@ -163,6 +164,35 @@ int build_tree_gated(const void *logits, int dtype, int R, int L, int V, int K_r
  */
 int build_tree_static(const void *logits, int dtype, int R, int L, int V, int K, int D,
                       const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * GRAFT target-distilled edge scores + best-first tree (GRAFT page, method: target-distilled
+ * edge scoring, inference). Candidates at depth d are the top K tokens of position d; the
+ * parent of depth 1 is root_tok[r]. An edge (p, c, d) scores
+ *   S = log q_d(c) + s * f,  f = w . ReLU(W [Gp[p]; Gc[c]; Ed[d-1]] + b) + b0,
+ * a prefix the sum of its edges, and the tree takes the best prefix (ties: lower parent
+ * slot, then the child's position among its siblings sorted by (S desc, rank asc)) until
+ * n_nodes = budget[r] (clamped to [0, B]; B for every round when budget is NULL) or no
+ * candidate is left. Nodes are stored in the order taken (parent before child); score =
+ * S(prefix), which may exceed the parent's.
+ * Gp [V][hp], Gc [V][hc] (projected token embeddings), Ed [L][hd], W [H][hp+hc+hd] row
+ * major, b [H], w [H]: float32 device arrays; Gp, Gc, W 16-byte aligned. root_tok values
+ * outside [0, V) read as token 0. Needs s > 0, 1 <= K <= min(V, DTREE_MAX_K),
+ * B <= DTREE_MAX_CAP, out->cap == B, hp, hc, hd <= 64 and multiples of 4, H <= 128.
+ */
+int build_tree_tdes(const void *logits, int dtype, int R, int L, int V, const int32_t *root_tok,
+                    const float *Gp, const float *Gc, const float *Ed, const float *W, const float *b,
+                    const float *w, float b0, float s, int hp, int hc, int hd, int H, int K, int B,
+                    const int32_t *budget, const dtree_tree *out, void *ws, size_t ws_bytes,
+                    dtree_stream_t st);
+
+/*
+ * GRAFT state-aware budget (GRAFT page, state-aware budget allocation): the integer B in
+ * [1, B_max] maximising G(B) / C(B) with G = a B^beta and C = B c_verify + c_fixed (the
+ * smaller B on ties). Host only. Returns B, or DTREE_E_INVAL unless a > 0, 0 < beta < 1,
+ * c_verify > 0, c_fixed >= 0 and B_max >= 1.
+ */
+int dtree_saba_budget(double a, double beta, double c_verify, double c_fixed, int B_max);
 
 /*
  * Tree verification walk (DARTree background "speculative sampling"; course notes unit 11).

@@ -122,6 +122,23 @@ def verification_target(draft_bf16: np.ndarray, depth: np.ndarray, seed: int = 5
     return out
 
 
+def edge_mlp(seed: int = 6, R: int = 64, L: int = 16, V: int = V_QWEN3, hp: int = 64, hc: int = 64,
+             hd: int = 16, H: int = 128):
+    """Random-init edge MLP (no trained weights), float32: projected token tables Gp [V, hp] and
+    Gc [V, hc] ~ N(0, 1), depth embeddings Ed [L, hd] ~ N(0, 1), W [H, hp+hc+hd] ~ N(0, 1/fan_in),
+    b [H] ~ N(0, 0.1^2), w [H] ~ N(0, 2/H), b0 = 0, scale s = 1; root_tok [R] uniform."""
+    rng = np.random.default_rng(seed)
+    n = hp + hc + hd
+    prm = dict(Gp=rng.standard_normal((V, hp), dtype=np.float32), Gc=rng.standard_normal((V, hc), dtype=np.float32),
+               Ed=rng.standard_normal((L, hd), dtype=np.float32),
+               W=(rng.standard_normal((H, n), dtype=np.float32) / np.float32(np.sqrt(n))).astype(np.float32),
+               b=(np.float32(0.1) * rng.standard_normal(H, dtype=np.float32)).astype(np.float32),
+               w=(rng.standard_normal(H, dtype=np.float32) * np.float32(np.sqrt(2.0 / H))).astype(np.float32),
+               b0=0.0, s=1.0)
+    root_tok = rng.integers(0, V, (R,)).astype(np.int32)
+    return prm, root_tok
+
+
 def tie_rows(V: int, rows: int, seed: int = 11) -> np.ndarray:
     """bf16 rows with many exact ties: values drawn from a small grid, so the top-K and argmax tie-breaks matter."""
     rng = np.random.default_rng(seed)

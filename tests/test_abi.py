@@ -118,6 +118,45 @@ def test_static_validation():
     assert L.build_tree_static(None, 0, 0, 16, 100, 10, 6, ctypes.byref(tree(60)), None, 0, None) == 0
 
 
+def test_tdes_validation():
+    L = dt.lib()
+    def call(K=32, B=128, hp=64, hc=64, hd=16, H=128, s=1.0, b0=0.0, cap=None, Gp=FAKE, V=151936, nbytes=0):
+        ct = tree(B if cap is None else cap)
+        return L.build_tree_tdes(FAKE, 0, 4, 16, V, FAKE, Gp, FAKE, FAKE, FAKE, FAKE, FAKE, b0, s, hp, hc, hd, H, K, B,
+                                 None, ctypes.byref(ct), FAKE, nbytes, None)
+    assert call(K=0) == -1
+    assert call(K=40, V=30) == -1
+    assert call(s=0.0) == -1
+    assert call(s=-1.0) == -1
+    assert call(b0=float("nan")) == -1
+    assert call(cap=64) == -1
+    assert call(K=65) == -4
+    assert call(B=129, cap=129) == -4
+    assert call(hp=66) == -4
+    assert call(hd=6) == -4
+    assert call(H=129) == -4
+    assert call(Gp=0x1004) == -1
+    assert call() == -3
+    need = dt.workspace_size(dt.OP_TDES, 4, 16, 151936, 32)
+    assert need >= 4 * 16 * 32 * 32 * 5
+
+
+@pytest.mark.parametrize("cv,cf,beta,bmax", [(1.0, 10.0, 0.5, 128), (0.37, 20.0, 0.5, 128), (0.05, 7.9, 0.3, 64),
+                                             (1.0, 0.0, 0.5, 128), (0.01, 500.0, 0.5, 128), (0.2, 3.0, 0.8, 16)])
+def test_saba_budget_matches_oracle(cv, cf, beta, bmax):
+    """The library's closed form against the oracle's exhaustive argmax."""
+    from oracle import tdes
+    for a in (1.0, 3.5):
+        assert dt.saba_budget(a, beta, cv, cf, bmax) == tdes.saba_budget(a, beta, cv, cf, bmax)
+
+
+def test_saba_budget_rejects_bad_arguments():
+    for args in [(0.0, 0.5, 1.0, 1.0, 8), (1.0, 1.0, 1.0, 1.0, 8), (1.0, 0.5, 0.0, 1.0, 8), (1.0, 0.5, 1.0, -1.0, 8),
+                 (1.0, 0.5, 1.0, 1.0, 0), (1.0, 0.5, 1.0, float("nan"), 8)]:
+        with pytest.raises(dt.DTreeError):
+            dt.saba_budget(*args)
+
+
 def test_depthwise_validation():
     L = dt.lib()
     def call(rank=64, dm=1024, K=8, W=32, B=128, beta=-0.5, cap=128, E=FAKE):

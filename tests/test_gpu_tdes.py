@@ -1,0 +1,152 @@
+"""GPU parity: GRAFT edge scores + best-first tree against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import draft_tree_construction_amd as dt
+import synth
+from oracle import rowsweep, tdes, treeout
+from parity_util import dev_bf16, dev_f32, tree_to_host
+
+pytestmark = pytest.mark.gpu
+
+# The edge MLP runs in float32 on the GPU and float64 in the oracle; a path sums up to L
+# edges, each within ~1e-6 of the oracle's, so scores agree to 1e-4. Trees must be identical
+# wherever the oracle's heap never had two prefixes within 1e-4 of each other; otherwise the
+# device tree must be a valid best-first tree under the oracle's scores to that tolerance.
+TOL_T = 1e-4
+
+
+def mlp_dev(prm):
+    out = {k: torch.from_numpy(np.ascontiguousarray(prm[k], dtype=np.float32)).to("cuda:0")
+           for k in ("Gp", "Gc", "Ed", "W", "b", "w")}
+    out["b0"], out["s"] = prm["b0"], prm["s"]
+    return out
+
+
+def mlp_f64(prm):
+    out = {k: np.asarray(prm[k], dtype=np.float32).astype(np.float64) for k in ("Gp", "Gc", "Ed", "W", "b", "w")}
+    out["b0"] = float(np.float32(prm["b0"]))
+    return out
+
+
+def assert_valid_best_first(z, root_tok, p64, K, s, par, tok, sc):
+    """Replays the device tree on the oracle's edge scores: each node taken must be an
+    untaken child of a node already taken, with a prefix score within 2 TOL_T of the best
+    such candidate at that step (several trees are correct when prefixes tie within the
+    float32 rounding of the edge MLP)."""
+    L = z.shape[0]
+    toks, rows = tdes.edge_rows(z, root_tok, p64, K, s)
+    S = [0.0]
+    pci = [0]
+    dep = [0]
+    taken = set()
+    for i in range(1, len(par)):
+        best = -np.inf
+        for n in range(i):
+            d = dep[n] + 1
+            if d > L:
+                continue
+            E = rows[(d, pci[n])][0]
+            for ci in range(K):
+                if (n, ci) not in taken:
+                    best = max(best, S[n] + E[ci])
+        n = int(par[i])
+        d = dep[n] + 1
+        ci = toks[d - 1].index(int(tok[i]))
+        assert (n, ci) not in taken
+        taken.add((n, ci))
+        S.append(S[n] + rows[(d, pci[n])][0][ci])
+        pci.append(ci)
+        dep.append(d)
+        assert S[-1] >= best - 2 * TOL_T
+        assert abs(S[-1] - sc[i]) <= TOL_T
+
+
+def check_tdes(host, dtype, prm, root, K, B, budget=None, rounds=None, root_ref=None):
+    R = host.shape[0]
+    d = dev_bf16(host) if dtype == "bf16" else dev_f32(host)
+    bud_dev = None if budget is None else torch.tensor(budget, dtype=torch.int32, device="cuda:0")
+    tr = dt.build_tree_tdes(d, torch.tensor(root, dtype=torch.int32, device="cuda:0"), mlp_dev(prm), K, B,
+                            budget=bud_dev)
+    h = tree_to_host(tr)
+    p64 = mlp_f64(prm)
+    s = float(np.float32(prm["s"]))
+    exact = 0
+    rr = range(R) if rounds is None else rounds
+    for r in rr:
+        bud = B if budget is None else min(max(budget[r], 0), B)
+        rt = root[r] if root_ref is None else root_ref[r]
+        ref, gap = tdes.build_tdes(rowsweep.as_f64(host[r], dtype), int(rt), p64, K, bud, s)
+        n = int(h["n"][r])
+        par, tok, dep = list(h["parent"][r, :n + 1]), list(h["token"][r, :n + 1]), list(h["depth"][r, :n + 1])
+        sc = [float(x) for x in h["score"][r, :n + 1]]
+        # validity: parent before child, depth = parent's + 1, padding, mask
+        assert par[0] == -1 and dep[0] == 0 and tok[0] == -1
+        for i in range(1, n + 1):
+            assert 0 <= par[i] < i and dep[i] == dep[par[i]] + 1
+        assert np.all(h["parent"][r, n + 1:] == -1) and np.all(h["token"][r, n + 1:] == -1)
+        np.testing.assert_array_equal(h["mask"][r], treeout.ancestor_mask(par, B))
+        assert n == ref.n
+        if gap > TOL_T:
+            assert par == ref.parent and tok == ref.token and dep == ref.depth
+            np.testing.assert_allclose(sc, ref.score, rtol=0, atol=TOL_T)
+            exact += 1
+        else:
+            assert_valid_best_first(rowsweep.as_f64(host[r], dtype), int(rt), p64, K, s, par, tok, sc)
+    return exact, len(rr)
+
+
+@pytest.mark.parametrize("R,L,V,K,B,hp,hd,H", [
+    (4, 6, 300, 8, 40, 16, 8, 32),
+    (3, 16, 1000, 16, 128, 64, 16, 128),   # depth 16, budget at the cap
+    (2, 4, 200, 64, 128, 64, 64, 128),     # K = 64 and the widest embeddings (96 KB of LDS)
+    (5, 2, 70, 5, 40, 8, 4, 12),           # 30 candidates under a budget of 40: every one taken
+])
+def test_tdes_small(R, L, V, K, B, hp, hd, H):
+    host = synth.ddtree_logits(seed=70 + V, R=R, L=L, V=V)
+    prm, root = synth.edge_mlp(seed=V, R=R, L=L, V=V, hp=hp, hc=hp, hd=hd, H=H)
+    exact, n = check_tdes(host, "bf16", prm, root, K, B)
+    assert exact >= n - 1
+
+
+def test_tdes_children_outscore_parents():
+    """A positive edge term (b0 = 3, s = 0.5) puts each child above its parent: the tree runs
+    depth first, which a Top-B builder could never produce."""
+    R, L, V = 3, 8, 500
+    host = synth.ddtree_logits(seed=81, R=R, L=L, V=V)
+    prm, root = synth.edge_mlp(seed=82, R=R, L=L, V=V, hp=16, hc=16, hd=8, H=32)
+    prm["b0"], prm["s"] = 3.0, 0.5
+    exact, n = check_tdes(host, "bf16", prm, root, 8, 50)
+    assert exact >= n - 1
+    tr = dt.build_tree_tdes(dev_bf16(host), torch.tensor(root, dtype=torch.int32, device="cuda:0"), mlp_dev(prm), 8,
+                            50)
+    h = tree_to_host(tr)
+    assert any(h["score"][r, i] > h["score"][r, h["parent"][r, i]] for r in range(R) for i in range(2, 51))
+
+
+def test_tdes_per_round_budgets_and_f32():
+    R, L, V, K, B = 6, 5, 400, 12, 64
+    host = synth.tiny_marginal(seed=9, R=R, L=L, V=V)
+    prm, root = synth.edge_mlp(seed=90, R=R, L=L, V=V, hp=16, hc=16, hd=8, H=48)
+    budget = [-3, 0, 1, 17, 64, 100]  # clamped to [0, B]
+    exact, n = check_tdes(host, "f32", prm, root, K, B, budget=budget)
+    assert exact >= n - 1
+
+
+def test_tdes_root_token_out_of_range_reads_token_zero():
+    R, L, V = 2, 4, 300
+    host = synth.ddtree_logits(seed=91, R=R, L=L, V=V)
+    prm, _ = synth.edge_mlp(seed=92, R=R, L=L, V=V, hp=16, hc=16, hd=8, H=32)
+    exact, n = check_tdes(host, "bf16", prm, np.array([V + 5, -1], dtype=np.int32), 8, 30,
+                          root_ref=np.zeros(R, dtype=np.int32))
+    assert exact >= n - 1
+
+
+def test_tdes_full_config_sampled():
+    """Full size: R = 64 rounds, L = 16, V = 151,936 bf16, K = 32, B = 128, hp = hc = 64,
+    hd = 16, H = 128; four rounds against the oracle."""
+    host = synth.ddtree_logits(seed=2)
+    prm, root = synth.edge_mlp(seed=6)
+    exact, n = check_tdes(host, "bf16", prm, root, 32, 128, rounds=(0, 21, 42, 63))
+    assert exact >= 1
