@@ -62,11 +62,6 @@ dt::TreeOut tree_out(const dtree_tree *t) {
 }
 
 int marginal_k(int K, int B, int V) { return K == 0 ? (B < V ? B : V) : K; }
-size_t tdes_table_bytes(int R, int L, int K) {
-  const size_t n = (size_t)R * L * K * K;
-  return dt::align256(n * sizeof(float)) + dt::align256(n);
-}
-
 int gated_k(int V) { return V < DTREE_MAX_K ? V : DTREE_MAX_K; }
 
 }  // namespace
@@ -108,7 +103,7 @@ size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int 
       return a1_bytes(R * L, V, K);
     case DTREE_OP_TDES:
       if (K < 1) return 0;
-      return a1_bytes(R * L, V, K) + tdes_table_bytes(R, L, K);
+      return a1_bytes(R * L, V, K) + dt::tdes_tables_bytes(R, L, K);
     case DTREE_OP_ACCEPT:
       if (B_or_N < 1) return 0;
       return dt::accept_ws_bytes(R, L, V, B_or_N);
@@ -226,8 +221,9 @@ int build_tree_tdes(const void *logits, int dtype, int R, int L, int V, const in
   if (R == 0) return DTREE_OK;
   if (!logits || !root_tok || !Gp || !Gc || !Ed || !W || !b || !w)
     return fail(DTREE_E_INVAL, "an input pointer is NULL");
-  if (((uintptr_t)Gp | (uintptr_t)Gc | (uintptr_t)W) & 15) return fail(DTREE_E_INVAL, "Gp, Gc and W must be 16-byte aligned");
-  const size_t need = a1_bytes(R * L, V, K) + tdes_table_bytes(R, L, K);
+  if (((uintptr_t)Gp | (uintptr_t)Gc | (uintptr_t)Ed | (uintptr_t)W) & 15)
+    return fail(DTREE_E_INVAL, "Gp, Gc, Ed and W must be 16-byte aligned");
+  const size_t need = a1_bytes(R * L, V, K) + dt::tdes_tables_bytes(R, L, K);
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(st_);
@@ -237,7 +233,7 @@ int build_tree_tdes(const void *logits, int dtype, int R, int L, int V, const in
   if (e != hipSuccess) return hip_fail(e, "build_tree_tdes (row sweep)");
   char *tw = static_cast<char *>(ws) + a1_bytes(R * L, V, K);
   float *TS = reinterpret_cast<float *>(tw);
-  uint8_t *TO = reinterpret_cast<uint8_t *>(tw + dt::align256((size_t)R * L * K * K * sizeof(float)));
+  uint8_t *TO = reinterpret_cast<uint8_t *>(tw + dt::tdes_ts_bytes(R, L, K));
   dt::TdesParams p{Gp, Gc, Ed, W, b, w, b0, s, hp, hc, hd, H};
   e = dt::launch_tdes(a.zk, a.ids, a.lse, root_tok, p, R, L, V, K, B, budget, TS, TO, tree_out(out), st);
   if (e != hipSuccess) return hip_fail(e, "build_tree_tdes");

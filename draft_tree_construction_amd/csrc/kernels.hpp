@@ -50,7 +50,10 @@ struct TdesParams {
   float b0, s;
   int hp, hc, hd, H;
 };
-// Edge tables: TS [R*L][K][K] float (each parent row sorted), TO [R*L][K][K] child index.
+// Edge tables: TS float and TO child index, per round [L][K][K] (each parent row sorted),
+// at padded per-round strides; tdes_tables_bytes is their workspace.
+size_t tdes_tables_bytes(int R, int L, int K);
+size_t tdes_ts_bytes(int R, int L, int K);  // TS part; TO follows it
 hipError_t launch_tdes(const float *zk, const int32_t *ids, const double *lse, const int32_t *root_tok,
                        const TdesParams &p, int R, int L, int V, int K, int B, const int32_t *budget, float *TS,
                        uint8_t *TO, const TreeOut &out, hipStream_t st);

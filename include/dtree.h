@@ -176,7 +176,7 @@ int build_tree_static(const void *logits, int dtype, int R, int L, int V, int K,
  * candidate is left. Nodes are stored in the order taken (parent before child); score =
  * S(prefix), which may exceed the parent's.
  * Gp [V][hp], Gc [V][hc] (projected token embeddings), Ed [L][hd], W [H][hp+hc+hd] row
- * major, b [H], w [H]: float32 device arrays; Gp, Gc, W 16-byte aligned. root_tok values
+ * major, b [H], w [H]: float32 device arrays; Gp, Gc, Ed, W 16-byte aligned. root_tok values
  * outside [0, V) read as token 0. Needs s > 0, 1 <= K <= min(V, DTREE_MAX_K),
  * B <= DTREE_MAX_CAP, out->cap == B, hp, hc, hd <= 64 and multiples of 4, H <= 128.
  */
