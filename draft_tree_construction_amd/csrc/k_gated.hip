@@ -50,12 +50,23 @@ __global__ __launch_bounds__(GT_NT) void k_gated(const float *__restrict__ zk, c
   const int tid = threadIdx.x;
   const float *zr = zk + (size_t)r * L * K;
   const int32_t *ir = ids + (size_t)r * L * K;
+  // the round's candidate logits and row normalisers, staged in LDS once: every depth's
+  // reads below are then LDS reads, not one dependent global read per depth
+  __shared__ float s_z[DTREE_MAX_L * DTREE_MAX_K];
+  __shared__ double s_lse[DTREE_MAX_L];
+  __shared__ int s_id[DTREE_MAX_L * DTREE_MAX_K];
+  for (int i = tid; i < L * K; i += GT_NT) {
+    s_z[i] = zr[i];
+    s_id[i] = ir[i];
+  }
+  for (int i = tid; i < L; i += GT_NT) s_lse[i] = lse[(size_t)r * L + i];
+  __syncthreads();
 
   if (tid == 0) {
     double a = 0.0;
     Lsum[0] = 0.0;
     for (int d = 1; d <= L; ++d) {
-      a += lse[(size_t)r * L + d - 1];
+      a += s_lse[d - 1];
       Lsum[d] = a;
     }
     opar[0] = -1;
@@ -69,11 +80,11 @@ __global__ __launch_bounds__(GT_NT) void k_gated(const float *__restrict__ zk, c
   __syncthreads();
   // root layer: top K_root tokens of position 1, in rank order
   for (int k = tid; k < K_root; k += GT_NT) {
-    const double Z = (double)zr[k];
+    const double Z = (double)s_z[k];
     lay_Z[k] = Z;
     lay_idx[k] = 1 + k;
     opar[1 + k] = 0;
-    otok[1 + k] = ir[k];
+    otok[1 + k] = s_id[k];
     odep[1 + k] = 1;
     osc[1 + k] = (float)(Z - Lsum[1]);
   }
@@ -85,7 +96,7 @@ __global__ __launch_bounds__(GT_NT) void k_gated(const float *__restrict__ zk, c
     const int np = s_np;
     const int room = N - nT;
     const int kt = room < K ? room : K;  // tokens per parent that can matter
-    const float *zd = zr + (size_t)d * K;
+    const float *zd = s_z + d * K;
     const double Zmax = lay_Z[0] + (double)zd[0];
     // survivors per parent: a prefix of the rank order
     for (int i = tid; i < np; i += GT_NT) {
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(GT_NT) void k_gated(const float *__restrict__ zk, c
         double s = c.Z - Lsum[d + 1];
         const float ps = osc[pidx];
         opar[idx] = pidx;
-        otok[idx] = ir[(size_t)d * K + rank];
+        otok[idx] = s_id[d * K + rank];
         odep[idx] = d + 1;
         // clamp to the parent's score (a child never outscores its parent)
         float sf = (float)s;

@@ -58,12 +58,19 @@ __global__ __launch_bounds__(MG_NT) void k_marginal(const float *__restrict__ zk
   const double beta = (double)beta_f;
   const float *zr = zk + (size_t)r * L * K;
   const int32_t *ir = ids + (size_t)r * L * K;
+  // the round's candidate logits and row normalisers, staged in LDS once: every depth's
+  // reads below are then LDS reads, not one dependent global read per depth
+  __shared__ float s_z[DTREE_MAX_L * DTREE_MAX_K];
+  __shared__ double s_lse[DTREE_MAX_L];
+  for (int i = tid; i < L * K; i += MG_NT) s_z[i] = zr[i];
+  for (int i = tid; i < L; i += MG_NT) s_lse[i] = lse[(size_t)r * L + i];
+  __syncthreads();
 
   if (tid == 0) {
     double a = 0.0;
     Lsum[0] = 0.0;
     for (int d = 1; d <= L; ++d) {
-      a += lse[(size_t)r * L + d - 1];
+      a += s_lse[d - 1];
       Lsum[d] = a;
     }
     s_g = 0;
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(MG_NT) void k_marginal(const float *__restrict__ zk
     if (tid == 0) s_nc = 0;
     __syncthreads();
     // 1. candidates (i, k) with (i+1)(k+1) <= B, scoring above G's last when G is full
-    const float *zd = zr + (size_t)(d - 1) * K;
+    const float *zd = s_z + (d - 1) * K;
     for (int t = tid; t < np * K; t += MG_NT) {
       const int i = t / K, k = t - i * K;
       if ((i + 1) * (k + 1) > B) continue;

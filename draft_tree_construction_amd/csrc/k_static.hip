@@ -39,12 +39,23 @@ __global__ __launch_bounds__(SG_NT) void k_static(const float *__restrict__ zk, 
   const int tid = threadIdx.x;
   const float *zr = zk + (size_t)r * L * Kc;
   const int32_t *ir = ids + (size_t)r * L * Kc;
+  // the round's candidate logits and row normalisers, staged in LDS once: every depth's
+  // reads below are then LDS reads, not one dependent global read per depth
+  __shared__ float s_z[DTREE_MAX_L * DTREE_MAX_K];
+  __shared__ double s_lse[DTREE_MAX_L];
+  __shared__ int s_id[DTREE_MAX_L * DTREE_MAX_K];
+  for (int i = tid; i < D * Kc; i += SG_NT) {
+    s_z[i] = zr[i];
+    s_id[i] = ir[i];
+  }
+  for (int i = tid; i < D; i += SG_NT) s_lse[i] = lse[(size_t)r * L + i];
+  __syncthreads();
 
   if (tid == 0) {
     double a = 0.0;
     Lsum[0] = 0.0;
     for (int d = 1; d <= D; ++d) {
-      a += lse[(size_t)r * L + d - 1];
+      a += s_lse[d - 1];
       Lsum[d] = a;
     }
     // pairs of parent i: k < floor(K / (i + 1)), i.e. (i + 1)(k + 1) <= K
@@ -62,10 +73,10 @@ __global__ __launch_bounds__(SG_NT) void k_static(const float *__restrict__ zk, 
   __syncthreads();
   // depth 1: the top K tokens of position 1, in rank order
   for (int k = tid; k < K; k += SG_NT) {
-    const double Z = (double)zr[k];
+    const double Z = (double)s_z[k];
     lay_Z[0][k] = Z;
     opar[1 + k] = 0;
-    otok[1 + k] = ir[k];
+    otok[1 + k] = s_id[k];
     odep[1 + k] = 1;
     osc[1 + k] = (float)(Z - Lsum[1]);
   }
@@ -74,7 +85,7 @@ __global__ __launch_bounds__(SG_NT) void k_static(const float *__restrict__ zk, 
   for (int d = 1; d < D; ++d) {
     const double *pz = lay_Z[(d - 1) & 1];
     double *nz = lay_Z[d & 1];
-    const float *zd = zr + (size_t)d * Kc;
+    const float *zd = s_z + d * Kc;
     const int pbase = 1 + (d - 1) * K;  // node index of kept parent 0
     for (int c = tid; c < nc; c += SG_NT) {
       int i = 0;
@@ -99,7 +110,7 @@ __global__ __launch_bounds__(SG_NT) void k_static(const float *__restrict__ zk, 
         const float s = (float)(Z - Lsum[d + 1]);
         const float ps = osc[pidx];
         opar[idx] = pidx;
-        otok[idx] = ir[(size_t)d * Kc + k];
+        otok[idx] = s_id[d * Kc + k];
         odep[idx] = d + 1;
         osc[idx] = s < ps ? s : ps;  // a child never outscores its parent
         nz[rank] = Z;
