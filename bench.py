@@ -48,10 +48,13 @@ def parse():
 
 
 def sweep_source_digest():
-    """Digest of the row sweep's source: the stored counter readings are used only while it matches."""
+    """Digest of the row sweep's sources (the kernel and the helpers it includes): the stored
+    counter readings are used only while it matches."""
     import hashlib
-    src = os.path.join(ROOT, "draft_tree_construction_amd", "csrc", "k_rowsweep.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in ("k_rowsweep.hip", "common.hpp"):
+        h.update(open(os.path.join(ROOT, "draft_tree_construction_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def main():

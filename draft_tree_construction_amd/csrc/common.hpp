@@ -87,16 +87,46 @@ DT_INLINE void block_sort_desc_u64(uint64_t *a, int n) {
   }
 }
 
-// Wave-level (64 lanes) reductions.
+// Wave-level (64 lanes, all active) reductions through DPP: row shifts by 1, 2, 4 and 8
+// leave each row's total in its lane 15, row broadcasts 15 and 31 carry them on to lane 63,
+// which every lane then reads. Lanes without a source take the identity. The order of the
+// operations is fixed, so the result is deterministic and the same in every lane.
+template <int CTRL, int ROW_MASK>
+DT_INLINE uint32_t dpp_u32(uint32_t v, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+DT_INLINE float dpp_f32(float v, float id) {
+  return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(v), __float_as_uint(id)));
+}
+template <int CTRL, int ROW_MASK>
+DT_INLINE double dpp_f64(double v, double id) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v), i = (uint64_t)__double_as_longlong(id);
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)u, (uint32_t)i);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(u >> 32), (uint32_t)(i >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 DT_INLINE float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  const float id = -__builtin_huge_valf();
+  v = fmaxf(v, dpp_f32<0x111, 0xF>(v, id));
+  v = fmaxf(v, dpp_f32<0x112, 0xF>(v, id));
+  v = fmaxf(v, dpp_f32<0x114, 0xF>(v, id));
+  v = fmaxf(v, dpp_f32<0x118, 0xF>(v, id));
+  v = fmaxf(v, dpp_f32<0x142, 0xA>(v, id));
+  v = fmaxf(v, dpp_f32<0x143, 0xC>(v, id));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
 DT_INLINE double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f64<0x111, 0xF>(v, 0.0);
+  v += dpp_f64<0x112, 0xF>(v, 0.0);
+  v += dpp_f64<0x114, 0xF>(v, 0.0);
+  v += dpp_f64<0x118, 0xF>(v, 0.0);
+  v += dpp_f64<0x142, 0xA>(v, 0.0);
+  v += dpp_f64<0x143, 0xC>(v, 0.0);
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // ---- wave-level (64-lane) sorting of 64-bit keys held one per lane, descending
