@@ -463,26 +463,23 @@ DT_INLINE uint64_t uni(uint64_t x) { return ((uint64_t)uni((uint32_t)(x >> 32)) 
 DT_INLINE float uni(float x) { return __uint_as_float(uni(__float_as_uint(x))); }
 DT_INLINE double uni(double x) { return __longlong_as_double((long long)uni((uint64_t)__double_as_longlong(x))); }
 
-// Wave sum of an unsigned 64-bit value (exact): xor swizzles within each half of the wave
-// (the lane pattern is an immediate), then the two halves' sums from lanes 0 and 32.
-template <int M>
-DT_INLINE uint64_t swz_xor(uint64_t v) {
-  constexpr int pat = 0x1F | (M << 10);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)v, pat);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(v >> 32), pat);
+// Wave sum of an unsigned 64-bit value (exact, so the order does not matter): DPP row
+// shifts and row broadcasts accumulate the total in lane 63, which every lane reads.
+template <int CTRL, int ROW_MASK>
+DT_INLINE uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)v, 0u);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32), 0u);
   return ((uint64_t)hi << 32) | lo;
 }
 DT_INLINE uint64_t wave_sum_u64(uint64_t v) {
-  v += swz_xor<1>(v);
-  v += swz_xor<2>(v);
-  v += swz_xor<4>(v);
-  v += swz_xor<8>(v);
-  v += swz_xor<16>(v);
-  const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 0) << 32) |
-                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 0);
-  const uint64_t b = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 32) << 32) |
-                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 32);
-  return a + b;
+  v += dpp_u64<0x111, 0xF>(v);
+  v += dpp_u64<0x112, 0xF>(v);
+  v += dpp_u64<0x114, 0xF>(v);
+  v += dpp_u64<0x118, 0xF>(v);
+  v += dpp_u64<0x142, 0xA>(v);
+  v += dpp_u64<0x143, 0xC>(v);
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
 }
 
 // Block sums of N unsigned 64-bit values per thread (exact, so any order): wave sums, then
