@@ -118,6 +118,43 @@ def walk_sampled(tab: ResidualTables, depth, seed: int, trial: int, rnd: int):
         j = nxt
 
 
+def inverse_cdf_margin(p: np.ndarray, u: float, v: int) -> float:
+    """How far the draw's target mass u * sum(p) lies from the CDF boundaries of the token v
+    it selected, as a fraction of sum(p): min(cdf[v] - target, target - cdf[v - 1])."""
+    cdf = np.cumsum(p)
+    tot = cdf[-1]
+    tgt = u * tot
+    hi = cdf[v] - tgt
+    lo = tgt - (cdf[v - 1] if v > 0 else 0.0)
+    return float(min(abs(hi), abs(lo)) / tot)
+
+
+def walk_sampled_margin(tab: ResidualTables, depth, seed: int, trial: int, rnd: int):
+    """walk_sampled plus the smallest decision margin of the walk: |u q(c) - p'(c)| over the
+    acceptance tests it made and the draw's distance to its CDF boundaries. A device walk
+    whose probabilities differ from these by float rounding can only decide differently
+    where this margin is of the order of that rounding. Returns ((accept_len,
+    accept_node, next_token), margin)."""
+    j = 0
+    step = 0
+    margin = np.inf
+    while True:
+        nxt = -1
+        for i, c in enumerate(tab.kids[j]):
+            u = uniform(seed, trial, rnd, step)
+            step += 1
+            margin = min(margin, abs(u * tab.qc[j][i] - tab.pc[j][i]))
+            if u * tab.qc[j][i] < tab.pc[j][i]:
+                nxt = c
+                break
+        if nxt < 0:
+            u = uniform(seed, trial, rnd, step)
+            v = sample_inverse_cdf(tab.final[j], u)
+            margin = min(margin, inverse_cdf_margin(tab.final[j], u, v))
+            return (depth[j], j, v), float(margin)
+        j = nxt
+
+
 def exact_outcomes(tab: ResidualTables):
     """Exact law of the walk: stop[j] = P(the walk ends at node j); the extra token then
     follows tab.final[j]. Also returns reach[j] = P(the walk visits j)."""
@@ -153,6 +190,30 @@ def walk_match(parent, token, depth, target_rows: np.ndarray, T: float, seed: in
                 break
         if nxt < 0:
             return depth[j], j, x
+        j = nxt
+
+
+def walk_match_margin(parent, token, depth, target_rows: np.ndarray, T: float, seed: int, trial: int, rnd: int):
+    """walk_match plus the smallest distance of its draws' target masses to their CDF
+    boundaries (as a fraction of the row's mass). Returns ((accept_len, accept_node,
+    next_token), margin)."""
+    kids = children_lists(parent)
+    j = 0
+    step = 0
+    margin = np.inf
+    while True:
+        u = uniform(seed, trial, rnd, step)
+        step += 1
+        p = softmax_row(target_rows[j], T)
+        x = sample_inverse_cdf(p, u)
+        margin = min(margin, inverse_cdf_margin(p, u, x))
+        nxt = -1
+        for c in kids[j]:
+            if token[c] == x:
+                nxt = c
+                break
+        if nxt < 0:
+            return (depth[j], j, x), float(margin)
         j = nxt
 
 

@@ -178,3 +178,75 @@ def test_match_walk_sharp_target_is_greedy():
     g = accept.walk_greedy(t.parent, t.token, t.depth, sharp)
     for tr in range(50):
         assert accept.walk_match(t.parent, t.token, t.depth, sharp, 1.0, 9, tr, 0) == g
+
+
+def _multichild():
+    g = json.load(open(os.path.join(GOLD, "multichild_example.json")))
+    tr = g["tree"]
+    target = np.log(np.array(g["target_rows"]))
+    draft = np.log(np.array(g["draft_rows"]))
+    return g, tr["parent"], tr["token"], tr["depth"], target, draft
+
+
+def _frac(x):
+    return x[0] / x[1]
+
+
+def test_multichild_closed_form():
+    """A node with three children and one with two, on two depths with different draft rows:
+    the sibling-by-sibling residual (q fixed per node, renormalised after every rejection)
+    against fractions worked by hand. Updating p' with the other depth's draft row, skipping
+    a renormalisation or keeping p instead of the residual each changes an acceptance
+    probability below."""
+    g, par, tok, dep, target, draft = _multichild()
+    tab = accept.ResidualTables(par, tok, dep, target, draft, 1.0)
+    for c, want in g["accept_prob"].items():
+        c = int(c)
+        j = par[c]
+        i = tab.kids[j].index(c)
+        a = min(1.0, tab.pc[j][i] / tab.qc[j][i])
+        assert abs(a - _frac(want)) < 1e-12, (c, a)
+    stop, reach = accept.exact_outcomes(tab)
+    np.testing.assert_allclose(reach, [_frac(x) for x in g["reach"]], atol=1e-12)
+    np.testing.assert_allclose(stop, [_frac(x) for x in g["stop"]], atol=1e-12)
+    assert abs(np.sum(stop) - 1.0) < 1e-12
+    for j, want in g["final_residual"].items():
+        np.testing.assert_allclose(tab.final[int(j)], [_frac(x) for x in want], atol=1e-12)
+    # leaves draw from their own target distribution
+    for j in (2, 3, 4, 5):
+        np.testing.assert_allclose(tab.final[j], np.array(g["target_rows"][j]), atol=1e-12)
+
+
+def test_multichild_sampled_against_hand_law():
+    """The sampled walk's stop frequencies over 20,000 Philox trials against the hand law."""
+    g, par, tok, dep, target, draft = _multichild()
+    tab = accept.ResidualTables(par, tok, dep, target, draft, 1.0)
+    n = 20000
+    nodes = np.array([accept.walk_sampled(tab, dep, 0x5EED5EED, t, 3)[1] for t in range(n)])
+    for j, want in enumerate(g["stop"]):
+        p = _frac(want)
+        f = np.mean(nodes == j)
+        assert abs(f - p) <= 4 * math.sqrt(max(p * (1 - p), 1e-12) / n) + 1e-12, (j, f, p)
+
+
+def test_walk_margin_is_distance_to_the_decision():
+    """The margin the oracle reports for a walk is the smallest |u q - p'| over its tests and
+    the draw's distance to its CDF boundaries: recomputed from the same uniforms."""
+    g, par, tok, dep, target, draft = _multichild()
+    tab = accept.ResidualTables(par, tok, dep, target, draft, 1.0)
+    for t in range(50):
+        res, m = accept.walk_sampled_margin(tab, dep, 0x5EED5EED, t, 0)
+        assert res == accept.walk_sampled(tab, dep, 0x5EED5EED, t, 0)
+        assert 0.0 <= m <= 1.0
+    # a draw exactly on a boundary has margin 0; one in the middle of a token has margin > 0
+    p = np.array([0.25, 0.25, 0.5])
+    assert accept.inverse_cdf_margin(p, 0.5, 2) == 0.0
+    assert abs(accept.inverse_cdf_margin(p, 0.75, 2) - 0.25) < 1e-15
+
+
+def test_match_walk_margin_agrees_with_walk():
+    g, par, tok, dep, target, draft = _multichild()
+    for t in range(30):
+        res, m = accept.walk_match_margin(par, tok, dep, target, 1.0, 0x5EED5EED, t, 1)
+        assert res == accept.walk_match(par, tok, dep, target, 1.0, 0x5EED5EED, t, 1)
+        assert 0.0 <= m <= 0.5
