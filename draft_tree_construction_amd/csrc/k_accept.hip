@@ -29,6 +29,9 @@
 // (q(c), p'(c)) and the block prefix sums of the final residual, and one thread per
 // (trial, round) walks on the tables. Both draw the token inside the chosen block in the
 // same order: 8 lane sums of 8 tokens in float, accumulated lane by lane in float64.
+#include <atomic>
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -65,7 +68,9 @@ DT_INLINE float philox_uniform(uint64_t seed, uint64_t trial, uint32_t rnd, uint
 
 // ---------------------------------------------------------------- rows in units of 8
 // A row of V elements read in units of 8. A 16-byte aligned row is read with buffer loads
-// (reads past its end return zero; those elements are masked), any other element-wise.
+// except for a ragged last unit, which is read element by element: the buffer's range check
+// zeroes whole dwords, so with an odd number of bf16 elements the dword holding the last
+// element and the first one past the end would read as zero. Any other row element-wise.
 template <typename T>
 struct Row {
   const T *p;
@@ -107,11 +112,6 @@ DT_INLINE void unit_elems(const Row<T> &r, int u, float *f) {
     f[e] = v < r.V ? load_elt(r.p, (size_t)v) : -kInf;
   }
 }
-DT_INLINE void unit_mask(float *f, int u, int V) {
-  const int nv = V - u * 8;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = e < nv ? f[e] : -kInf;
-}
 
 // Units in flight per thread and row (the ring depth): a pass is bound by the bytes one
 // workgroup keeps in flight, so bf16 rows use a deeper ring than fp32 rows (whose units
@@ -145,9 +145,9 @@ DT_INLINE void stream2(const Row<T> &A, const Row<T> &B, F &&f) {
           raw_widen(rb[j], xb);
           ra[j] = raw_load(A, u + D * AC_NT);
           rb[j] = raw_load(B, u + D * AC_NT);
-          if (u * 8 + 8 > V) {
-            unit_mask(xa, u, V);
-            unit_mask(xb, u, V);
+          if (u * 8 + 8 > V) {  // the ragged last unit, element by element (see make_row)
+            unit_elems(A, u, xa);
+            unit_elems(B, u, xb);
           }
           f(u, xa, xb);
         }
@@ -182,7 +182,7 @@ DT_INLINE void stream1(const Row<T> &A, F &&f) {
           float xa[8];
           raw_widen(ra[j], xa);
           ra[j] = raw_load(A, u + D * AC_NT);
-          if (u * 8 + 8 > V) unit_mask(xa, u, V);
+          if (u * 8 + 8 > V) unit_elems(A, u, xa);  // the ragged last unit, element by element
           f(u, xa);
         }
       }
@@ -980,24 +980,33 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
 // combine the partials in the same order and so take identical decisions. C(t) is exact
 // (integer sums), so it equals the one-workgroup value; the LSE and the final draw's block
 // prefix are summed in another order, within float rounding of the one-workgroup walk.
-// Every wait is bounded: past the bound the walk records an error and finishes.
+// The host launches this grid only when all of it fits on the device at once. Every wait
+// is bounded (Xch::spin polls): a wait that runs out, or a walk that outgrows the exchange
+// area, marks its round failed (err[r]); the round's other workgroups stop at their next
+// wait instead of polling to the bound, every workgroup of the round leaves the walk, and
+// the round's outputs are -1.
 constexpr int AC_NS = 4;          // workgroups per round
 constexpr int AC_XK = 4;          // exchanged values per workgroup and pass
 constexpr int AC_MAXPASS = 512;   // passes per round the exchange area holds
 constexpr uint64_t AC_SENT = ~0ull;
+constexpr int AC_SPIN = 1 << 22;  // default poll bound of one wait (about 0.1 s)
 
 struct Xch {
   uint64_t *slot;  // [R][AC_MAXPASS][AC_NS][AC_XK], AC_SENT before the walk
-  int *err;        // set when a wait ran out or the passes overflowed
+  int *err;        // [R]: set when a wait of that round ran out or its passes overflowed
+  int spin;        // polls before a wait gives up
 };
 DT_INLINE void xch_put(uint64_t *p, uint64_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-DT_INLINE uint64_t xch_wait(uint64_t *p, int *err) {
+// The slot's value once it is written; false (and the round marked failed) when the wait
+// runs out or the round has already failed.
+DT_INLINE bool xch_wait(uint64_t *p, int *err, int spin, uint64_t &v) {
   for (int it = 0;; ++it) {
-    const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (v != AC_SENT) return v;
-    if (it > (1 << 22)) {
+    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v != AC_SENT) return true;
+    if (it >= spin || __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
       __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return 0ull;
+      v = 0ull;
+      return false;
     }
     __builtin_amdgcn_s_sleep(1);
   }
@@ -1005,10 +1014,10 @@ DT_INLINE uint64_t xch_wait(uint64_t *p, int *err) {
 DT_INLINE uint64_t dbits(double x) { return (uint64_t)__double_as_longlong(x); }
 DT_INLINE double bitsd(uint64_t x) { return __longlong_as_double((long long)x); }
 
-__global__ void k_accept_xch_init(uint64_t *slot, size_t n, int *err) {
+__global__ void k_accept_xch_init(uint64_t *slot, size_t n, int *err, int R) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     slot[i] = AC_SENT;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < R; i += gridDim.x * blockDim.x) err[i] = 0;
 }
 
 template <typename T>
@@ -1019,6 +1028,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
   __shared__ Red red;
   __shared__ float cz1[DTREE_MAX_CAP + 1], cz2[DTREE_MAX_CAP + 1], cu[DTREE_MAX_CAP + 1];
   __shared__ uint64_t got[AC_NS][AC_XK];
+  __shared__ int xfail;
   extern __shared__ double dyn[];  // [nblk] prefix (double) then [nblk] block sums (float)
   const int r = blockIdx.x / AC_NS, q = blockIdx.x - r * AC_NS;
   const int cap = a.tree.cap;
@@ -1037,23 +1047,32 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
   double *pre = dyn;
   float *blk = reinterpret_cast<float *>(dyn + nblk_all);
   int pass = 0;
-  bool bad = false;
-  // publish k values, then gather every workgroup's k values into got[][] (all threads)
-  auto exchange = [&](const uint64_t *v, int k) {
+  int *const err_r = x.err + r;
+  if (threadIdx.x == 0) xfail = 0;  // made visible by the first exchange's barrier
+  // publish k values, then gather every workgroup's k values into got[][] (all threads);
+  // returns true when the round has failed (a wait gave up or the passes overflowed)
+  auto exchange = [&](const uint64_t *v, int k) -> bool {
     uint64_t *S = x.slot + ((size_t)r * AC_MAXPASS + (size_t)min(pass, AC_MAXPASS - 1)) * (AC_NS * AC_XK);
-    if (pass >= AC_MAXPASS) bad = true;
     __syncthreads();
-    // lanes 0 .. AC_NS * AC_XK - 1 of the first wave: each publishes (its own workgroup's
-    // slots) and polls one slot, all at once
-    if (threadIdx.x < AC_NS * AC_XK) {
+    if (pass >= AC_MAXPASS) {
+      if (threadIdx.x == 0) {
+        xfail = 1;
+        __hip_atomic_store(err_r, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else if (threadIdx.x < AC_NS * AC_XK) {
+      // lanes 0 .. AC_NS * AC_XK - 1 of the first wave: each publishes (its own workgroup's
+      // slots) and polls one slot, all at once
       const int w = threadIdx.x / AC_XK, i = threadIdx.x % AC_XK;
       if (i < k) {
         if (w == q) xch_put(S + q * AC_XK + i, i == 0 ? v[0] : i == 1 ? v[k > 1 ? 1 : 0] : i == 2 ? v[k > 2 ? 2 : 0] : v[k > 3 ? 3 : 0]);
-        got[w][i] = xch_wait(S + w * AC_XK + i, x.err);
+        uint64_t g;
+        if (!xch_wait(S + w * AC_XK + i, err_r, x.spin, g)) xfail = 1;
+        got[w][i] = g;
       }
     }
     __syncthreads();
     ++pass;
+    return xfail != 0;
   };
   const T *target = static_cast<const T *>(a.target) + (size_t)r * (cap + 1) * a.V;
   const T *draft = static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V;
@@ -1061,7 +1080,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
   const uint64_t trial = a.trial0;
   uint32_t step = 0;
   int j = 0, out_tok = -1;
-  bool lists = false;
+  bool lists = false, failed = false;
   // each workgroup bins the residual support of its own range (its own list slice); the
   // exchanged partials are the sums over S(t), exact, so the totals do not depend on it
   Bins bn;
@@ -1078,7 +1097,10 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
       double sa, sb;
       wg_lse2_part(A, B, s, red, ma, sa, mb, sb);
       const uint64_t v[4] = {(uint64_t)__float_as_uint(ma), dbits(sa), (uint64_t)__float_as_uint(mb), dbits(sb)};
-      exchange(v, 4);
+      if (exchange(v, 4)) {
+        failed = true;
+        break;
+      }
       float MA = -kInf, MB = -kInf;
       for (int w = 0; w < AC_NS; ++w) {
         MA = fmaxf(MA, __uint_as_float((uint32_t)got[w][0]));
@@ -1134,7 +1156,10 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
         wg_c_sums(A, B, nt, nd, t2, blk, nblk, red, v[0], v[1]);
       }
       const bool direct = !built;
-      exchange(v, 2);
+      if (exchange(v, 2)) {
+        failed = true;
+        break;
+      }
       uint64_t P = 0, Q = 0;
       for (int w = 0; w < AC_NS; ++w) {
         P += got[w][0];
@@ -1147,6 +1172,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
         C = C2;
       }
     }
+    if (failed) break;
     if (nxt >= 0) {
       j = nxt;
       continue;
@@ -1159,7 +1185,10 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
     const double tot_q = nblk > 0 ? pre[nblk - 1] : 0.0;
     {
       const uint64_t v[1] = {dbits(tot_q)};
-      exchange(v, 1);
+      if (exchange(v, 1)) {
+        failed = true;
+        break;
+      }
     }
     double off[AC_NS + 1];
     off[0] = 0.0;
@@ -1180,13 +1209,17 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
     }
     {
       const uint64_t v[1] = {mine};
-      exchange(v, 1);
+      if (exchange(v, 1)) {
+        failed = true;
+        break;
+      }
     }
     out_tok = (int)(uint32_t)got[owner][0];
     break;
   }
+  // a failed round (this workgroup's wait or another's of the same round) reports -1
   if (q == 0) {
-    const bool err = bad || __hip_atomic_load(x.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    const bool err = failed || __hip_atomic_load(err_r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
     for (int i = threadIdx.x; i < a.n_trials; i += AC_NT) {
       const size_t o = (size_t)i * a.R + r;
       a.accept_len[o] = err ? -1 : dep[j];
@@ -1374,13 +1407,47 @@ size_t accept_ws_bytes(int R, int L, int V, int cap) {
   const int nblk = (V + AC_BLK - 1) / AC_BLK;
   const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
   const size_t lists = (size_t)R * V * sizeof(float2);  // the lazy walk's binned supports
-  // then the cooperative walk's exchange slots and error flag
-  return align256(tables > lists ? tables : lists) + align256(xch_slots(R) * sizeof(uint64_t)) + 256;
+  // then the cooperative walk's exchange slots and per-round error flags
+  return align256(tables > lists ? tables : lists) + align256(xch_slots(R) * sizeof(uint64_t)) +
+         align256((size_t)R * sizeof(int));
 }
 
 size_t accept_lds_bytes(int V) {
   const int nblk = (V + AC_BLK - 1) / AC_BLK;
   return (size_t)nblk * (sizeof(double) + sizeof(float));
+}
+
+// Workgroups of k_accept_coop<T> (with shm bytes of dynamic LDS) that the current device
+// holds at once: multiprocessors times the occupancy query. The answer depends only on the
+// device and the kernel, so it is kept per device; 0 when a query fails.
+template <typename T>
+static int coop_capacity(size_t shm) {
+  static std::atomic<int> cache[64];
+  static std::atomic<size_t> cache_shm[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache_shm[dev].load() == shm + 1) return cache[dev].load();
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_accept_coop<T>, AC_NT, shm) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int cap = cus * per;
+  if (dev >= 0 && dev < 64) {
+    cache[dev].store(cap);
+    cache_shm[dev].store(shm + 1);
+  }
+  return cap;
+}
+
+// Poll bound of the cooperative walk's waits: DTREE_ACCEPT_SPIN_LIMIT when set (a positive
+// integer; a diagnostic that makes the bounded waits give up early), else AC_SPIN.
+static int spin_limit() {
+  const char *e = getenv("DTREE_ACCEPT_SPIN_LIMIT");
+  if (!e || !*e) return AC_SPIN;
+  const long v = strtol(e, nullptr, 10);
+  return v >= 0 && v < AC_SPIN ? (int)v : AC_SPIN;
 }
 
 hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
@@ -1389,28 +1456,28 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
     const size_t shm = accept_lds_bytes(a.V);
     if (a.T > 0.f && !a.match) {
       // residual walk with one trial: AC_NS workgroups per round when the whole grid fits on
-      // the device at once (a cooperative launch checks that), else one workgroup per round
-      const size_t slots = (size_t)a.R * (a.tree.cap + 1);
-      const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
-      const size_t lists = (size_t)a.R * a.V * sizeof(float2);
-      char *w = static_cast<char *>(ws) + align256(tables > lists ? tables : lists);
-      Xch x;
-      x.slot = reinterpret_cast<uint64_t *>(w);
-      x.err = reinterpret_cast<int *>(w + align256(xch_slots(a.R) * sizeof(uint64_t)));
-      hipLaunchKernelGGL(k_accept_xch_init, dim3(256), dim3(256), 0, st, x.slot, xch_slots(a.R), x.err);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      AcceptArgs ac = a;
-      float2 *lists_p = static_cast<float2 *>(ws);
-      void *args[3] = {&ac, &x, &lists_p};
-      const dim3 grid((unsigned)(a.R * AC_NS)), block(AC_NT);
-      e = a.dtype == DTREE_BF16
-              ? hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_accept_coop<uint16_t>), grid, block, args,
-                                           (unsigned)shm, st)
-              : hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_accept_coop<float>), grid, block, args,
-                                           (unsigned)shm, st);
-      if (e == hipSuccess) return hipSuccess;
-      (void)hipGetLastError();  // too large for one wave of workgroups: the one-workgroup walk
+      // the device at once (its workgroups wait for each other), else one workgroup per round
+      const int capacity = a.dtype == DTREE_BF16 ? coop_capacity<uint16_t>(shm) : coop_capacity<float>(shm);
+      if ((long long)a.R * AC_NS <= (long long)capacity) {
+        const size_t slots = (size_t)a.R * (a.tree.cap + 1);
+        const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
+        const size_t lists = (size_t)a.R * a.V * sizeof(float2);
+        char *w = static_cast<char *>(ws) + align256(tables > lists ? tables : lists);
+        Xch x;
+        x.slot = reinterpret_cast<uint64_t *>(w);
+        x.err = reinterpret_cast<int *>(w + align256(xch_slots(a.R) * sizeof(uint64_t)));
+        x.spin = spin_limit();
+        hipLaunchKernelGGL(k_accept_xch_init, dim3(256), dim3(256), 0, st, x.slot, xch_slots(a.R), x.err, a.R);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        float2 *lists_p = static_cast<float2 *>(ws);
+        const dim3 grid((unsigned)(a.R * AC_NS)), block(AC_NT);
+        if (a.dtype == DTREE_BF16)
+          hipLaunchKernelGGL(k_accept_coop<uint16_t>, grid, block, shm, st, a, x, lists_p);
+        else
+          hipLaunchKernelGGL(k_accept_coop<float>, grid, block, shm, st, a, x, lists_p);
+        return hipGetLastError();
+      }
     }
     if (a.dtype == DTREE_BF16)
       hipLaunchKernelGGL(k_accept_lazy<uint16_t>, dim3(a.R), dim3(AC_NT), shm, st, a, static_cast<float2 *>(ws));

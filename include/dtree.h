@@ -20,8 +20,9 @@
  *     the dtree_tree struct itself and scalar arguments, which live on the host.
  *   - The caller owns every buffer, including the workspace `ws` of at least
  *     dtree_workspace_size(...) bytes, 256-byte aligned (as hipMalloc and torch allocations
- *     are; else DTREE_E_INVAL). The library never allocates or frees memory, keeps
- *     no state between calls and holds no pointer after it returns.
+ *     are; else DTREE_E_INVAL). The library never allocates or frees memory and holds no
+ *     pointer after it returns; the only state kept between calls is a per-device cache of
+ *     one occupancy query (how many workgroups of the acceptance walk fit at once).
  *   - Every call only enqueues kernels on stream `s` (a hipStream_t; NULL = null stream)
  *     and returns; results are valid once the stream reaches that point. Calls are
  *     reentrant; calls that share an output or workspace buffer must be ordered by the caller.
@@ -213,6 +214,14 @@ int dtree_saba_budget(double a, double beta, double c_verify, double c_fixed, in
  * accept_node (slot index), next_token (bonus or correction token).
  * Needs cap <= DTREE_MAX_CAP, L <= DTREE_MAX_L, V <= DTREE_MAX_ACCEPT_V, n_trials >= 1,
  * temperature >= 0.
+ * Device-side failure (temperature > 0 with n_trials == 1 only): when the whole grid fits
+ * on the device at once, four workgroups share each round and wait for each other's
+ * partial sums with bounded waits. A round whose wait runs out (its workgroups could not
+ * all run at once, e.g. beside other work on the device) gets accept_len = accept_node =
+ * next_token = -1; the call itself still returns DTREE_OK, since the failure happens after
+ * it returns. Valid outputs are never negative, so callers check for -1. The environment
+ * variable DTREE_ACCEPT_SPIN_LIMIT (polls per wait, default 4194304, about 0.1 s) lowers
+ * the bound; it exists to exercise this path.
  */
 int accept_tree(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype,
                 int R, int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials,
