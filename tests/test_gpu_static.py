@@ -5,6 +5,7 @@ import pytest
 import draft_tree_construction_amd as dt
 import synth
 from oracle import rowsweep, static
+import oracle_pool as op
 from parity_util import assert_tree_equal, dev_bf16, dev_f32, tree_to_host
 
 pytestmark = pytest.mark.gpu
@@ -47,8 +48,12 @@ def test_static_ties():
     check_static(host, "bf16", 10, 6)
 
 
-def test_static_full_config_sampled():
+def test_static_full_config_all_rounds():
     """Full size: R = 64 rounds, L = 16, V = 151,936 bf16, K = 10, D = 6 (60 nodes), every
-    eighth round against the oracle's literal K x V pool."""
+    round against the oracle's literal K x V pool."""
     host = synth.talon_logits(seed=4)
-    check_static(host, "bf16", 10, 6, rounds=range(0, 64, 8))
+    h = tree_to_host(dt.build_tree_static(dev_bf16(host), 10, 6))
+    ref = op.pmap(op.static_task, [(host[r], 10, 6) for r in range(64)])
+    for r in range(64):
+        assert h["n"][r] == 60
+        assert_tree_equal(h, r, ref[r], 60)
