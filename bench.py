@@ -136,27 +136,35 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = R / (ms_per_step / 1e3)
 
-    # ---- roofline: the row sweep kernel, timed live over its own launches on this stream
-    flat = draft.view(R * L, V)
+    # ---- roofline: the row sweep kernel, timed live over its own launches on this stream,
+    # alternating between two distinct 311 MB logits tensors (the DDTree-shape and TALON-shape
+    # inputs) so no launch re-reads what the previous one left in the 256 MB last-level cache
+    flats = (draft.view(R * L, V), talon.view(R * L, V))
     K = 64
     lse = torch.empty(R * L, dtype=torch.float32, device=dev)
     ids = torch.empty(R * L, K, dtype=torch.int32, device=dev)
     lp = torch.empty(R * L, K, dtype=torch.float32, device=dev)
     ws_t = torch.empty(max(dt.workspace_size(dt.OP_TOPK, R * L, 1, V, K), 1), dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        dt.topk_logsoftmax(flat, K, ws=ws_t)
+    for i in range(4):
+        dt.topk_logsoftmax(flats[i % 2], K, ws=ws_t)
     torch.cuda.synchronize()
-    n_sweep = max(args.steps, 10)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(n_sweep):
-        dt.lib().dtree_topk_logsoftmax(flat.data_ptr(), 0, R * L, V, K, lse.data_ptr(), ids.data_ptr(),
-                                       lp.data_ptr(), ws_t.data_ptr(), ws_t.numel(), stream.cuda_stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    sweep_us = e0.elapsed_time(e1) * 1e3 / n_sweep
+
+    def sweep_us(n, alternate):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            x = flats[i % 2 if alternate else 0]
+            dt.lib().dtree_topk_logsoftmax(x.data_ptr(), 0, R * L, V, K, lse.data_ptr(), ids.data_ptr(),
+                                           lp.data_ptr(), ws_t.data_ptr(), ws_t.numel(), stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    n_sweep = max(2 * args.steps, 20)
+    sweep_alt = sweep_us(n_sweep, True)
+    sweep_same = sweep_us(n_sweep, False)
     alg_bytes = R * L * V * 2 + R * L * (4 + K * 8)
-    achieved = alg_bytes / (sweep_us * 1e-6) / 1e9
+    achieved = alg_bytes / (sweep_alt * 1e-6) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
@@ -168,7 +176,9 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "k_rowsweep<bf16> (dtree_topk_logsoftmax, R*L=1024 rows, K=64)",
-                "us_per_launch": round(sweep_us, 2), "alg_bytes_per_launch": alg_bytes}
+                "us_per_launch": round(sweep_alt, 2), "alg_bytes_per_launch": alg_bytes,
+                "launches": "alternating two distinct 311 MB tensors",
+                "us_per_launch_same_tensor": round(sweep_same, 2)}
 
     # ---- outside the step: exact target-sample matching (T = 1, one trial per round) on the
     # same trees and target rows, timed per call with events on this stream
@@ -250,6 +260,47 @@ def main():
     torch.cuda.synchronize()
     extra_ms["tdes_k32_b128"] = round(float(np.mean([es[i].elapsed_time(es[i + 1]) for i in range(5)])), 4)
 
+    # ---- single-round latency (R = 1): each builder and walk on the first round's inputs, the
+    # median over 50 calls of HIP events around the call (the GRAFT figure it compares with is
+    # a per-round overhead below 0.5 ms)
+    def one(t, cap):
+        return dt.Tree(*(x[0:1] for x in (t.parent, t.token, t.depth, t.score, t.mask, t.n_nodes)), cap)
+
+    r1 = dict(draft=draft[0:1], talon=talon[0:1], target=target[0:1], root=root[0:1], root_g=root_g[0:1])
+    tm1, td1, tg1, ts1, tt1 = (dt.Tree.empty(1, c, dev) for c in (64, 128, 60, 60, 128))
+    o1r = tuple(torch.empty(1, 1, dtype=torch.int32, device=dev) for _ in range(3))
+    w1 = {k: torch.empty(max(dt.workspace_size(*a), 1), dtype=torch.uint8, device=dev) for k, a in dict(
+        m=(dt.OP_MARGINAL, 1, L, V, 64, 64), d=(dt.OP_DEPTHWISE, 1, L, V, 8, 128, 32, 64, 1024),
+        g=(dt.OP_GATED, 1, L, V, 0, 60), s=(dt.OP_STATIC, 1, L, V, 10), e=(dt.OP_TDES, 1, L, V, 32),
+        a=(dt.OP_ACCEPT, 1, L, V, 0, 64)).items()}
+    tm_1 = one(t_m, 64)
+    ops1 = {
+        "marginal": lambda i: dt.build_tree_marginal(r1["draft"], 64, 64, 0.0, ws=w1["m"], out=tm1),
+        "depthwise": lambda i: dt.build_tree_depthwise(r1["draft"], E, U, P, r1["root"], 8, 32, 128, -0.5, ws=w1["d"],
+                                                       out=td1),
+        "gated": lambda i: dt.build_tree_gated(r1["talon"], 10, 0.03, 60, ws=w1["g"], out=tg1),
+        "static_k10_d6": lambda i: dt.build_tree_static(r1["talon"], 10, 6, ws=w1["s"], out=ts1),
+        "tdes_k32_b128": lambda i: dt.build_tree_tdes(r1["draft"], r1["root_g"], mlp, 32, 128, ws=w1["e"], out=tt1),
+        "accept_t0": lambda i: dt.accept_tree(tm_1, r1["target"], None, 0.0, synth.PHILOX_SEED, i, 1, ws=w1["a"],
+                                              outs=o1r),
+        "accept_t1": lambda i: dt.accept_tree(tm_1, r1["target"], r1["draft"], 1.0, synth.PHILOX_SEED, i, 1,
+                                              ws=w1["a"], outs=o1r),
+        "accept_match_t1": lambda i: dt.accept_tree_match(tm_1, r1["target"], 1.0, synth.PHILOX_SEED, i, 1,
+                                                          ws=w1["a"], outs=o1r),
+    }
+    r1_us = {}
+    for name, fn in ops1.items():
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            fn(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        r1_us[name] = round(float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3, 2)
+
     out = {
         "metric": "tree-build rounds/sec + us/round at V=151936,L=16,B=128; HBM GB/s vs peak",
         "value": round(value, 1), "unit": "rounds/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -264,6 +315,7 @@ def main():
         "event_ms_per_step": round(step_ms, 4),
         "roofline": roofline,
         "extra_ms": extra_ms,
+        "r1_latency_us": r1_us,
         "covered_draft_mass": mass,
     }
     if not args.no_cpu:
@@ -289,50 +341,117 @@ def traffic_probe(dt, synth, torch, np, dev):
                       "source_digest": sweep_source_digest()}), flush=True)
 
 
-def cpu_baseline(draft_h, talon_h, head, n_rounds=16):
-    """The oracle, as it stands, on a bounded sample: the first `n_rounds` rounds of the same
-    step (all five operations, each round's own inputs), float64 numpy on one thread."""
+_ORACLE = {}
+
+
+def _oracle_init(U_bits, P_bits):
+    """Worker set-up for the oracle leg: one BLAS thread, the head's U and P widened once."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
+        _ORACLE["limit"] = threadpool_limits(1)
     except Exception:  # pragma: no cover
-        threadpool_limits = None
+        pass
+    widen = lambda b: (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    _ORACLE["U"], _ORACLE["P"] = widen(U_bits), widen(P_bits)
+
+
+class _Rows:
+    """Rows of E gathered for one round, indexed like the full table."""
+
+    def __init__(self, toks, rows):
+        import numpy as np
+        self.at = {int(t): i for i, t in enumerate(toks)}
+        self.rows = (np.asarray(rows, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+    def __getitem__(self, idx):
+        import numpy as np
+        idx = np.atleast_1d(np.asarray(idx))
+        return self.rows[[self.at[int(t)] for t in idx]].astype(np.float64)
+
+
+def _oracle_round(args):
+    """One round of the whole step on the oracle, each operation timed on its own (seconds).
+    The round's target rows follow its marginal tree and are drawn untimed."""
+    import numpy as np
     import synth
     from oracle import accept, depthwise, gated, marginal, rowsweep
+    r, draft_r, talon_r, toks, erows, root_r = args
+    z = rowsweep.as_f64(draft_r, "bf16")
+    tal = rowsweep.as_f64(talon_r, "bf16")
+    out = {}
+    t0 = time.perf_counter()
+    tm = marginal.build_marginal(z, 64, 64, 0.0)
+    out["cfg2_marginal"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    depthwise.build_depthwise(z, _Rows(toks, erows), _ORACLE["U"], _ORACLE["P"], int(root_r), 8, 32, 128, -0.5)
+    out["cfg3_depthwise"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    gated.build_gated(tal, 10, float(np.float32(0.03)), 60, full_pool=False)
+    out["cfg4_gated"] = time.perf_counter() - t0
+    depth = np.array(tm.arrays(64)[2])[None, :]
+    tgt = rowsweep.as_f64(synth.verification_target(draft_r[None], depth, seed=5)[0], "bf16")
+    t0 = time.perf_counter()
+    accept.walk_greedy(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1])
+    out["cfg5_accept_t0"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    tab = accept.ResidualTables(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1], z, 1.0)
+    accept.walk_sampled(tab, tm.depth, synth.PHILOX_SEED, 0, r)
+    out["cfg5_accept_t1"] = time.perf_counter() - t0
+    return out
 
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    try:
-        E_h, U_h, P_h, root_h = head
-        U64 = synth.f32_from_bf16(U_h).astype(np.float64)
-        P64 = synth.f32_from_bf16(P_h).astype(np.float64)
 
-        class Rows:  # rows of E gathered on demand
-            def __getitem__(self, idx):
-                return synth.f32_from_bf16(E_h[idx]).astype(np.float64)
+def cpu_baseline(draft_h, talon_h, head, n_single=3, n_par=32):
+    """The oracle, as it stands, on a bounded sample of the same step: (1) n_single rounds one
+    after another in this process on one thread, each operation timed (ms per round per
+    config, and the tiny marginal config); (2) the first n_par rounds spread over
+    min(16, cpu count) worker processes, one round per task, one thread each: value = rounds
+    per second of the whole step, wall clock. float64 numpy throughout."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
 
-        elapsed = 0.0
-        for r in range(n_rounds):
-            z = rowsweep.as_f64(draft_h[r], "bf16")
-            tal = rowsweep.as_f64(talon_h[r], "bf16")
-            t0 = time.perf_counter()
-            tm = marginal.build_marginal(z, 64, 64, 0.0)
-            depthwise.build_depthwise(z, Rows(), U64, P64, int(root_h[r]), 8, 32, 128, -0.5)
-            gated.build_gated(tal, 10, float(np.float32(0.03)), 60, full_pool=False)
-            elapsed += time.perf_counter() - t0
-            # the target rows follow this round's marginal tree (input preparation, untimed)
-            depth = np.array(tm.arrays(64)[2])[None, :]
-            tgt = rowsweep.as_f64(synth.verification_target(draft_h[r:r + 1], depth, seed=5)[0], "bf16")
-            t0 = time.perf_counter()
-            accept.walk_greedy(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1])
-            tab = accept.ResidualTables(tm.parent, tm.token, tm.depth, tgt[:tm.n + 1], z, 1.0)
-            accept.walk_sampled(tab, tm.depth, synth.PHILOX_SEED, 0, r)
-            elapsed += time.perf_counter() - t0
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    return {"value": round(n_rounds / elapsed, 4), "unit": "rounds/s", "cores": 1, "kind": "oracle",
-            "sample": f"rounds 0..{n_rounds - 1} of the full step (marginal + depthwise + gated + accept T=0 "
-                      f"+ T=1 per round), float64 numpy, 1 thread; {elapsed:.2f} s"}
+    import numpy as np
+    import synth
+    from oracle import marginal, rowsweep
+
+    E_h, U_h, P_h, root_h = head
+
+    def task(r):
+        z = rowsweep.as_f64(draft_h[r], "bf16")
+        toks = {int(root_h[r])}
+        for d in range(z.shape[0]):
+            kth = np.partition(z[d], -8)[-8]
+            toks.update(int(t) for t in np.nonzero(z[d] >= kth)[0])
+        toks = sorted(toks)
+        return (r, draft_h[r], talon_h[r], toks, E_h[toks], int(root_h[r]))
+
+    # (1) one thread, rounds in sequence
+    _oracle_init(U_h, P_h)
+    single = [_oracle_round(task(r)) for r in range(n_single)]
+    per_cfg = {k: round(1e3 * float(np.mean([x[k] for x in single])), 2) for k in single[0]}
+    tiny = synth.tiny_marginal()
+    t0 = time.perf_counter()
+    for r in range(tiny.shape[0]):
+        marginal.build_marginal(rowsweep.as_f64(tiny[r], "f32"), 8, 8, 0.0)
+    per_cfg["cfg1_tiny_marginal"] = round(1e3 * (time.perf_counter() - t0) / tiny.shape[0], 3)
+    step_1core = sum(float(np.mean([x[k] for x in single])) for k in single[0])
+    _ORACLE.clear()
+    # (2) rounds in parallel
+    workers = max(1, min(16, os.cpu_count() or 1))
+    tasks = [task(r) for r in range(n_par)]
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"), initializer=_oracle_init,
+                                initargs=(U_h, P_h)) as pool:
+        list(pool.map(_oracle_round, tasks[:workers]))  # start-up and first imports, untimed
+        t0 = time.perf_counter()
+        list(pool.map(_oracle_round, tasks, chunksize=1))
+        wall = time.perf_counter() - t0
+    return {"value": round(n_par / wall, 4), "unit": "rounds/s", "cores": workers, "kind": "oracle",
+            "sample": f"rounds 0..{n_par - 1} of the full step (marginal + depthwise + gated + accept T=0 + T=1 per "
+                      f"round), one round per task over {workers} worker processes of one thread each, float64 "
+                      f"numpy; {wall:.2f} s wall",
+            "single_thread": {"rounds_per_s": round(1.0 / step_1core, 4), "cores": 1,
+                              "ms_per_round": per_cfg,
+                              "sample": f"rounds 0..{n_single - 1} in sequence, one thread; cfg1 over its 4 rounds"}}
 
 
 if __name__ == "__main__":
