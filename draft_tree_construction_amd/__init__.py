@@ -8,6 +8,7 @@ load, every call raises.
 Entry points (same names as the C ABI):
     topk_logsoftmax(logits, K)                          -> (lse, ids, lp)
     build_tree_marginal(logits, K, B, beta)             -> Tree
+    build_tree_marginal_noalloc(logits, K, B, beta, out) -> Tree (no workspace, no allocation)
     build_tree_depthwise(logits, E, U, P, root_tok, K, W, B, beta) -> Tree
     build_tree_gated(logits, K_root, mu, N)             -> Tree
     build_tree_static(logits, K, D)                     -> Tree  (K*D nodes)
@@ -35,7 +36,8 @@ STATUS = {0: "DTREE_OK", -1: "DTREE_E_INVAL", -2: "DTREE_E_BETA", -3: "DTREE_E_W
           -4: "DTREE_E_UNSUPPORTED", -5: "DTREE_E_HIP"}
 
 # every symbol include/dtree.h declares
-SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_depthwise",
+SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_marginal_noalloc",
+           "build_tree_depthwise",
            "build_tree_gated", "build_tree_static", "build_tree_tdes", "dtree_saba_budget", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
 
 
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.dtree_topk_logsoftmax.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.build_tree_marginal.restype = i32
     L.build_tree_marginal.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, ctypes.POINTER(CTree), vp, sz, vp]
+    L.build_tree_marginal_noalloc.restype = i32
+    L.build_tree_marginal_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, ctypes.POINTER(CTree), vp]
     L.build_tree_depthwise.restype = i32
     L.build_tree_depthwise.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32, f32,
                                        ctypes.POINTER(CTree), vp, sz, vp]
@@ -182,6 +186,17 @@ def build_tree_marginal(logits: torch.Tensor, K: int, B: int, beta: float, ws: t
     st = out.c_struct()
     _check(lib().build_tree_marginal(_ptr(logits), _dtype(logits), R, L, V, K, B, float(beta), ctypes.byref(st),
                                      _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def build_tree_marginal_noalloc(logits: torch.Tensor, K: int, B: int, beta: float, out: Tree) -> Tree:
+    """build_tree_marginal with the library's own per-device scratch (no workspace); `out`
+    must be given, so the call allocates nothing."""
+    _require_device(logits)
+    R, L, V = logits.shape
+    st = out.c_struct()
+    _check(lib().build_tree_marginal_noalloc(_ptr(logits), _dtype(logits), R, L, V, K, B, float(beta),
+                                             ctypes.byref(st), _stream(logits.device)))
     return out
 
 

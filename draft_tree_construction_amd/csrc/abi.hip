@@ -3,9 +3,15 @@
 // device->host copy); see include/dtree.h for the contract of each entry point.
 #include <math.h>
 #include <stdio.h>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
+
+// Scratch of build_tree_marginal_noalloc: one copy per device, kept until the process ends.
+// Host code never passes the array's name to a kernel (on the host it stands in for the
+// symbol, not a device address); it uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[DTREE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -62,6 +68,64 @@ dt::TreeOut tree_out(const dtree_tree *t) {
 }
 
 int marginal_k(int K, int B, int V) { return K == 0 ? (B < V ? B : V) : K; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up once per device.
+int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DTREE_E_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DTREE_OK;
+}
+
+// build_tree_marginal's checks and launches for a given workspace (null ws: the caller
+// supplies none and `scratch` is used, looked up after validation).
+int marginal_impl(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta, const dtree_tree *out,
+                  void *ws, size_t ws_bytes, bool use_scratch, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || B < 1 || K < 0) return fail(DTREE_E_INVAL, "need R >= 0, L, V, B >= 1, K >= 0");
+  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
+  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
+  const int k = marginal_k(K, B, V);
+  if (k > V) return fail(DTREE_E_INVAL, "K > V");
+  if (k > DTREE_MAX_K || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "K, B or L beyond the compiled envelope");
+  int rc = check_tree(out, B);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits) return fail(DTREE_E_INVAL, "logits is NULL");
+  const size_t need = a1_bytes(R * L, V, k);
+  if (use_scratch) {
+    if (need > (size_t)DTREE_NOALLOC_SCRATCH_BYTES)
+      return fail(DTREE_E_UNSUPPORTED, ("needs " + std::to_string(need) +
+                                        " bytes of scratch, more than DTREE_NOALLOC_SCRATCH_BYTES").c_str());
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    ws_bytes = DTREE_NOALLOC_SCRATCH_BYTES;
+  }
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(s);
+  A1Ws a = a1_carve(ws, R * L, k);
+  dt::RowOut o{a.lse, nullptr, a.ids, a.zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, k, o, a.rest, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_marginal (row sweep)");
+  e = dt::launch_marginal(a.zk, a.ids, a.lse, R, L, k, B, beta, tree_out(out), st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_marginal (top-B)");
+  return DTREE_OK;
+}
 int gated_k(int V) { return V < DTREE_MAX_K ? V : DTREE_MAX_K; }
 
 }  // namespace
@@ -130,29 +194,12 @@ int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K,
 
 int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta,
                         const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s) {
-  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
-  if (R < 0 || L < 1 || V < 1 || B < 1 || K < 0) return fail(DTREE_E_INVAL, "need R >= 0, L, V, B >= 1, K >= 0");
-  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
-  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
-  const int k = marginal_k(K, B, V);
-  if (k > V) return fail(DTREE_E_INVAL, "K > V");
-  if (k > DTREE_MAX_K || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
-    return fail(DTREE_E_UNSUPPORTED, "K, B or L beyond the compiled envelope");
-  int rc = check_tree(out, B);
-  if (rc) return rc;
-  if (R == 0) return DTREE_OK;
-  if (!logits) return fail(DTREE_E_INVAL, "logits is NULL");
-  const size_t need = a1_bytes(R * L, V, k);
-  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
-  hipStream_t st = static_cast<hipStream_t>(s);
-  A1Ws a = a1_carve(ws, R * L, k);
-  dt::RowOut o{a.lse, nullptr, a.ids, a.zk, nullptr};
-  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, k, o, a.rest, st);
-  if (e != hipSuccess) return hip_fail(e, "build_tree_marginal (row sweep)");
-  e = dt::launch_marginal(a.zk, a.ids, a.lse, R, L, k, B, beta, tree_out(out), st);
-  if (e != hipSuccess) return hip_fail(e, "build_tree_marginal (top-B)");
-  return DTREE_OK;
+  return marginal_impl(logits, dtype, R, L, V, K, B, beta, out, ws, ws_bytes, false, s);
+}
+
+int build_tree_marginal_noalloc(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta,
+                                const dtree_tree *out, dtree_stream_t s) {
+  return marginal_impl(logits, dtype, R, L, V, K, B, beta, out, nullptr, 0, true, s);
 }
 
 int build_tree_gated(const void *logits, int dtype, int R, int L, int V, int K_root, float mu, int N,

@@ -21,8 +21,9 @@
  *   - The caller owns every buffer, including the workspace `ws` of at least
  *     dtree_workspace_size(...) bytes, 256-byte aligned (as hipMalloc and torch allocations
  *     are; else DTREE_E_INVAL). The library never allocates or frees memory and holds no
- *     pointer after it returns; the only state kept between calls is a per-device cache of
- *     one occupancy query (how many workgroups of the acceptance walk fit at once).
+ *     pointer after it returns. State kept between calls: a per-device cache of one
+ *     occupancy query (how many workgroups of the acceptance walk fit at once), and the
+ *     per-device scratch array of build_tree_marginal_noalloc with its address.
  *   - Every call only enqueues kernels on stream `s` (a hipStream_t; NULL = null stream)
  *     and returns; results are valid once the stream reaches that point. Calls are
  *     reentrant; calls that share an output or workspace buffer must be ordered by the caller.
@@ -122,6 +123,21 @@ int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K,
  */
 int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta,
                         const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * build_tree_marginal without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, checks and results as build_tree_marginal; its scratch is a
+ * device array inside the library of DTREE_NOALLOC_SCRATCH_BYTES per device (held until the
+ * process ends), and the call allocates nothing. A call whose scratch need,
+ * dtree_workspace_size(DTREE_OP_MARGINAL, ...), exceeds that size returns
+ * DTREE_E_UNSUPPORTED (R * L = 1024 rows at K = 64 need about 0.5 MiB). All calls on one
+ * device share the array and nothing in it has to start at zero: calls that may overlap on
+ * one device (other streams, other threads) race on it and must be ordered by the caller.
+ */
+#define DTREE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int build_tree_marginal_noalloc(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta,
+                                const dtree_tree *out, dtree_stream_t s);
 
 /*
  * DARTree depth-wise super-tree + deferred Top-B (DARTree Algorithm 1) with a Markov

@@ -214,3 +214,18 @@ def test_topk_validation():
     assert call(dtype=5) == -1
     assert call(rows=2, V=151936, K=8) == -3   # split rows need a workspace
     assert call(rows=0) == 0
+
+
+def test_marginal_noalloc_validation():
+    """The no-workspace variant checks like build_tree_marginal and rejects a scratch need
+    beyond DTREE_NOALLOC_SCRATCH_BYTES (4 MiB) before touching the device."""
+    L = dt.lib()
+    def call(R=4, V=32, K=8, B=8, beta=0.0, t=None):
+        t = tree(B) if t is None else t
+        return L.build_tree_marginal_noalloc(FAKE, 0, R, 4 if V == 32 else 16, V, K, B, beta, ctypes.byref(t), None)
+    assert call(beta=0.5) == -2
+    assert call(K=33) == -1
+    assert call(B=129, t=tree(129)) == -4
+    assert call(R=4096, V=151936, K=64, B=64) == -4
+    assert b"DTREE_NOALLOC_SCRATCH_BYTES" in L.dtree_last_error()
+    assert call(R=0) == 0
