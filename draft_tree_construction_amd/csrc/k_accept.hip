@@ -44,6 +44,7 @@ constexpr int AC_WT = 256;         // threads per workgroup of the table walk
 constexpr int AC_NB = 2048;        // p/q bins of a node's residual support
 constexpr int AC_BSH = 16;         // bin width: 2^(23 - AC_BSH) = 128 bins per octave of p/q
 constexpr int AC_BINS_MIN = 3;     // children left to try that make a node build its bins
+constexpr int AC_NS = 4;           // workgroups per round of the one-trial walk at T > 0
 
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11).
@@ -971,6 +972,139 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
   }
 }
 
+// ---------------------------------------------------------------- merged bins (four-workgroup walk)
+// When a node of the four-workgroup walk has several children left after a rejection,
+// every workgroup sorts the members of S(t0) in its own range into ratio bins (as
+// wg_bins_build) and also records the exact per-bin sums of p and q (fixed point, see fx60).
+// It publishes its bin offsets and sums; one workgroup (the leader) then adds the four sets
+// of sums into suffix sums over the bins and answers every further C(t) of the node by
+// itself: the bins from bt + 2 up come whole from the suffix sums, and only the members of
+// bins bt - 1 .. bt + 1 (bt the query's bin) are tested, across the four ranges. A query
+// needs no exchange, so a node costs one exchange for the bins and one for the leader's
+// result however many of its children are rejected.
+struct CoopBins {
+  int *off;       // [R][AC_NS][AC_NB + 1]: each workgroup's bin offsets into its list slice
+  uint64_t *sum;  // [R][AC_NS][2][AC_NB]: each workgroup's per-bin sums of p and q
+};
+
+// wg_bins_build plus the per-bin sums (into bsP / bsQ, LDS) and their publication.
+template <typename T>
+DT_INLINE void wg_bins_build_publish(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t0,
+                                     Bins &bn, uint64_t *bsP, uint64_t *bsQ, int *gl_off, uint64_t *gl_sum,
+                                     Red &red) {
+  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) {
+    bn.cnt[i] = 0;
+    bsP[i] = 0ull;
+    bsQ[i] = 0ull;
+  }
+  bn.tbb = uni(__float_as_uint(t0));
+  __syncthreads();
+  stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = prob(za[e], nt), q = prob(zb[e], nd);
+      const int b = ratio_bin(p, q, bn.tbb);
+      if (in_s(p, q, t0)) atomicAdd(&bn.cnt[b], 1);
+    }
+  });
+  __syncthreads();
+  wg_scan_int(bn.cnt, bn.off, AC_NB, red);
+  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) bn.cnt[i] = bn.off[i];
+  __syncthreads();
+  stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = prob(za[e], nt), q = prob(zb[e], nd);
+      const int b = ratio_bin(p, q, bn.tbb);
+      if (in_s(p, q, t0)) {
+        bn.list[atomicAdd(&bn.cnt[b], 1)] = make_float2(p, q);
+        atomicAdd(reinterpret_cast<unsigned long long *>(&bsP[b]), (unsigned long long)fx60(p));
+        atomicAdd(reinterpret_cast<unsigned long long *>(&bsQ[b]), (unsigned long long)fx60(q));
+      }
+    }
+  });
+  __syncthreads();
+  for (int i = threadIdx.x; i <= AC_NB; i += AC_NT) gl_off[i] = bn.off[i];
+  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) {
+    gl_sum[i] = bsP[i];
+    gl_sum[AC_NB + i] = bsQ[i];
+  }
+  // the list slice, offsets and sums reach device scope before the exchange announces them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+
+// Suffix sums in place: a[b] <- sum of a[b .. n-1], a[n] = 0 (n = 2 AC_NT, exact).
+DT_INLINE void wg_suffix_u64(uint64_t *a, int n, Red &red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i0 = n - 2 - 2 * (int)threadIdx.x;  // thread k takes entries i0, i0 + 1 (from the top)
+  const uint64_t x0 = a[i0], x1 = a[i0 + 1];
+  const uint64_t s = x0 + x1;
+  uint64_t incl = s;  // inclusive prefix over threads 0..k (entries from the top down)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)incl, o, 64), hi = __shfl_up((uint32_t)(incl >> 32), o, 64);
+    if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
+  }
+  __syncthreads();
+  if (lane == 63) red.u[w] = incl;
+  __syncthreads();
+  uint64_t run = 0;
+  for (int i = 0; i < w; ++i) run += red.u[i];
+  run += incl - s;  // sum of the entries above i0 + 1
+  a[i0 + 1] = run + x1;
+  a[i0] = run + x1 + x0;
+  if (threadIdx.x == 0) a[n] = 0ull;
+  __syncthreads();
+}
+
+// Leader: the four workgroups' offsets into xoff, the summed per-bin sums as suffix sums.
+DT_INLINE void leader_merge(const int *gl_off_r, const uint64_t *gl_sum_r, int (*xoff)[AC_NB + 1], uint64_t *sufP,
+                            uint64_t *sufQ, Red &red) {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int i = threadIdx.x; i < AC_NS * (AC_NB + 1); i += AC_NT) xoff[i / (AC_NB + 1)][i % (AC_NB + 1)] = gl_off_r[i];
+  for (int b = threadIdx.x; b < AC_NB; b += AC_NT) {
+    uint64_t P = 0, Q = 0;
+#pragma unroll
+    for (int w = 0; w < AC_NS; ++w) {
+      P += gl_sum_r[(size_t)w * 2 * AC_NB + b];
+      Q += gl_sum_r[(size_t)w * 2 * AC_NB + AC_NB + b];
+    }
+    sufP[b] = P;
+    sufQ[b] = Q;
+  }
+  __syncthreads();
+  static_assert(AC_NB == 2 * AC_NT, "wg_suffix_u64 takes two entries per thread");
+  wg_suffix_u64(sufP, AC_NB, red);
+  wg_suffix_u64(sufQ, AC_NB, red);
+}
+
+// Leader: C(t) for t >= t0 from the merged bins (exact; see above). list_r is the round's
+// list area; workgroup w's slice starts at its first element, e0(w) = (nblk w / AC_NS) 64.
+DT_INLINE double leader_query(float t, uint32_t tbb, const int (*xoff)[AC_NB + 1], const uint64_t *sufP,
+                              const uint64_t *sufQ, const float2 *list_r, int nblk_all, Red &red) {
+  static_assert(AC_NS == 4, "the four ranges are spelled out");
+  const int bt = t_bin(t, tbb);
+  const int lo = max(bt - 1, 0), hi = min(bt + 1, AC_NB - 1);
+  // element offsets of the four ranges [xoff[w][lo], xoff[w][hi + 1]) in list_r, and their
+  // running lengths n1 <= n2 <= n3 <= n4
+  const int s0 = xoff[0][lo], s1 = (nblk_all * 1 / 4) * AC_BLK + xoff[1][lo];
+  const int s2 = (nblk_all * 2 / 4) * AC_BLK + xoff[2][lo], s3 = (nblk_all * 3 / 4) * AC_BLK + xoff[3][lo];
+  const int n1 = xoff[0][hi + 1] - xoff[0][lo];
+  const int n2 = n1 + xoff[1][hi + 1] - xoff[1][lo];
+  const int n3 = n2 + xoff[2][hi + 1] - xoff[2][lo];
+  const int n4 = n3 + xoff[3][hi + 1] - xoff[3][lo];
+  uint64_t v[2] = {0, 0};
+  for (int i = threadIdx.x; i < n4; i += AC_NT) {
+    const int at = i < n1 ? s0 + i : i < n2 ? s1 + (i - n1) : i < n3 ? s2 + (i - n2) : s3 + (i - n3);
+    const float2 x = list_r[at];
+    const bool m = in_s(x.x, x.y, t);
+    v[0] += m ? fx60(x.x) : 0ull;
+    v[1] += m ? fx60(x.y) : 0ull;
+  }
+  wg_sum_u64<2>(v, red);
+  return uni(c_from(sufP[hi + 1] + v[0], sufQ[hi + 1] + v[1], t));
+}
+
 // ---------------------------------------------------------------- cooperative walk (one trial, T > 0)
 // AC_NS workgroups per round, one per CU, each streaming its own contiguous range of whole
 // 64-token blocks of the two rows, so every pass takes a quarter of the time. After each
@@ -985,7 +1119,6 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
 // area, marks its round failed (err[r]); the round's other workgroups stop at their next
 // wait instead of polling to the bound, every workgroup of the round leaves the walk, and
 // the round's outputs are -1.
-constexpr int AC_NS = 4;          // workgroups per round
 constexpr int AC_XK = 4;          // exchanged values per workgroup and pass
 constexpr int AC_MAXPASS = 512;   // passes per round the exchange area holds
 constexpr uint64_t AC_SENT = ~0ull;
@@ -1021,7 +1154,7 @@ __global__ void k_accept_xch_init(uint64_t *slot, size_t n, int *err, int R) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, float2 *a_list) {
+__global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, float2 *a_list, CoopBins cb) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
   __shared__ int bcnt[AC_NB], boff[AC_NB + 1];
   __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1], sr[DTREE_MAX_CAP + 1], pv[DTREE_MAX_CAP + 1];
@@ -1029,6 +1162,8 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
   __shared__ float cz1[DTREE_MAX_CAP + 1], cz2[DTREE_MAX_CAP + 1], cu[DTREE_MAX_CAP + 1];
   __shared__ uint64_t got[AC_NS][AC_XK];
   __shared__ int xfail;
+  __shared__ uint64_t sufP[AC_NB + 1], sufQ[AC_NB + 1];  // per-bin sums, then (leader) suffix sums
+  __shared__ int xoff[AC_NS][AC_NB + 1];                 // leader: every workgroup's bin offsets
   extern __shared__ double dyn[];  // [nblk] prefix (double) then [nblk] block sums (float)
   const int r = blockIdx.x / AC_NS, q = blockIdx.x - r * AC_NS;
   const int cap = a.tree.cap;
@@ -1129,7 +1264,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
     const Norm nt = make_norm(s, la), nd = make_norm(s, lb);
     float t = 0.f;
     double C = 1.0;
-    bool built = false, blk_at_t = false;
+    bool blk_at_t = false;
     int nxt = -1;
     for (int c = fc[j]; c >= 0; c = ns[c]) {
       const float qv = prob(cz2[c], nd);
@@ -1142,20 +1277,58 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
       const float t2 = t + (float)C;
       int left = 0;
       for (int k = ns[c]; k >= 0 && left < AC_BINS_MIN; k = ns[k]) ++left;
-      uint64_t v[2];
-      if (built) {
-        (void)wg_bins_query(bn, t2, red);
-        v[0] = bn.Pt;
-        v[1] = bn.Qt;
-      } else if (left >= AC_BINS_MIN) {
-        (void)wg_bins_build(A, B, nt, nd, t2, bn, red);
-        built = true;
-        v[0] = bn.Pt;
-        v[1] = bn.Qt;
-      } else {
-        wg_c_sums(A, B, nt, nd, t2, blk, nblk, red, v[0], v[1]);
+      if (left >= AC_BINS_MIN) {
+        // merged bins: every workgroup bins its range, then the leader takes C(t2) and every
+        // remaining child of the node by itself and sends (accepted child, t, C, step)
+        int *gl_off = cb.off + ((size_t)r * AC_NS + q) * (AC_NB + 1);
+        uint64_t *gl_sum = cb.sum + ((size_t)r * AC_NS + q) * 2 * AC_NB;
+        wg_bins_build_publish(A, B, nt, nd, t2, bn, sufP, sufQ, gl_off, gl_sum, red);
+        const uint64_t dummy[1] = {0};
+        if (exchange(dummy, 1)) {
+          failed = true;
+          break;
+        }
+        uint64_t res[4] = {0, 0, 0, 0};
+        if (q == 0) {
+          leader_merge(cb.off + (size_t)r * AC_NS * (AC_NB + 1), cb.sum + (size_t)r * AC_NS * 2 * AC_NB, xoff, sufP,
+                       sufQ, red);
+          const float2 *list_r = a_list + (size_t)r * a.V;
+          float tt = t2;
+          for (int cc = c;;) {
+            const double C2 = leader_query(tt, bn.tbb, xoff, sufP, sufQ, list_r, nblk_all, red);
+            if (C2 > 0.0) {
+              t = tt;
+              C = C2;
+            }
+            cc = ns[cc];
+            if (cc < 0) break;
+            const float qc = prob(cz2[cc], nd);
+            const float pcc = resid(prob(cz1[cc], nt), qc, t) / (float)C;
+            ++step;
+            if (cu[cc] * qc < pcc) {
+              nxt = cc;
+              break;
+            }
+            tt = t + (float)C;
+          }
+          res[0] = (uint64_t)(uint32_t)nxt;
+          res[1] = (uint64_t)__float_as_uint(t);
+          res[2] = dbits(C);
+          res[3] = (uint64_t)step;
+        }
+        if (exchange(res, 4)) {
+          failed = true;
+          break;
+        }
+        nxt = (int)(uint32_t)got[0][0];
+        t = __uint_as_float((uint32_t)got[0][1]);
+        C = bitsd(got[0][2]);
+        step = (uint32_t)got[0][3];
+        blk_at_t = false;
+        break;
       }
-      const bool direct = !built;
+      uint64_t v[2];
+      wg_c_sums(A, B, nt, nd, t2, blk, nblk, red, v[0], v[1]);
       if (exchange(v, 2)) {
         failed = true;
         break;
@@ -1166,7 +1339,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
         Q += got[w][1];
       }
       const double C2 = c_from(P, Q, t2);
-      blk_at_t = direct && C2 > 0.0;
+      blk_at_t = C2 > 0.0;
       if (C2 > 0.0) {
         t = t2;
         C = C2;
@@ -1400,6 +1573,10 @@ static AccTables carve_tables(void *ws, int R, int V, int cap) {
 }
 
 static size_t xch_slots(int R) { return (size_t)R * AC_MAXPASS * AC_NS * AC_XK; }
+static size_t coop_off_bytes(int R) { return align256((size_t)R * AC_NS * (AC_NB + 1) * sizeof(int)); }
+static size_t coop_bins_bytes(int R) {
+  return coop_off_bytes(R) + align256((size_t)R * AC_NS * 2 * AC_NB * sizeof(uint64_t));
+}
 
 size_t accept_ws_bytes(int R, int L, int V, int cap) {
   (void)L;
@@ -1407,9 +1584,9 @@ size_t accept_ws_bytes(int R, int L, int V, int cap) {
   const int nblk = (V + AC_BLK - 1) / AC_BLK;
   const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
   const size_t lists = (size_t)R * V * sizeof(float2);  // the lazy walk's binned supports
-  // then the cooperative walk's exchange slots and per-round error flags
+  // then the cooperative walk's exchange slots, per-round error flags and merged-bin areas
   return align256(tables > lists ? tables : lists) + align256(xch_slots(R) * sizeof(uint64_t)) +
-         align256((size_t)R * sizeof(int));
+         align256((size_t)R * sizeof(int)) + coop_bins_bytes(R);
 }
 
 size_t accept_lds_bytes(int V) {
@@ -1467,15 +1644,19 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
         x.slot = reinterpret_cast<uint64_t *>(w);
         x.err = reinterpret_cast<int *>(w + align256(xch_slots(a.R) * sizeof(uint64_t)));
         x.spin = spin_limit();
+        char *wb = w + align256(xch_slots(a.R) * sizeof(uint64_t)) + align256((size_t)a.R * sizeof(int));
+        CoopBins cb;
+        cb.off = reinterpret_cast<int *>(wb);
+        cb.sum = reinterpret_cast<uint64_t *>(wb + coop_off_bytes(a.R));
         hipLaunchKernelGGL(k_accept_xch_init, dim3(256), dim3(256), 0, st, x.slot, xch_slots(a.R), x.err, a.R);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         float2 *lists_p = static_cast<float2 *>(ws);
         const dim3 grid((unsigned)(a.R * AC_NS)), block(AC_NT);
         if (a.dtype == DTREE_BF16)
-          hipLaunchKernelGGL(k_accept_coop<uint16_t>, grid, block, shm, st, a, x, lists_p);
+          hipLaunchKernelGGL(k_accept_coop<uint16_t>, grid, block, shm, st, a, x, lists_p, cb);
         else
-          hipLaunchKernelGGL(k_accept_coop<float>, grid, block, shm, st, a, x, lists_p);
+          hipLaunchKernelGGL(k_accept_coop<float>, grid, block, shm, st, a, x, lists_p, cb);
         return hipGetLastError();
       }
     }
