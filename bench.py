@@ -3,8 +3,9 @@
 One step = one pass of the whole hot path over a batch of R = 64 rounds
 (L = 16 draft positions, V = 151,936, bf16 logits, synthetic seeded inputs):
   1. build_tree_marginal   DDTree-shape logits, K = B = 64, beta = 0
-  2. build_tree_depthwise  same logits as base, Markov head E 151936x1024, U 16x1024x64,
-                           P 64x151936, K = 8, W = 32, B = 128, beta = -0.5
+  2. build_tree_depthwise_prepared  same logits as base, Markov head E 151936x1024,
+                           U 16x1024x64, P 64x151936 (its transposes prepared once before timing,
+                           as constant weights are), K = 8, W = 32, B = 128, beta = -0.5
   3. build_tree_gated      TALON-shape logits, K_root = 10, mu = 0.03, N = 60
   4. accept_tree T = 0     the step's marginal trees against draft-correlated target logits
   5. accept_tree T = 1     same, one Philox-seeded trial per round (trial index = step)
@@ -89,7 +90,9 @@ def main():
     root = torch.from_numpy(root_h).to(dev)
 
     ws_m = torch.empty(dt.workspace_size(dt.OP_MARGINAL, R, L, V, 64, 64), dtype=torch.uint8, device=dev)
-    ws_d = torch.empty(dt.workspace_size(dt.OP_DEPTHWISE, R, L, V, 8, 128, 32, 64, 1024), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(dt.workspace_size(dt.OP_DEPTHWISE_PREPARED, R, L, V, 8, 128, 32, 64, 1024), dtype=torch.uint8,
+                       device=dev)
+    head_d = dt.prepare_depthwise_head(U, P)  # constant weights: transposed once
     ws_g = torch.empty(dt.workspace_size(dt.OP_GATED, R, L, V, 0, 60), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(dt.workspace_size(dt.OP_ACCEPT, R, L, V, 0, 64), dtype=torch.uint8, device=dev)
     t_m, t_d, t_g = dt.Tree.empty(R, 64, dev), dt.Tree.empty(R, 128, dev), dt.Tree.empty(R, 60, dev)
@@ -111,7 +114,7 @@ def main():
         mark(0)
         dt.build_tree_marginal(draft, 64, 64, 0.0, ws=ws_m, out=t_m)
         mark(1)
-        dt.build_tree_depthwise(draft, E, U, P, root, 8, 32, 128, -0.5, ws=ws_d, out=t_d)
+        dt.build_tree_depthwise_prepared(draft, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_d, out=t_d)
         mark(2)
         dt.build_tree_gated(talon, 10, 0.03, 60, ws=ws_g, out=t_g)
         mark(3)
@@ -209,18 +212,27 @@ def main():
     t_w = dt.Tree.empty(R, 128, dev)
     extra_ms = {"accept_match_t1": round(match_ms, 4)}
     mass = {"pruned_w32_beta-0.5": round(covered(t_d, -0.5), 4)}
-    for name, W in (("exact_w128", 128), ("fixed_w8", 8)):
+
+    def timed(fn, n=5):
         for _ in range(2):
-            dt.build_tree_depthwise(draft, E, U, P, root, 8, W, 128, 0.0, ws=ws_w, out=t_w)
+            fn()
         torch.cuda.synchronize()
-        ew = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ew = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         ew[0].record(stream)
-        for i in range(5):
-            dt.build_tree_depthwise(draft, E, U, P, root, 8, W, 128, 0.0, ws=ws_w, out=t_w)
+        for i in range(n):
+            fn()
             ew[i + 1].record(stream)
         torch.cuda.synchronize()
-        extra_ms["depthwise_" + name] = round(float(np.mean([ew[i].elapsed_time(ew[i + 1]) for i in range(5)])), 4)
+        return round(float(np.mean([ew[i].elapsed_time(ew[i + 1]) for i in range(n)])), 4)
+
+    for name, W in (("exact_w128", 128), ("fixed_w8", 8)):
+        extra_ms["depthwise_" + name] = timed(lambda: dt.build_tree_depthwise_prepared(
+            draft, E, head_d, 1024, 64, root, 8, W, 128, 0.0, ws=ws_w, out=t_w))
         mass[name] = round(covered(t_w, 0.0), 4)
+    # the builder that also transposes the head on every call (build_tree_depthwise), W = 32
+    extra_ms["depthwise_w32_unprepared_head"] = timed(lambda: dt.build_tree_depthwise(
+        draft, E, U, P, root, 8, 32, 128, -0.5, ws=ws_w, out=t_w))
+    extra_ms["prepare_depthwise_head"] = timed(lambda: dt.prepare_depthwise_head(U, P, head=head_d))
 
     # ---- outside the step: the static D x K grid, K = 10, D = 6 (60 nodes, TALON's budget N),
     # on the TALON-shape logits: the fixed-shape builder of TALON's tree-build comparison,
@@ -270,14 +282,14 @@ def main():
     tm1, td1, tg1, ts1, tt1 = (dt.Tree.empty(1, c, dev) for c in (64, 128, 60, 60, 128))
     o1r = tuple(torch.empty(1, 1, dtype=torch.int32, device=dev) for _ in range(3))
     w1 = {k: torch.empty(max(dt.workspace_size(*a), 1), dtype=torch.uint8, device=dev) for k, a in dict(
-        m=(dt.OP_MARGINAL, 1, L, V, 64, 64), d=(dt.OP_DEPTHWISE, 1, L, V, 8, 128, 32, 64, 1024),
+        m=(dt.OP_MARGINAL, 1, L, V, 64, 64), d=(dt.OP_DEPTHWISE_PREPARED, 1, L, V, 8, 128, 32, 64, 1024),
         g=(dt.OP_GATED, 1, L, V, 0, 60), s=(dt.OP_STATIC, 1, L, V, 10), e=(dt.OP_TDES, 1, L, V, 32),
         a=(dt.OP_ACCEPT, 1, L, V, 0, 64)).items()}
     tm_1 = one(t_m, 64)
     ops1 = {
         "marginal": lambda i: dt.build_tree_marginal(r1["draft"], 64, 64, 0.0, ws=w1["m"], out=tm1),
-        "depthwise": lambda i: dt.build_tree_depthwise(r1["draft"], E, U, P, r1["root"], 8, 32, 128, -0.5, ws=w1["d"],
-                                                       out=td1),
+        "depthwise": lambda i: dt.build_tree_depthwise_prepared(r1["draft"], E, head_d, 1024, 64, r1["root"], 8, 32,
+                                                                128, -0.5, ws=w1["d"], out=td1),
         "gated": lambda i: dt.build_tree_gated(r1["talon"], 10, 0.03, 60, ws=w1["g"], out=tg1),
         "static_k10_d6": lambda i: dt.build_tree_static(r1["talon"], 10, 6, ws=w1["s"], out=ts1),
         "tdes_k32_b128": lambda i: dt.build_tree_tdes(r1["draft"], r1["root_g"], mlp, 32, 128, ws=w1["e"], out=tt1),
@@ -307,7 +319,7 @@ def main():
         "ms_per_step": round(ms_per_step, 4), "us_per_round": round(ms_per_step * 1e3 / R, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "R=64 rounds, L=16, V=151936 bf16: marginal K=B=64 + depthwise K=8,W=32,B=128,"
-                               "beta=-0.5,E 151936x1024,rank 64 + gated K_root=10,mu=0.03,N=60 + "
+                               "beta=-0.5,E 151936x1024,rank 64 (head prepared once) + gated K_root=10,mu=0.03,N=60 + "
                                "accept T=0 and T=1 (1 trial/round) on the marginal trees",
                    "rounds": R, "L": L, "V": V},
         "breakdown_us_per_round": {n: round(float(per[:, k].mean()) * 1e3 / R, 3) for k, n in enumerate(names)},

@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
     build_tree_marginal(logits, K, B, beta)             -> Tree
     build_tree_marginal_noalloc(logits, K, B, beta, out) -> Tree (no workspace, no allocation)
     build_tree_depthwise(logits, E, U, P, root_tok, K, W, B, beta) -> Tree
+    prepare_depthwise_head(U, P) -> head;  build_tree_depthwise_prepared(logits, E, head, d_model, rank,
+        root_tok, K, W, B, beta) -> Tree  (the head's transposes done once)
     build_tree_gated(logits, K_root, mu, N)             -> Tree
     build_tree_static(logits, K, D)                     -> Tree  (K*D nodes)
     build_tree_tdes(logits, root_tok, mlp, K, B, budget=None) -> Tree
@@ -31,13 +33,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdtree.so")
 
 DTREE_BF16, DTREE_F32 = 0, 1
-OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT, OP_STATIC, OP_TDES = range(7)
+OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT, OP_STATIC, OP_TDES, OP_DEPTHWISE_HEAD, \
+    OP_DEPTHWISE_PREPARED = range(9)
 STATUS = {0: "DTREE_OK", -1: "DTREE_E_INVAL", -2: "DTREE_E_BETA", -3: "DTREE_E_WORKSPACE",
           -4: "DTREE_E_UNSUPPORTED", -5: "DTREE_E_HIP"}
 
 # every symbol include/dtree.h declares
 SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_marginal_noalloc",
-           "build_tree_depthwise",
+           "build_tree_depthwise", "dtree_prepare_depthwise_head", "build_tree_depthwise_prepared",
            "build_tree_gated", "build_tree_static", "build_tree_tdes", "dtree_saba_budget", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
 
 
@@ -77,6 +80,11 @@ def lib() -> ctypes.CDLL:
     L.build_tree_depthwise.restype = i32
     L.build_tree_depthwise.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, i32, i32, i32, f32,
                                        ctypes.POINTER(CTree), vp, sz, vp]
+    L.dtree_prepare_depthwise_head.restype = i32
+    L.dtree_prepare_depthwise_head.argtypes = [vp, vp, i32, i32, i32, i32, vp, sz, vp]
+    L.build_tree_depthwise_prepared.restype = i32
+    L.build_tree_depthwise_prepared.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, i32, i32, i32, f32,
+                                                ctypes.POINTER(CTree), vp, sz, vp]
     L.build_tree_gated.restype = i32
     L.build_tree_gated.argtypes = [vp, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(CTree), vp, sz, vp]
     L.build_tree_static.restype = i32
@@ -219,6 +227,38 @@ def build_tree_depthwise(logits: torch.Tensor, E: torch.Tensor, U: torch.Tensor,
     _check(lib().build_tree_depthwise(_ptr(logits), _dtype(logits), R, L, V, _ptr(E), _ptr(U), _ptr(P), d_model, rank,
                                       _ptr(root_tok), K, W, B, float(beta), ctypes.byref(st), _ptr(ws), ws.numel(),
                                       _stream(dev)))
+    return out
+
+
+def prepare_depthwise_head(U: torch.Tensor, P: torch.Tensor, V: int | None = None,
+                           head: torch.Tensor | None = None) -> torch.Tensor:
+    """U [L, d_model, rank], P [rank, V] bf16 -> the prepared head (a uint8 device buffer)."""
+    _require_device(U, P)
+    L, d_model, rank = U.shape
+    V = P.shape[1] if V is None else V
+    dev = U.device
+    need = workspace_size(OP_DEPTHWISE_HEAD, 0, L, V, 0, 0, 0, rank, d_model)
+    head = _workspace(need, dev) if head is None else head
+    _check(lib().dtree_prepare_depthwise_head(_ptr(U), _ptr(P), L, V, d_model, rank, _ptr(head), head.numel(),
+                                              _stream(dev)))
+    return head
+
+
+def build_tree_depthwise_prepared(logits: torch.Tensor, E: torch.Tensor, head: torch.Tensor, d_model: int, rank: int,
+                                  root_tok: torch.Tensor, K: int, W: int, B: int, beta: float,
+                                  ws: torch.Tensor | None = None, out: Tree | None = None) -> Tree:
+    """build_tree_depthwise with a head from prepare_depthwise_head."""
+    _require_device(logits, E, head, root_tok)
+    if E.dtype != torch.bfloat16 or root_tok.dtype != torch.int32:
+        raise TypeError("E must be torch.bfloat16 and root_tok int32")
+    R, L, V = logits.shape
+    dev = logits.device
+    out = Tree.empty(R, B, dev) if out is None else out
+    ws = _workspace(workspace_size(OP_DEPTHWISE_PREPARED, R, L, V, K, B, W, rank, d_model), dev) if ws is None else ws
+    st = out.c_struct()
+    _check(lib().build_tree_depthwise_prepared(_ptr(logits), _dtype(logits), R, L, V, _ptr(E), _ptr(head), d_model,
+                                               rank, _ptr(root_tok), K, W, B, float(beta), ctypes.byref(st), _ptr(ws),
+                                               ws.numel(), _stream(dev)))
     return out
 
 

@@ -128,6 +128,38 @@ int marginal_impl(const void *logits, int dtype, int R, int L, int V, int K, int
 }
 int gated_k(int V) { return V < DTREE_MAX_K ? V : DTREE_MAX_K; }
 
+// build_tree_depthwise with the head either prepared (head) or made in the workspace (U, P).
+int depthwise_impl(const void *logits, int dtype, int R, int L, int V, const uint16_t *E, const uint16_t *U,
+                   const uint16_t *P, const void *head, int d_model, int rank, const int32_t *root_tok, int K, int W,
+                   int B, float beta, const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || K < 1 || K > V || W < 1 || B < 1 || d_model < 1 || rank < 1)
+    return fail(DTREE_E_INVAL, "need R >= 0, L, V, W, B, d_model, rank >= 1, 1 <= K <= V");
+  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
+  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
+  if (rank != 64 || d_model % 64 != 0 || K > DTREE_MAX_K || W > 128 || W * K > 1024 || L * W > 2048 ||
+      B > DTREE_MAX_CAP || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "rank, d_model, K, W, B or L beyond the compiled envelope");
+  int rc = check_tree(out, B);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits || !E || !root_tok) return fail(DTREE_E_INVAL, "an input pointer is NULL");
+  if ((uintptr_t)E & 15) return fail(DTREE_E_INVAL, "E, U and P must be 16-byte aligned");
+  const size_t need = a1_bytes(R * L, V, K) + (head ? dt::depthwise_call_bytes(R, L, V, K, W, B, d_model)
+                                                    : dt::depthwise_ws_bytes(R, L, V, K, W, B, rank, d_model));
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(s);
+  A1Ws a1 = a1_carve(ws, R * L, K);
+  dt::RowOut o{a1.lse, nullptr, a1.ids, a1.zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, K, o, a1.rest, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise (row sweep)");
+  dt::DepthwiseArgs a{logits, dtype, R, L, V, K, W, B, d_model, rank, beta, E, U, P, root_tok};
+  e = dt::launch_depthwise(a, a1.zk, a1.ids, tree_out(out), static_cast<char *>(ws) + a1_bytes(R * L, V, K), head, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise");
+  return DTREE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +194,12 @@ size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int 
     case DTREE_OP_DEPTHWISE:
       if (K < 1 || W < 1 || B_or_N < 1 || d_model < 1) return 0;
       return a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B_or_N, rank, d_model);
+    case DTREE_OP_DEPTHWISE_HEAD:
+      if (d_model < 1) return 0;
+      return dt::depthwise_head_bytes(L, V, d_model);
+    case DTREE_OP_DEPTHWISE_PREPARED:
+      if (K < 1 || W < 1 || B_or_N < 1 || d_model < 1) return 0;
+      return a1_bytes(R * L, V, K) + dt::depthwise_call_bytes(R, L, V, K, W, B_or_N, d_model);
     case DTREE_OP_STATIC:
       if (K < 1) return 0;
       return a1_bytes(R * L, V, K);
@@ -304,31 +342,35 @@ int dtree_saba_budget(double a, double beta, double c_verify, double c_fixed, in
 int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, const uint16_t *E, const uint16_t *U,
                          const uint16_t *P, int d_model, int rank, const int32_t *root_tok, int K, int W, int B,
                          float beta, const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s) {
-  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
-  if (R < 0 || L < 1 || V < 1 || K < 1 || K > V || W < 1 || B < 1 || d_model < 1 || rank < 1)
-    return fail(DTREE_E_INVAL, "need R >= 0, L, V, W, B, d_model, rank >= 1, 1 <= K <= V");
-  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
-  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
-  if (rank != 64 || d_model % 64 != 0 || K > DTREE_MAX_K || W > 128 || W * K > 1024 || L * W > 2048 ||
-      B > DTREE_MAX_CAP || L > DTREE_MAX_L)
-    return fail(DTREE_E_UNSUPPORTED, "rank, d_model, K, W, B or L beyond the compiled envelope");
-  int rc = check_tree(out, B);
-  if (rc) return rc;
-  if (R == 0) return DTREE_OK;
-  if (!logits || !E || !U || !P || !root_tok) return fail(DTREE_E_INVAL, "an input pointer is NULL");
-  if (((uintptr_t)E | (uintptr_t)U | (uintptr_t)P) & 15) return fail(DTREE_E_INVAL, "E, U and P must be 16-byte aligned");
-  const size_t need = a1_bytes(R * L, V, K) + dt::depthwise_ws_bytes(R, L, V, K, W, B, rank, d_model);
-  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
-  hipStream_t st = static_cast<hipStream_t>(s);
-  A1Ws a1 = a1_carve(ws, R * L, K);
-  dt::RowOut o{a1.lse, nullptr, a1.ids, a1.zk, nullptr};
-  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, K, o, a1.rest, st);
-  if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise (row sweep)");
-  dt::DepthwiseArgs a{logits, dtype, R, L, V, K, W, B, d_model, rank, beta, E, U, P, root_tok};
-  e = dt::launch_depthwise(a, a1.zk, a1.ids, tree_out(out), static_cast<char *>(ws) + a1_bytes(R * L, V, K), st);
-  if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise");
+  if (!U || !P) return fail(DTREE_E_INVAL, "an input pointer is NULL");
+  if (((uintptr_t)U | (uintptr_t)P) & 15) return fail(DTREE_E_INVAL, "E, U and P must be 16-byte aligned");
+  return depthwise_impl(logits, dtype, R, L, V, E, U, P, nullptr, d_model, rank, root_tok, K, W, B, beta, out, ws,
+                        ws_bytes, s);
+}
+
+int dtree_prepare_depthwise_head(const uint16_t *U, const uint16_t *P, int L, int V, int d_model, int rank,
+                                 void *head, size_t head_bytes, dtree_stream_t s) {
+  if (L < 1 || V < 1 || d_model < 1 || rank < 1) return fail(DTREE_E_INVAL, "need L, V, d_model, rank >= 1");
+  if (rank != 64 || d_model % 64 != 0 || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "rank, d_model or L beyond the compiled envelope");
+  if (!U || !P) return fail(DTREE_E_INVAL, "U or P is NULL");
+  if (((uintptr_t)U | (uintptr_t)P) & 15) return fail(DTREE_E_INVAL, "U and P must be 16-byte aligned");
+  const size_t need = dt::depthwise_head_bytes(L, V, d_model);
+  if (!head || head_bytes < need) return fail(DTREE_E_WORKSPACE, "head buffer too small");
+  if (reinterpret_cast<uintptr_t>(head) & 255) return fail(DTREE_E_INVAL, "head must be 256-byte aligned");
+  hipError_t e = dt::launch_depthwise_head(U, P, L, V, d_model, head, static_cast<hipStream_t>(s));
+  if (e != hipSuccess) return hip_fail(e, "dtree_prepare_depthwise_head");
   return DTREE_OK;
+}
+
+int build_tree_depthwise_prepared(const void *logits, int dtype, int R, int L, int V, const uint16_t *E,
+                                  const void *head, int d_model, int rank, const int32_t *root_tok, int K, int W,
+                                  int B, float beta, const dtree_tree *out, void *ws, size_t ws_bytes,
+                                  dtree_stream_t s) {
+  if (!head) return fail(DTREE_E_INVAL, "head is NULL");
+  if (reinterpret_cast<uintptr_t>(head) & 255) return fail(DTREE_E_INVAL, "head must be 256-byte aligned");
+  return depthwise_impl(logits, dtype, R, L, V, E, nullptr, nullptr, head, d_model, rank, root_tok, K, W, B, beta, out,
+                        ws, ws_bytes, s);
 }
 
 int accept_tree(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype, int R,

@@ -854,8 +854,12 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
 }
 
 // ---------------------------------------------------------------- host side
+// Workspace layout. The head part (P^T, U^T and the column bounds of P) depends only on the
+// weights; the rest is per call.
 struct DwLayout {
-  size_t PT, UT, pmax, pm_part, hx, bref, wide, part_s, part_m, lq, total;
+  size_t PT, UT, pmax, pm_part, head;         // offsets into the head part, and its size
+  size_t hx, bref, wide, part_s, part_m, lq;  // offsets into the per-call part
+  size_t calls;                               // size of the per-call part
 };
 
 static DwLayout dw_layout(const DwDims &g) {
@@ -870,31 +874,56 @@ static DwLayout dw_layout(const DwDims &g) {
   l.UT = take((size_t)g.L * 64 * g.dm * 2);
   l.pmax = take(64 * sizeof(float));
   l.pm_part = take((size_t)((g.V + DW_TP - 1) / DW_TP) * 64 * sizeof(float));
+  l.head = o;
+  o = 0;
   l.hx = take((size_t)g.S * DW_HX * 2);
   l.bref = take((size_t)g.S * sizeof(float));
   l.wide = take((size_t)g.ntile * sizeof(int));
   l.part_s = take((size_t)g.S * DW_NC * sizeof(double));
   l.part_m = take((size_t)g.S * DW_NC * sizeof(float));
   l.lq = take((size_t)g.S * g.K * sizeof(double));
-  l.total = o;
+  l.calls = o;
   return l;
 }
 
 size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank, int dm) {
   (void)rank;
-  return dw_layout(dw_dims(R, L, V, K, W, B, dm)).total;
+  const DwLayout l = dw_layout(dw_dims(R, L, V, K, W, B, dm));
+  return l.head + l.calls;
+}
+size_t depthwise_head_bytes(int L, int V, int dm) { return dw_layout(dw_dims(1, L, V, 1, 1, 1, dm)).head; }
+size_t depthwise_call_bytes(int R, int L, int V, int K, int W, int B, int dm) {
+  return dw_layout(dw_dims(R, L, V, K, W, B, dm)).calls;
+}
+
+// P^T, U^T and the column bounds of P into a head area (two launches).
+static hipError_t launch_head(const uint16_t *U, const uint16_t *P, int L, int V, int dm, char *h, const DwLayout &l,
+                              hipStream_t st) {
+  const int ntp = (V + DW_TP - 1) / DW_TP;
+  uint16_t *PT = reinterpret_cast<uint16_t *>(h + l.PT), *UT = reinterpret_cast<uint16_t *>(h + l.UT);
+  float *pmax = reinterpret_cast<float *>(h + l.pmax), *pm_part = reinterpret_cast<float *>(h + l.pm_part);
+  hipLaunchKernelGGL(k_dw_transpose_p, dim3(ntp), dim3(DW_NT), 0, st, P, V, PT, pm_part);
+  hipLaunchKernelGGL(k_dw_transpose_u, dim3(dm / 64, L + 1), dim3(DW_NT), 0, st, U, dm, L, UT, pm_part, ntp, pmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_depthwise_head(const uint16_t *U, const uint16_t *P, int L, int V, int dm, void *head,
+                                 hipStream_t st) {
+  return launch_head(U, P, L, V, dm, static_cast<char *>(head), dw_layout(dw_dims(1, L, V, 1, 1, 1, dm)), st);
 }
 
 hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
-                            void *ws, hipStream_t st) {
+                            void *ws, const void *head, hipStream_t st) {
   const DwDims g = dw_dims(a.R, a.L, a.V, a.K, a.W, a.B, a.dm);
   const DwLayout l = dw_layout(g);
-  char *w = static_cast<char *>(ws);
+  // without a prepared head, the head part leads the workspace and is written first
+  char *h = head ? static_cast<char *>(const_cast<void *>(head)) : static_cast<char *>(ws);
+  char *w = head ? static_cast<char *>(ws) : static_cast<char *>(ws) + l.head;
   DwState s;
-  s.PT = reinterpret_cast<uint16_t *>(w + l.PT);
-  s.UT = reinterpret_cast<uint16_t *>(w + l.UT);
-  s.pmax = reinterpret_cast<float *>(w + l.pmax);
-  s.pm_part = reinterpret_cast<float *>(w + l.pm_part);
+  s.PT = reinterpret_cast<uint16_t *>(h + l.PT);
+  s.UT = reinterpret_cast<uint16_t *>(h + l.UT);
+  s.pmax = reinterpret_cast<float *>(h + l.pmax);
+  s.pm_part = reinterpret_cast<float *>(h + l.pm_part);
   s.hx = reinterpret_cast<uint16_t *>(w + l.hx);
   s.bref = reinterpret_cast<float *>(w + l.bref);
   s.wide = reinterpret_cast<int *>(w + l.wide);
@@ -908,10 +937,10 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   dv.root_tok = a.root_tok;
   dv.beta = a.beta;
 
-  const int ntp = (a.V + DW_TP - 1) / DW_TP;
-  hipLaunchKernelGGL(k_dw_transpose_p, dim3(ntp), dim3(DW_NT), 0, st, a.P, a.V, s.PT, s.pm_part);
-  hipLaunchKernelGGL(k_dw_transpose_u, dim3(a.dm / 64, a.L + 1), dim3(DW_NT), 0, st, a.U, a.dm, a.L, s.UT, s.pm_part,
-                     ntp, s.pmax);
+  if (!head) {
+    const hipError_t e = launch_head(a.U, a.P, a.L, a.V, a.dm, h, l, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_dw_states, dim3(g.ntile), dim3(DW_NT), 0, st, s, dv, g, a.dtype == DTREE_BF16 ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -68,8 +68,13 @@ struct DepthwiseArgs {
   const int32_t *root_tok;
 };
 size_t depthwise_ws_bytes(int R, int L, int V, int K, int W, int B, int rank, int dm);
+size_t depthwise_head_bytes(int L, int V, int dm);                                  // the prepared head
+size_t depthwise_call_bytes(int R, int L, int V, int K, int W, int B, int dm);     // the rest
+hipError_t launch_depthwise_head(const uint16_t *U, const uint16_t *P, int L, int V, int dm, void *head,
+                                 hipStream_t st);
+// head == null: the head is prepared in the workspace first (its first depthwise_head_bytes)
 hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
-                            void *ws, hipStream_t st);
+                            void *ws, const void *head, hipStream_t st);
 
 // ---- a7: acceptance walk ------------------------------------------------------------------------
 struct AcceptArgs {

@@ -77,7 +77,9 @@ enum dtree_op {
   DTREE_OP_GATED = 3,
   DTREE_OP_ACCEPT = 4,
   DTREE_OP_STATIC = 5,
-  DTREE_OP_TDES = 6
+  DTREE_OP_TDES = 6,
+  DTREE_OP_DEPTHWISE_HEAD = 7,     /* the prepared correction head of dtree_prepare_depthwise_head */
+  DTREE_OP_DEPTHWISE_PREPARED = 8  /* the workspace of build_tree_depthwise_prepared */
 };
 
 /* Compiled envelope (DTREE_E_UNSUPPORTED beyond it). */
@@ -99,8 +101,9 @@ typedef struct {
 /*
  * Bytes of workspace an operation needs. `op` is a dtree_op; unused size arguments are
  * ignored: TOPK(rows = R*L, V, K), MARGINAL(R, L, V, K, B), DEPTHWISE(R, L, V, K, B, W,
- * rank, d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap), STATIC(R, L, V, K), TDES(R, L, V, K). Returns 0
- * for an unknown op or invalid sizes.
+ * rank, d_model), DEPTHWISE_HEAD(L, V, d_model), DEPTHWISE_PREPARED(R, L, V, K, B, W, rank,
+ * d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap), STATIC(R, L, V, K),
+ * TDES(R, L, V, K). Returns 0 for an unknown op or invalid sizes.
  */
 size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank, int d_model);
 
@@ -157,6 +160,25 @@ int build_tree_depthwise(const void *logits, int dtype, int R, int L, int V, con
                          const uint16_t *U, const uint16_t *P, int d_model, int rank,
                          const int32_t *root_tok, int K, int W, int B, float beta,
                          const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * The depth-wise builder with its correction head prepared once (DARTree Algorithm 1 steps
+ * 5-6: the head's weights are the same for every round and call). dtree_prepare_depthwise_head
+ * writes P transposed (token-major, 128 bytes per token, as the correction sweep reads it), U
+ * transposed per depth and the column bounds max_v |P[j][v]| into `head`, a caller-owned
+ * device buffer of dtree_workspace_size(DTREE_OP_DEPTHWISE_HEAD, 0, L, V, 0, 0, 0, rank,
+ * d_model) bytes, 256-byte aligned. build_tree_depthwise_prepared then takes `head` instead of
+ * U and P and gives the same tree as build_tree_depthwise; its workspace is
+ * dtree_workspace_size(DTREE_OP_DEPTHWISE_PREPARED, ...). The head must come from the same
+ * U, P, L, V, d_model and rank (not checked); it is only read, so many calls may share it.
+ * Same envelope and errors as build_tree_depthwise (head NULL or misaligned: DTREE_E_INVAL).
+ */
+int dtree_prepare_depthwise_head(const uint16_t *U, const uint16_t *P, int L, int V, int d_model, int rank,
+                                 void *head, size_t head_bytes, dtree_stream_t s);
+int build_tree_depthwise_prepared(const void *logits, int dtype, int R, int L, int V, const uint16_t *E,
+                                  const void *head, int d_model, int rank, const int32_t *root_tok, int K, int W,
+                                  int B, float beta, const dtree_tree *out, void *ws, size_t ws_bytes,
+                                  dtree_stream_t s);
 
 /*
  * TALON gated tree (TALON key designs 1-2): the root's children are the top K_root

@@ -229,3 +229,30 @@ def test_marginal_noalloc_validation():
     assert call(R=4096, V=151936, K=64, B=64) == -4
     assert b"DTREE_NOALLOC_SCRATCH_BYTES" in L.dtree_last_error()
     assert call(R=0) == 0
+
+
+def test_depthwise_head_validation():
+    L = dt.lib()
+    ws = dt.workspace_size
+    assert ws(dt.OP_DEPTHWISE_HEAD, 0, 16, 151936, 0, 0, 0, 64, 1024) >= 151936 * 128
+    full = ws(dt.OP_DEPTHWISE, 64, 16, 151936, 8, 128, 32, 64, 1024)
+    prep = ws(dt.OP_DEPTHWISE_PREPARED, 64, 16, 151936, 8, 128, 32, 64, 1024)
+    head = ws(dt.OP_DEPTHWISE_HEAD, 0, 16, 151936, 0, 0, 0, 64, 1024)
+    assert prep > 0 and prep + head == full
+    def prep_call(rank=64, dm=1024, nbytes=1 << 40, head=FAKE2):
+        return L.dtree_prepare_depthwise_head(FAKE2, FAKE2, 16, 151936, dm, rank, head, nbytes, None)
+    assert prep_call(rank=32) == -4
+    assert prep_call(dm=100) == -4
+    assert prep_call(nbytes=10) == -3
+    assert prep_call(head=None) == -3
+    assert prep_call(head=ctypes.c_void_p(0x1010)) == -1
+    t = tree(128)
+    def build(head=FAKE2, beta=-0.5, nbytes=0):
+        return L.build_tree_depthwise_prepared(FAKE2, 0, 4, 16, 1000, FAKE2, head, 1024, 64, FAKE2, 8, 32, 128, beta,
+                                               ctypes.byref(t), FAKE2, nbytes, None)
+    assert build(head=None) == -1
+    assert build(beta=0.5) == -2
+    assert build() == -3
+
+
+FAKE2 = ctypes.c_void_p(0x100000)  # 256-byte aligned, never dereferenced

@@ -164,3 +164,25 @@ def test_depthwise_full_config_exact_best_first():
     oracle, invariants on all 64."""
     exact, near = check_full(8, 128, 128, 0.0, list(range(3, 64, 8)))
     assert exact >= 6, (exact, near)
+
+
+@pytest.mark.parametrize("R,L,V,dm,K,W,B,beta,seed", [
+    (3, 6, 1001, 64, 8, 32, 60, -0.5, 21),            # ragged V
+    (64, 16, 151936, 1024, 8, 32, 128, -0.5, 3),      # the DARTree config
+])
+def test_depthwise_prepared_head_gives_the_same_tree(R, L, V, dm, K, W, B, beta, seed):
+    """The head prepared once (P^T, U^T, column bounds) and reused over two calls gives the
+    builder's tree exactly, on a small ragged shape and the full DARTree config."""
+    if V == 151936:
+        base, (E, U, P, root) = full_head()
+    else:
+        base = synth.ddtree_logits(seed=seed, R=R, L=L, V=V)
+        E, U, P, root = synth.correction_head(seed=100 + seed, R=R, L=L, V=V, d_model=dm, rank=64)
+    bd = dev_bf16(base)
+    Ed, Ud, Pd, rd = head_to_device(E, U, P, root)
+    want = tree_to_host(dt.build_tree_depthwise(bd, Ed, Ud, Pd, rd, K, W, B, beta))
+    head = dt.prepare_depthwise_head(Ud, Pd)
+    for _ in range(2):
+        got = tree_to_host(dt.build_tree_depthwise_prepared(bd, Ed, head, dm, 64, rd, K, W, B, beta))
+        for k in ("parent", "token", "depth", "mask", "n", "score"):
+            np.testing.assert_array_equal(got[k], want[k], err_msg=k)
