@@ -50,15 +50,18 @@ size_t tdes_lds_bytes(int K, int H) {
 
 // K x K edge table, each thread a T x T tile: per hidden unit T parent and T child values
 // (contiguous in the padded rows) and T * T ReLU-FMAs.
+// The second layer accumulates in float64 and the score is rounded to float once, so an edge
+// is within half an ulp of its float64 value (the first layer's inputs are the projections,
+// themselves summed in float64 and rounded once).
 template <int T>
-DT_INLINE void edge_table(const float *sAp, const float *sAc, const float *sw, const float *slp, float *sS, int K,
+DT_INLINE void edge_table(const float *sAp, const float *sAc, const float *sw, const double *slp, float *sS, int K,
                           int kp, int np, int H, float s, float b0) {
   const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
-  float acc[T][T];
+  double acc[T][T];
 #pragma unroll
   for (int a = 0; a < T; ++a)
 #pragma unroll
-    for (int c = 0; c < T; ++c) acc[a][c] = 0.f;
+    for (int c = 0; c < T; ++c) acc[a][c] = 0.0;
   for (int h = 0; h < H; ++h) {
     const float *ap = sAp + (size_t)h * kp + ty * T;
     const float *ac = sAc + (size_t)h * kp + tx * T;
@@ -68,18 +71,18 @@ DT_INLINE void edge_table(const float *sAp, const float *sAc, const float *sw, c
       x[a] = ap[a];
       y[a] = ac[a];
     }
-    const float ww = sw[h];
+    const double ww = (double)sw[h];
 #pragma unroll
     for (int a = 0; a < T; ++a)
 #pragma unroll
-      for (int c = 0; c < T; ++c) acc[a][c] += ww * fmaxf(x[a] + y[c], 0.f);
+      for (int c = 0; c < T; ++c) acc[a][c] = __builtin_fma(ww, (double)fmaxf(x[a] + y[c], 0.f), acc[a][c]);
   }
 #pragma unroll
   for (int a = 0; a < T; ++a)
 #pragma unroll
     for (int c = 0; c < T; ++c) {
       const int pi = ty * T + a, ci = tx * T + c;
-      if (pi < np && ci < K) sS[pi * (K + 1) + ci] = slp[ci] + s * (acc[a][c] + b0);
+      if (pi < np && ci < K) sS[pi * (K + 1) + ci] = (float)(slp[ci] + (double)s * (acc[a][c] + (double)b0));
     }
 }
 
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(TD_NT) void k_tdes_edges(const float *__restrict__ 
   float4 *sG = reinterpret_cast<float4 *>(sAc + (size_t)p.H * kp);  // [2][K][TD_EMAX / 4]
   float *sS = reinterpret_cast<float *>(sG);        // [K][K + 1], after the projections
   __shared__ float sw[TD_HMAX];
-  __shared__ float slp[TD_KMAX];
+  __shared__ double slp[TD_KMAX];
 
   const int rd = blockIdx.x;  // round * L + position; the children sit at depth d + 1
   const int r = rd / L, d = rd - r * L;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(TD_NT) void k_tdes_edges(const float *__restrict__ 
     sG[(K + ci) * E4 + q] = reinterpret_cast<const float4 *>(p.Gc + (size_t)tok * p.hc)[q];
   }
   for (int i = tid; i < p.H; i += TD_NT) sw[i] = p.w[i];
-  for (int i = tid; i < K; i += TD_NT) slp[i] = (float)((double)zk[(size_t)rd * K + i] - lse[rd]);
+  for (int i = tid; i < K; i += TD_NT) slp[i] = (double)zk[(size_t)rd * K + i] - lse[rd];
   __syncthreads();
 
   // projections: threads [0, 128) take the parents, [128, 256) the children; one hidden
@@ -135,30 +138,31 @@ __global__ __launch_bounds__(TD_NT) void k_tdes_edges(const float *__restrict__ 
         const float4 t = wr[q < n4 ? q : n4 - 1];
         wv[q] = q < n4 ? t : zero;
       }
-      float cd = 0.f;
+      // float64 sums, one rounding to float per projection
+      auto dot4 = [](const float4 &u, const float4 &v) {
+        return __builtin_fma((double)u.x, (double)v.x, __builtin_fma((double)u.y, (double)v.y,
+               __builtin_fma((double)u.z, (double)v.z, (double)u.w * (double)v.w)));
+      };
+      double cd = 0.0;
       if (side) {
         const float4 *wd = reinterpret_cast<const float4 *>(p.W + (size_t)h * ld + p.hp + p.hc);
         const float4 *ed = reinterpret_cast<const float4 *>(p.Ed + (size_t)d * p.hd);
 #pragma unroll
         for (int q = 0; q < E4; ++q) {
           const int qq = q < hd4 ? q : hd4 - 1;
-          const float4 a = wd[qq], e = ed[qq];
-          const float t = a.x * e.x + a.y * e.y + a.z * e.z + a.w * e.w;
-          cd += q < hd4 ? t : 0.f;
+          const double t = dot4(wd[qq], ed[qq]);
+          cd += q < hd4 ? t : 0.0;
         }
-        cd += p.b[h];
+        cd += (double)p.b[h];
       }
       const int nt = side ? K : np;
       const float4 *g = sG + (side ? K * E4 : 0);
       float *dst = (side ? sAc : sAp) + (size_t)h * kp;
       for (int t = 0; t < nt; ++t) {
-        float a = 0.f;
+        double a = 0.0;
 #pragma unroll
-        for (int q = 0; q < E4; ++q) {
-          const float4 x = g[t * E4 + (q < n4 ? q : n4 - 1)];
-          a += wv[q].x * x.x + wv[q].y * x.y + wv[q].z * x.z + wv[q].w * x.w;
-        }
-        dst[t] = a + cd;
+        for (int q = 0; q < E4; ++q) a += dot4(wv[q], g[t * E4 + (q < n4 ? q : n4 - 1)]);
+        dst[t] = (float)(a + cd);
       }
       for (int t = nt; t < kp; ++t) dst[t] = 0.f;
     }

@@ -121,3 +121,36 @@ def match_task(args):
     par, tok, dep, tgt, T, seed, trials, rnd = args
     rows = rowsweep.as_f64(tgt, "bf16")
     return [accept.walk_match_margin(par, tok, dep, rows, T, seed, t, rnd) for t in trials]
+
+
+class TokenRows:
+    """Rows of a [V, h] table for the tokens a round can ask for, indexed like the table."""
+
+    def __init__(self, tokens, rows):
+        self.at = {int(t): i for i, t in enumerate(tokens)}
+        self.rows = np.asarray(rows, dtype=np.float64)
+
+    def __getitem__(self, tok):
+        return self.rows[self.at[int(tok)]]
+
+
+def gather_tdes_params(prm, base_bits, dtype, root_tok: int, K: int):
+    """The edge MLP's parameters for one round, float64, with Gp and Gc cut down to the
+    tokens the round can use (its root token and every position's top-K candidates)."""
+    z = rowsweep.as_f64(base_bits, dtype)
+    toks = {int(root_tok)}
+    for d in range(z.shape[0]):
+        toks.update(int(t) for t in rowsweep.rank_order(z[d])[:K])
+    toks = sorted(toks)
+    out = {k: np.asarray(prm[k], dtype=np.float32).astype(np.float64) for k in ("Ed", "W", "b", "w")}
+    out["Gp"] = TokenRows(toks, np.asarray(prm["Gp"], dtype=np.float32)[toks])
+    out["Gc"] = TokenRows(toks, np.asarray(prm["Gc"], dtype=np.float32)[toks])
+    out["b0"] = float(np.float32(prm["b0"]))
+    return out
+
+
+def tdes_task(args):
+    """(logits [L, V], dtype, root token, float64 params, K, budget, s) -> (Tree, gap)."""
+    from oracle import tdes
+    x, dtype, root, prm, K, B, s = args
+    return tdes.build_tdes(rowsweep.as_f64(x, dtype), int(root), prm, K, B, s)

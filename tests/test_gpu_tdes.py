@@ -6,15 +6,19 @@ import torch
 import draft_tree_construction_amd as dt
 import synth
 from oracle import rowsweep, tdes, treeout
+import oracle_pool as op
 from parity_util import dev_bf16, dev_f32, tree_to_host
 
 pytestmark = pytest.mark.gpu
 
-# The edge MLP runs in float32 on the GPU and float64 in the oracle; a path sums up to L
-# edges, each within ~1e-6 of the oracle's, so scores agree to 1e-4. Trees must be identical
-# wherever the oracle's heap never had two prefixes within 1e-4 of each other; otherwise the
-# device tree must be a valid best-first tree under the oracle's scores to that tolerance.
-TOL_T = 1e-4
+# The GPU sums the edge MLP in float64 from the same float32 parameters as the oracle and
+# rounds each edge score to float once: an edge is within half an ulp of the oracle's value
+# (<= 4.8e-7 for |S| < 16, the scores here), plus ~1e-7 from the float hidden
+# pre-activations, and a prefix sums at most L = 16 edges in float64, so scores agree to
+# 1e-5. Trees must be identical wherever the oracle's heap never had two prefixes within
+# 1e-5 of each other; otherwise the device tree must be a valid best-first tree under the
+# oracle's scores to that tolerance.
+TOL_T = 1e-5
 
 
 def mlp_dev(prm):
@@ -143,10 +147,41 @@ def test_tdes_root_token_out_of_range_reads_token_zero():
     assert exact >= n - 1
 
 
-def test_tdes_full_config_sampled():
+def test_tdes_full_config():
     """Full size: R = 64 rounds, L = 16, V = 151,936 bf16, K = 32, B = 128, hp = hc = 64,
-    hd = 16, H = 128; four rounds against the oracle."""
+    hd = 16, H = 128; 16 rounds against the oracle (run round-parallel), at least half of
+    them with no heap tie within 1e-5 and so identical, the rest valid best-first trees."""
     host = synth.ddtree_logits(seed=2)
     prm, root = synth.edge_mlp(seed=6)
-    exact, n = check_tdes(host, "bf16", prm, root, 32, 128, rounds=(0, 21, 42, 63))
-    assert exact >= 1
+    K, B = 32, 128
+    s = float(np.float32(prm["s"]))
+    rounds = list(range(0, 64, 4))
+    tr = dt.build_tree_tdes(dev_bf16(host), torch.tensor(root, dtype=torch.int32, device="cuda:0"), mlp_dev(prm), K, B)
+    h = tree_to_host(tr)
+    refs = op.pmap(op.tdes_task, [(host[r], "bf16", int(root[r]), op.gather_tdes_params(prm, host[r], "bf16",
+                                                                                        int(root[r]), K), K, B, s)
+                                  for r in rounds])
+    exact = 0
+    for r, (ref, gap) in zip(rounds, refs):
+        n = int(h["n"][r])
+        par, tok, dep = list(h["parent"][r, :n + 1]), list(h["token"][r, :n + 1]), list(h["depth"][r, :n + 1])
+        sc = [float(x) for x in h["score"][r, :n + 1]]
+        assert n == ref.n == B
+        np.testing.assert_array_equal(h["mask"][r], treeout.ancestor_mask(par, B))
+        if gap > TOL_T:
+            assert par == ref.parent and tok == ref.token and dep == ref.depth
+            np.testing.assert_allclose(sc, ref.score, rtol=0, atol=TOL_T)
+            exact += 1
+        else:
+            # shared prefixes score the same; validity of the order is the small tests' replay
+            got = {}
+            for i in range(1, n + 1):
+                got[i] = (got.get(par[i], ()) + (tok[i],))
+            want = {}
+            for i in range(1, ref.n + 1):
+                want[i] = (want.get(ref.parent[i], ()) + (ref.token[i],))
+            wsc = {want[i]: ref.score[i] for i in want}
+            for i in got:
+                if got[i] in wsc:
+                    assert abs(sc[i] - wsc[got[i]]) <= TOL_T
+    assert exact >= len(rounds) // 2, (exact, len(rounds))
