@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "rowsweep_traffic.json"))
+    ap.add_argument("--step-only", action="store_true",
+                    help="run only the warm-up and timed steps and print their line (for profiler passes: no "
+                         "roofline sweeps, extra builders, single-round latencies or cpu leg)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run 5 row sweeps and 5 plain copies of the same bytes (for rocprofv3 --pmc "
                          "FETCH_SIZE / WRITE_SIZE runs: the copy calibrates the counters)")
@@ -56,6 +59,44 @@ def sweep_source_digest():
     for f in ("k_rowsweep.hip", "common.hpp"):
         h.update(open(os.path.join(ROOT, "draft_tree_construction_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def depthwise_source_digest():
+    """Digest of the depth-wise kernels' sources: the stored counter readings of the correction
+    sweep are used only while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("k_depthwise.hip", "common.hpp"):
+        h.update(open(os.path.join(ROOT, "draft_tree_construction_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def correction_gemm(path, K=8):
+    """The depth-wise correction sweep (k_dw_corr) against its ceilings, from the rocprofv3
+    readings stored with the source digest: MFMA utilisation of the algorithmic h . P product
+    (live states x 2 x rank x V flop) at the traced kernel time, the matrix cores' busy
+    fraction, and the vector-issue floor from the instruction counts (a wave64 VALU
+    instruction takes 4 cycles on a 16-lane SIMD, a transcendental 16; 1024 SIMDs at
+    2.4 GHz). None when the readings are missing or stale."""
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_digest") != depthwise_source_digest():
+        return None
+    c = rec["per_dispatch"]
+    t = rec["trace_us_mean"] * 1e-6
+    simd_cycles = 1024 * 2.4e9
+    live = R * (1 + (L - 1) * K)
+    alg_flops = live * 2 * 64 * V
+    trans = c["SQ_INSTS_VALU_TRANS_F32"]
+    exp_floor = trans * 16 / simd_cycles
+    valu_floor = ((c["SQ_INSTS_VALU"] - trans) * 4 + trans * 16) / simd_cycles
+    return {"kernel": "k_dw_corr<bf16>", "us_per_launch": rec["trace_us_mean"], "source": os.path.relpath(path, ROOT),
+            "alg_flops": alg_flops, "mfma_util": round(alg_flops / t / 2.5e15, 4),
+            "mfma_busy": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (simd_cycles * t), 4),
+            "exps": trans * 64, "exp_floor_us": round(exp_floor * 1e6, 1),
+            "valu_issue_floor_us": round(valu_floor * 1e6, 1), "frac_of_valu_floor": round(valu_floor / t, 4),
+            "bound": "valu (transcendental exp2 plus the per-element adds), not mfma"}
 
 
 def main():
@@ -138,6 +179,13 @@ def main():
     step_ms = float(np.sum(per, axis=1).mean())
     ms_per_step = wall * 1e3 / args.steps
     value = R / (ms_per_step / 1e3)
+    if args.step_only:
+        print(json.dumps({"metric": "tree-build rounds/sec (step only, profiler pass)", "value": round(value, 1),
+                          "unit": "rounds/s", "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": round(ms_per_step, 4),
+                          "breakdown_ms": {n: round(float(per[:, k].mean()), 4) for k, n in enumerate(names)}}),
+              flush=True)
+        return
 
     # ---- roofline: the row sweep kernel, timed live over its own launches on this stream,
     # alternating between two distinct 311 MB logits tensors (the DDTree-shape and TALON-shape
@@ -328,6 +376,7 @@ def main():
         "roofline": roofline,
         "extra_ms": extra_ms,
         "r1_latency_us": r1_us,
+        "correction_gemm": correction_gemm(os.path.join(ROOT, "profiles", "depthwise_corr_counters.json")),
         "covered_draft_mass": mass,
     }
     if not args.no_cpu:
