@@ -100,7 +100,7 @@ int marginal_impl(const void *logits, int dtype, int R, int L, int V, int K, int
   if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
   const int k = marginal_k(K, B, V);
   if (k > V) return fail(DTREE_E_INVAL, "K > V");
-  if (k > DTREE_MAX_K || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
+  if (k > DTREE_MAX_K_MARGINAL || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
     return fail(DTREE_E_UNSUPPORTED, "K, B or L beyond the compiled envelope");
   int rc = check_tree(out, B);
   if (rc) return rc;
@@ -218,7 +218,7 @@ int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K,
                           float *lp, void *ws, size_t ws_bytes, dtree_stream_t s) {
   if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
   if (rows < 0 || V < 1 || K < 1 || K > V) return fail(DTREE_E_INVAL, "need rows >= 0, 1 <= K <= V");
-  if (K > DTREE_MAX_K) return fail(DTREE_E_UNSUPPORTED, "K > DTREE_MAX_K");
+  if (K > DTREE_MAX_K_MARGINAL) return fail(DTREE_E_UNSUPPORTED, "K > DTREE_MAX_K_MARGINAL");
   if (rows == 0) return DTREE_OK;
   if (!logits || !ids) return fail(DTREE_E_INVAL, "logits and ids must not be NULL");
   const size_t need = dt::rowsweep_ws_bytes(rows, V, K);

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(MG_NT) void k_marginal(const float *__restrict__ zk
   const int32_t *ir = ids + (size_t)r * L * K;
   // the round's candidate logits and row normalisers, staged in LDS once: every depth's
   // reads below are then LDS reads, not one dependent global read per depth
-  __shared__ float s_z[DTREE_MAX_L * DTREE_MAX_K];
+  __shared__ float s_z[DTREE_MAX_L * DTREE_MAX_K_MARGINAL];
   __shared__ double s_lse[DTREE_MAX_L];
   for (int i = tid; i < L * K; i += MG_NT) s_z[i] = zr[i];
   for (int i = tid; i < L; i += MG_NT) s_lse[i] = lse[(size_t)r * L + i];

@@ -83,7 +83,8 @@ enum dtree_op {
 };
 
 /* Compiled envelope (DTREE_E_UNSUPPORTED beyond it). */
-#define DTREE_MAX_K 64      /* per-position candidates */
+#define DTREE_MAX_K 64      /* per-position candidates (depth-wise, gated, static, GRAFT builders) */
+#define DTREE_MAX_K_MARGINAL 128 /* per-position candidates of the row sweep and the marginal builder */
 #define DTREE_MAX_L 64      /* draft positions */
 #define DTREE_MAX_CAP 128   /* B or N */
 #define DTREE_MAX_ACCEPT_V 262144 /* vocabulary of accept_tree */
@@ -112,7 +113,7 @@ size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int 
  * log-probs; DARTree Algorithm 1 step 4: C_d = TopK(L_d^base, K)).
  * logits [rows][V]; outputs lse [rows] = ln sum_v exp(z_v), ids [rows][K] in rank order
  * (logit desc, id asc), lp [rows][K] = z - lse. Any of lse / lp may be NULL.
- * Needs 1 <= K <= min(V, DTREE_MAX_K).
+ * Needs 1 <= K <= min(V, DTREE_MAX_K_MARGINAL).
  */
 int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K, float *lse,
                           int32_t *ids, float *lp, void *ws, size_t ws_bytes, dtree_stream_t s);
@@ -121,8 +122,9 @@ int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K,
  * Marginal draft tree (DDTree; DARTree background "tree verification and DDTree"):
  * the B prefixes u, |u| <= L, with the largest s_beta(u) = sum_i log q_i(u_i) + beta*|u|,
  * q_i = softmax(logits[r][i-1]), over each position's top K tokens. K = 0 means
- * min(B, V) (DDTree's S_K lemma), which gives the exact global Top-B. Needs beta <= 0
- * (else DTREE_E_BETA), 1 <= B <= DTREE_MAX_CAP, K <= DTREE_MAX_K, out->cap == B.
+ * min(B, V) (DDTree's S_K lemma), which gives the exact global Top-B up to B = DTREE_MAX_CAP.
+ * Needs beta <= 0 (else DTREE_E_BETA), 1 <= B <= DTREE_MAX_CAP, K <= DTREE_MAX_K_MARGINAL,
+ * out->cap == B.
  */
 int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta,
                         const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);

@@ -67,7 +67,8 @@ def marg(**kw):
     (dict(beta=float("nan")), -1),
     (dict(dtype=3), -1),
     (dict(K=33), -1),
-    (dict(K=65, V=1000), -4),
+    (dict(K=129, V=1000), -4),
+    (dict(K=65, V=1000), -3),          # K up to 128 is in the envelope: next check is the workspace
     (dict(B=129, t=tree(129)), -4),
     (dict(L=65), -4),
     (dict(t=tree(7)), -1),
@@ -210,7 +211,8 @@ def test_topk_validation():
         return L.dtree_topk_logsoftmax(FAKE, dtype, rows, V, K, FAKE, FAKE, FAKE, None, 0, None)
     assert call(K=0) == -1
     assert call(K=33) == -1
-    assert call(K=65, V=100) == -4
+    assert call(K=129, V=200) == -4
+    assert call(K=100, V=50) == -1    # K > V (the envelope allows up to 128)
     assert call(dtype=5) == -1
     assert call(rows=2, V=151936, K=8) == -3   # split rows need a workspace
     assert call(rows=0) == 0

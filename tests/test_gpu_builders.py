@@ -51,15 +51,13 @@ def test_marginal_tiny_config():
 
 @pytest.mark.parametrize("R,L,V,K,B,beta", [
     (6, 16, 20000, 64, 64, 0.0),
-    (5, 16, 3001, 0, 128, 0.0),     # K = min(B, V) is beyond 64 -> use 64 explicitly below
+    (5, 16, 3001, 0, 128, 0.0),     # K = min(B, V) = 128: DDTree's exact tree at B = 128
     (4, 7, 500, 16, 100, -0.3),
     (3, 3, 50, 50, 30, -2.0),
     (3, 1, 1000, 10, 10, 0.0),      # L = 1
     (2, 5, 40, 1, 5, 0.0),          # K = 1: argmax chain
 ])
 def test_marginal_ddtree_shape_small(R, L, V, K, B, beta):
-    if K == 0 and min(B, V) > 64:
-        K = 64
     host = synth.ddtree_logits(seed=20 + V, R=R, L=L, V=V)
     check_marginal(host, "bf16", K, B, beta)
 
@@ -83,10 +81,10 @@ def test_marginal_full_ddtree_config_all_rounds():
 
 
 def test_marginal_b128_full_vocabulary():
-    """B = 128 on full-vocabulary rows (K = 64, the compiled envelope), eight rounds."""
+    """B = 128 with K = min(B, V) = 128 (DDTree's exact tree) on full-vocabulary rows, eight rounds."""
     host = synth.ddtree_logits(seed=2, R=8)
-    h = tree_to_host(dt.build_tree_marginal(dev_bf16(host), 64, 128, -0.25))
-    ref = op.pmap(op.marginal_task, [(host[r], "bf16", 64, 128, -0.25) for r in range(8)])
+    h = tree_to_host(dt.build_tree_marginal(dev_bf16(host), 0, 128, -0.25))
+    ref = op.pmap(op.marginal_task, [(host[r], "bf16", 0, 128, -0.25) for r in range(8)])
     exact = sum(assert_tree_equal(h, r, t, 128, near_tie=gap <= 1e-5) for r, (t, gap) in enumerate(ref))
     assert exact >= 7
 

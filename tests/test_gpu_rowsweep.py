@@ -36,6 +36,8 @@ def assert_lse_close(got, want):
     (2, 1, 1, "bf16", 5),         # V = 1
     (33, 2049, 8, "f32", 6),
     (9, 40000, 64, "bf16", 7),
+    (9, 40000, 128, "bf16", 8),   # the marginal envelope's widest list
+    (4, 151936, 128, "bf16", 9),
 ])
 def test_rowsweep_random(rows, V, K, dtype, seed):
     rng = np.random.default_rng(seed)
@@ -44,7 +46,7 @@ def test_rowsweep_random(rows, V, K, dtype, seed):
     run_and_compare(host, dtype, K)
 
 
-@pytest.mark.parametrize("V,K", [(4096, 64), (151936, 64), (3000, 8)])
+@pytest.mark.parametrize("V,K", [(4096, 64), (151936, 64), (3000, 8), (151936, 128)])
 def test_rowsweep_planted_ties(V, K):
     """Rows drawn from an 8-value grid: thousands of exact ties at the K-th value."""
     run_and_compare(synth.tie_rows(V, 6, seed=V), "bf16", K)
@@ -58,6 +60,7 @@ def test_rowsweep_constant_and_sorted_rows():
     # large magnitudes: the exponent's fp32 rounding of log2 e must only ever scale x - max(x)
     big = np.stack([np.arange(V) * 0.5 + 1.0e5, 1.0e5 - np.arange(V) * 0.5, np.arange(V) * 0.5 - 1.0e5]).astype(np.float32)
     run_and_compare(big, "f32", 64)
+    run_and_compare(synth.bf16_from_f32(rows), "bf16", 128)
 
 
 def test_rowsweep_full_ddtree_shape_sampled():
