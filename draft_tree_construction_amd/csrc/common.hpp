@@ -129,35 +129,44 @@ DT_INLINE double wave_sum(double v) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// ---- wave-level (64-lane) sorting of 64-bit keys held one per lane, descending
-DT_INLINE uint64_t wave_sort64_desc_u64(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t o = __shfl_xor(v, j, 64);
-      const bool desc_blk = (lane & k) == 0;
-      const bool lower = (lane & j) == 0;
-      const uint64_t hi = v > o ? v : o, lo = v > o ? o : v;
-      v = (lower == desc_blk) ? hi : lo;
-    }
+// ---- lane exchanges without the LDS: the value of lane (lane ^ J), J a power of two
+// known at compile time. J = 1, 2: a quad permutation; J = 4, 8: row shifts both ways (each
+// lane takes the one that stays in its row); J = 16, 32: the permlane swaps of rows or
+// halves, which hand every lane the pair's lower and upper values.
+template <int J>
+DT_INLINE uint32_t lane_xor_u32(uint32_t v) {
+  const int lane = __lane_id();
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+  } else if constexpr (J == 4 || J == 8) {
+    // lanes whose source leaves the row read 0 there; they take the other shift
+    const int up = __builtin_amdgcn_mov_dpp((int)v, 0x100 | J, 0xF, 0xF, true);  // row_shl: lane + J
+    const int dn = __builtin_amdgcn_mov_dpp((int)v, 0x110 | J, 0xF, 0xF, true);  // row_shr: lane - J
+    return (uint32_t)((lane & J) ? dn : up);
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // r[0] lane & ~16, r[1] lane | 16
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane_xor_u32: J must be 1, 2, 4, 8, 16 or 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // r[0] lane & ~32, r[1] lane | 32
+    return (lane & 32) ? r[0] : r[1];
   }
-  return v;
 }
-// Top 64 (sorted descending across lanes) of two descending 64-key lists.
-DT_INLINE uint64_t wave_merge_top64_u64(uint64_t a, uint64_t b) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t rb = __shfl(b, 63 - lane, 64);
-  uint64_t v = a > rb ? a : rb;  // bitonic; holds the 64 largest
-#pragma unroll
-  for (int j = 32; j > 0; j >>= 1) {
-    const uint64_t o = __shfl_xor(v, j, 64);
-    const bool lower = (lane & j) == 0;
-    v = lower ? (v > o ? v : o) : (v > o ? o : v);
-  }
-  return v;
+template <int J>
+DT_INLINE uint64_t lane_xor_u64(uint64_t v) {
+  return ((uint64_t)lane_xor_u32<J>((uint32_t)(v >> 32)) << 32) | lane_xor_u32<J>((uint32_t)v);
 }
+// The value of lane 63 - lane: a mirror in each row of 16, then the rows swapped end for end.
+DT_INLINE uint32_t lane_reverse_u32(uint32_t v) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);  // row_mirror
+  return lane_xor_u32<32>(lane_xor_u32<16>(m));
+}
+DT_INLINE uint64_t lane_reverse_u64(uint64_t v) {
+  return ((uint64_t)lane_reverse_u32((uint32_t)(v >> 32)) << 32) | lane_reverse_u32((uint32_t)v);
+}
+
 // Lane prefix count of set bits below this lane in a 64-bit wave mask.
 DT_INLINE int lane_prefix(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -646,13 +646,11 @@ __global__ __launch_bounds__(DW_NT) void k_dw_lq(DwState s, DwDev a, DwDims g) {
 // One workgroup per round: the depths in order (children scored from the log q~ rows of
 // their parents' states, the best W kept), then the deferred Top-B and the outputs.
 struct DwTreeLds {
-  double lqs[64 * 64];       // this depth's log q~ rows, [state][candidate]
+  double lqs[64 * 64];       // log q~ rows, [state][candidate]: every depth's, or this one's
   double bs[DW_WMAX];        // current branches: score, state index
   int bk[DW_WMAX];
-  double cs[DW_CH];          // children, [branch][candidate rank]
-  int cpk[DW_CH];
-  double ss[DW_CH];          // children of each branch in order
-  int spk[DW_CH];
+  uint64_t mk[2][DW_CH / 64][128];  // sorted lists being merged (ping-pong): score code,
+  uint32_t mp[2][DW_CH / 64][128];  //   complement of parent position << 6 | rank
   double fs[DW_SUP];         // the super-tree, S_1 .. S_L: score, parent position << 16 | rank
   int fpk[DW_SUP];
   int off[DTREE_MAX_L + 2], cnt[DTREE_MAX_L + 2];
@@ -660,8 +658,188 @@ struct DwTreeLds {
   float osc[DTREE_MAX_CAP + 1];
 };
 
-// y comes before x in the order (score desc, parent position asc, rank asc)
-DT_INLINE bool dw_before(double sy, int py, double sx, int px) { return (sy > sx) | ((sy == sx) & (py < px)); }
+// A child's place in the order (score desc, parent position asc, rank asc) as a pair that
+// compares larger-first: the order-preserving code of the score (a double, -0 as +0) and
+// the complement of (parent position << 6 | rank) (positions < 128, ranks < 64). Pairs are
+// unique; (0, 0) lies below every real child and pads the lists.
+struct DwKey {
+  uint64_t k;
+  uint32_t p;
+};
+DT_INLINE DwKey dw_key(double sc, int b, int kc) {
+  const uint64_t u = (uint64_t)__double_as_longlong(sc == 0.0 ? 0.0 : sc);
+  return {(u >> 63) ? ~u : (u | 0x8000000000000000ull), (uint32_t)(0x1FFF - ((b << 6) | kc))};
+}
+DT_INLINE bool dw_gt(DwKey x, DwKey y) { return (x.k > y.k) | ((x.k == y.k) & (x.p > y.p)); }
+// field-wise select (a select of whole structs would be one of their addresses)
+DT_INLINE DwKey dw_sel(bool c, DwKey x, DwKey y) { return {c ? x.k : y.k, c ? x.p : y.p}; }
+template <int J>
+DT_INLINE DwKey dw_xor_t(DwKey x) { return {lane_xor_u64<J>(x.k), lane_xor_u32<J>(x.p)}; }
+// j is a constant wherever this is called (fully unrolled loops), so the switch folds away
+DT_INLINE DwKey dw_xor(DwKey x, int j) {
+  switch (j) {
+    case 1: return dw_xor_t<1>(x);
+    case 2: return dw_xor_t<2>(x);
+    case 4: return dw_xor_t<4>(x);
+    case 8: return dw_xor_t<8>(x);
+    case 16: return dw_xor_t<16>(x);
+    default: return dw_xor_t<32>(x);
+  }
+}
+DT_INLINE DwKey dw_reverse(DwKey x) { return {lane_reverse_u64(x.k), lane_reverse_u32(x.p)}; }
+
+// Bitonic sort, descending, of 64 * R keys held R per lane (element q * 64 + lane in v[q]).
+template <int R>
+DT_INLINE void dw_sort_desc(DwKey (&v)[R]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64 * R; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {  // partner in the same lane, another register
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          if (q & (j >> 6)) continue;
+          const int q2 = q | (j >> 6);
+          const bool desc = ((q * 64 + lane) & k) == 0;
+          const bool g = dw_gt(v[q], v[q2]);
+          const DwKey hi = dw_sel(g, v[q], v[q2]), lo = dw_sel(g, v[q2], v[q]);
+          v[q] = dw_sel(desc, hi, lo);
+          v[q2] = dw_sel(desc, lo, hi);
+        }
+      } else {
+        const bool lower = (lane & j) == 0;
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          const DwKey o = dw_xor(v[q], j);
+          const bool desc = ((q * 64 + lane) & k) == 0;
+          const bool g = dw_gt(v[q], o);
+          v[q] = dw_sel((lower == desc) == g, v[q], o);
+        }
+      }
+    }
+  }
+}
+// The 64 * R largest of two descending lists of 64 * R keys, descending, into x.
+template <int R>
+DT_INLINE void dw_merge_top(DwKey (&x)[R], const DwKey (&y)[R]) {
+  const int lane = threadIdx.x & 63;
+  // x's element e against y's element 64R - 1 - e: a bitonic sequence of the 64R largest
+  DwKey v[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const DwKey o = dw_reverse(y[R - 1 - q]);
+    v[q] = dw_sel(dw_gt(x[q], o), x[q], o);
+  }
+#pragma unroll
+  for (int j = 32 * R; j > 0; j >>= 1) {
+    if (j >= 64) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        if (q & (j >> 6)) continue;
+        const int q2 = q | (j >> 6);
+        const bool g = dw_gt(v[q], v[q2]);
+        const DwKey hi = dw_sel(g, v[q], v[q2]), lo = dw_sel(g, v[q2], v[q]);
+        v[q] = hi;
+        v[q2] = lo;
+      }
+    } else {
+      const bool lower = (lane & j) == 0;
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        const DwKey o = dw_xor(v[q], j);
+        v[q] = dw_sel(lower == dw_gt(v[q], o), v[q], o);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q) x[q] = v[q];
+}
+
+DT_INLINE double dw_key_score(uint64_t k) {
+  return __longlong_as_double((long long)((k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
+}
+
+// One depth: scores the nc = nb * K children (branch b's score and state in Ls.bs, Ls.bk, the
+// states' log q~ rows at Ls.lqs + lb) and keeps the best `keep` of them, in order, as S_d at
+// Ls.fs / Ls.fpk + o0 and as the next depth's branches. Each wave sorts 64 * R children in
+// registers, then pairs of sorted lists merge through LDS, each merge keeping its 64 * R best,
+// until one list is left; the wave holding it writes the kept children from its registers.
+// Ends without a barrier: what it writes is read after the caller's next one.
+template <int R, typename LdsT>
+DT_INLINE void dw_depth(LdsT &Ls, int nb, int K, double beta, int lb, int keep, int o0) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  constexpr int M = 64 * R;
+  const int nc = nb * K;
+  const int nl = (nc + M - 1) / M;
+  auto emit = [&](const DwKey (&v)[R]) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int e = q * 64 + lane;
+      if (e < keep) {
+        const double sc = dw_key_score(v[q].k);
+        const int pk13 = 0x1FFF - (int)v[q].p;
+        const int b = min(pk13 >> 6, nb - 1), kc = min(pk13 & 63, K - 1);  // in range by construction
+        Ls.fs[o0 + e] = sc;
+        Ls.fpk[o0 + e] = (b << 16) | kc;
+        Ls.bs[e] = sc;
+        Ls.bk[e] = kc;
+      }
+    }
+  };
+  if (w < nl) {
+    DwKey v[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int t = w * M + q * 64 + lane;
+      v[q] = {0ull, 0u};
+      if (t < nc) {
+        const int b = t / K, kc = t - b * K;
+        const double sb = Ls.bs[b];
+        v[q] = dw_key(fmin((sb + Ls.lqs[lb + Ls.bk[b] * K + kc]) + beta, sb), b, kc);
+      }
+    }
+    dw_sort_desc<R>(v);
+    if (nl == 1) {
+      emit(v);
+    } else {
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        Ls.mk[0][w][q * 64 + lane] = v[q].k;
+        Ls.mp[0][w][q * 64 + lane] = v[q].p;
+      }
+    }
+  }
+  int buf = 0;
+  for (int n = nl; n > 1; n = (n + 1) >> 1) {
+    __syncthreads();
+    if (w < (n >> 1)) {
+      DwKey x[R], y[R];
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        x[q] = {Ls.mk[buf][2 * w][q * 64 + lane], Ls.mp[buf][2 * w][q * 64 + lane]};
+        y[q] = {Ls.mk[buf][2 * w + 1][q * 64 + lane], Ls.mp[buf][2 * w + 1][q * 64 + lane]};
+      }
+      dw_merge_top<R>(x, y);
+      if (n == 2) {
+        emit(x);
+      } else {
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          Ls.mk[buf ^ 1][w][q * 64 + lane] = x[q].k;
+          Ls.mp[buf ^ 1][w][q * 64 + lane] = x[q].p;
+        }
+      }
+    } else if ((n & 1) && w == (n >> 1)) {  // the odd list out moves on as it is
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        Ls.mk[buf ^ 1][w][q * 64 + lane] = Ls.mk[buf][2 * w][q * 64 + lane];
+        Ls.mp[buf ^ 1][w][q * 64 + lane] = Ls.mp[buf][2 * w][q * 64 + lane];
+      }
+    }
+    buf ^= 1;
+  }
+}
 
 __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g, TreeOut out) {
   __shared__ DwTreeLds Ls;
@@ -670,6 +848,10 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
   const int K = g.K, W = g.W, L = g.L;
   constexpr int PF = 64 * 64 / DW_TT;  // log q~ entries per thread and depth
   auto slab = [&](int d) { return s.lq + (size_t)dw_slot(g, d, r, 0) * K; };
+  // every depth's log q~ rows at once when they fit (depth 1 at 0, depth d >= 2 at
+  // K + (d - 2) K^2), else one depth at a time, the next one prefetched into registers
+  const bool all = (1 + (L - 1) * K) * K <= 64 * 64;
+  auto lbase = [&](int d) { return d == 1 ? 0 : K + (d - 2) * K * K; };
   double pre[PF];
   auto prefetch = [&](int d) {
     const int n = (d == 1 ? 1 : K) * K;
@@ -680,102 +862,43 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
       if (x < n) pre[i] = src[x];
     }
   };
-  prefetch(1);
+  if (all) {
+    const int tot = (1 + (L - 1) * K) * K;
+    for (int x = tid; x < tot; x += DW_TT) {
+      const int d = x < K ? 1 : 2 + (x - K) / (K * K);
+      Ls.lqs[x] = slab(d)[x - lbase(d)];
+    }
+  } else {
+    prefetch(1);
+  }
   if (tid == 0) {
     Ls.bs[0] = 0.0;
     Ls.bk[0] = 0;
     Ls.off[1] = 0;
   }
-  int nb = 1;  // branches at the current depth (the root)
+  int nb = 1, o0 = 0;  // branches at the current depth (the root), start of S_d
   for (int d = 1; d <= L; ++d) {
-    {
+    if (!all) {
+      if (d > 1) __syncthreads();  // the previous depth is done reading the rows
       const int n = (d == 1 ? 1 : K) * K;
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
         const int x = tid + DW_TT * i;
         if (x < n) Ls.lqs[x] = pre[i];
       }
-    }
-    if (d < L) prefetch(d + 1);
-    __syncthreads();
-    // score every child (b, kc) of the nb branches
-    const int nc = nb * K;
-    for (int t = tid; t < nc; t += DW_TT) {
-      const int b = t / K, kc = t - b * K;
-      const double sb = Ls.bs[b];
-      const double sc = (sb + Ls.lqs[Ls.bk[b] * K + kc]) + (double)a.beta;
-      Ls.cs[t] = fmin(sc, sb);
-      Ls.cpk[t] = (b << 16) | kc;
+      if (d < L) prefetch(d + 1);
     }
     __syncthreads();
-    // each branch's K children in order: its own place among them
-    for (int t = tid; t < nc; t += DW_TT) {
-      const int b0 = t - t % K;
-      const double ms = Ls.cs[t];
-      const int mp = Ls.cpk[t];
-      int i = 0;
-      for (int y0 = 0; y0 < K; y0 += 8) {  // eight reads in flight (clamped to the branch)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int y = b0 + min(y0 + u, K - 1);
-          i += (y0 + u < K) & dw_before(Ls.cs[y], Ls.cpk[y], ms, mp);
-        }
-      }
-      Ls.ss[b0 + i] = ms;
-      Ls.spk[b0 + i] = mp;
-    }
-    __syncthreads();
-    // place among all children = place in its branch + for every other branch the length of
-    // the prefix of that branch's ordered children that comes before it (a binary search);
-    // G lanes share a child, each over every G-th branch (eight in lockstep), and stop once
-    // their count alone reaches `keep` (the child is then not kept)
-    const int keep = nc < W ? nc : W;
-    const int o0 = Ls.off[d];
-    {
-      const int G = nc <= DW_TT / 8 ? 8 : nc <= DW_TT / 4 ? 4 : nc <= DW_TT / 2 ? 2 : 1;
-      const int part = tid & (G - 1);
-      int kp = 1;
-      while (kp * 2 <= K) kp *= 2;
-      for (int x = tid / G; x < nc; x += DW_TT / G) {
-        const double ms = Ls.ss[x];
-        const int mp = Ls.spk[x];
-        const int b = x / K;
-        int rank = 0;
-        // eight branches searched in lockstep (independent LDS reads)
-        for (int c0 = part; c0 < nb && rank < keep; c0 += 8 * G) {
-          int lo[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) lo[i] = 0;
-          for (int step = kp; step >= 1; step >>= 1) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {  // unconditional clamped reads, branch-free update
-              const int b2 = c0 + i * G, j = lo[i] + step;
-              const int e = min(b2, nb - 1) * K + min(j, K) - 1;
-              const bool ok = (b2 < nb) & (b2 != b) & (j <= K) & dw_before(Ls.ss[e], Ls.spk[e], ms, mp);
-              lo[i] = ok ? j : lo[i];
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) rank += lo[i];
-        }
-        for (int o = 1; o < G; o <<= 1) rank += __shfl_xor(rank, o, 64);
-        rank += x - b * K;
-        if (part == 0 && rank < keep) {
-          Ls.fs[o0 + rank] = ms;
-          Ls.fpk[o0 + rank] = mp;
-        }
-      }
-    }
-    __syncthreads();
-    // the kept children become the next depth's branches (state = candidate rank)
-    for (int i = tid; i < keep; i += DW_TT) {
-      Ls.bs[i] = Ls.fs[o0 + i];
-      Ls.bk[i] = Ls.fpk[o0 + i] & 0xFFFF;
-    }
-    if (tid == 0) Ls.off[d + 1] = o0 + keep;
+    const int keep = nb * K < W ? nb * K : W;
+    if (W <= 64)
+      dw_depth<1>(Ls, nb, K, (double)a.beta, all ? lbase(d) : 0, keep, o0);
+    else
+      dw_depth<2>(Ls, nb, K, (double)a.beta, all ? lbase(d) : 0, keep, o0);
+    o0 += keep;
+    if (tid == 0) Ls.off[d + 1] = o0;
     nb = keep;
-    __syncthreads();
   }
+  __syncthreads();
   // ---- deferred Top-B over the super-tree by (s desc, depth asc, position asc). Each S_d
   // is sorted, so a node's rank is its position plus, per other depth, the length of the
   // prefix that comes before it (a branch-free binary search, four depths in lockstep); the
@@ -837,17 +960,17 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
     Ls.osc[0] = 0.f;
   }
   __syncthreads();
-  for (int d = 1; d <= L; ++d) {
-    const int nd = Ls.cnt[d + 1] - Ls.cnt[d];
-    for (int p = tid; p < nd; p += DW_TT) {
-      const int x = Ls.off[d] + p;
-      const int idx = Ls.cnt[d] + p;
-      const int pk = Ls.fpk[x];
-      Ls.opar[idx] = (d == 1) ? 0 : Ls.cnt[d - 1] + (pk >> 16);
-      Ls.otok[idx] = a.ids[((size_t)r * L + (d - 1)) * K + (pk & 0xFFFF)];
-      Ls.odep[idx] = d;
-      Ls.osc[idx] = (float)Ls.fs[x];
-    }
+  // one node per thread: its depth d is the last with canonical offset <= idx
+  for (int idx = 1 + tid; idx <= keep; idx += DW_TT) {
+    int d = 1;
+    for (int step = 32; step >= 1; step >>= 1)
+      if (d + step <= L && Ls.cnt[d + step] <= idx) d += step;
+    const int x = Ls.off[d] + (idx - Ls.cnt[d]);
+    const int pk = Ls.fpk[x];
+    Ls.opar[idx] = (d == 1) ? 0 : Ls.cnt[d - 1] + (pk >> 16);
+    Ls.otok[idx] = a.ids[((size_t)r * L + (d - 1)) * K + (pk & 0xFFFF)];
+    Ls.odep[idx] = d;
+    Ls.osc[idx] = (float)Ls.fs[x];
   }
   __syncthreads();
   write_tree(r, keep, Ls.opar, Ls.otok, Ls.odep, Ls.osc, out);
