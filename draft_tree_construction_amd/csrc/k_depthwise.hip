@@ -666,10 +666,11 @@ struct DwKey {
   uint64_t k;
   uint32_t p;
 };
-DT_INLINE DwKey dw_key(double sc, int b, int kc) {
+DT_INLINE uint64_t dw_code(double sc) {  // order-preserving, -0 as +0
   const uint64_t u = (uint64_t)__double_as_longlong(sc == 0.0 ? 0.0 : sc);
-  return {(u >> 63) ? ~u : (u | 0x8000000000000000ull), (uint32_t)(0x1FFF - ((b << 6) | kc))};
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
+DT_INLINE DwKey dw_key(double sc, int b, int kc) { return {dw_code(sc), (uint32_t)(0x1FFF - ((b << 6) | kc))}; }
 DT_INLINE bool dw_gt(DwKey x, DwKey y) { return (x.k > y.k) | ((x.k == y.k) & (x.p > y.p)); }
 // field-wise select (a select of whole structs would be one of their addresses)
 DT_INLINE DwKey dw_sel(bool c, DwKey x, DwKey y) { return {c ? x.k : y.k, c ? x.p : y.p}; }
@@ -876,7 +877,26 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
     Ls.bk[0] = 0;
     Ls.off[1] = 0;
   }
-  int nb = 1, o0 = 0;  // branches at the current depth (the root), start of S_d
+  if (tid <= L + 1) Ls.cnt[tid] = 0;
+  // The deferred Top-B over the super-tree by (s desc, depth asc, position asc), kept as it
+  // grows: the last wave holds the best 128 (>= B) nodes of S_1 .. S_{d-1} in its registers
+  // and merges each finished S_d in (it is sorted in that order already) while the other
+  // waves rank the next depth. Key: (score code, complement of depth << 7 | position).
+  const int w = tid >> 6, lane = tid & 63;
+  constexpr int TW = DW_TT / 64 - 1;
+  DwKey top[2] = {{0ull, 0u}, {0ull, 0u}};
+  auto fold = [&](int dd, int start, int len) {
+    len = len < 128 ? len : 128;  // deeper positions cannot be among the best 128
+    DwKey y[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = q * 64 + lane;
+      y[q] = {0ull, 0u};
+      if (e < len) y[q] = {dw_code(Ls.fs[start + e]), (uint32_t)(0x3FFF - ((dd << 7) | e))};
+    }
+    dw_merge_top<2>(top, y);
+  };
+  int nb = 1, o0 = 0, prev = 0;  // branches at the current depth (the root), start of S_d, |S_{d-1}|
   for (int d = 1; d <= L; ++d) {
     if (!all) {
       if (d > 1) __syncthreads();  // the previous depth is done reading the rows
@@ -889,6 +909,7 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
       if (d < L) prefetch(d + 1);
     }
     __syncthreads();
+    if (w == TW && d > 1) fold(d - 1, o0 - prev, prev);
     const int keep = nb * K < W ? nb * K : W;
     if (W <= 64)
       dw_depth<1>(Ls, nb, K, (double)a.beta, all ? lbase(d) : 0, keep, o0);
@@ -896,54 +917,17 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
       dw_depth<2>(Ls, nb, K, (double)a.beta, all ? lbase(d) : 0, keep, o0);
     o0 += keep;
     if (tid == 0) Ls.off[d + 1] = o0;
-    nb = keep;
+    nb = prev = keep;
   }
   __syncthreads();
-  // ---- deferred Top-B over the super-tree by (s desc, depth asc, position asc). Each S_d
-  // is sorted, so a node's rank is its position plus, per other depth, the length of the
-  // prefix that comes before it (a branch-free binary search, four depths in lockstep); the
-  // kept nodes of a depth are a prefix of S_d.
-  const int n = Ls.off[L + 1];
+  // the last depth, then each depth's share of the B best (a prefix of its S_d)
+  const int n = o0;
   const int keep = n < g.B ? n : g.B;
-  if (tid <= L + 1) Ls.cnt[tid] = 0;
-  __syncthreads();
-  // GF lanes per node, each searching every GF-th group of four depths
-  const int GF = n <= DW_TT / 8 ? 8 : n <= DW_TT / 4 ? 4 : n <= DW_TT / 2 ? 2 : 1;
-  const int part = tid & (GF - 1);
-  for (int x = tid / GF; x < n; x += DW_TT / GF) {
-    int d = 1;
-    while (Ls.off[d + 1] <= x) ++d;
-    const double sp = Ls.fs[x];
-    int rank = 0;
-    for (int d0 = 1 + 4 * part; d0 <= L; d0 += 4 * GF) {
-      int lo[4], base[4], size[4];
-      bool ge[4];
+  if (w == TW) {
+    fold(L, o0 - prev, prev);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d2 = d0 + i;
-        const bool in = d2 <= L && d2 != d;
-        base[i] = in ? Ls.off[d2] : 0;
-        size[i] = in ? Ls.off[d2 + 1] - Ls.off[d2] : 0;
-        ge[i] = d2 < d;  // shallower depths win ties
-        lo[i] = 0;
-      }
-#pragma unroll
-      for (int step = DW_WMAX; step >= 1; step >>= 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = lo[i] + step;
-          if (j <= size[i]) {
-            const double sq = Ls.fs[base[i] + j - 1];
-            if (ge[i] ? sq >= sp : sq > sp) lo[i] = j;
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rank += lo[i];
-    }
-    for (int o = 1; o < GF; o <<= 1) rank += __shfl_xor(rank, o, 64);
-    rank += x - Ls.off[d];
-    if (part == 0 && rank < keep) atomicAdd(&Ls.cnt[d], 1);
+    for (int q = 0; q < 2; ++q)
+      if (q * 64 + lane < keep) atomicAdd(&Ls.cnt[(0x3FFF - (int)top[q].p) >> 7], 1);
   }
   __syncthreads();
   if (tid == 0) {
