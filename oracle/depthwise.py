@@ -127,3 +127,59 @@ def deferred_topb(levels, B: int) -> Tree:
         p = index_of[(d - 1, nd["ppos"])]
         index_of[(d, pos)] = t.add(p, nd["token"], d, nd["s"])
     return t
+
+
+def build_sequential(base_rows: np.ndarray, E: np.ndarray, U: np.ndarray, P: np.ndarray,
+                     root_tok: int, K: int, B: int, beta: float, with_gaps: bool = False):
+    """The exact path-dependent best-first tree the DARTree summary sets against its own
+    method ("decoupling causal correction from best-first search"; the tree-construction
+    ablation's "sequential correction with heap"): a max-heap of candidate prefixes; each
+    step pops the best one, runs the correction head once for that node alone (its own
+    token history; with the Markov head, its last token), scores its children over C_{d+1}
+    and pushes them, before the next pop. B nodes are popped (or the heap runs dry).
+
+    Same correction and child score as build_depthwise, the clamp to the parent included.
+    Heap order: larger s, then smaller depth (ancestor first), then the parent's pop order,
+    then the candidate's rank. The tree is laid out depth by depth, each depth in pop order
+    (which within a depth is the depth-wise builder's S_d order). with_gaps also returns,
+    per pop, the popped score minus the best one left in the heap when the two are at the
+    same depth or the pop is the last (inf otherwise)."""
+    L, V = base_rows.shape
+    if beta > 0:
+        raise ValueError("Lemma 1 needs beta <= 0")
+    if not (1 <= K <= V and B >= 1):
+        raise ValueError("bad sizes")
+    P64 = np.asarray(P, dtype=np.float64)
+    cands = [rank_order(base_rows[d])[:K] for d in range(L)]
+
+    def expand(pop_index, depth, tok, s, heap):
+        """One correction call for one node: push its children at depth + 1."""
+        if depth >= L:
+            return
+        h = bf16_round(np.asarray(E[tok], dtype=np.float64) @ np.asarray(U[depth], dtype=np.float64))
+        z = base_rows[depth] + h @ P64
+        lse = logsumexp_row(z)
+        for k, c in enumerate(cands[depth]):
+            cs = min(s + (z[c] - lse) + beta, s)
+            heapq.heappush(heap, (-cs, depth + 1, pop_index, k, int(c)))
+
+    popped = []  # (s, depth, parent pop index, token), pop index = position + 1 (root = 0)
+    gaps = []
+    heap = []
+    expand(0, 0, int(root_tok), 0.0, heap)
+    while heap and len(popped) < B:
+        ns, d, par, _k, c = heapq.heappop(heap)
+        if with_gaps:
+            last = len(popped) + 1 == B
+            gaps.append(-ns - (-heap[0][0]) if heap and (heap[0][1] == d or last) else np.inf)
+        popped.append((-ns, d, par, c))
+        if len(popped) < B:  # the last node's children could never be popped
+            expand(len(popped), d, c, -ns, heap)
+    # canonical layout: depth by depth, pop order within a depth
+    order = sorted(range(len(popped)), key=lambda i: (popped[i][1], i))
+    index_of = {0: 0}
+    t = Tree()
+    for i in order:
+        s, d, par, c = popped[i]
+        index_of[i + 1] = t.add(index_of[par], c, d, s)
+    return (t, gaps) if with_gaps else t

@@ -130,3 +130,69 @@ def test_super_tree_invariants_workload_shape_small():
         assert len(levels[0]) == 8 and all(len(lv) <= 32 for lv in levels)
         for d in range(1, len(levels)):
             assert all(nd["ppos"] < len(levels[d - 1]) for nd in levels[d])
+
+
+# ---- the sequential correction-with-heap builder (exact path-dependent best-first)
+
+@pytest.mark.parametrize("seed,beta", [(7, 0.0), (8, -0.1), (9, -0.6)])
+def test_sequential_equals_corrected_brute_force(seed, beta):
+    """Popping one node at a time and correcting only that node gives the B best prefixes
+    over every path scored with its own corrections (monotone scores, ancestors first)."""
+    rng = np.random.default_rng(seed)
+    L, V, K, B = 3, 20, 3, 11
+    base = rng.standard_normal((L, V)) * 1.5
+    E, U, P = small_head(rng, V, 8, 4, L, 0.8)
+    t = depthwise.build_sequential(base, E, U, P, 4, K, B, beta)
+    ref = corrected_brute_force(base, E, U, P, 4, K, B, beta)
+    got = {p: s for p, s in zip(t.paths()[1:], t.score[1:])}
+    assert set(got) == set(ref)
+    for p in got:
+        assert abs(got[p] - ref[p]) < 1e-12
+    treeout.check_invariants(t, B, L)
+
+
+@pytest.mark.parametrize("B", [1, 9, 40])
+def test_sequential_equals_width_b_depthwise_node_for_node(B):
+    """Same tree as the depth-wise builder at W = B, in the same canonical layout (pop order
+    within a depth is S_d's order), on workload-shaped inputs with bf16 weights."""
+    R, L, V, dm, rank = 3, 6, 500, 32, 16
+    base_b = synth.ddtree_logits(seed=11, R=R, L=L, V=V)
+    E, U, P, root = synth.correction_head(seed=12, R=R, L=L, V=V, d_model=dm, rank=rank)
+    base = rowsweep.as_f64(base_b, "bf16")
+    E64, U64, P64 = (synth.f32_from_bf16(a).astype(np.float64) for a in (E, U, P))
+    for r in range(R):
+        q = depthwise.build_sequential(base[r], E64, U64, P64, int(root[r]), 8, B, -0.2)
+        t = depthwise.build_depthwise(base[r], E64, U64, P64, int(root[r]), K=8, W=B, B=B, beta=-0.2)
+        assert (q.parent, q.token, q.depth) == (t.parent, t.token, t.depth)
+        np.testing.assert_allclose(q.score, t.score, rtol=0, atol=1e-12)
+        treeout.check_invariants(q, B, L)
+
+
+def test_sequential_pops_in_score_order_and_reports_gaps():
+    rng = np.random.default_rng(13)
+    L, V, K, B = 5, 30, 4, 25
+    base = rng.standard_normal((L, V))
+    E, U, P = small_head(rng, V, 8, 4, L, 0.8)
+    t, gaps = depthwise.build_sequential(base, E, U, P, 1, K, B, -0.3, with_gaps=True)
+    assert t.n == B and len(gaps) == B and all(g >= 0 for g in gaps)
+    # every node scores at most its parent, and no dropped prefix beats a kept one: the
+    # last pop's gap is to the best prefix left out
+    for i in range(1, len(t.parent)):
+        assert t.score[i] <= t.score[t.parent[i]]
+    assert np.isfinite(gaps[-1])
+
+
+def test_sequential_chain_and_dry_heap():
+    """K = 1: the heap holds one prefix at a time, so the tree is the corrected chain; a
+    budget above the number of prefixes takes them all."""
+    rng = np.random.default_rng(14)
+    L, V = 4, 12
+    base = rng.standard_normal((L, V))
+    E, U, P = small_head(rng, V, 8, 4, L, 0.8)
+    t = depthwise.build_sequential(base, E, U, P, 0, 1, 10, 0.0)
+    assert t.n == L and t.parent == [-1, 0, 1, 2, 3]
+    assert t.token[1:] == [int(np.argmax(base[d])) for d in range(L)]
+    t2 = depthwise.build_sequential(base, E, U, P, 0, 2, 1000, -0.1)
+    assert t2.n == 2 + 4 + 8 + 16
+    with pytest.raises(ValueError):
+        depthwise.build_sequential(base, E, U, P, 0, 2, 5, 0.1)
