@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
     build_tree_depthwise(logits, E, U, P, root_tok, K, W, B, beta) -> Tree
     prepare_depthwise_head(U, P) -> head;  build_tree_depthwise_prepared(logits, E, head, d_model, rank,
         root_tok, K, W, B, beta) -> Tree  (the head's transposes done once)
+    build_tree_sequential(logits, E, head, d_model, rank, root_tok, K, B, beta) -> Tree
+        (exact best-first, one correction per popped node)
     build_tree_gated(logits, K_root, mu, N)             -> Tree
     build_tree_static(logits, K, D)                     -> Tree  (K*D nodes)
     build_tree_tdes(logits, root_tok, mlp, K, B, budget=None) -> Tree
@@ -34,13 +36,14 @@ LIB_PATH = os.path.join(_HERE, "libdtree.so")
 
 DTREE_BF16, DTREE_F32 = 0, 1
 OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT, OP_STATIC, OP_TDES, OP_DEPTHWISE_HEAD, \
-    OP_DEPTHWISE_PREPARED = range(9)
+    OP_DEPTHWISE_PREPARED, OP_SEQUENTIAL = range(10)
 STATUS = {0: "DTREE_OK", -1: "DTREE_E_INVAL", -2: "DTREE_E_BETA", -3: "DTREE_E_WORKSPACE",
           -4: "DTREE_E_UNSUPPORTED", -5: "DTREE_E_HIP"}
 
 # every symbol include/dtree.h declares
 SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_marginal_noalloc",
            "build_tree_depthwise", "dtree_prepare_depthwise_head", "build_tree_depthwise_prepared",
+           "build_tree_sequential",
            "build_tree_gated", "build_tree_static", "build_tree_tdes", "dtree_saba_budget", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
 
 
@@ -85,6 +88,9 @@ def lib() -> ctypes.CDLL:
     L.build_tree_depthwise_prepared.restype = i32
     L.build_tree_depthwise_prepared.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, i32, i32, i32, f32,
                                                 ctypes.POINTER(CTree), vp, sz, vp]
+    L.build_tree_sequential.restype = i32
+    L.build_tree_sequential.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, i32, i32, f32,
+                                        ctypes.POINTER(CTree), vp, sz, vp]
     L.build_tree_gated.restype = i32
     L.build_tree_gated.argtypes = [vp, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(CTree), vp, sz, vp]
     L.build_tree_static.restype = i32
@@ -259,6 +265,25 @@ def build_tree_depthwise_prepared(logits: torch.Tensor, E: torch.Tensor, head: t
     _check(lib().build_tree_depthwise_prepared(_ptr(logits), _dtype(logits), R, L, V, _ptr(E), _ptr(head), d_model,
                                                rank, _ptr(root_tok), K, W, B, float(beta), ctypes.byref(st), _ptr(ws),
                                                ws.numel(), _stream(dev)))
+    return out
+
+
+def build_tree_sequential(logits: torch.Tensor, E: torch.Tensor, head: torch.Tensor, d_model: int, rank: int,
+                          root_tok: torch.Tensor, K: int, B: int, beta: float, ws: torch.Tensor | None = None,
+                          out: Tree | None = None) -> Tree:
+    """Exact path-dependent best-first tree, one correction per popped node, with a head from
+    prepare_depthwise_head."""
+    _require_device(logits, E, head, root_tok)
+    if E.dtype != torch.bfloat16 or root_tok.dtype != torch.int32:
+        raise TypeError("E must be torch.bfloat16 and root_tok int32")
+    R, L, V = logits.shape
+    dev = logits.device
+    out = Tree.empty(R, B, dev) if out is None else out
+    ws = _workspace(workspace_size(OP_SEQUENTIAL, R, L, V, K, B, 0, rank, d_model), dev) if ws is None else ws
+    st = out.c_struct()
+    _check(lib().build_tree_sequential(_ptr(logits), _dtype(logits), R, L, V, _ptr(E), _ptr(head), d_model, rank,
+                                       _ptr(root_tok), K, B, float(beta), ctypes.byref(st), _ptr(ws), ws.numel(),
+                                       _stream(dev)))
     return out
 
 

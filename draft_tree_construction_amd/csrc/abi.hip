@@ -200,6 +200,9 @@ size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int 
     case DTREE_OP_DEPTHWISE_PREPARED:
       if (K < 1 || W < 1 || B_or_N < 1 || d_model < 1) return 0;
       return a1_bytes(R * L, V, K) + dt::depthwise_call_bytes(R, L, V, K, W, B_or_N, d_model);
+    case DTREE_OP_SEQUENTIAL:
+      if (K < 1 || B_or_N < 1 || d_model < 1) return 0;
+      return a1_bytes(R * L, V, K) + dt::sequential_call_bytes(R, L, V, K, B_or_N, d_model);
     case DTREE_OP_STATIC:
       if (K < 1) return 0;
       return a1_bytes(R * L, V, K);
@@ -371,6 +374,36 @@ int build_tree_depthwise_prepared(const void *logits, int dtype, int R, int L, i
   if (reinterpret_cast<uintptr_t>(head) & 255) return fail(DTREE_E_INVAL, "head must be 256-byte aligned");
   return depthwise_impl(logits, dtype, R, L, V, E, nullptr, nullptr, head, d_model, rank, root_tok, K, W, B, beta, out,
                         ws, ws_bytes, s);
+}
+
+int build_tree_sequential(const void *logits, int dtype, int R, int L, int V, const uint16_t *E, const void *head,
+                          int d_model, int rank, const int32_t *root_tok, int K, int B, float beta,
+                          const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || K < 1 || K > V || B < 1 || d_model < 1 || rank < 1)
+    return fail(DTREE_E_INVAL, "need R >= 0, L, V, B, d_model, rank >= 1, 1 <= K <= V");
+  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
+  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
+  if (rank != 64 || d_model % 64 != 0 || d_model > 4096 || K > DTREE_MAX_K || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "rank, d_model, K, B or L beyond the compiled envelope");
+  int rc = check_tree(out, B);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits || !E || !root_tok || !head) return fail(DTREE_E_INVAL, "an input pointer is NULL");
+  if ((uintptr_t)E & 15) return fail(DTREE_E_INVAL, "E must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(head) & 255) return fail(DTREE_E_INVAL, "head must be 256-byte aligned");
+  const size_t need = a1_bytes(R * L, V, K) + dt::sequential_call_bytes(R, L, V, K, B, d_model);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(s);
+  A1Ws a1 = a1_carve(ws, R * L, K);
+  dt::RowOut o{a1.lse, nullptr, a1.ids, a1.zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, K, o, a1.rest, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_sequential (row sweep)");
+  dt::SequentialArgs a{logits, dtype, R, L, V, K, B, d_model, beta, E, root_tok};
+  e = dt::launch_sequential(a, a1.zk, a1.ids, tree_out(out), static_cast<char *>(ws) + a1_bytes(R * L, V, K), head, st);
+  if (e != hipSuccess) return hip_fail(e, "build_tree_sequential");
+  return DTREE_OK;
 }
 
 int accept_tree(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype, int R,

@@ -1014,6 +1014,13 @@ static hipError_t launch_head(const uint16_t *U, const uint16_t *P, int L, int V
   return hipGetLastError();
 }
 
+HeadView depthwise_head_view(const void *head, int L, int V, int dm) {
+  const DwLayout l = dw_layout(dw_dims(1, L, V, 1, 1, 1, dm));
+  const char *h = static_cast<const char *>(head);
+  return HeadView{reinterpret_cast<const uint16_t *>(h + l.PT), reinterpret_cast<const uint16_t *>(h + l.UT),
+                  reinterpret_cast<const float *>(h + l.pmax)};
+}
+
 hipError_t launch_depthwise_head(const uint16_t *U, const uint16_t *P, int L, int V, int dm, void *head,
                                  hipStream_t st) {
   return launch_head(U, P, L, V, dm, static_cast<char *>(head), dw_layout(dw_dims(1, L, V, 1, 1, 1, dm)), st);

@@ -76,6 +76,26 @@ hipError_t launch_depthwise_head(const uint16_t *U, const uint16_t *P, int L, in
 hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
                             void *ws, const void *head, hipStream_t st);
 
+// The prepared head's parts (layout of depthwise_head_bytes).
+struct HeadView {
+  const uint16_t *PT, *UT;
+  const float *pmax;
+};
+HeadView depthwise_head_view(const void *head, int L, int V, int dm);
+
+// ---- exact best-first with one correction per popped node (DARTree's sequential baseline) -----------
+struct SequentialArgs {
+  const void *base;  // [R][L][V]
+  int dtype;
+  int R, L, V, K, B, dm;
+  float beta;
+  const uint16_t *E;
+  const int32_t *root_tok;
+};
+size_t sequential_call_bytes(int R, int L, int V, int K, int B, int dm);
+hipError_t launch_sequential(const SequentialArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
+                             void *ws, const void *head, hipStream_t st);
+
 // ---- a7: acceptance walk ------------------------------------------------------------------------
 struct AcceptArgs {
   TreeOut tree;

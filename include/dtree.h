@@ -79,7 +79,8 @@ enum dtree_op {
   DTREE_OP_STATIC = 5,
   DTREE_OP_TDES = 6,
   DTREE_OP_DEPTHWISE_HEAD = 7,     /* the prepared correction head of dtree_prepare_depthwise_head */
-  DTREE_OP_DEPTHWISE_PREPARED = 8  /* the workspace of build_tree_depthwise_prepared */
+  DTREE_OP_DEPTHWISE_PREPARED = 8, /* the workspace of build_tree_depthwise_prepared */
+  DTREE_OP_SEQUENTIAL = 9          /* the workspace of build_tree_sequential */
 };
 
 /* Compiled envelope (DTREE_E_UNSUPPORTED beyond it). */
@@ -103,8 +104,9 @@ typedef struct {
  * Bytes of workspace an operation needs. `op` is a dtree_op; unused size arguments are
  * ignored: TOPK(rows = R*L, V, K), MARGINAL(R, L, V, K, B), DEPTHWISE(R, L, V, K, B, W,
  * rank, d_model), DEPTHWISE_HEAD(L, V, d_model), DEPTHWISE_PREPARED(R, L, V, K, B, W, rank,
- * d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V, B_or_N = cap), STATIC(R, L, V, K),
- * TDES(R, L, V, K). Returns 0 for an unknown op or invalid sizes.
+ * d_model), SEQUENTIAL(R, L, V, K, B, d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V,
+ * B_or_N = cap), STATIC(R, L, V, K), TDES(R, L, V, K). Returns 0 for an unknown op or invalid
+ * sizes.
  */
 size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int W, int rank, int d_model);
 
@@ -181,6 +183,26 @@ int build_tree_depthwise_prepared(const void *logits, int dtype, int R, int L, i
                                   const void *head, int d_model, int rank, const int32_t *root_tok, int K, int W,
                                   int B, float beta, const dtree_tree *out, void *ws, size_t ws_bytes,
                                   dtree_stream_t s);
+
+/*
+ * The exact path-dependent best-first tree built one node at a time: the DARTree summary's
+ * own baseline (method, "decoupling causal correction from best-first search"; results,
+ * tree-construction ablation: sequential correction with a heap). Per round a max-heap of
+ * candidate prefixes; each step pops the best one, runs the correction head for that node
+ * alone (same Markov head, child score and clamp as build_tree_depthwise) and pushes its
+ * children over C_{d+1}, until B nodes are popped or the heap runs dry. Heap order: larger
+ * s, then smaller depth, then the parent's pop order, then the candidate's rank. The tree
+ * is the one build_tree_depthwise gives at W = B, in the same layout; the cost is the point:
+ * B dependent steps (two launches each, all rounds of the call batched in each step).
+ * Takes the prepared head of dtree_prepare_depthwise_head (256-byte aligned); workspace
+ * dtree_workspace_size(DTREE_OP_SEQUENTIAL, R, L, V, K, B, 0, rank, d_model).
+ * Needs beta <= 0 (else DTREE_E_BETA), rank == 64, d_model % 64 == 0, d_model <= 4096,
+ * K <= DTREE_MAX_K, B <= DTREE_MAX_CAP, L <= DTREE_MAX_L, out->cap == B; E 16-byte aligned.
+ * root_tok values must lie in [0, V) (an out-of-range value is read as token 0).
+ */
+int build_tree_sequential(const void *logits, int dtype, int R, int L, int V, const uint16_t *E, const void *head,
+                          int d_model, int rank, const int32_t *root_tok, int K, int B, float beta,
+                          const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
 
 /*
  * TALON gated tree (TALON key designs 1-2): the root's children are the top K_root

@@ -156,7 +156,8 @@ def build_sequential(base_rows: np.ndarray, E: np.ndarray, U: np.ndarray, P: np.
         """One correction call for one node: push its children at depth + 1."""
         if depth >= L:
             return
-        h = bf16_round(np.asarray(E[tok], dtype=np.float64) @ np.asarray(U[depth], dtype=np.float64))
+        erow = np.asarray(E[np.array([tok])], dtype=np.float64)[0]  # rows by index array, as above
+        h = bf16_round(erow @ np.asarray(U[depth], dtype=np.float64))
         z = base_rows[depth] + h @ P64
         lse = logsumexp_row(z)
         for k, c in enumerate(cands[depth]):

@@ -99,6 +99,14 @@ def depthwise_task(args):
     return tree, gaps
 
 
+def sequential_task(args):
+    """(base [L, V] bf16 bits, (tokens, E rows), U bits, P bits, root, K, B, beta) -> (Tree, gaps)."""
+    base, (toks, erows), U_bits, P_bits, root, K, B, beta = args
+    widen = lambda b: (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return depthwise.build_sequential(rowsweep.as_f64(base, "bf16"), GatheredRows(toks, erows), widen(U_bits),
+                                      widen(P_bits), int(root), K, B, beta, with_gaps=True)
+
+
 def greedy_task(args):
     """(parent, token, depth, target rows [n+1, V] bf16 bits) -> (accept_len, node, token)."""
     par, tok, dep, tgt = args

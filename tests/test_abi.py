@@ -258,3 +258,25 @@ def test_depthwise_head_validation():
 
 
 FAKE2 = ctypes.c_void_p(0x100000)  # 256-byte aligned, never dereferenced
+
+
+def test_sequential_validation():
+    """build_tree_sequential rejects bad arguments on the host before any launch."""
+    L = dt.lib()
+    assert dt.workspace_size(dt.OP_SEQUENTIAL, 64, 16, 151936, 8, 128, 0, 64, 1024) > 0
+    assert dt.workspace_size(dt.OP_SEQUENTIAL, 64, 16, 151936, 0, 128, 0, 64, 1024) == 0
+    def call(K=8, B=128, beta=0.0, dm=1024, rank=64, head=FAKE2, E=FAKE2, cap=None, R=4):
+        t = tree(B if cap is None else cap)
+        return L.build_tree_sequential(FAKE2, 0, R, 16, 1000, E, head, dm, rank, FAKE2, K, B, beta,
+                                       ctypes.byref(t), FAKE2, 0, None)
+    assert call(beta=0.1) == -2
+    assert call(K=65) == -4
+    assert call(B=129, cap=129) == -4
+    assert call(rank=32) == -4
+    assert call(dm=8192) == -4
+    assert call(cap=64) == -1          # the tree's cap must equal B
+    assert call(head=None) == -1
+    assert call(head=ctypes.c_void_p(0x100010)) == -1   # head must be 256-byte aligned
+    assert call(E=ctypes.c_void_p(0x100002)) == -1      # E is read with 16-byte loads
+    assert call() == -3
+    assert call(R=0) == 0
