@@ -277,6 +277,14 @@ def main():
         extra_ms["depthwise_" + name] = timed(lambda: dt.build_tree_depthwise_prepared(
             draft, E, head_d, 1024, 64, root, 8, W, 128, 0.0, ws=ws_w, out=t_w))
         mass[name] = round(covered(t_w, 0.0), 4)
+    # the same exact tree built one node at a time: DARTree's sequential correction with a heap
+    # (one correction sweep per popped node, B = 128 dependent steps, the rounds batched per step)
+    ws_q = torch.empty(dt.workspace_size(dt.OP_SEQUENTIAL, R, L, V, 8, 128, 0, 64, 1024), dtype=torch.uint8,
+                       device=dev)
+    t_q = dt.Tree.empty(R, 128, dev)
+    extra_ms["sequential_exact_b128"] = timed(lambda: dt.build_tree_sequential(
+        draft, E, head_d, 1024, 64, root, 8, 128, 0.0, ws=ws_q, out=t_q), n=3)
+    mass["sequential_exact_b128"] = round(covered(t_q, 0.0), 4)
     # the builder that also transposes the head on every call (build_tree_depthwise), W = 32
     extra_ms["depthwise_w32_unprepared_head"] = timed(lambda: dt.build_tree_depthwise(
         draft, E, U, P, root, 8, 32, 128, -0.5, ws=ws_w, out=t_w))
@@ -332,12 +340,18 @@ def main():
     w1 = {k: torch.empty(max(dt.workspace_size(*a), 1), dtype=torch.uint8, device=dev) for k, a in dict(
         m=(dt.OP_MARGINAL, 1, L, V, 64, 64), d=(dt.OP_DEPTHWISE_PREPARED, 1, L, V, 8, 128, 32, 64, 1024),
         g=(dt.OP_GATED, 1, L, V, 0, 60), s=(dt.OP_STATIC, 1, L, V, 10), e=(dt.OP_TDES, 1, L, V, 32),
-        a=(dt.OP_ACCEPT, 1, L, V, 0, 64)).items()}
+        a=(dt.OP_ACCEPT, 1, L, V, 0, 64), q=(dt.OP_SEQUENTIAL, 1, L, V, 8, 128, 0, 64, 1024),
+        x=(dt.OP_DEPTHWISE_PREPARED, 1, L, V, 8, 128, 128, 64, 1024)).items()}
+    tq1, tx1 = dt.Tree.empty(1, 128, dev), dt.Tree.empty(1, 128, dev)
     tm_1 = one(t_m, 64)
     ops1 = {
         "marginal": lambda i: dt.build_tree_marginal(r1["draft"], 64, 64, 0.0, ws=w1["m"], out=tm1),
         "depthwise": lambda i: dt.build_tree_depthwise_prepared(r1["draft"], E, head_d, 1024, 64, r1["root"], 8, 32,
                                                                 128, -0.5, ws=w1["d"], out=td1),
+        "depthwise_exact_w128": lambda i: dt.build_tree_depthwise_prepared(
+            r1["draft"], E, head_d, 1024, 64, r1["root"], 8, 128, 128, 0.0, ws=w1["x"], out=tx1),
+        "sequential_exact_b128": lambda i: dt.build_tree_sequential(r1["draft"], E, head_d, 1024, 64, r1["root"], 8,
+                                                                    128, 0.0, ws=w1["q"], out=tq1),
         "gated": lambda i: dt.build_tree_gated(r1["talon"], 10, 0.03, 60, ws=w1["g"], out=tg1),
         "static_k10_d6": lambda i: dt.build_tree_static(r1["talon"], 10, 6, ws=w1["s"], out=ts1),
         "tdes_k32_b128": lambda i: dt.build_tree_tdes(r1["draft"], r1["root_g"], mlp, 32, 128, ws=w1["e"], out=tt1),

@@ -384,7 +384,7 @@ int build_tree_sequential(const void *logits, int dtype, int R, int L, int V, co
     return fail(DTREE_E_INVAL, "need R >= 0, L, V, B, d_model, rank >= 1, 1 <= K <= V");
   if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
   if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
-  if (rank != 64 || d_model % 64 != 0 || d_model > 4096 || K > DTREE_MAX_K || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
+  if (rank != 64 || d_model % 256 != 0 || K > DTREE_MAX_K || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
     return fail(DTREE_E_UNSUPPORTED, "rank, d_model, K, B or L beyond the compiled envelope");
   int rc = check_tree(out, B);
   if (rc) return rc;

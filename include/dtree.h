@@ -196,8 +196,8 @@ int build_tree_depthwise_prepared(const void *logits, int dtype, int R, int L, i
  * B dependent steps (two launches each, all rounds of the call batched in each step).
  * Takes the prepared head of dtree_prepare_depthwise_head (256-byte aligned); workspace
  * dtree_workspace_size(DTREE_OP_SEQUENTIAL, R, L, V, K, B, 0, rank, d_model).
- * Needs beta <= 0 (else DTREE_E_BETA), rank == 64, d_model % 64 == 0, d_model <= 4096,
- * K <= DTREE_MAX_K, B <= DTREE_MAX_CAP, L <= DTREE_MAX_L, out->cap == B; E 16-byte aligned.
+ * Needs beta <= 0 (else DTREE_E_BETA), rank == 64, d_model % 256 == 0, K <= DTREE_MAX_K,
+ * B <= DTREE_MAX_CAP, L <= DTREE_MAX_L, out->cap == B; E 16-byte aligned.
  * root_tok values must lie in [0, V) (an out-of-range value is read as token 0).
  */
 int build_tree_sequential(const void *logits, int dtype, int R, int L, int V, const uint16_t *E, const void *head,

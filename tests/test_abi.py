@@ -273,7 +273,7 @@ def test_sequential_validation():
     assert call(K=65) == -4
     assert call(B=129, cap=129) == -4
     assert call(rank=32) == -4
-    assert call(dm=8192) == -4
+    assert call(dm=1088) == -4         # d_model % 256 != 0
     assert call(cap=64) == -1          # the tree's cap must equal B
     assert call(head=None) == -1
     assert call(head=ctypes.c_void_p(0x100010)) == -1   # head must be 256-byte aligned
