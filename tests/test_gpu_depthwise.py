@@ -41,6 +41,9 @@ def check(base_host, dtype, E, U, P, root, K, W, B, beta, rounds=None):
     (3, 5, 1001, 64, 4, 16, 30, -0.2, 3),     # odd V: ragged 32-token block
     (2, 4, 500, 64, 16, 64, 100, 0.0, 4),     # two 32-branch tiles per round
     (3, 7, 300, 64, 5, 1, 7, -0.1, 5),        # width 1: one corrected chain
+    (3, 5, 900, 64, 32, 32, 90, -0.3, 6),     # L K^2 > 4096: log q~ rows staged depth by depth
+    (2, 3, 700, 64, 64, 16, 40, 0.0, 7),      # K = 64: sixteen sorted lists per depth
+    (2, 4, 800, 64, 10, 100, 128, -0.2, 8),   # W = 100 (two keys per lane), ragged last list
 ])
 def test_depthwise_small(R, L, V, dm, K, W, B, beta, seed):
     base = synth.ddtree_logits(seed=seed, R=R, L=L, V=V)
