@@ -370,11 +370,11 @@ DT_INLINE double wg_lse2_1(const Row<T> &A, float s, Red &red) {
   return (double)MA + log2(SA);
 }
 
-// First index of the maximum of one row. Each thread sees its elements in increasing index
-// order and keeps the first of its largest (compare and select); the threads' results are
-// combined as (value desc, id asc) keys.
+// The largest (value desc, id asc) key of a row whose element i has id id0 + i (0 for an
+// empty row). Each thread sees its elements in increasing index order and keeps the first of
+// its largest (compare and select); the threads' keys are combined by their maximum.
 template <typename T>
-DT_INLINE int wg_row_argmax(const Row<T> &A, Red &red) {
+DT_INLINE uint64_t wg_row_argmax_key(const Row<T> &A, Red &red, int id0) {
   float bm = -kInf;
   int bi = -1;
   stream1(A, [&](int u, const float *z) {
@@ -385,7 +385,7 @@ DT_INLINE int wg_row_argmax(const Row<T> &A, Red &red) {
       bi = gt ? u * 8 + e : bi;
     }
   });
-  uint64_t best = bi >= 0 ? make_key(bm, (uint32_t)bi) : 0ull;
+  uint64_t best = bi >= 0 ? make_key(bm, (uint32_t)(id0 + bi)) : 0ull;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const uint64_t x = __shfl_xor(best, o, 64);
@@ -397,7 +397,12 @@ DT_INLINE int wg_row_argmax(const Row<T> &A, Red &red) {
   uint64_t b = red.k[0];
 #pragma unroll
   for (int i = 1; i < AC_NW; ++i) b = red.k[i] > b ? red.k[i] : b;
-  return (int)key_id(b);
+  return b;
+}
+// First index of the maximum of one row.
+template <typename T>
+DT_INLINE int wg_row_argmax(const Row<T> &A, Red &red) {
+  return (int)key_id(wg_row_argmax_key(A, red, 0));
 }
 
 // C(t) = sum_v (p - t q)_+; the float sums of the 64-token blocks go to blk[] (block b is
@@ -1210,7 +1215,8 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
     return xfail != 0;
   };
   const T *target = static_cast<const T *>(a.target) + (size_t)r * (cap + 1) * a.V;
-  const T *draft = static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V;
+  // no draft rows at T = 0
+  const T *draft = a.draft ? static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V : nullptr;
   const float s = log2_scale(a.T);
   const uint64_t trial = a.trial0;
   uint32_t step = 0;
@@ -1222,7 +1228,36 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
   bn.cnt = bcnt;
   bn.off = boff;
   bn.list = a_list + (size_t)r * a.V + e0;
-  for (;;) {
+  if (a.T == 0.f) {
+    // greedy walk: each workgroup's argmax key over its range of the node's target row, the
+    // four combined by their maximum (value desc, id asc); then the child carrying it
+    for (bool lists0 = false;;) {
+      const uint64_t k[1] = {wg_row_argmax_key(make_row(target + (size_t)j * a.V + e0, len), red, e0)};
+      if (exchange(k, 1)) {
+        failed = true;
+        break;
+      }
+      uint64_t best = got[0][0];
+      for (int w = 1; w < AC_NS; ++w) best = got[w][0] > best ? got[w][0] : best;
+      const int ts = (int)key_id(best);
+      if (!lists0) {
+        build_children(par, tok, n, a.V, fc, ns, sr, pv);
+        lists0 = true;
+      }
+      int nxt = -1;
+      for (int c = fc[j]; c >= 0; c = ns[c])
+        if (tok[c] == ts) {
+          nxt = c;
+          break;
+        }
+      if (nxt < 0) {
+        out_tok = ts;
+        break;
+      }
+      j = nxt;
+    }
+  }
+  for (; a.T > 0.f;) {
     const T *zt = target + (size_t)j * a.V;
     const T *zd = draft + (size_t)draft_row(j == 0 ? a.tree.depth[tb] : dep[j], a.L) * a.V;
     const Row<T> A = make_row(zt + e0, len), B = make_row(zd + e0, len);
@@ -1631,9 +1666,10 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
   const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
   if (a.T == 0.f || a.n_trials == 1) {
     const size_t shm = accept_lds_bytes(a.V);
-    if (a.T > 0.f && !a.match) {
-      // residual walk with one trial: AC_NS workgroups per round when the whole grid fits on
-      // the device at once (its workgroups wait for each other), else one workgroup per round
+    if (a.T == 0.f || !a.match) {
+      // greedy walk, or residual walk with one trial: AC_NS workgroups per round when the
+      // whole grid fits on the device at once (its workgroups wait for each other), else one
+      // workgroup per round
       const int capacity = a.dtype == DTREE_BF16 ? coop_capacity<uint16_t>(shm) : coop_capacity<float>(shm);
       if ((long long)a.R * AC_NS <= (long long)capacity) {
         const size_t slots = (size_t)a.R * (a.tree.cap + 1);

@@ -54,6 +54,37 @@ def test_greedy_walk_matches_oracle(R, L, V, B):
             assert (alen[t, r], anode[t, r], nxt[t, r]) == ref
 
 
+def test_greedy_walk_one_workgroup_fallback():
+    """600 rounds do not fit as four workgroups each, so the greedy walk runs one workgroup
+    per round (the path every R up to the device's capacity / 4 skips); against the oracle."""
+    R, L, V, B = 600, 4, 1000, 16
+    draft = synth.ddtree_logits(seed=41, R=R, L=L, V=V)
+    trees = [t for t, _ in op.pmap(op.marginal_task, [(draft[r], "bf16", 16, B, 0.0) for r in range(R)])]
+    depth = np.stack([t.arrays(B)[2] for t in trees])
+    target = synth.verification_target(draft, depth, seed=42)
+    alen, anode, nxt = host_outs(dt.accept_tree(oracle_to_device(trees, B), dev_bf16(target), None, 0.0, SEED, 0, 1))
+    for r in range(R):
+        ref = accept.walk_greedy(trees[r].parent, trees[r].token, trees[r].depth,
+                                 rowsweep.as_f64(target[r, :trees[r].n + 1], "bf16"))
+        assert (alen[0, r], anode[0, r], nxt[0, r]) == ref
+
+
+@pytest.mark.parametrize("V", [1, 63, 200])
+def test_greedy_walk_vocabulary_smaller_than_four_ranges(V):
+    """V below four 64-token blocks leaves some of a round's four ranges empty."""
+    R, L, B = 6, 3, 8
+    draft = synth.ddtree_logits(seed=43 + V, R=R, L=L, V=V)
+    trees = [marginal.build_marginal(rowsweep.as_f64(draft[r], "bf16"), min(B, V), B, 0.0) for r in range(R)]
+    depth = np.stack([t.arrays(B)[2] for t in trees])
+    target = synth.verification_target(draft, depth, seed=44)
+    alen, anode, nxt = host_outs(dt.accept_tree(oracle_to_device(trees, B), dev_bf16(target), None, 0.0, SEED, 0, 2))
+    for r in range(R):
+        ref = accept.walk_greedy(trees[r].parent, trees[r].token, trees[r].depth,
+                                 rowsweep.as_f64(target[r, :trees[r].n + 1], "bf16"))
+        for t in range(2):
+            assert (alen[t, r], anode[t, r], nxt[t, r]) == ref
+
+
 def test_greedy_walk_noise_free_target_follows_argmax_chain():
     R, L, V, B = 4, 16, 3000, 64
     draft = synth.ddtree_logits(seed=9, R=R, L=L, V=V)
