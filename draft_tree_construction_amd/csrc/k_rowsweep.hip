@@ -575,46 +575,65 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   }
 }
 
-// Merge the S partials of each row.
+// Merge the S partials of each row. Each split's K keys arrive sorted (value desc, id asc;
+// 0 pads a split with fewer than K elements) and keys are unique, so a key's rank in the row
+// is its position in its own split plus, per other split, the number of that split's keys
+// above it (a binary search); a key ranked below K writes its output entry. The row's LSE
+// folds the splits' (max, sum) pairs, one exp2 per split in parallel, summed in split order.
 __global__ __launch_bounds__(RS_NT) void k_rowsweep_merge(int K, int S, RowPart part, RowOut out) {
   __shared__ uint64_t buf[RS_MBUF];
-  __shared__ double s_lse;
+  __shared__ double s_term[RS_MBUF];  // S <= RS_MBUF / K splits
+  __shared__ int s_real;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = S * K;
-  const int np = next_pow2(n);
-  for (int i = tid; i < np; i += RS_NT) buf[i] = (i < n) ? part.keys[(size_t)row * S * K + i] : 0ull;
-  if (tid == 0) {
-    // partials: (MH, sum) with the sum relative to 2^MH, MH on the log2 scale
-    float M = -kInf;
-    for (int i = 0; i < S; ++i) M = fmaxf(M, part.m[(size_t)row * S + i]);
-    double St = 0.0;
-    for (int i = 0; i < S; ++i) {
-      const float mi = part.m[(size_t)row * S + i];
-      if (mi != -kInf) St += part.s[(size_t)row * S + i] * exp2((double)mi - (double)M);
-    }
-    s_lse = kLn2d * ((double)M + log2(St));
+  for (int i = tid; i < n; i += RS_NT) buf[i] = part.keys[(size_t)row * n + i];
+  if (tid == 0) s_real = 0;
+  // partials: (MH, sum) with the sum relative to 2^MH, MH on the log2 scale
+  float M = -kInf;
+  for (int i = 0; i < S; ++i) M = fmaxf(M, part.m[(size_t)row * S + i]);
+  for (int i = tid; i < S; i += RS_NT) {
+    const float mi = part.m[(size_t)row * S + i];
+    s_term[i] = mi != -kInf ? part.s[(size_t)row * S + i] * exp2((double)mi - (double)M) : 0.0;
   }
   __syncthreads();
-  block_sort_desc_u64<RS_NT>(buf, np);
-  const double lse = s_lse;
+  double St = 0.0;
+  for (int i = 0; i < S; ++i) St += s_term[i];
+  const double lse = kLn2d * ((double)M + log2(St));
   if (tid == 0) {
     if (out.lse_d) out.lse_d[row] = lse;
     if (out.lse_f) out.lse_f[row] = (float)lse;
   }
-  for (int k = tid; k < K; k += RS_NT) {
-    const size_t o = (size_t)row * K + k;
-    const uint64_t key = buf[k];
-    if (key != 0) {
+  int real = 0;
+  for (int x = tid; x < n; x += RS_NT) {
+    const uint64_t key = buf[x];
+    if (key == 0) continue;
+    ++real;
+    const int l = x / K;
+    int rank = x - l * K;
+    for (int l2 = 0; l2 < S; ++l2) {
+      if (l2 == l) continue;
+      const uint64_t *b2 = buf + (size_t)l2 * K;
+      int lo = 0;  // keys of split l2 above key: a prefix of its sorted list
+      for (int step = next_pow2(K); step >= 1; step >>= 1)
+        if (lo + step <= K && b2[lo + step - 1] > key) lo += step;
+      rank += lo;
+    }
+    if (rank < K) {
+      const size_t o = (size_t)row * K + rank;
       const float zv = key_val(key);
       out.ids[o] = (int32_t)key_id(key);
       if (out.zk) out.zk[o] = zv;
       if (out.lp) out.lp[o] = (float)((double)zv - lse);
-    } else {
-      out.ids[o] = -1;
-      if (out.zk) out.zk[o] = -kInf;
-      if (out.lp) out.lp[o] = -kInf;
     }
+  }
+  if (real) atomicAdd(&s_real, real);
+  __syncthreads();
+  for (int k = min(s_real, K) + tid; k < K; k += RS_NT) {  // fewer than K elements in the row
+    const size_t o = (size_t)row * K + k;
+    out.ids[o] = -1;
+    if (out.zk) out.zk[o] = -kInf;
+    if (out.lp) out.lp[o] = -kInf;
   }
 }
 
