@@ -47,7 +47,7 @@ constexpr int DW_NT = 256;
 constexpr int DW_TT = 1024;  // per-round tree workgroup
 constexpr int DW_CNT = 1024;   // correction sweep workgroup: DW_CW tiles share each staged P^T block
 constexpr int DW_CW = DW_CNT / 64;
-constexpr int DW_NC = 64;      // V chunks (partials per state)
+constexpr int DW_NC = 64;      // V chunks (partials per state) when the tiles alone fill the GPU
 constexpr int DW_HX = 80;      // state row: h (64), -ref, one-hot base (8), 1 (mask), zero padding
 constexpr int DW_SUP = 2048;   // super-tree nodes per round (L * W)
 constexpr int DW_CH = 1024;    // children per depth (W * K)
@@ -74,6 +74,7 @@ DT_INLINE uint16_t f32_to_bf16_up(float x) {
 struct DwDims {
   int R, L, V, K, W, B, dm;
   int Kp, np, Rp, S, ntile;
+  int NC;  // V chunks of the correction sweep: DW_NC, more when few tiles would leave CUs idle
 };
 static DwDims dw_dims(int R, int L, int V, int K, int W, int B, int dm) {
   DwDims g;
@@ -90,6 +91,10 @@ static DwDims dw_dims(int R, int L, int V, int K, int W, int B, int dm) {
   g.Rp = (R + g.np - 1) / g.np * g.np;
   g.S = L * g.Rp * g.Kp;
   g.ntile = g.S / 32;
+  // the sweep runs (tile groups of DW_CW) x NC workgroups: at least 256 of them (the CUs)
+  const int TG = (g.ntile + DW_CW - 1) / DW_CW;
+  g.NC = DW_NC;
+  if (TG * DW_NC < 256) g.NC = min(256, ((256 + TG - 1) / TG + 7) / 8 * 8);
   return g;
 }
 DT_INLINE int dw_slot(const DwDims &g, int d, int r, int k) { return ((d - 1) * g.Rp + r) * g.Kp + k; }
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(DW_CNT) void k_dw_corr(DwState s, const T *__restri
   const int i = blockIdx.x, xcd = i & 7, j = i >> 3;
   const int c = xcd + 8 * (j / TG);
   const int gi = j - (j / TG) * TG;
-  if (c >= DW_NC) return;
+  if (c >= g.NC) return;
   // the wave index is uniform: tile and the quantities built from it live in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int t = gi * DW_CW + wave;
@@ -373,8 +378,8 @@ __global__ __launch_bounds__(DW_CNT) void k_dw_corr(DwState s, const T *__restri
   for (int kb = 0; kb < 5; ++kb) bfr[kb] = as_bf16x8(hrow[2 * kb + half]);
   const bool wide = s.wide[tc] != 0;
   const int ng = ((V + 31) / 32 + 5) / 6;  // six-block groups over the row
-  const int blk0 = 6 * (int)(((long long)ng * c) / DW_NC);
-  const int nblk = 6 * (int)(((long long)ng * (c + 1)) / DW_NC) - blk0;
+  const int blk0 = 6 * (int)(((long long)ng * c) / g.NC);
+  const int nblk = 6 * (int)(((long long)ng * (c + 1)) / g.NC) - blk0;
   const int blast = blk0 + nblk - 1;
   // fp32 bases are added after the MFMA: this lane's state column belongs to round r0 + col / Kp
   const T *lane_base = base + ((size_t)min(tile_r0(tc) + (g.Kp <= 32 ? col / g.Kp : 0), g.R - 1) * g.L +
@@ -567,15 +572,15 @@ __global__ __launch_bounds__(DW_CNT) void k_dw_corr(DwState s, const T *__restri
     tot = ((m == -kInf) ? 0.0 : acc * exp((double)m - (double)mm)) + ((mo == -kInf) ? 0.0 : ao * exp((double)mo - (double)mm));
   }
   if (active && half == 0) {
-    const size_t o = ((size_t)t * 32 + col) * DW_NC + c;
+    const size_t o = ((size_t)t * 32 + col) * g.NC + c;
     s.part_s[o] = tot;
     s.part_m[o] = mm;
   }
 }
 
 // ---------------------------------------------------------------- log q~ of every state
-// One workgroup per tile of 32 slots: the state's logsumexp from its DW_NC chunk partials
-// (8 lanes per state, each folding DW_NC/8 partials relative to their own maxima), then
+// One workgroup per tile of 32 slots: the state's logsumexp from its NC chunk partials
+// (8 lanes per state, each folding NC/8 partials relative to their own maxima), then
 // log q~(c | state) = z[c] - LSE for the K candidates c of the depth, with
 // z[c] = base(c) + h . P[:, c] summed in the slot order of the P^T row. None of this depends
 // on which branches get selected, so it runs for all depths at once.
@@ -590,15 +595,16 @@ __global__ __launch_bounds__(DW_NT) void k_dw_lq(DwState s, DwDev a, DwDims g) {
   {
     const int row = tid >> 3, l8 = tid & 7;
     const int sl = t * 32 + row;
-    const size_t o = (size_t)sl * DW_NC + l8 * (DW_NC / 8);
+    const int per = g.NC / 8;
+    const size_t o = (size_t)sl * g.NC + l8 * per;
     float M = -kInf;
 #pragma unroll
-    for (int c = 0; c < DW_NC / 8; ++c) M = fmaxf(M, s.part_m[o + c]);
+    for (int c = 0; c < per; ++c) M = fmaxf(M, s.part_m[o + c]);
 #pragma unroll
     for (int x = 1; x < 8; x <<= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
     double S = 0.0;
 #pragma unroll
-    for (int c = 0; c < DW_NC / 8; ++c) {
+    for (int c = 0; c < per; ++c) {
       const float mc = s.part_m[o + c];
       if (mc != -kInf) S += s.part_s[o + c] * (double)__builtin_amdgcn_exp2f((mc - M) * kLog2e);
     }
@@ -986,8 +992,8 @@ static DwLayout dw_layout(const DwDims &g) {
   l.hx = take((size_t)g.S * DW_HX * 2);
   l.bref = take((size_t)g.S * sizeof(float));
   l.wide = take((size_t)g.ntile * sizeof(int));
-  l.part_s = take((size_t)g.S * DW_NC * sizeof(double));
-  l.part_m = take((size_t)g.S * DW_NC * sizeof(float));
+  l.part_s = take((size_t)g.S * g.NC * sizeof(double));
+  l.part_m = take((size_t)g.S * g.NC * sizeof(float));
   l.lq = take((size_t)g.S * g.K * sizeof(double));
   l.calls = o;
   return l;
@@ -1059,7 +1065,7 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int TG = (g.ntile + DW_CW - 1) / DW_CW;
-  const dim3 gcorr((unsigned)(8 * TG * (DW_NC / 8)));
+  const dim3 gcorr((unsigned)(8 * TG * (g.NC / 8)));
   if (a.dtype == DTREE_BF16) {
     const uint16_t *b16 = static_cast<const uint16_t *>(a.base);
     const bool bvec = (a.V & 7) == 0 && (reinterpret_cast<uintptr_t>(b16) & 15) == 0;
