@@ -597,16 +597,38 @@ __global__ __launch_bounds__(DW_NT) void k_dw_lq(DwState s, DwDev a, DwDims g) {
     const int sl = t * 32 + row;
     const int per = g.NC / 8;
     const size_t o = (size_t)sl * g.NC + l8 * per;
+    // the lane's partials in 16-byte pieces when they come in fours (NC % 32 == 0; the
+    // arrays are 256-byte aligned), else one by one; the same terms in the same order
+    const bool v4 = (per & 3) == 0;
     float M = -kInf;
-#pragma unroll
-    for (int c = 0; c < per; ++c) M = fmaxf(M, s.part_m[o + c]);
+    if (v4) {
+      const float4 *pm = reinterpret_cast<const float4 *>(s.part_m + o);
+      for (int c = 0; c < per / 4; ++c) {
+        const float4 m4 = pm[c];
+        M = fmaxf(fmaxf(fmaxf(M, m4.x), m4.y), fmaxf(m4.z, m4.w));
+      }
+    } else {
+      for (int c = 0; c < per; ++c) M = fmaxf(M, s.part_m[o + c]);
+    }
 #pragma unroll
     for (int x = 1; x < 8; x <<= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
     double S = 0.0;
-#pragma unroll
-    for (int c = 0; c < per; ++c) {
-      const float mc = s.part_m[o + c];
-      if (mc != -kInf) S += s.part_s[o + c] * (double)__builtin_amdgcn_exp2f((mc - M) * kLog2e);
+    auto term = [&](float mc, double sc) {
+      if (mc != -kInf) S += sc * (double)__builtin_amdgcn_exp2f((mc - M) * kLog2e);
+    };
+    if (v4) {
+      const float4 *pm = reinterpret_cast<const float4 *>(s.part_m + o);
+      const double2 *ps = reinterpret_cast<const double2 *>(s.part_s + o);
+      for (int c = 0; c < per / 4; ++c) {
+        const float4 m4 = pm[c];
+        const double2 s0 = ps[2 * c], s1 = ps[2 * c + 1];
+        term(m4.x, s0.x);
+        term(m4.y, s0.y);
+        term(m4.z, s1.x);
+        term(m4.w, s1.y);
+      }
+    } else {
+      for (int c = 0; c < per; ++c) term(s.part_m[o + c], s.part_s[o + c]);
     }
 #pragma unroll
     for (int x = 1; x < 8; x <<= 1) S += __shfl_xor(S, x, 64);
