@@ -13,8 +13,8 @@ Timed outside the step and reported under extra_ms: the matching walk, DARTree's
 (W = B) and fixed (W = B / L) widths, the static D x K grid (K = 10, D = 6) and GRAFT's
 edge-scored best-first tree (K = 32, B = 128).
 value = rounds per second of that whole step (R / step time). The step's independent parts
-run concurrently: 1 -> 4 -> 5 (the walks need the marginal trees) on the main stream, 2 and
-3 on two more streams of default priority, joined at the end of every step; the
+run concurrently: 1 -> 4 -> 5 (the walks need the marginal trees) on the main stream,
+2 -> 3 on a second stream of default priority, joined at the end of every step; the
 per-operation breakdown comes from the same work serialised on one stream after the timed
 region. Inputs are resident in HBM before timing. Prints one JSON line.
 
@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "rowsweep_traffic.json"))
     ap.add_argument("--step-only", action="store_true",
@@ -151,28 +151,25 @@ def main():
     stream = torch.cuda.current_stream(dev)
     names = ["marginal", "depthwise", "gated", "accept_t0", "accept_t1"]
     # the step's schedule: the marginal tree and the two walks on it (a chain) on the main
-    # stream, the depth-wise and the gated builders (independent of it and of each other) on
-    # two more streams of default priority, joined at the end of the step
-    s_dw, s_g = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    # stream, the depth-wise then the gated builder (independent of it) on one more stream of
+    # default priority, forked at the start of the step and joined at its end; of the orders
+    # tried (each side builder on its own stream, the side work started after the marginal
+    # tree or after the walks) this one finished soonest
+    s_side = torch.cuda.Stream(dev)
 
     def step_overlap(i):
-        # the marginal tree first (the walks wait for it), then the two independent builders
-        # on their streams, then the walks; of the orders tried this one finished soonest
         fork = torch.cuda.Event()
         fork.record(stream)
-        for s2 in (s_dw, s_g):
-            s2.wait_event(fork)
-        dt.build_tree_marginal(draft, 64, 64, 0.0, ws=ws_m, out=t_m)
-        with torch.cuda.stream(s_dw):
+        s_side.wait_event(fork)
+        with torch.cuda.stream(s_side):
             dt.build_tree_depthwise_prepared(draft, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_d, out=t_d)
-        with torch.cuda.stream(s_g):
             dt.build_tree_gated(talon, 10, 0.03, 60, ws=ws_g, out=t_g)
+        dt.build_tree_marginal(draft, 64, 64, 0.0, ws=ws_m, out=t_m)
         dt.accept_tree(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
         dt.accept_tree(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
-        for s2 in (s_dw, s_g):
-            join = torch.cuda.Event()
-            join.record(s2)
-            stream.wait_event(join)
+        join = torch.cuda.Event()
+        join.record(s_side)
+        stream.wait_event(join)
 
     def step(i, ev=None):
         def mark(k):
@@ -420,7 +417,7 @@ def main():
                                "beta=-0.5,E 151936x1024,rank 64 (head prepared once) + gated K_root=10,mu=0.03,N=60 + "
                                "accept T=0 and T=1 (1 trial/round) on the marginal trees",
                    "rounds": R, "L": L, "V": V},
-        "schedule": "marginal -> accept T=0 -> accept T=1 on one stream, depthwise and gated on two more "
+        "schedule": "marginal -> accept T=0 -> accept T=1 on one stream, depthwise -> gated on a second "
                     "(default priority), forked and joined per step",
         "walk_failures": walk_failures,
         "breakdown_us_per_round": {n: round(float(per[:, k].mean()) * 1e3 / R, 3) for k, n in enumerate(names)},
