@@ -16,12 +16,15 @@ value = rounds per second of that whole step (R / step time). The step's indepen
 run concurrently: 1 -> 4 -> 5 (the walks need the marginal trees) on the main stream,
 2 -> 3 on a second stream of default priority, joined at the end of every step; the
 per-operation breakdown comes from the same work serialised on one stream after the timed
-region. Inputs are resident in HBM before timing. Prints one JSON line.
+region (breakdown_ms: the median per operation over as many serialised steps as timed
+steps; breakdown_ms_mean the mean). Inputs are resident in HBM before timing. Prints one
+JSON line.
 
 The roofline object is for the logits row sweep (fused log-softmax + top-K), the
 kernel every builder runs over its [R, L, V] logits, timed live with HIP events over
 K launches of dtree_topk_logsoftmax on the same stream; algorithmic bytes per launch
-= R*L*V*2 (each bf16 logit read once) + the K-list outputs.
+= R*L*V*2 (each bf16 logit read once) + the K-list outputs; traffic_gbps is the counter
+bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled) over the same launch time.
 """
 from __future__ import annotations
 
@@ -205,7 +208,7 @@ def main():
     walk_failures = int((o0[0] < 0).sum().item() + (o1[0] < 0).sum().item())
     # the same work serialised on one stream, timed per operation with HIP events (outside
     # the timed region): the per-operation breakdown
-    n_ser = 2 if args.step_only else max(5, args.steps // 2)
+    n_ser = 2 if args.step_only else max(5, args.steps)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_ser)]
     for i in range(n_ser):
         step(args.warmup + args.steps + i, evs[i])
@@ -216,7 +219,7 @@ def main():
         print(json.dumps({"metric": "tree-build rounds/sec (step serialised, profiler pass)", "value": round(value, 1),
                           "unit": "rounds/s", "steps": args.steps, "warmup": args.warmup,
                           "ms_per_step": round(ms_per_step, 4),
-                          "breakdown_ms": {n: round(float(per[:, k].mean()), 4) for k, n in enumerate(names)}}),
+                          "breakdown_ms": {n: round(float(np.median(per[:, k])), 4) for k, n in enumerate(names)}}),
               flush=True)
         return
 
@@ -259,6 +262,7 @@ def main():
             traffic = None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_gbps": round(traffic / (sweep_alt * 1e-6) / 1e9, 1) if traffic else None,
                 "kernel": "k_rowsweep<bf16> (dtree_topk_logsoftmax, R*L=1024 rows, K=64)",
                 "us_per_launch": round(sweep_alt, 2), "alg_bytes_per_launch": alg_bytes,
                 "launches": "alternating two distinct 311 MB tensors",
@@ -420,8 +424,10 @@ def main():
         "schedule": "marginal -> accept T=0 -> accept T=1 on one stream, depthwise -> gated on a second "
                     "(default priority), forked and joined per step",
         "walk_failures": walk_failures,
-        "breakdown_us_per_round": {n: round(float(per[:, k].mean()) * 1e3 / R, 3) for k, n in enumerate(names)},
-        "breakdown_ms": {n: round(float(per[:, k].mean()), 4) for k, n in enumerate(names)},
+        "breakdown_us_per_round": {n: round(float(np.median(per[:, k])) * 1e3 / R, 3) for k, n in enumerate(names)},
+        "breakdown_ms": {n: round(float(np.median(per[:, k])), 4) for k, n in enumerate(names)},
+        "breakdown_ms_mean": {n: round(float(per[:, k].mean()), 4) for k, n in enumerate(names)},
+        "breakdown_calls": n_ser,
         "event_ms_per_step_serial": round(step_ms, 4),
         "roofline": roofline,
         "extra_ms": extra_ms,
