@@ -161,6 +161,34 @@ def test_sampled_walk_full_config_one_trial_against_oracle():
     assert n == 512 and bad <= n // 1000, (bad, n)
 
 
+MAX_ACCEPT_V = 262144  # DTREE_MAX_ACCEPT_V in include/dtree.h
+
+
+def test_walks_at_the_largest_vocabulary():
+    """accept_tree's envelope edge, V = 262,144 (the walk's dynamic LDS is largest there):
+    the four-workgroup walks -- greedy, and T = 1 with one trial for trial indices 0..3 --
+    against the oracle; a T = 1 mismatch only where the oracle's margin is <= 1e-6."""
+    R, L, V, B = 3, 4, MAX_ACCEPT_V, 16
+    draft, trees, target = verification_case(R, L, V, B)
+    dtree, tg, dr = oracle_to_device(trees, B), dev_bf16(target), dev_bf16(draft)
+    alen, anode, nxt = host_outs(dt.accept_tree(dtree, tg, None, 0.0, SEED, 0, 1))
+    for r in range(R):
+        ref = accept.walk_greedy(trees[r].parent, trees[r].token, trees[r].depth,
+                                 rowsweep.as_f64(target[r, :trees[r].n + 1], "bf16"))
+        assert (alen[0, r], anode[0, r], nxt[0, r]) == ref
+    trials = range(4)
+    ref = sampled_oracle(trees, target, draft, trials)
+    bad = n = 0
+    for t in trials:
+        alen, anode, nxt = host_outs(dt.accept_tree(dtree, tg, dr, 1.0, SEED, t, 1))
+        assert np.all(alen >= 0), "a round reported a failed walk"
+        for r in range(R):
+            b, k = compare_with_margins([(alen[0, r], anode[0, r], nxt[0, r])], [ref[r][0][t]])
+            bad += b
+            n += k
+    assert n == R * len(trials) and bad <= 1, (bad, n)
+
+
 def test_sampled_walk_full_vocab_frequencies():
     """Four rounds of the full-size verification config, 10^6 trials each (the table walk):
     stop-node frequencies within 3 sigma of the oracle's exact law, and the extra token's

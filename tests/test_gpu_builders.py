@@ -56,6 +56,7 @@ def test_marginal_tiny_config():
     (3, 3, 50, 50, 30, -2.0),
     (3, 1, 1000, 10, 10, 0.0),      # L = 1
     (2, 5, 40, 1, 5, 0.0),          # K = 1: argmax chain
+    (2, 64, 700, 8, 128, -0.1),     # L = DTREE_MAX_L: 64 positions
 ])
 def test_marginal_ddtree_shape_small(R, L, V, K, B, beta):
     host = synth.ddtree_logits(seed=20 + V, R=R, L=L, V=V)
@@ -105,6 +106,7 @@ def check_gated(host, K_root, mu, N, full_pool):
     (4, 6, 64, 5, 1e-30, 40),
     (3, 10, 200, 3, 1.0, 50),
     (3, 16, 2000, 10, 0.03, 60),
+    (2, 64, 400, 6, 0.05, 70),   # L = DTREE_MAX_L, N - K_root = DTREE_MAX_K
 ])
 def test_gated_small(R, L, V, K_root, mu, N):
     host = synth.talon_logits(seed=40 + V, R=R, L=L, V=V)

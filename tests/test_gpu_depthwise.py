@@ -50,6 +50,7 @@ def check(base_host, dtype, E, U, P, root, K, W, B, beta, rounds=None):
     (2, 4, 800, 64, 10, 100, 128, -0.2, 8),   # W = 100 (two keys per lane), ragged last list
     (12, 16, 2500, 64, 8, 32, 128, -0.5, 9),  # three tile groups: 88 V chunks, partials one by one
     (8, 16, 2500, 64, 8, 32, 128, -0.5, 10),  # two tile groups: 128 V chunks
+    (2, 64, 600, 64, 4, 8, 128, -0.3, 11),    # L = DTREE_MAX_L: 64 depths, 512 super-tree nodes
 ])
 def test_depthwise_small(R, L, V, dm, K, W, B, beta, seed):
     base = synth.ddtree_logits(seed=seed, R=R, L=L, V=V)

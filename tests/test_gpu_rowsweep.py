@@ -38,6 +38,7 @@ def assert_lse_close(got, want):
     (9, 40000, 64, "bf16", 7),
     (9, 40000, 128, "bf16", 8),   # the marginal envelope's widest list
     (4, 151936, 128, "bf16", 9),
+    (3, 262144, 128, "bf16", 10),  # a wider vocabulary than Qwen3's, split rows, K = 128
 ])
 def test_rowsweep_random(rows, V, K, dtype, seed):
     rng = np.random.default_rng(seed)

@@ -49,6 +49,7 @@ def check(base_host, dtype, E, U, P, root, K, B, beta, dm):
     (2, 1, 64, 256, 8, 1, 0.0, 8),        # L = 1, B = 1: the best root child
     (2, 3, 8, 256, 8, 30, -0.2, 9),       # K = V = 8: one 32-token block, most chunks empty
     (2, 4, 600, 256, 64, 128, -0.1, 10),  # K = 64, B = 128: pools of up to 8192 entries
+    (2, 64, 300, 256, 4, 128, -0.2, 11),  # L = DTREE_MAX_L: chains down to depth 64
 ])
 def test_sequential_small(R, L, V, dm, K, B, beta, seed):
     base = synth.ddtree_logits(seed=seed, R=R, L=L, V=V)

@@ -29,6 +29,7 @@ def check_static(host, dtype, K, D, rounds=None):
     (2, 5, 50, 1, 5),        # greedy chain
     (5, 3, 7000, 7, 1),      # one depth
     (1, 16, 151936, 10, 6),  # one round, full vocabulary
+    (2, 64, 300, 2, 64),     # D = L = DTREE_MAX_L, K * D = DTREE_MAX_CAP
 ])
 def test_static_small(R, L, V, K, D):
     host = synth.talon_logits(seed=60 + V, R=R, L=L, V=V)

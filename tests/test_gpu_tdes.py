@@ -106,6 +106,7 @@ def check_tdes(host, dtype, prm, root, K, B, budget=None, rounds=None, root_ref=
     (3, 16, 1000, 16, 128, 64, 16, 128),   # depth 16, budget at the cap
     (2, 4, 200, 64, 128, 64, 64, 128),     # K = 64 and the widest embeddings (96 KB of LDS)
     (5, 2, 70, 5, 40, 8, 4, 12),           # 30 candidates under a budget of 40: every one taken
+    (2, 64, 300, 4, 128, 16, 8, 32),       # L = DTREE_MAX_L: best-first paths down to depth 64
 ])
 def test_tdes_small(R, L, V, K, B, hp, hd, H):
     host = synth.ddtree_logits(seed=70 + V, R=R, L=L, V=V)
