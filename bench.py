@@ -2,22 +2,27 @@
 
 One step = one pass of the whole hot path over a batch of R = 64 rounds
 (L = 16 draft positions, V = 151,936, bf16 logits, synthetic seeded inputs):
-  1. build_tree_marginal   DDTree-shape logits, K = B = 64, beta = 0
-  2. build_tree_depthwise_prepared  same logits as base, Markov head E 151936x1024,
-                           U 16x1024x64, P 64x151936 (its transposes prepared once before timing,
-                           as constant weights are), K = 8, W = 32, B = 128, beta = -0.5
-  3. build_tree_gated      TALON-shape logits, K_root = 10, mu = 0.03, N = 60
+  0. dtree_topk_lists      the row sweep of the DDTree-shape logits, K = 64, once: both
+                           builders of those logits take their candidates from it
+  1. build_tree_marginal_lists   K = B = 64, beta = 0
+  2. build_tree_depthwise_lists  the same logits as base (C_d = the first 8 of each list),
+                           Markov head E 151936x1024, U 16x1024x64, P 64x151936 (its
+                           transposes prepared once before timing, as constant weights are),
+                           K = 8, W = 32, B = 128, beta = -0.5
+  3. build_tree_gated      TALON-shape logits (its own sweep), K_root = 10, mu = 0.03, N = 60
   4. accept_tree T = 0     the step's marginal trees against draft-correlated target logits
   5. accept_tree T = 1     same, one Philox-seeded trial per round (trial index = step)
+Each configuration's builder as a user calls it alone (its own sweep included) is timed too:
+per_config_ms, the median of as many calls as timed steps.
 Timed outside the step and reported under extra_ms: the matching walk, DARTree's exact
 (W = B) and fixed (W = B / L) widths, the static D x K grid (K = 10, D = 6) and GRAFT's
 edge-scored best-first tree (K = 32, B = 128).
 value = rounds per second of that whole step (R / step time). The step's independent parts
-run concurrently: 1 -> 4 -> 5 (the walks need the marginal trees) on the main stream,
-2 -> 3 on a second stream of default priority, joined at the end of every step; the
-per-operation breakdown comes from the same work serialised on one stream after the timed
-region (breakdown_ms: the median per operation over as many serialised steps as timed
-steps; breakdown_ms_mean the mean). Inputs are resident in HBM before timing. Prints one
+run concurrently on three streams of default priority: 0 -> 1 -> 4 -> 5 on the main one
+(the walks need the marginal trees), 2 on a second once the lists are written, 3 on a third
+from the start, all joined at the end of every step; the per-operation breakdown comes from
+the same work serialised on one stream after the timed region (breakdown_ms: the median per
+operation over as many serialised steps as timed steps; breakdown_ms_mean the mean). Inputs are resident in HBM before timing. Prints one
 JSON line.
 
 The roofline object is for the logits row sweep (fused log-softmax + top-K), the
@@ -139,6 +144,10 @@ def main():
     ws_m = torch.empty(dt.workspace_size(dt.OP_MARGINAL, R, L, V, 64, 64), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(dt.workspace_size(dt.OP_DEPTHWISE_PREPARED, R, L, V, 8, 128, 32, 64, 1024), dtype=torch.uint8,
                        device=dev)
+    ws_dl = torch.empty(dt.workspace_size(dt.OP_DEPTHWISE_LISTS, R, L, V, 8, 128, 32, 64, 1024), dtype=torch.uint8,
+                        device=dev)
+    lists = dt.Lists.empty(R * L, 64, dev)  # the draft logits' candidate lists, shared by two builders
+    ws_l = torch.empty(max(dt.workspace_size(dt.OP_TOPK, R * L, 1, V, 64), 1), dtype=torch.uint8, device=dev)
     head_d = dt.prepare_depthwise_head(U, P)  # constant weights: transposed once
     ws_g = torch.empty(dt.workspace_size(dt.OP_GATED, R, L, V, 0, 60), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(dt.workspace_size(dt.OP_ACCEPT, R, L, V, 0, 64), dtype=torch.uint8, device=dev)
@@ -152,43 +161,52 @@ def main():
     target = bf(synth.verification_target(draft_h, t_m.depth.cpu().numpy(), seed=5))
 
     stream = torch.cuda.current_stream(dev)
-    names = ["marginal", "depthwise", "gated", "accept_t0", "accept_t1"]
-    # the step's schedule: the marginal tree and the two walks on it (a chain) on the main
-    # stream, the depth-wise then the gated builder (independent of it) on one more stream of
-    # default priority, forked at the start of the step and joined at its end; of the orders
-    # tried (each side builder on its own stream, the side work started after the marginal
-    # tree or after the walks) this one finished soonest
-    s_side = torch.cuda.Stream(dev)
+    names = ["row_sweep_draft", "marginal", "depthwise", "gated", "accept_t0", "accept_t1"]
+    # the step's schedule: the draft logits' row sweep, the marginal tree from its lists and
+    # the two walks on that tree (a chain) on the main stream; the depth-wise tree from the
+    # same lists on a second stream once they are written; the gated tree (other logits, its
+    # own sweep) on a third from the start; joined at the end. Of the orders tried this one
+    # finished soonest.
+    s_dw, s_g = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
 
     def step_overlap(i):
         fork = torch.cuda.Event()
         fork.record(stream)
-        s_side.wait_event(fork)
-        with torch.cuda.stream(s_side):
-            dt.build_tree_depthwise_prepared(draft, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_d, out=t_d)
+        s_g.wait_event(fork)
+        with torch.cuda.stream(s_g):
             dt.build_tree_gated(talon, 10, 0.03, 60, ws=ws_g, out=t_g)
-        dt.build_tree_marginal(draft, 64, 64, 0.0, ws=ws_m, out=t_m)
+        dt.topk_lists(draft, 64, ws=ws_l, out=lists)
+        have_lists = torch.cuda.Event()
+        have_lists.record(stream)
+        s_dw.wait_event(have_lists)
+        with torch.cuda.stream(s_dw):
+            dt.build_tree_depthwise_lists(draft, lists, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_dl,
+                                          out=t_d)
+        dt.build_tree_marginal_lists(lists, R, L, 64, 0.0, out=t_m)
         dt.accept_tree(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
         dt.accept_tree(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
-        join = torch.cuda.Event()
-        join.record(s_side)
-        stream.wait_event(join)
+        for s2 in (s_dw, s_g):
+            join = torch.cuda.Event()
+            join.record(s2)
+            stream.wait_event(join)
 
     def step(i, ev=None):
         def mark(k):
             if ev is not None:
                 ev[k].record(stream)
         mark(0)
-        dt.build_tree_marginal(draft, 64, 64, 0.0, ws=ws_m, out=t_m)
+        dt.topk_lists(draft, 64, ws=ws_l, out=lists)
         mark(1)
-        dt.build_tree_depthwise_prepared(draft, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_d, out=t_d)
+        dt.build_tree_marginal_lists(lists, R, L, 64, 0.0, out=t_m)
         mark(2)
-        dt.build_tree_gated(talon, 10, 0.03, 60, ws=ws_g, out=t_g)
+        dt.build_tree_depthwise_lists(draft, lists, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_dl, out=t_d)
         mark(3)
-        dt.accept_tree(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
+        dt.build_tree_gated(talon, 10, 0.03, 60, ws=ws_g, out=t_g)
         mark(4)
-        dt.accept_tree(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
+        dt.accept_tree(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
         mark(5)
+        dt.accept_tree(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
+        mark(6)
 
     # (profiler passes run the serialised step only: device-wide counters of one dispatch
     # must not include kernels of the other streams)
@@ -209,11 +227,11 @@ def main():
     # the same work serialised on one stream, timed per operation with HIP events (outside
     # the timed region): the per-operation breakdown
     n_ser = 2 if args.step_only else max(5, args.steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_ser)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_ser)]
     for i in range(n_ser):
         step(args.warmup + args.steps + i, evs[i])
     torch.cuda.synchronize()
-    per = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(5)] for i in range(n_ser)])
+    per = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(len(names))] for i in range(n_ser)])
     step_ms = float(np.sum(per, axis=1).mean())
     if args.step_only:
         print(json.dumps({"metric": "tree-build rounds/sec (step serialised, profiler pass)", "value": round(value, 1),
@@ -222,6 +240,36 @@ def main():
                           "breakdown_ms": {n: round(float(np.median(per[:, k])), 4) for k, n in enumerate(names)}}),
               flush=True)
         return
+
+    # ---- each configuration's builder (and the two walks) as a user calls it on its own,
+    # row sweep included: events around every call, the median of n_ser calls
+    def cfg_marginal(i):
+        dt.build_tree_marginal(draft, 64, 64, 0.0, ws=ws_m, out=t_m)
+
+    def cfg_depthwise(i):
+        dt.build_tree_depthwise_prepared(draft, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_d, out=t_d)
+
+    def cfg_gated(i):
+        dt.build_tree_gated(talon, 10, 0.03, 60, ws=ws_g, out=t_g)
+
+    def cfg_t0(i):
+        dt.accept_tree(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
+
+    def cfg_t1(i):
+        dt.accept_tree(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
+
+    per_config = {}
+    for name, f in (("cfg2_marginal", cfg_marginal), ("cfg3_depthwise", cfg_depthwise), ("cfg4_gated", cfg_gated),
+                    ("cfg5_accept_t0", cfg_t0), ("cfg5_accept_t1", cfg_t1)):
+        for i in range(3):
+            f(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ser + 1)]
+        ev[0].record(stream)
+        for i in range(n_ser):
+            f(args.warmup + i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_config[name] = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(n_ser)]))
 
     # ---- roofline: the row sweep kernel, timed live over its own launches on this stream,
     # alternating between two distinct 311 MB logits tensors (the DDTree-shape and TALON-shape
@@ -417,12 +465,16 @@ def main():
         "value": round(value, 1), "unit": "rounds/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "us_per_round": round(ms_per_step * 1e3 / R, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "R=64 rounds, L=16, V=151936 bf16: marginal K=B=64 + depthwise K=8,W=32,B=128,"
-                               "beta=-0.5,E 151936x1024,rank 64 (head prepared once) + gated K_root=10,mu=0.03,N=60 + "
+        "config": {"workload": "R=64 rounds, L=16, V=151936 bf16: one row sweep (K=64) of the DDTree-shape logits "
+                               "shared by marginal K=B=64 and depthwise K=8,W=32,B=128,beta=-0.5,E 151936x1024,rank 64 "
+                               "(head prepared once) + gated K_root=10,mu=0.03,N=60 (TALON-shape logits, own sweep) + "
                                "accept T=0 and T=1 (1 trial/round) on the marginal trees",
                    "rounds": R, "L": L, "V": V},
-        "schedule": "marginal -> accept T=0 -> accept T=1 on one stream, depthwise -> gated on a second "
-                    "(default priority), forked and joined per step",
+        "per_config_ms": {n: round(v, 4) for n, v in per_config.items()},
+        "per_config_us_per_round": {n: round(v * 1e3 / R, 3) for n, v in per_config.items()},
+        "schedule": "draft row sweep -> marginal (its lists) -> accept T=0 -> accept T=1 on one stream, depthwise "
+                    "(the same lists) on a second once they are written, gated (own sweep) on a third (default "
+                    "priority), forked and joined per step",
         "walk_failures": walk_failures,
         "breakdown_us_per_round": {n: round(float(np.median(per[:, k])) * 1e3 / R, 3) for k, n in enumerate(names)},
         "breakdown_ms": {n: round(float(np.median(per[:, k])), 4) for k, n in enumerate(names)},

@@ -36,13 +36,15 @@ LIB_PATH = os.path.join(_HERE, "libdtree.so")
 
 DTREE_BF16, DTREE_F32 = 0, 1
 OP_TOPK, OP_MARGINAL, OP_DEPTHWISE, OP_GATED, OP_ACCEPT, OP_STATIC, OP_TDES, OP_DEPTHWISE_HEAD, \
-    OP_DEPTHWISE_PREPARED, OP_SEQUENTIAL = range(10)
+    OP_DEPTHWISE_PREPARED, OP_SEQUENTIAL, OP_DEPTHWISE_LISTS = range(11)
 STATUS = {0: "DTREE_OK", -1: "DTREE_E_INVAL", -2: "DTREE_E_BETA", -3: "DTREE_E_WORKSPACE",
           -4: "DTREE_E_UNSUPPORTED", -5: "DTREE_E_HIP"}
 
 # every symbol include/dtree.h declares
-SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "build_tree_marginal", "build_tree_marginal_noalloc",
+SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "dtree_topk_lists", "build_tree_marginal",
+           "build_tree_marginal_lists", "build_tree_marginal_noalloc",
            "build_tree_depthwise", "dtree_prepare_depthwise_head", "build_tree_depthwise_prepared",
+           "build_tree_depthwise_lists",
            "build_tree_sequential",
            "build_tree_gated", "build_tree_static", "build_tree_tdes", "dtree_saba_budget", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
 
@@ -76,6 +78,13 @@ def lib() -> ctypes.CDLL:
     L.dtree_workspace_size.argtypes = [i32] * 9
     L.dtree_topk_logsoftmax.restype = i32
     L.dtree_topk_logsoftmax.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.dtree_topk_lists.restype = i32
+    L.dtree_topk_lists.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.build_tree_marginal_lists.restype = i32
+    L.build_tree_marginal_lists.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, ctypes.POINTER(CTree), vp]
+    L.build_tree_depthwise_lists.restype = i32
+    L.build_tree_depthwise_lists.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, i32, i32,
+                                             i32, f32, ctypes.POINTER(CTree), vp, sz, vp]
     L.build_tree_marginal.restype = i32
     L.build_tree_marginal.argtypes = [vp, i32, i32, i32, i32, i32, i32, f32, ctypes.POINTER(CTree), vp, sz, vp]
     L.build_tree_marginal_noalloc.restype = i32
@@ -190,6 +199,49 @@ def topk_logsoftmax(logits: torch.Tensor, K: int, ws: torch.Tensor | None = None
     return lse, ids, lp
 
 
+@dataclass
+class Lists:
+    """dtree_topk_lists' result for [R*L] rows: zk, ids [rows, K] and lse [rows] (float64)."""
+    zk: torch.Tensor
+    ids: torch.Tensor
+    lse: torch.Tensor
+
+    @property
+    def K(self) -> int:
+        return self.ids.shape[1]
+
+    @staticmethod
+    def empty(rows: int, K: int, dev) -> "Lists":
+        return Lists(torch.empty(rows, K, dtype=torch.float32, device=dev),
+                     torch.empty(rows, K, dtype=torch.int32, device=dev),
+                     torch.empty(rows, dtype=torch.float64, device=dev))
+
+
+def topk_lists(logits: torch.Tensor, K: int, ws: torch.Tensor | None = None, out: Lists | None = None) -> Lists:
+    """logits [R, L, V] or [rows, V] -> the candidate lists the *_lists builders take."""
+    _require_device(logits)
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    dev = logits.device
+    out = Lists.empty(rows, K, dev) if out is None else out
+    need = workspace_size(OP_TOPK, rows, 1, V, K)
+    ws = _workspace(need, dev) if ws is None else ws
+    _check(lib().dtree_topk_lists(_ptr(logits), _dtype(logits), rows, V, K, _ptr(out.zk), _ptr(out.ids),
+                                  _ptr(out.lse), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+def build_tree_marginal_lists(lists: Lists, R: int, L: int, B: int, beta: float, out: Tree | None = None) -> Tree:
+    """build_tree_marginal from topk_lists over the same logits (K = the lists' K)."""
+    _require_device(lists.zk, lists.ids, lists.lse)
+    dev = lists.zk.device
+    out = Tree.empty(R, B, dev) if out is None else out
+    st = out.c_struct()
+    _check(lib().build_tree_marginal_lists(_ptr(lists.zk), _ptr(lists.ids), _ptr(lists.lse), R, L, lists.K, B,
+                                           float(beta), ctypes.byref(st), _stream(dev)))
+    return out
+
+
 def build_tree_marginal(logits: torch.Tensor, K: int, B: int, beta: float, ws: torch.Tensor | None = None,
                         out: Tree | None = None) -> Tree:
     _require_device(logits)
@@ -265,6 +317,25 @@ def build_tree_depthwise_prepared(logits: torch.Tensor, E: torch.Tensor, head: t
     _check(lib().build_tree_depthwise_prepared(_ptr(logits), _dtype(logits), R, L, V, _ptr(E), _ptr(head), d_model,
                                                rank, _ptr(root_tok), K, W, B, float(beta), ctypes.byref(st), _ptr(ws),
                                                ws.numel(), _stream(dev)))
+    return out
+
+
+def build_tree_depthwise_lists(logits: torch.Tensor, lists: Lists, E: torch.Tensor, head: torch.Tensor, d_model: int,
+                               rank: int, root_tok: torch.Tensor, K: int, W: int, B: int, beta: float,
+                               ws: torch.Tensor | None = None, out: Tree | None = None) -> Tree:
+    """build_tree_depthwise_prepared with C_d from topk_lists over the same logits (K <= the
+    lists' K)."""
+    _require_device(logits, lists.zk, lists.ids, E, head, root_tok)
+    if E.dtype != torch.bfloat16 or root_tok.dtype != torch.int32:
+        raise TypeError("E must be torch.bfloat16 and root_tok int32")
+    R, L, V = logits.shape
+    dev = logits.device
+    out = Tree.empty(R, B, dev) if out is None else out
+    ws = _workspace(workspace_size(OP_DEPTHWISE_LISTS, R, L, V, K, B, W, rank, d_model), dev) if ws is None else ws
+    st = out.c_struct()
+    _check(lib().build_tree_depthwise_lists(_ptr(logits), _dtype(logits), _ptr(lists.zk), _ptr(lists.ids), lists.K, R,
+                                            L, V, _ptr(E), _ptr(head), d_model, rank, _ptr(root_tok), K, W, B,
+                                            float(beta), ctypes.byref(st), _ptr(ws), ws.numel(), _stream(dev)))
     return out
 
 

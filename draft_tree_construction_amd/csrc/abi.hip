@@ -155,7 +155,8 @@ int depthwise_impl(const void *logits, int dtype, int R, int L, int V, const uin
   hipError_t e = dt::launch_rowsweep(logits, dtype, R * L, V, K, o, a1.rest, st);
   if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise (row sweep)");
   dt::DepthwiseArgs a{logits, dtype, R, L, V, K, W, B, d_model, rank, beta, E, U, P, root_tok};
-  e = dt::launch_depthwise(a, a1.zk, a1.ids, tree_out(out), static_cast<char *>(ws) + a1_bytes(R * L, V, K), head, st);
+  e = dt::launch_depthwise(a, a1.zk, a1.ids, K, tree_out(out), static_cast<char *>(ws) + a1_bytes(R * L, V, K), head,
+                           st);
   if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise");
   return DTREE_OK;
 }
@@ -200,6 +201,9 @@ size_t dtree_workspace_size(int op, int R, int L, int V, int K, int B_or_N, int 
     case DTREE_OP_DEPTHWISE_PREPARED:
       if (K < 1 || W < 1 || B_or_N < 1 || d_model < 1) return 0;
       return a1_bytes(R * L, V, K) + dt::depthwise_call_bytes(R, L, V, K, W, B_or_N, d_model);
+    case DTREE_OP_DEPTHWISE_LISTS:
+      if (K < 1 || W < 1 || B_or_N < 1 || d_model < 1) return 0;
+      return dt::depthwise_call_bytes(R, L, V, K, W, B_or_N, d_model);
     case DTREE_OP_SEQUENTIAL:
       if (K < 1 || B_or_N < 1 || d_model < 1) return 0;
       return a1_bytes(R * L, V, K) + dt::sequential_call_bytes(R, L, V, K, B_or_N, d_model);
@@ -230,6 +234,38 @@ int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K,
   dt::RowOut o{nullptr, lse, ids, nullptr, lp};
   hipError_t e = dt::launch_rowsweep(logits, dtype, rows, V, K, o, ws, static_cast<hipStream_t>(s));
   if (e != hipSuccess) return hip_fail(e, "dtree_topk_logsoftmax");
+  return DTREE_OK;
+}
+
+int dtree_topk_lists(const void *logits, int dtype, int rows, int V, int K, float *zk, int32_t *ids, double *lse,
+                     void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (rows < 0 || V < 1 || K < 1 || K > V) return fail(DTREE_E_INVAL, "need rows >= 0, 1 <= K <= V");
+  if (K > DTREE_MAX_K_MARGINAL) return fail(DTREE_E_UNSUPPORTED, "K > DTREE_MAX_K_MARGINAL");
+  if (rows == 0) return DTREE_OK;
+  if (!logits || !zk || !ids || !lse) return fail(DTREE_E_INVAL, "logits, zk, ids and lse must not be NULL");
+  const size_t need = dt::rowsweep_ws_bytes(rows, V, K);
+  if (need > 0 && (!ws || ws_bytes < need)) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(ws) & 255)) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
+  dt::RowOut o{lse, nullptr, ids, zk, nullptr};
+  hipError_t e = dt::launch_rowsweep(logits, dtype, rows, V, K, o, ws, static_cast<hipStream_t>(s));
+  if (e != hipSuccess) return hip_fail(e, "dtree_topk_lists");
+  return DTREE_OK;
+}
+
+int build_tree_marginal_lists(const float *zk, const int32_t *ids, const double *lse, int R, int L, int K, int B,
+                              float beta, const dtree_tree *out, dtree_stream_t s) {
+  if (R < 0 || L < 1 || K < 1 || B < 1) return fail(DTREE_E_INVAL, "need R >= 0, L, K, B >= 1");
+  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
+  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
+  if (K > DTREE_MAX_K_MARGINAL || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "K, B or L beyond the compiled envelope");
+  int rc = check_tree(out, B);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!zk || !ids || !lse) return fail(DTREE_E_INVAL, "zk, ids and lse must not be NULL");
+  hipError_t e = dt::launch_marginal(zk, ids, lse, R, L, K, B, beta, tree_out(out), static_cast<hipStream_t>(s));
+  if (e != hipSuccess) return hip_fail(e, "build_tree_marginal_lists");
   return DTREE_OK;
 }
 
@@ -374,6 +410,33 @@ int build_tree_depthwise_prepared(const void *logits, int dtype, int R, int L, i
   if (reinterpret_cast<uintptr_t>(head) & 255) return fail(DTREE_E_INVAL, "head must be 256-byte aligned");
   return depthwise_impl(logits, dtype, R, L, V, E, nullptr, nullptr, head, d_model, rank, root_tok, K, W, B, beta, out,
                         ws, ws_bytes, s);
+}
+
+int build_tree_depthwise_lists(const void *logits, int dtype, const float *zk, const int32_t *ids, int ks, int R,
+                               int L, int V, const uint16_t *E, const void *head, int d_model, int rank,
+                               const int32_t *root_tok, int K, int W, int B, float beta, const dtree_tree *out,
+                               void *ws, size_t ws_bytes, dtree_stream_t s) {
+  if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
+  if (R < 0 || L < 1 || V < 1 || K < 1 || K > V || K > ks || W < 1 || B < 1 || d_model < 1 || rank < 1)
+    return fail(DTREE_E_INVAL, "need R >= 0, L, V, W, B, d_model, rank >= 1, 1 <= K <= min(V, ks)");
+  if (isnan(beta)) return fail(DTREE_E_INVAL, "beta is NaN");
+  if (beta > 0.f) return fail(DTREE_E_BETA, "beta > 0");
+  if (rank != 64 || d_model % 64 != 0 || K > DTREE_MAX_K || ks > DTREE_MAX_K_MARGINAL || W > 128 || W * K > 1024 ||
+      L * W > 2048 || B > DTREE_MAX_CAP || L > DTREE_MAX_L)
+    return fail(DTREE_E_UNSUPPORTED, "rank, d_model, K, ks, W, B or L beyond the compiled envelope");
+  int rc = check_tree(out, B);
+  if (rc) return rc;
+  if (R == 0) return DTREE_OK;
+  if (!logits || !zk || !ids || !E || !head || !root_tok) return fail(DTREE_E_INVAL, "an input pointer is NULL");
+  if ((uintptr_t)E & 15) return fail(DTREE_E_INVAL, "E must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(head) & 255) return fail(DTREE_E_INVAL, "head must be 256-byte aligned");
+  const size_t need = dt::depthwise_call_bytes(R, L, V, K, W, B, d_model);
+  if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
+  dt::DepthwiseArgs a{logits, dtype, R, L, V, K, W, B, d_model, rank, beta, E, nullptr, nullptr, root_tok};
+  hipError_t e = dt::launch_depthwise(a, zk, ids, ks, tree_out(out), ws, head, static_cast<hipStream_t>(s));
+  if (e != hipSuccess) return hip_fail(e, "build_tree_depthwise_lists");
+  return DTREE_OK;
 }
 
 int build_tree_sequential(const void *logits, int dtype, int R, int L, int V, const uint16_t *E, const void *head,

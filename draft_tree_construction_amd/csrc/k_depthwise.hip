@@ -113,8 +113,9 @@ struct DwState {
 };
 
 struct DwDev {
-  const float *zk;     // [R*L][K] candidate base logits
-  const int32_t *ids;  // [R*L][K]
+  const float *zk;     // [R*L][ks] candidate base logits (the first K of each list are used)
+  const int32_t *ids;  // [R*L][ks]
+  int ks;              // list stride (>= K)
   const uint16_t *E;
   const int32_t *root_tok;
   float beta;
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_states(DwState s, DwDev a, DwDims 
           tk = (t0 >= 0 && t0 < g.V) ? t0 : 0;  // out-of-range root tokens are a precondition violation
         }
       } else if (k < g.K) {
-        tk = a.ids[((size_t)r * g.L + (d - 2)) * g.K + k];
+        tk = a.ids[((size_t)r * g.L + (d - 2)) * a.ks + k];
       }
     }
     stok[threadIdx.x] = tk;
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_states(DwState s, DwDev a, DwDims 
       // bound per row: sum over j of |h_j| max|P_j.|, in column order
       float bound = 0.f;
       for (int jj = 0; jj < 64; ++jj) bound += hacc[jj >> 5][0][row][jj & 31];
-      const float mnext = a.zk[((size_t)r * g.L + (d - 1)) * g.K];
+      const float mnext = a.zk[((size_t)r * g.L + (d - 1)) * a.ks];
       const bool wide = bound > DW_WIDE;
       const uint16_t ru = f32_to_bf16_up(wide ? mnext : mnext + bound * 1.0001f + 1e-6f);
       s.bref[sl] = bf16_to_f32(ru);
@@ -649,7 +650,7 @@ __global__ __launch_bounds__(DW_NT) void k_dw_lq(DwState s, DwDev a, DwDims g) {
     if (!stok_ok[row]) continue;
     const int sl = t * 32 + row;
     const int r = (sl % per_d) / g.Kp;
-    const size_t ci = ((size_t)r * g.L + (d - 1)) * K + kc;
+    const size_t ci = ((size_t)r * g.L + (d - 1)) * a.ks + kc;
     const int cid = a.ids[ci];
     const u32x4 *pr = reinterpret_cast<const u32x4 *>(s.PT + (size_t)cid * 64);
     float corr = 0.f;
@@ -980,7 +981,7 @@ __global__ __launch_bounds__(DW_TT) void k_dw_tree(DwState s, DwDev a, DwDims g,
     const int x = Ls.off[d] + (idx - Ls.cnt[d]);
     const int pk = Ls.fpk[x];
     Ls.opar[idx] = (d == 1) ? 0 : Ls.cnt[d - 1] + (pk >> 16);
-    Ls.otok[idx] = a.ids[((size_t)r * L + (d - 1)) * K + (pk & 0xFFFF)];
+    Ls.otok[idx] = a.ids[((size_t)r * L + (d - 1)) * a.ks + (pk & 0xFFFF)];
     Ls.odep[idx] = d;
     Ls.osc[idx] = (float)Ls.fs[x];
   }
@@ -1054,7 +1055,7 @@ hipError_t launch_depthwise_head(const uint16_t *U, const uint16_t *P, int L, in
   return launch_head(U, P, L, V, dm, static_cast<char *>(head), dw_layout(dw_dims(1, L, V, 1, 1, 1, dm)), st);
 }
 
-hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
+hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, int ks, const TreeOut &out,
                             void *ws, const void *head, hipStream_t st) {
   const DwDims g = dw_dims(a.R, a.L, a.V, a.K, a.W, a.B, a.dm);
   const DwLayout l = dw_layout(g);
@@ -1075,6 +1076,7 @@ hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32
   DwDev dv;
   dv.zk = zk;
   dv.ids = ids;
+  dv.ks = ks;
   dv.E = a.E;
   dv.root_tok = a.root_tok;
   dv.beta = a.beta;

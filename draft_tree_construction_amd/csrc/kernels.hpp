@@ -73,7 +73,8 @@ size_t depthwise_call_bytes(int R, int L, int V, int K, int W, int B, int dm);  
 hipError_t launch_depthwise_head(const uint16_t *U, const uint16_t *P, int L, int V, int dm, void *head,
                                  hipStream_t st);
 // head == null: the head is prepared in the workspace first (its first depthwise_head_bytes)
-hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, const TreeOut &out,
+// zk, ids: the candidate lists, stride ks >= K (the first K of each are used)
+hipError_t launch_depthwise(const DepthwiseArgs &a, const float *zk, const int32_t *ids, int ks, const TreeOut &out,
                             void *ws, const void *head, hipStream_t st);
 
 // The prepared head's parts (layout of depthwise_head_bytes).

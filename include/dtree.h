@@ -80,7 +80,8 @@ enum dtree_op {
   DTREE_OP_TDES = 6,
   DTREE_OP_DEPTHWISE_HEAD = 7,     /* the prepared correction head of dtree_prepare_depthwise_head */
   DTREE_OP_DEPTHWISE_PREPARED = 8, /* the workspace of build_tree_depthwise_prepared */
-  DTREE_OP_SEQUENTIAL = 9          /* the workspace of build_tree_sequential */
+  DTREE_OP_SEQUENTIAL = 9,         /* the workspace of build_tree_sequential */
+  DTREE_OP_DEPTHWISE_LISTS = 10    /* the workspace of build_tree_depthwise_lists */
 };
 
 /* Compiled envelope (DTREE_E_UNSUPPORTED beyond it). */
@@ -104,7 +105,8 @@ typedef struct {
  * Bytes of workspace an operation needs. `op` is a dtree_op; unused size arguments are
  * ignored: TOPK(rows = R*L, V, K), MARGINAL(R, L, V, K, B), DEPTHWISE(R, L, V, K, B, W,
  * rank, d_model), DEPTHWISE_HEAD(L, V, d_model), DEPTHWISE_PREPARED(R, L, V, K, B, W, rank,
- * d_model), SEQUENTIAL(R, L, V, K, B, d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V,
+ * d_model), DEPTHWISE_LISTS(R, L, V, K, B, W, rank, d_model), SEQUENTIAL(R, L, V, K, B,
+ * d_model), GATED(R, L, V, B_or_N = N), ACCEPT(R, L, V,
  * B_or_N = cap), STATIC(R, L, V, K), TDES(R, L, V, K). Returns 0 for an unknown op or invalid
  * sizes.
  */
@@ -121,6 +123,18 @@ int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K,
                           int32_t *ids, float *lp, void *ws, size_t ws_bytes, dtree_stream_t s);
 
 /*
+ * The same row sweep in the form the builders take its result, so that one sweep of a
+ * logits tensor serves every builder of those logits (DDTree blog 3.3; DARTree Algorithm 1
+ * step 4). Outputs zk [rows][K] = the candidates' logits themselves (as float), ids
+ * [rows][K] in rank order (logit desc, id asc), lse [rows] = ln sum_v exp(z_v) in float64;
+ * all three are required. Needs 1 <= K <= min(V, DTREE_MAX_K_MARGINAL); workspace
+ * dtree_workspace_size(DTREE_OP_TOPK, rows, 1, V, K) (0 bytes when every row fills a
+ * workgroup).
+ */
+int dtree_topk_lists(const void *logits, int dtype, int rows, int V, int K, float *zk, int32_t *ids,
+                     double *lse, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
  * Marginal draft tree (DDTree; DARTree background "tree verification and DDTree"):
  * the B prefixes u, |u| <= L, with the largest s_beta(u) = sum_i log q_i(u_i) + beta*|u|,
  * q_i = softmax(logits[r][i-1]), over each position's top K tokens. K = 0 means
@@ -130,6 +144,16 @@ int dtree_topk_logsoftmax(const void *logits, int dtype, int rows, int V, int K,
  */
 int build_tree_marginal(const void *logits, int dtype, int R, int L, int V, int K, int B, float beta,
                         const dtree_tree *out, void *ws, size_t ws_bytes, dtree_stream_t s);
+
+/*
+ * build_tree_marginal from lists that dtree_topk_lists made over the R*L rows of the
+ * logits with the same K (1 <= K <= min(V, DTREE_MAX_K_MARGINAL); K = 0 is not accepted
+ * here): the same tree, bit for bit, without a second sweep of the logits. zk, ids
+ * [R*L][K] and lse [R*L] are only read. Needs beta <= 0 (else DTREE_E_BETA),
+ * 1 <= B <= DTREE_MAX_CAP, L <= DTREE_MAX_L, out->cap == B. No workspace.
+ */
+int build_tree_marginal_lists(const float *zk, const int32_t *ids, const double *lse, int R, int L, int K, int B,
+                              float beta, const dtree_tree *out, dtree_stream_t s);
 
 /*
  * build_tree_marginal without a workspace argument, for callers that cannot allocate device
@@ -183,6 +207,20 @@ int build_tree_depthwise_prepared(const void *logits, int dtype, int R, int L, i
                                   const void *head, int d_model, int rank, const int32_t *root_tok, int K, int W,
                                   int B, float beta, const dtree_tree *out, void *ws, size_t ws_bytes,
                                   dtree_stream_t s);
+
+/*
+ * build_tree_depthwise_prepared with C_d taken from lists that dtree_topk_lists made over
+ * the same logits with ks >= K candidates per row (the first K of each list are C_d: a
+ * list's first K entries are the top K). zk, ids are [R*L][ks]; the logits are still read
+ * (the correction sweep adds base_d to every corrected row). Same tree, bit for bit, without
+ * a second sweep when another builder shares the lists. Needs K <= ks <=
+ * DTREE_MAX_K_MARGINAL and the envelope of build_tree_depthwise; workspace
+ * dtree_workspace_size(DTREE_OP_DEPTHWISE_LISTS, R, L, V, K, B, W, rank, d_model).
+ */
+int build_tree_depthwise_lists(const void *logits, int dtype, const float *zk, const int32_t *ids, int ks, int R,
+                               int L, int V, const uint16_t *E, const void *head, int d_model, int rank,
+                               const int32_t *root_tok, int K, int W, int B, float beta, const dtree_tree *out,
+                               void *ws, size_t ws_bytes, dtree_stream_t s);
 
 /*
  * The exact path-dependent best-first tree built one node at a time: the DARTree summary's

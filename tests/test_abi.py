@@ -280,3 +280,45 @@ def test_sequential_validation():
     assert call(E=ctypes.c_void_p(0x100002)) == -1      # E is read with 16-byte loads
     assert call() == -3
     assert call(R=0) == 0
+
+
+def test_lists_entry_points_validation():
+    """dtree_topk_lists and the builders that take its lists reject bad arguments on the host."""
+    L = dt.lib()
+    def lists(K=64, V=1000, zk=FAKE2, rows=64, nbytes=0, ws=FAKE2):
+        return L.dtree_topk_lists(FAKE2, 0, rows, V, K, zk, FAKE2, FAKE2, ws, nbytes, None)
+    assert lists(K=0) == -1
+    assert lists(K=65, V=64) == -1
+    assert lists(K=129, V=1000) == -4
+    assert lists(zk=None) == -1
+    assert lists(rows=0, zk=None) == 0
+    assert lists(rows=2, V=1 << 20, ws=None) == -3   # two long rows are split: partials need a workspace
+    t = tree(64)
+    def marg(K=64, B=64, beta=0.0, Lp=16, cap=None, zk=FAKE2, R=4):
+        ct = t if cap is None else tree(cap)
+        return L.build_tree_marginal_lists(zk, FAKE2, FAKE2, R, Lp, K, B, beta, ctypes.byref(ct), None)
+    assert marg(beta=0.5) == -2
+    assert marg(beta=float("nan")) == -1
+    assert marg(K=0) == -1                     # the lists' K, never the automatic 0
+    assert marg(K=129) == -4
+    assert marg(Lp=65) == -4
+    assert marg(B=129, cap=129) == -4
+    assert marg(cap=63) == -1
+    assert marg(zk=None) == -1
+    assert marg(R=0, zk=None) == 0
+    ws = dt.workspace_size
+    prep = ws(dt.OP_DEPTHWISE_PREPARED, 64, 16, 151936, 8, 128, 32, 64, 1024)
+    dl = ws(dt.OP_DEPTHWISE_LISTS, 64, 16, 151936, 8, 128, 32, 64, 1024)
+    assert 0 < dl < prep                       # no candidate lists or sweep partials of its own
+    t2 = tree(128)
+    def dw(K=8, ks=64, head=FAKE2, beta=-0.5, nbytes=0, zk=FAKE2):
+        return L.build_tree_depthwise_lists(FAKE2, 0, zk, FAKE2, ks, 4, 16, 1000, FAKE2, head, 1024, 64, FAKE2, K, 32,
+                                            128, beta, ctypes.byref(t2), FAKE2, nbytes, None)
+    assert dw(K=9, ks=8) == -1
+    assert dw(ks=129) == -4
+    assert dw(K=65, ks=128) == -4
+    assert dw(beta=0.5) == -2
+    assert dw(head=None) == -1
+    assert dw(head=ctypes.c_void_p(0x100010)) == -1
+    assert dw(zk=None) == -1
+    assert dw() == -3
