@@ -5,8 +5,9 @@
 // 3.3; DARTree Algorithm 1 step 4).
 //
 // Design (gfx950). A workgroup of 256 threads streams a row segment in chunks of 256 x 2
-// sixteen-byte vectors; the 64 lanes of a wave read 1 KiB contiguous per load (fully
-// coalesced), two chunks in flight per thread through a register ring. Each thread keeps an
+// sixteen-byte vectors; a thread's two vectors of a chunk are adjacent (its span of 32
+// bytes, so the 64 lanes of a wave read 2 KiB contiguous per pair of loads and a span never
+// straddles a 128-byte line), two chunks in flight per thread through a register ring. Each thread keeps an
 // online (max, sum-exp) pair -- exp2 of one FMA per element, fp32 terms, float64
 // accumulation -- and records each chunk's maximum (its "span" of 16 or 8 elements) in LDS
 // as a 16-bit code rounded up, so the record can only over-select. Nothing else happens
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   const int kw = (K + RS_NW - 1) / RS_NW;
 
   // element layout: vector u of chunk c on lane ln starts at element c*CH + (u*256 + ln)*EPV
-  auto elem0 = [&](int c, int u, int ln) { return v0 + c * CH + (u * RS_NT + ln) * EPV; };
+  auto elem0 = [&](int c, int u, int ln) { return v0 + c * CH + (ln * RS_U + u) * EPV; };
   // vectors of chunk c of lane ln (ln = tid in the stream)
   auto load_span = [&](int c, int ln, u32x4 *r) {
     if constexpr (FAST) {
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
           const_cast<T *>(p + v0), (short)0, len * (int)sizeof(T), 0x00020000);
 #pragma unroll
       for (int u = 0; u < RS_U; ++u)
-        r[u] = (u32x4)__builtin_amdgcn_raw_buffer_load_b128(rs, (c * CH + (u * RS_NT + ln) * EPV) * (int)sizeof(T),
+        r[u] = (u32x4)__builtin_amdgcn_raw_buffer_load_b128(rs, (c * CH + (ln * RS_U + u) * EPV) * (int)sizeof(T),
                                                             0, 0);
     } else {
 #pragma unroll
@@ -197,9 +198,12 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
       m = cm;
       mh = nh;
     }
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    float a0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[0], kLog2e, -mh));
+    float a1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[1], kLog2e, -mh));
+    float a2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2], kLog2e, -mh));
+    float a3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[3], kLog2e, -mh));
 #pragma unroll
-    for (int e = 0; e < E; e += 4) {
+    for (int e = 4; e < E; e += 4) {
       a0 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], kLog2e, -mh));
       a1 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 1], kLog2e, -mh));
       a2 += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 2], kLog2e, -mh));
