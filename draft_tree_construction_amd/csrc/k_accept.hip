@@ -987,6 +987,22 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
 // bins bt - 1 .. bt + 1 (bt the query's bin) are tested, across the four ranges. A query
 // needs no exchange, so a node costs one exchange for the bins and one for the leader's
 // result however many of its children are rejected.
+// The bins a workgroup publishes are stored, and read by the leader, with device-coherent
+// (agent-scope) accesses, which go past the non-coherent caches: the data needs no cache-wide
+// write-back or invalidation (which would also hit every other workgroup on the die), only
+// the writer's wait for its stores to complete before the exchange announces them.
+DT_INLINE void st_dev(int *p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DT_INLINE void st_dev(uint64_t *p, uint64_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DT_INLINE void st_dev(float2 *p, float2 v) {
+  st_dev(reinterpret_cast<uint64_t *>(p), ((uint64_t)__float_as_uint(v.y) << 32) | __float_as_uint(v.x));
+}
+DT_INLINE int ld_dev(const int *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DT_INLINE uint64_t ld_dev(const uint64_t *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+DT_INLINE float2 ld_dev(const float2 *p) {
+  const uint64_t v = ld_dev(reinterpret_cast<const uint64_t *>(p));
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
 struct CoopBins {
   int *off;       // [R][AC_NS][AC_NB + 1]: each workgroup's bin offsets into its list slice
   uint64_t *sum;  // [R][AC_NS][2][AC_NB]: each workgroup's per-bin sums of p and q
@@ -1022,20 +1038,20 @@ DT_INLINE void wg_bins_build_publish(const Row<T> &A, const Row<T> &B, const Nor
       const float p = prob(za[e], nt), q = prob(zb[e], nd);
       const int b = ratio_bin(p, q, bn.tbb);
       if (in_s(p, q, t0)) {
-        bn.list[atomicAdd(&bn.cnt[b], 1)] = make_float2(p, q);
+        st_dev(bn.list + atomicAdd(&bn.cnt[b], 1), make_float2(p, q));
         atomicAdd(reinterpret_cast<unsigned long long *>(&bsP[b]), (unsigned long long)fx60(p));
         atomicAdd(reinterpret_cast<unsigned long long *>(&bsQ[b]), (unsigned long long)fx60(q));
       }
     }
   });
   __syncthreads();
-  for (int i = threadIdx.x; i <= AC_NB; i += AC_NT) gl_off[i] = bn.off[i];
+  for (int i = threadIdx.x; i <= AC_NB; i += AC_NT) st_dev(gl_off + i, bn.off[i]);
   for (int i = threadIdx.x; i < AC_NB; i += AC_NT) {
-    gl_sum[i] = bsP[i];
-    gl_sum[AC_NB + i] = bsQ[i];
+    st_dev(gl_sum + i, bsP[i]);
+    st_dev(gl_sum + AC_NB + i, bsQ[i]);
   }
-  // the list slice, offsets and sums reach device scope before the exchange announces them
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // every store above has completed (device-coherent) before the exchange announces them
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Suffix sums in place: a[b] <- sum of a[b .. n-1], a[n] = 0 (n = 2 AC_NT, exact).
@@ -1065,14 +1081,13 @@ DT_INLINE void wg_suffix_u64(uint64_t *a, int n, Red &red) {
 // Leader: the four workgroups' offsets into xoff, the summed per-bin sums as suffix sums.
 DT_INLINE void leader_merge(const int *gl_off_r, const uint64_t *gl_sum_r, int (*xoff)[AC_NB + 1], uint64_t *sufP,
                             uint64_t *sufQ, Red &red) {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int i = threadIdx.x; i < AC_NS * (AC_NB + 1); i += AC_NT) xoff[i / (AC_NB + 1)][i % (AC_NB + 1)] = gl_off_r[i];
+  for (int i = threadIdx.x; i < AC_NS * (AC_NB + 1); i += AC_NT) xoff[i / (AC_NB + 1)][i % (AC_NB + 1)] = ld_dev(gl_off_r + i);
   for (int b = threadIdx.x; b < AC_NB; b += AC_NT) {
     uint64_t P = 0, Q = 0;
 #pragma unroll
     for (int w = 0; w < AC_NS; ++w) {
-      P += gl_sum_r[(size_t)w * 2 * AC_NB + b];
-      Q += gl_sum_r[(size_t)w * 2 * AC_NB + AC_NB + b];
+      P += ld_dev(gl_sum_r + (size_t)w * 2 * AC_NB + b);
+      Q += ld_dev(gl_sum_r + (size_t)w * 2 * AC_NB + AC_NB + b);
     }
     sufP[b] = P;
     sufQ[b] = Q;
@@ -1101,13 +1116,40 @@ DT_INLINE double leader_query(float t, uint32_t tbb, const int (*xoff)[AC_NB + 1
   uint64_t v[2] = {0, 0};
   for (int i = threadIdx.x; i < n4; i += AC_NT) {
     const int at = i < n1 ? s0 + i : i < n2 ? s1 + (i - n1) : i < n3 ? s2 + (i - n2) : s3 + (i - n3);
-    const float2 x = list_r[at];
+    const float2 x = ld_dev(list_r + at);
     const bool m = in_s(x.x, x.y, t);
     v[0] += m ? fx60(x.x) : 0ull;
     v[1] += m ? fx60(x.y) : 0ull;
   }
   wg_sum_u64<2>(v, red);
   return uni(c_from(sufP[hi + 1] + v[0], sufQ[hi + 1] + v[1], t));
+}
+
+// Leader, late in a chain: the members of bins bs .. AC_NB - 1 of the four ranges copied to
+// LDS (range after range, each range's members in bin order, starting at base[w]), and C(t)
+// for a query whose bins bt - 1 .. bt + 1 all lie at or above bs answered by the calling wave
+// alone: the same exact integer sums as leader_query over the same members, so the same C.
+DT_INLINE double wave_query_cached(float t, uint32_t tbb, int bs, const int (*xoff)[AC_NB + 1], const int *base,
+                                   const uint64_t *sufP, const uint64_t *sufQ, const float2 *cache) {
+  const int bt = t_bin(t, tbb);
+  const int lo = max(bt - 1, bs), hi = min(bt + 1, AC_NB - 1);
+  const int s0 = base[0] + xoff[0][lo] - xoff[0][bs], s1 = base[1] + xoff[1][lo] - xoff[1][bs];
+  const int s2 = base[2] + xoff[2][lo] - xoff[2][bs], s3 = base[3] + xoff[3][lo] - xoff[3][bs];
+  const int n1 = xoff[0][hi + 1] - xoff[0][lo];
+  const int n2 = n1 + xoff[1][hi + 1] - xoff[1][lo];
+  const int n3 = n2 + xoff[2][hi + 1] - xoff[2][lo];
+  const int n4 = n3 + xoff[3][hi + 1] - xoff[3][lo];
+  uint64_t v0 = 0, v1 = 0;
+  for (int i = (int)(threadIdx.x & 63); i < n4; i += 64) {
+    const int at = i < n1 ? s0 + i : i < n2 ? s1 + (i - n1) : i < n3 ? s2 + (i - n2) : s3 + (i - n3);
+    const float2 x = cache[at];
+    const bool m = in_s(x.x, x.y, t);
+    v0 += m ? fx60(x.x) : 0ull;
+    v1 += m ? fx60(x.y) : 0ull;
+  }
+  v0 = wave_sum_u64(v0);
+  v1 = wave_sum_u64(v1);
+  return uni(c_from(sufP[hi + 1] + v0, sufQ[hi + 1] + v1, t));
 }
 
 // ---------------------------------------------------------------- cooperative walk (one trial, T > 0)
@@ -1159,7 +1201,8 @@ __global__ void k_accept_xch_init(uint64_t *slot, size_t n, int *err, int R) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, float2 *a_list, CoopBins cb) {
+__global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, float2 *a_list, CoopBins cb,
+                                                       int cache_cap) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
   __shared__ int bcnt[AC_NB], boff[AC_NB + 1];
   __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1], sr[DTREE_MAX_CAP + 1], pv[DTREE_MAX_CAP + 1];
@@ -1169,7 +1212,11 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
   __shared__ int xfail;
   __shared__ uint64_t sufP[AC_NB + 1], sufQ[AC_NB + 1];  // per-bin sums, then (leader) suffix sums
   __shared__ int xoff[AC_NS][AC_NB + 1];                 // leader: every workgroup's bin offsets
-  extern __shared__ double dyn[];  // [nblk] prefix (double) then [nblk] block sums (float)
+  __shared__ int s_bs;                                   // leader: first bin of the LDS copy
+  __shared__ uint64_t s_res[4];                          // leader: the late chain's result
+  // [nblk] prefix (double) then [nblk] block sums (float); during the leader's chain, the
+  // copy of the late bins' members (cache_cap float2)
+  extern __shared__ double dyn[];
   const int r = blockIdx.x / AC_NS, q = blockIdx.x - r * AC_NS;
   const int cap = a.tree.cap;
   const int n = clamp_nodes(a.tree.n_nodes[r], cap);
@@ -1328,23 +1375,108 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
           leader_merge(cb.off + (size_t)r * AC_NS * (AC_NB + 1), cb.sum + (size_t)r * AC_NS * 2 * AC_NB, xoff, sufP,
                        sufQ, red);
           const float2 *list_r = a_list + (size_t)r * a.V;
+          // the remaining children's p and q, once (the same values the tests below would form)
+          for (int k = threadIdx.x; k <= n; k += AC_NT)
+            if (pv[k] == j && k > c) {
+              cz1[k] = prob(cz1[k], nt);
+              cz2[k] = prob(cz2[k], nd);
+            }
+          // the copy: bs is the lowest bin whose members from there to the last bin, over the
+          // four ranges, fit in cache_cap (counts fall with the bin, so exactly one b in
+          // [0, AC_NB] has M(b) <= cap < M(b - 1))
+          auto above = [&](int b) {  // members of bins b .. AC_NB - 1
+            int m = 0;
+#pragma unroll
+            for (int w = 0; w < AC_NS; ++w) m += xoff[w][AC_NB] - xoff[w][b];
+            return m;
+          };
+          for (int b = threadIdx.x; b <= AC_NB; b += AC_NT)
+            if (above(b) <= cache_cap && (b == 0 || above(b - 1) > cache_cap)) s_bs = b;
+          __syncthreads();
+          const int bs = s_bs;
+          int base[AC_NS + 1];
+          base[0] = 0;
+#pragma unroll
+          for (int w = 0; w < AC_NS; ++w) base[w + 1] = base[w] + xoff[w][AC_NB] - xoff[w][bs];
+          float2 *cache = reinterpret_cast<float2 *>(dyn);
+          auto src = [&](int i) {  // where member i of the copy sits in the round's list area
+            const int w = (i >= base[1]) + (i >= base[2]) + (i >= base[3]);
+            return (nblk_all * w / AC_NS) * AC_BLK + xoff[w][bs] + (i - base[w]);
+          };
+          // eight loads in flight per thread before any is stored
+          for (int i0 = 0; i0 < base[AC_NS]; i0 += 8 * AC_NT) {
+            float2 g[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int i = i0 + k * AC_NT + (int)threadIdx.x;
+              if (i < base[AC_NS]) g[k] = ld_dev(list_r + src(i));
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int i = i0 + k * AC_NT + (int)threadIdx.x;
+              if (i < base[AC_NS]) cache[i] = g[k];
+            }
+          }
+          __syncthreads();
+          // the chain: the whole workgroup while a query's bins reach below the copy, then the
+          // first wave alone from the copy (no barrier per query); each step moves to the next
+          // sibling, so both loops end within the node's children
           float tt = t2;
-          for (int cc = c;;) {
+          int cc = c;
+          bool done = false;
+          for (;;) {
+            if (max(t_bin(tt, bn.tbb) - 1, 0) >= bs) break;
             const double C2 = leader_query(tt, bn.tbb, xoff, sufP, sufQ, list_r, nblk_all, red);
             if (C2 > 0.0) {
               t = tt;
               C = C2;
             }
             cc = ns[cc];
-            if (cc < 0) break;
-            const float qc = prob(cz2[cc], nd);
-            const float pcc = resid(prob(cz1[cc], nt), qc, t) / (float)C;
+            if (cc < 0) {
+              done = true;
+              break;
+            }
+            const float qc = cz2[cc];
+            const float pcc = resid(cz1[cc], qc, t) / (float)C;
             ++step;
             if (cu[cc] * qc < pcc) {
               nxt = cc;
+              done = true;
               break;
             }
             tt = t + (float)C;
+          }
+          if (!done) {
+            if (threadIdx.x < 64) {
+              for (;;) {
+                const double C2 = wave_query_cached(tt, bn.tbb, bs, xoff, base, sufP, sufQ, cache);
+                if (C2 > 0.0) {
+                  t = tt;
+                  C = C2;
+                }
+                cc = ns[cc];
+                if (cc < 0) break;
+                const float qc = cz2[cc];
+                const float pcc = resid(cz1[cc], qc, t) / (float)C;
+                ++step;
+                if (cu[cc] * qc < pcc) {
+                  nxt = cc;
+                  break;
+                }
+                tt = t + (float)C;
+              }
+              if (threadIdx.x == 0) {
+                s_res[0] = (uint64_t)(uint32_t)nxt;
+                s_res[1] = (uint64_t)__float_as_uint(t);
+                s_res[2] = dbits(C);
+                s_res[3] = (uint64_t)step;
+              }
+            }
+            __syncthreads();
+            nxt = (int)(uint32_t)s_res[0];
+            t = __uint_as_float((uint32_t)s_res[1]);
+            C = bitsd(s_res[2]);
+            step = (uint32_t)s_res[3];
           }
           res[0] = (uint64_t)(uint32_t)nxt;
           res[1] = (uint64_t)__float_as_uint(t);
@@ -1629,6 +1761,28 @@ size_t accept_lds_bytes(int V) {
   return (size_t)nblk * (sizeof(double) + sizeof(float));
 }
 
+// Dynamic LDS of k_accept_coop<T>: the draw's block sums and prefix (accept_lds_bytes), or
+// all the LDS a workgroup may hold beside the kernel's static arrays when that is more (the
+// leader's copy of the late bins lives there). The answer depends only on the device and
+// the kernel, so it is kept per device; 0 when a query fails.
+template <typename T>
+static size_t coop_lds_avail() {
+  static std::atomic<size_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev].load() != 0) return cache[dev].load() - 1;
+  int max_lds = 0;
+  hipFuncAttributes fa;
+  if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k_accept_coop<T>)) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const size_t avail = (size_t)max_lds > fa.sharedSizeBytes ? ((size_t)max_lds - fa.sharedSizeBytes) & ~(size_t)15 : 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(avail + 1);
+  return avail;
+}
+
 // Workgroups of k_accept_coop<T> (with shm bytes of dynamic LDS) that the current device
 // holds at once: multiprocessors times the occupancy query. The answer depends only on the
 // device and the kernel, so it is kept per device; 0 when a query fails.
@@ -1670,7 +1824,9 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
       // greedy walk, or residual walk with one trial: AC_NS workgroups per round when the
       // whole grid fits on the device at once (its workgroups wait for each other), else one
       // workgroup per round
-      const int capacity = a.dtype == DTREE_BF16 ? coop_capacity<uint16_t>(shm) : coop_capacity<float>(shm);
+      const size_t avail = a.dtype == DTREE_BF16 ? coop_lds_avail<uint16_t>() : coop_lds_avail<float>();
+      const size_t shm_c = avail > shm ? avail : shm;
+      const int capacity = a.dtype == DTREE_BF16 ? coop_capacity<uint16_t>(shm_c) : coop_capacity<float>(shm_c);
       if ((long long)a.R * AC_NS <= (long long)capacity) {
         const size_t slots = (size_t)a.R * (a.tree.cap + 1);
         const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
@@ -1689,10 +1845,11 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
         if (e != hipSuccess) return e;
         float2 *lists_p = static_cast<float2 *>(ws);
         const dim3 grid((unsigned)(a.R * AC_NS)), block(AC_NT);
+        const int cache_cap = (int)(shm_c / sizeof(float2));
         if (a.dtype == DTREE_BF16)
-          hipLaunchKernelGGL(k_accept_coop<uint16_t>, grid, block, shm, st, a, x, lists_p, cb);
+          hipLaunchKernelGGL(k_accept_coop<uint16_t>, grid, block, shm_c, st, a, x, lists_p, cb, cache_cap);
         else
-          hipLaunchKernelGGL(k_accept_coop<float>, grid, block, shm, st, a, x, lists_p, cb);
+          hipLaunchKernelGGL(k_accept_coop<float>, grid, block, shm_c, st, a, x, lists_p, cb, cache_cap);
         return hipGetLastError();
       }
     }
