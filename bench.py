@@ -82,13 +82,19 @@ def depthwise_source_digest():
     return h.hexdigest()[:16]
 
 
+# Issue cost of one wave64 vector instruction on a gfx950 SIMD, measured with a throughput
+# probe (eight independent chains per lane, eight waves per SIMD, every CU busy; cycles at
+# the 2.4 GHz clock the device reports): v_add_f32 / v_fma_f32 2.9-3.1 cycles, v_exp_f32 9.6.
+VALU_CYC, TRANS_CYC = 3.0, 9.6
+
+
 def correction_gemm(path, K=8):
     """The depth-wise correction sweep (k_dw_corr) against its ceilings, from the rocprofv3
     readings stored with the source digest: MFMA utilisation of the algorithmic h . P product
     (live states x 2 x rank x V flop) at the traced kernel time, the matrix cores' busy
-    fraction, and the vector-issue floor from the instruction counts (a wave64 VALU
-    instruction takes 4 cycles on a 16-lane SIMD, a transcendental 16; 1024 SIMDs at
-    2.4 GHz). None when the readings are missing or stale."""
+    fraction, and the vector-issue floor from the instruction counts at the measured issue
+    costs (VALU_CYC, TRANS_CYC; 1024 SIMDs at 2.4 GHz). None when the readings are missing
+    or stale."""
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -100,14 +106,15 @@ def correction_gemm(path, K=8):
     live = R * (1 + (L - 1) * K)
     alg_flops = live * 2 * 64 * V
     trans = c["SQ_INSTS_VALU_TRANS_F32"]
-    exp_floor = trans * 16 / simd_cycles
-    valu_floor = ((c["SQ_INSTS_VALU"] - trans) * 4 + trans * 16) / simd_cycles
+    exp_floor = trans * TRANS_CYC / simd_cycles
+    valu_floor = ((c["SQ_INSTS_VALU"] - trans) * VALU_CYC + trans * TRANS_CYC) / simd_cycles
     return {"kernel": "k_dw_corr<bf16>", "us_per_launch": rec["trace_us_mean"], "source": os.path.relpath(path, ROOT),
             "alg_flops": alg_flops, "mfma_util": round(alg_flops / t / 2.5e15, 4),
             "mfma_busy": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (simd_cycles * t), 4),
             "exps": trans * 64, "exp_floor_us": round(exp_floor * 1e6, 1),
             "valu_issue_floor_us": round(valu_floor * 1e6, 1), "frac_of_valu_floor": round(valu_floor / t, 4),
-            "bound": "valu (transcendental exp2 plus the per-element adds), not mfma"}
+            "valu_cycles_per_wave_instr": VALU_CYC, "trans_cycles_per_wave_instr": TRANS_CYC,
+            "bound": "neither issue floor: VALU and MFMA pipes both part-idle (per-block barrier, LDS and MFMA latencies)"}
 
 
 def main():
