@@ -43,7 +43,7 @@ constexpr int RS_U = 2;                 // 16-byte vectors per thread per chunk
 constexpr int RS_NG = 48;               // recorded chunk(-group) maxima per thread
 constexpr int RS_WL = 128;              // listed spans per wave
 constexpr int RS_PRE = 4;               // chunks streamed after the bound (even)
-constexpr int RS_WSP = 32;              // spans of those chunks kept per wave
+constexpr int RS_WSP = 48;              // spans of those chunks kept per wave
 constexpr int RS_KEYS = 512;            // candidate keys
 constexpr int RS_WK = RS_KEYS / RS_NW;  // candidate keys per wave region
 constexpr int RS_FB = 2048;             // keys the re-stream fallback holds (in the record)
