@@ -1200,7 +1200,10 @@ __global__ void k_accept_xch_init(uint64_t *slot, size_t n, int *err, int R) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < R; i += gridDim.x * blockDim.x) err[i] = 0;
 }
 
-template <typename T>
+// SAMPLED selects the walk at compile time (the greedy walk when false, a.T == 0; the
+// residual walk with one trial when true), so each kernel's registers are allocated for its
+// own code alone.
+template <typename T, bool SAMPLED>
 __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, float2 *a_list, CoopBins cb,
                                                        int cache_cap) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
@@ -1275,7 +1278,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
   bn.cnt = bcnt;
   bn.off = boff;
   bn.list = a_list + (size_t)r * a.V + e0;
-  if (a.T == 0.f) {
+  if constexpr (!SAMPLED) {
     // greedy walk: each workgroup's argmax key over its range of the node's target row, the
     // four combined by their maximum (value desc, id asc); then the child carrying it
     for (bool lists0 = false;;) {
@@ -1304,7 +1307,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
       j = nxt;
     }
   }
-  for (; a.T > 0.f;) {
+  for (; SAMPLED;) {
     const T *zt = target + (size_t)j * a.V;
     const T *zd = draft + (size_t)draft_row(j == 0 ? a.tree.depth[tb] : dep[j], a.L) * a.V;
     const Row<T> A = make_row(zt + e0, len), B = make_row(zd + e0, len);
@@ -1761,7 +1764,7 @@ size_t accept_lds_bytes(int V) {
   return (size_t)nblk * (sizeof(double) + sizeof(float));
 }
 
-// Dynamic LDS of k_accept_coop<T>: the draw's block sums and prefix (accept_lds_bytes), or
+// Dynamic LDS of k_accept_coop<T, true>: the draw's block sums and prefix (accept_lds_bytes), or
 // all the LDS a workgroup may hold beside the kernel's static arrays when that is more (the
 // leader's copy of the late bins lives there). The answer depends only on the device and
 // the kernel, so it is kept per device; 0 when a query fails.
@@ -1774,7 +1777,7 @@ static size_t coop_lds_avail() {
   int max_lds = 0;
   hipFuncAttributes fa;
   if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-      hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k_accept_coop<T>)) != hipSuccess) {
+      hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k_accept_coop<T, true>)) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -1783,10 +1786,10 @@ static size_t coop_lds_avail() {
   return avail;
 }
 
-// Workgroups of k_accept_coop<T> (with shm bytes of dynamic LDS) that the current device
-// holds at once: multiprocessors times the occupancy query. The answer depends only on the
-// device and the kernel, so it is kept per device; 0 when a query fails.
-template <typename T>
+// Workgroups of k_accept_coop<T, SAMPLED> (with shm bytes of dynamic LDS) that the current
+// device holds at once: multiprocessors times the occupancy query. The answer depends only on
+// the device and the kernel, so it is kept per device; 0 when a query fails.
+template <typename T, bool SAMPLED>
 static int coop_capacity(size_t shm) {
   static std::atomic<int> cache[64];
   static std::atomic<size_t> cache_shm[64];
@@ -1795,7 +1798,7 @@ static int coop_capacity(size_t shm) {
   if (dev >= 0 && dev < 64 && cache_shm[dev].load() == shm + 1) return cache[dev].load();
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_accept_coop<T>, AC_NT, shm) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_accept_coop<T, SAMPLED>, AC_NT, shm) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -1824,9 +1827,16 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
       // greedy walk, or residual walk with one trial: AC_NS workgroups per round when the
       // whole grid fits on the device at once (its workgroups wait for each other), else one
       // workgroup per round
-      const size_t avail = a.dtype == DTREE_BF16 ? coop_lds_avail<uint16_t>() : coop_lds_avail<float>();
-      const size_t shm_c = avail > shm ? avail : shm;
-      const int capacity = a.dtype == DTREE_BF16 ? coop_capacity<uint16_t>(shm_c) : coop_capacity<float>(shm_c);
+      // the greedy walk uses no dynamic LDS; the sampled one all it may have (see coop_lds_avail)
+      const bool sampled = a.T != 0.f;
+      const bool bf = a.dtype == DTREE_BF16;
+      size_t shm_c = 0;
+      if (sampled) {
+        const size_t avail = bf ? coop_lds_avail<uint16_t>() : coop_lds_avail<float>();
+        shm_c = avail > shm ? avail : shm;
+      }
+      const int capacity = sampled ? (bf ? coop_capacity<uint16_t, true>(shm_c) : coop_capacity<float, true>(shm_c))
+                                   : (bf ? coop_capacity<uint16_t, false>(shm_c) : coop_capacity<float, false>(shm_c));
       if ((long long)a.R * AC_NS <= (long long)capacity) {
         const size_t slots = (size_t)a.R * (a.tree.cap + 1);
         const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
@@ -1846,10 +1856,14 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
         float2 *lists_p = static_cast<float2 *>(ws);
         const dim3 grid((unsigned)(a.R * AC_NS)), block(AC_NT);
         const int cache_cap = (int)(shm_c / sizeof(float2));
-        if (a.dtype == DTREE_BF16)
-          hipLaunchKernelGGL(k_accept_coop<uint16_t>, grid, block, shm_c, st, a, x, lists_p, cb, cache_cap);
+        if (sampled && bf)
+          hipLaunchKernelGGL((k_accept_coop<uint16_t, true>), grid, block, shm_c, st, a, x, lists_p, cb, cache_cap);
+        else if (sampled)
+          hipLaunchKernelGGL((k_accept_coop<float, true>), grid, block, shm_c, st, a, x, lists_p, cb, cache_cap);
+        else if (bf)
+          hipLaunchKernelGGL((k_accept_coop<uint16_t, false>), grid, block, shm_c, st, a, x, lists_p, cb, cache_cap);
         else
-          hipLaunchKernelGGL(k_accept_coop<float>, grid, block, shm_c, st, a, x, lists_p, cb, cache_cap);
+          hipLaunchKernelGGL((k_accept_coop<float, false>), grid, block, shm_c, st, a, x, lists_p, cb, cache_cap);
         return hipGetLastError();
       }
     }
