@@ -808,7 +808,9 @@ DT_INLINE int draft_row(int depth, int L) { return depth < 0 ? 0 : (depth > L - 
 DT_INLINE float log2_scale(float T) { return (float)(1.4426950408889634 / (double)T); }
 
 // ---------------------------------------------------------------- lazy walk (one trial / T = 0)
-template <typename T>
+// MODE selects the walk at compile time: 0 greedy (a.T == 0), 1 target-sample matching,
+// 2 residual sampling; each kernel's registers are allocated for its own walk alone.
+template <typename T, int MODE>
 __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_list) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
   __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1], sr[DTREE_MAX_CAP + 1], pv[DTREE_MAX_CAP + 1];
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
   }
   const T *target = static_cast<const T *>(a.target) + (size_t)r * (cap + 1) * a.V;
   int j = 0, out_tok = -1;
-  if (a.T == 0.f) {
+  if constexpr (MODE == 0) {
     bool lists = false;
     for (;;) {
       const int ts = wg_row_argmax(make_row(target + (size_t)j * a.V, a.V), red);
@@ -850,7 +852,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
       }
       j = nxt;
     }
-  } else if (a.match) {
+  } else if constexpr (MODE == 1) {
     const float s = log2_scale(a.T);
     const int nblk = (a.V + AC_BLK - 1) / AC_BLK;
     double *pre = dyn;
@@ -1867,10 +1869,17 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
         return hipGetLastError();
       }
     }
-    if (a.dtype == DTREE_BF16)
-      hipLaunchKernelGGL(k_accept_lazy<uint16_t>, dim3(a.R), dim3(AC_NT), shm, st, a, static_cast<float2 *>(ws));
-    else
-      hipLaunchKernelGGL(k_accept_lazy<float>, dim3(a.R), dim3(AC_NT), shm, st, a, static_cast<float2 *>(ws));
+    float2 *lp = static_cast<float2 *>(ws);
+    const int mode = a.T == 0.f ? 0 : a.match ? 1 : 2;
+    if (a.dtype == DTREE_BF16) {
+      if (mode == 0) hipLaunchKernelGGL((k_accept_lazy<uint16_t, 0>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
+      else if (mode == 1) hipLaunchKernelGGL((k_accept_lazy<uint16_t, 1>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
+      else hipLaunchKernelGGL((k_accept_lazy<uint16_t, 2>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
+    } else {
+      if (mode == 0) hipLaunchKernelGGL((k_accept_lazy<float, 0>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
+      else if (mode == 1) hipLaunchKernelGGL((k_accept_lazy<float, 1>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
+      else hipLaunchKernelGGL((k_accept_lazy<float, 2>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
+    }
     return hipGetLastError();
   }
   AccTables tb = carve_tables(ws, a.R, a.V, a.tree.cap);
