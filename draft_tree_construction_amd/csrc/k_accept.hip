@@ -547,19 +547,24 @@ DT_INLINE void wg_c_sums(const Row<T> &A, const Row<T> &B, const Norm &nt, const
 // Ratio bins. Once a node's first rejection has fixed t0, every later t is >= t0, so S(t) is
 // a subset of S(t0). The members of S(t0) are sorted into AC_NB bins by their ratio: with
 // e_b the float whose bits are bits(t0) + b 2^AC_BSH, bin b covers [e_b, e_{b+1}) (the last
-// one open-ended), and a float t lies in bin (bits(t) - bits(t0)) >> AC_BSH. A member is
-// placed by an approximate ratio p rcp(q), within a few ulp of p / q while a bin is 2^AC_BSH
-// ulp wide, so it sits at most one bin away from the bin of its exact ratio. (Where the
-// approximation can be further off -- q = 0, or a reciprocal out of range -- the exact ratio
-// is beyond the last edge, or p < 2^-60 and the term adds nothing.) For a query t in bin bt,
-// a member placed in bin bt - 2 or lower has p < t q, one placed in bin bt + 2 or higher has
-// p > t q, and only bins bt - 1 .. bt + 1 need the exact test. With the bins' members listed
-// contiguously, a query removes the bins it has left behind (each member once per node) and
-// tests the three bins around t.
+// one open-ended), and a float t lies in bin (bits(t) - bits(t0)) >> AC_BSH. A member's bin
+// is that of its exact ratio: an approximate ratio p rcp(q), within a few ulp of p / q while a
+// bin is 2^AC_BSH ulp wide, names a bin at most one away, and the exact signs of p - e q at
+// that bin's two edges (the fma's sign is exact, as in in_s) move it to the right one. (Where
+// the approximation can be further off -- q = 0, or a reciprocal out of range -- the exact
+// ratio is beyond the last edge, or p < 2^-60 and the term adds nothing to either sum.) For a
+// query t in bin bt, every member of a bin below bt has p < t q and every member of a bin
+// above it p > t q, so only bin bt needs the exact test. (The one-workgroup walk still tests
+// bins bt - 1 .. bt + 1, which stays exact.) With the bins' members listed contiguously, a
+// query removes the bins it has left behind (each member once per node).
+DT_INLINE float bin_edge(int b, uint32_t tbb) { return __uint_as_float(tbb + ((uint32_t)b << AC_BSH)); }
 DT_INLINE int ratio_bin(float p, float q, uint32_t tbb) {
   const float rho = q > 0.f ? p * __builtin_amdgcn_rcpf(q) : kInf;
   const int d = (int)(__float_as_uint(rho) - tbb);
-  return d < 0 ? 0 : min(d >> AC_BSH, AC_NB - 1);
+  const int b = d < 0 ? 0 : min(d >> AC_BSH, AC_NB - 1);
+  const bool below = b > 0 && __builtin_fmaf(-bin_edge(b, tbb), q, p) < 0.f;
+  const bool above = b < AC_NB - 1 && __builtin_fmaf(-bin_edge(b + 1, tbb), q, p) >= 0.f;
+  return below ? b - 1 : above ? b + 1 : b;
 }
 DT_INLINE int t_bin(float t, uint32_t tbb) { return min((int)(__float_as_uint(t) - tbb) >> AC_BSH, AC_NB - 1); }
 
@@ -985,8 +990,8 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
 // wg_bins_build) and also records the exact per-bin sums of p and q (fixed point, see fx60).
 // It publishes its bin offsets and sums; one workgroup (the leader) then adds the four sets
 // of sums into suffix sums over the bins and answers every further C(t) of the node by
-// itself: the bins from bt + 2 up come whole from the suffix sums, and only the members of
-// bins bt - 1 .. bt + 1 (bt the query's bin) are tested, across the four ranges. A query
+// itself: the bins from bt + 1 up come whole from the suffix sums, and only the members of
+// bin bt (the query's bin) are tested, across the four ranges. A query
 // needs no exchange, so a node costs one exchange for the bins and one for the leader's
 // result however many of its children are rejected.
 // The bins a workgroup publishes are stored, and read by the leader, with device-coherent
@@ -1106,7 +1111,7 @@ DT_INLINE double leader_query(float t, uint32_t tbb, const int (*xoff)[AC_NB + 1
                               const uint64_t *sufQ, const float2 *list_r, int nblk_all, Red &red) {
   static_assert(AC_NS == 4, "the four ranges are spelled out");
   const int bt = t_bin(t, tbb);
-  const int lo = max(bt - 1, 0), hi = min(bt + 1, AC_NB - 1);
+  const int lo = bt, hi = bt;  // exact bins: only t's own bin needs the test
   // element offsets of the four ranges [xoff[w][lo], xoff[w][hi + 1]) in list_r, and their
   // running lengths n1 <= n2 <= n3 <= n4
   const int s0 = xoff[0][lo], s1 = (nblk_all * 1 / 4) * AC_BLK + xoff[1][lo];
@@ -1129,12 +1134,12 @@ DT_INLINE double leader_query(float t, uint32_t tbb, const int (*xoff)[AC_NB + 1
 
 // Leader, late in a chain: the members of bins bs .. AC_NB - 1 of the four ranges copied to
 // LDS (range after range, each range's members in bin order, starting at base[w]), and C(t)
-// for a query whose bins bt - 1 .. bt + 1 all lie at or above bs answered by the calling wave
-// alone: the same exact integer sums as leader_query over the same members, so the same C.
+// for a query whose bin bt lies at or above bs answered by the calling wave alone: the same
+// exact integer sums as leader_query over the same members, so the same C.
 DT_INLINE double wave_query_cached(float t, uint32_t tbb, int bs, const int (*xoff)[AC_NB + 1], const int *base,
                                    const uint64_t *sufP, const uint64_t *sufQ, const float2 *cache) {
   const int bt = t_bin(t, tbb);
-  const int lo = max(bt - 1, bs), hi = min(bt + 1, AC_NB - 1);
+  const int lo = max(bt, bs), hi = bt;  // exact bins: only t's own bin needs the test
   const int s0 = base[0] + xoff[0][lo] - xoff[0][bs], s1 = base[1] + xoff[1][lo] - xoff[1][bs];
   const int s2 = base[2] + xoff[2][lo] - xoff[2][bs], s3 = base[3] + xoff[3][lo] - xoff[3][bs];
   const int n1 = xoff[0][hi + 1] - xoff[0][lo];
@@ -1423,14 +1428,14 @@ __global__ __launch_bounds__(AC_NT) void k_accept_coop(AcceptArgs a, Xch x, floa
             }
           }
           __syncthreads();
-          // the chain: the whole workgroup while a query's bins reach below the copy, then the
+          // the chain: the whole workgroup while a query's bin lies below the copy, then the
           // first wave alone from the copy (no barrier per query); each step moves to the next
           // sibling, so both loops end within the node's children
           float tt = t2;
           int cc = c;
           bool done = false;
           for (;;) {
-            if (max(t_bin(tt, bn.tbb) - 1, 0) >= bs) break;
+            if (t_bin(tt, bn.tbb) >= bs) break;
             const double C2 = leader_query(tt, bn.tbb, xoff, sufP, sufQ, list_r, nblk_all, red);
             if (C2 > 0.0) {
               t = tt;
