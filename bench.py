@@ -10,10 +10,13 @@ One step = one pass of the whole hot path over a batch of R = 64 rounds
                            transposes prepared once before timing, as constant weights are),
                            K = 8, W = 32, B = 128, beta = -0.5
   3. build_tree_gated      TALON-shape logits (its own sweep), K_root = 10, mu = 0.03, N = 60
-  4. accept_tree T = 0     the step's marginal trees against draft-correlated target logits
-  5. accept_tree T = 1     same, one Philox-seeded trial per round (trial index = step)
+  4. accept_tree_narrow T = 0   the step's marginal trees against draft-correlated target
+                           logits (one workgroup per round: the walks run beside the
+                           depth-wise builder, so they take a CU per round, not four)
+  5. accept_tree_narrow T = 1   same, one Philox-seeded trial per round (trial index = step)
 Each configuration's builder as a user calls it alone (its own sweep included) is timed too:
-per_config_ms, the median of as many calls as timed steps.
+per_config_ms, the median of as many calls as timed steps; the walks there are accept_tree
+(four workgroups per round, the lower latency for a call that has the device to itself).
 Timed outside the step and reported under extra_ms: the matching walk, DARTree's exact
 (W = B) and fixed (W = B / L) widths, the static D x K grid (K = 10, D = 6) and GRAFT's
 edge-scored best-first tree (K = 32, B = 128).
@@ -190,8 +193,8 @@ def main():
             dt.build_tree_depthwise_lists(draft, lists, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_dl,
                                           out=t_d)
         dt.build_tree_marginal_lists(lists, R, L, 64, 0.0, out=t_m)
-        dt.accept_tree(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
-        dt.accept_tree(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
+        dt.accept_tree_narrow(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
+        dt.accept_tree_narrow(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
         for s2 in (s_dw, s_g):
             join = torch.cuda.Event()
             join.record(s2)
@@ -210,9 +213,9 @@ def main():
         mark(3)
         dt.build_tree_gated(talon, 10, 0.03, 60, ws=ws_g, out=t_g)
         mark(4)
-        dt.accept_tree(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
+        dt.accept_tree_narrow(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
         mark(5)
-        dt.accept_tree(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
+        dt.accept_tree_narrow(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
         mark(6)
 
     # (profiler passes run the serialised step only: device-wide counters of one dispatch
@@ -381,6 +384,11 @@ def main():
     extra_ms["depthwise_w32_unprepared_head"] = timed(lambda: dt.build_tree_depthwise(
         draft, E, U, P, root, 8, 32, 128, -0.5, ws=ws_w, out=t_w))
     extra_ms["prepare_depthwise_head"] = timed(lambda: dt.prepare_depthwise_head(U, P, head=head_d))
+    # the step's walks (one workgroup per round) each called alone
+    extra_ms["accept_t0_narrow"] = timed(lambda: dt.accept_tree_narrow(t_m, target, None, 0.0, synth.PHILOX_SEED, 7,
+                                                                       1, ws=ws_a, outs=o0))
+    extra_ms["accept_t1_narrow"] = timed(lambda: dt.accept_tree_narrow(t_m, target, draft, 1.0, synth.PHILOX_SEED, 7,
+                                                                       1, ws=ws_a, outs=o1))
 
     # ---- outside the step: the static D x K grid, K = 10, D = 6 (60 nodes, TALON's budget N),
     # on the TALON-shape logits: the fixed-shape builder of TALON's tree-build comparison,
@@ -475,11 +483,11 @@ def main():
         "config": {"workload": "R=64 rounds, L=16, V=151936 bf16: one row sweep (K=64) of the DDTree-shape logits "
                                "shared by marginal K=B=64 and depthwise K=8,W=32,B=128,beta=-0.5,E 151936x1024,rank 64 "
                                "(head prepared once) + gated K_root=10,mu=0.03,N=60 (TALON-shape logits, own sweep) + "
-                               "accept T=0 and T=1 (1 trial/round) on the marginal trees",
+                               "accept T=0 and T=1 (1 trial/round, one workgroup per round) on the marginal trees",
                    "rounds": R, "L": L, "V": V},
         "per_config_ms": {n: round(v, 4) for n, v in per_config.items()},
         "per_config_us_per_round": {n: round(v * 1e3 / R, 3) for n, v in per_config.items()},
-        "schedule": "draft row sweep -> marginal (its lists) -> accept T=0 -> accept T=1 on one stream, depthwise "
+        "schedule": "draft row sweep -> marginal (its lists) -> accept_tree_narrow T=0 -> T=1 on one stream, depthwise "
                     "(the same lists) on a second once they are written, gated (own sweep) on a third (default "
                     "priority), forked and joined per step",
         "walk_failures": walk_failures,

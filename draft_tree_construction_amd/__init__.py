@@ -20,6 +20,8 @@ Entry points (same names as the C ABI):
     saba_budget(a, beta, c_verify, c_fixed, B_max)      -> int   (host only)
     accept_tree(tree, target, draft, temperature, seed, trial0, n_trials)
         -> (accept_len, accept_node, next_token), each [n_trials, R]
+    accept_tree_narrow(tree, target, draft, temperature, seed, trial0, n_trials)
+        (accept_tree with one workgroup per round; same outputs)
     accept_tree_match(tree, target, temperature, seed, trial0, n_trials)   (same outputs)
 Logits are torch.bfloat16 or torch.float32 device tensors ([R, L, V] for the builders).
 """
@@ -46,7 +48,7 @@ SYMBOLS = ("dtree_workspace_size", "dtree_topk_logsoftmax", "dtree_topk_lists", 
            "build_tree_depthwise", "dtree_prepare_depthwise_head", "build_tree_depthwise_prepared",
            "build_tree_depthwise_lists",
            "build_tree_sequential",
-           "build_tree_gated", "build_tree_static", "build_tree_tdes", "dtree_saba_budget", "accept_tree", "accept_tree_match", "dtree_status_string", "dtree_last_error")
+           "build_tree_gated", "build_tree_static", "build_tree_tdes", "dtree_saba_budget", "accept_tree", "accept_tree_narrow", "accept_tree_match", "dtree_status_string", "dtree_last_error")
 
 
 class DTreeError(RuntimeError):
@@ -112,6 +114,8 @@ def lib() -> ctypes.CDLL:
     L.accept_tree.restype = i32
     L.accept_tree.argtypes = [ctypes.POINTER(CTree), vp, vp, i32, i32, i32, i32, f32, u64, u64, i32, vp, vp, vp,
                               vp, sz, vp]
+    L.accept_tree_narrow.restype = i32
+    L.accept_tree_narrow.argtypes = L.accept_tree.argtypes
     L.accept_tree_match.restype = i32
     L.accept_tree_match.argtypes = [ctypes.POINTER(CTree), vp, i32, i32, i32, f32, u64, u64, i32, vp, vp, vp, vp, sz,
                                     vp]
@@ -418,9 +422,8 @@ def saba_budget(a: float, beta: float, c_verify: float, c_fixed: float, B_max: i
     return rc
 
 
-def accept_tree(tree: Tree, target: torch.Tensor, draft: torch.Tensor | None, temperature: float, seed: int,
-                trial0: int = 0, n_trials: int = 1, ws: torch.Tensor | None = None, outs=None):
-    """target [R, cap+1, V]; draft [R, L, V] (None allowed at temperature 0)."""
+def _accept(fn: str, tree: Tree, target: torch.Tensor, draft: torch.Tensor | None, temperature: float, seed: int,
+            trial0: int, n_trials: int, ws: torch.Tensor | None, outs):
     _require_device(target, draft)
     R, rows, V = target.shape
     if rows != tree.cap + 1:
@@ -431,10 +434,22 @@ def accept_tree(tree: Tree, target: torch.Tensor, draft: torch.Tensor | None, te
         outs = tuple(torch.empty(n_trials, R, dtype=torch.int32, device=dev) for _ in range(3))
     ws = _workspace(workspace_size(OP_ACCEPT, R, L, V, 0, tree.cap), dev) if ws is None else ws
     st = tree.c_struct()
-    _check(lib().accept_tree(ctypes.byref(st), _ptr(target), _ptr(draft), _dtype(target), R, L, V, float(temperature),
-                             int(seed), int(trial0), int(n_trials), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
-                             _ptr(ws), ws.numel(), _stream(dev)))
+    _check(getattr(lib(), fn)(ctypes.byref(st), _ptr(target), _ptr(draft), _dtype(target), R, L, V, float(temperature),
+                              int(seed), int(trial0), int(n_trials), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                              _ptr(ws), ws.numel(), _stream(dev)))
     return outs
+
+
+def accept_tree(tree: Tree, target: torch.Tensor, draft: torch.Tensor | None, temperature: float, seed: int,
+                trial0: int = 0, n_trials: int = 1, ws: torch.Tensor | None = None, outs=None):
+    """target [R, cap+1, V]; draft [R, L, V] (None allowed at temperature 0)."""
+    return _accept("accept_tree", tree, target, draft, temperature, seed, trial0, n_trials, ws, outs)
+
+
+def accept_tree_narrow(tree: Tree, target: torch.Tensor, draft: torch.Tensor | None, temperature: float, seed: int,
+                       trial0: int = 0, n_trials: int = 1, ws: torch.Tensor | None = None, outs=None):
+    """accept_tree with one workgroup per round (for a walk that runs beside other work)."""
+    return _accept("accept_tree_narrow", tree, target, draft, temperature, seed, trial0, n_trials, ws, outs)
 
 
 def accept_tree_match(tree: Tree, target: torch.Tensor, temperature: float, seed: int, trial0: int = 0,

@@ -469,9 +469,10 @@ int build_tree_sequential(const void *logits, int dtype, int R, int L, int V, co
   return DTREE_OK;
 }
 
-int accept_tree(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype, int R,
-                int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials, int32_t *accept_len,
-                int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes, dtree_stream_t s) {
+static int accept_tree_impl(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype,
+                            int R, int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials,
+                            int32_t *accept_len, int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes,
+                            dtree_stream_t s, int narrow, const char *name) {
   if (!dtype_ok(dtype)) return fail(DTREE_E_INVAL, "dtype must be DTREE_BF16 or DTREE_F32");
   if (!tree) return fail(DTREE_E_INVAL, "tree struct is NULL");
   if (R < 0 || L < 1 || V < 1 || n_trials < 1) return fail(DTREE_E_INVAL, "need R >= 0, L, V, n_trials >= 1");
@@ -489,10 +490,25 @@ int accept_tree(const dtree_tree *tree, const void *target_logits, const void *d
   if (!ws || ws_bytes < need) return fail(DTREE_E_WORKSPACE, "workspace too small");
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   dt::AcceptArgs a{tree_out(tree), target_logits, draft_logits, dtype, R, L, V, temperature, seed, trial0, n_trials,
-                   accept_len, accept_node, next_token, 0};
+                   accept_len, accept_node, next_token, 0, narrow};
   hipError_t e = dt::launch_accept(a, ws, static_cast<hipStream_t>(s));
-  if (e != hipSuccess) return hip_fail(e, "accept_tree");
+  if (e != hipSuccess) return hip_fail(e, name);
   return DTREE_OK;
+}
+
+int accept_tree(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype, int R,
+                int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials, int32_t *accept_len,
+                int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes, dtree_stream_t s) {
+  return accept_tree_impl(tree, target_logits, draft_logits, dtype, R, L, V, temperature, seed, trial0, n_trials,
+                          accept_len, accept_node, next_token, ws, ws_bytes, s, 0, "accept_tree");
+}
+
+int accept_tree_narrow(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype, int R,
+                       int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials,
+                       int32_t *accept_len, int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes,
+                       dtree_stream_t s) {
+  return accept_tree_impl(tree, target_logits, draft_logits, dtype, R, L, V, temperature, seed, trial0, n_trials,
+                          accept_len, accept_node, next_token, ws, ws_bytes, s, 1, "accept_tree_narrow");
 }
 
 int accept_tree_match(const dtree_tree *tree, const void *target_logits, int dtype, int R, int V, float temperature,
@@ -515,7 +531,7 @@ int accept_tree_match(const dtree_tree *tree, const void *target_logits, int dty
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(DTREE_E_INVAL, "ws must be 256-byte aligned");
   // at T = 0 the target's draw is its argmax: the greedy walk
   dt::AcceptArgs a{tree_out(tree), target_logits, nullptr, dtype, R, 1, V, temperature, seed, trial0, n_trials,
-                   accept_len, accept_node, next_token, temperature > 0.f ? 1 : 0};
+                   accept_len, accept_node, next_token, temperature > 0.f ? 1 : 0, 0};
   hipError_t e = dt::launch_accept(a, ws, static_cast<hipStream_t>(s));
   if (e != hipSuccess) return hip_fail(e, "accept_tree_match");
   return DTREE_OK;

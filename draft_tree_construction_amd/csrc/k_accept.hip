@@ -1844,7 +1844,7 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
       }
       const int capacity = sampled ? (bf ? coop_capacity<uint16_t, true>(shm_c) : coop_capacity<float, true>(shm_c))
                                    : (bf ? coop_capacity<uint16_t, false>(shm_c) : coop_capacity<float, false>(shm_c));
-      if ((long long)a.R * AC_NS <= (long long)capacity) {
+      if (!a.narrow && (long long)a.R * AC_NS <= (long long)capacity) {
         const size_t slots = (size_t)a.R * (a.tree.cap + 1);
         const size_t tables = 7 * align256(slots * sizeof(float)) + align256(slots * (size_t)nblk * sizeof(double));
         const size_t lists = (size_t)a.R * a.V * sizeof(float2);

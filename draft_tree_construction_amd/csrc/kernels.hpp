@@ -106,7 +106,8 @@ struct AcceptArgs {
   uint64_t seed, trial0;
   int n_trials;
   int32_t *accept_len, *accept_node, *next_token;
-  int match;  // target-sample matching instead of residual acceptance (T > 0)
+  int match;   // target-sample matching instead of residual acceptance (T > 0)
+  int narrow;  // one workgroup per round even when four per round fit
 };
 size_t accept_ws_bytes(int R, int L, int V, int cap);
 hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st);

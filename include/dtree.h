@@ -329,6 +329,23 @@ int accept_tree(const dtree_tree *tree, const void *target_logits, const void *d
                 dtree_stream_t s);
 
 /*
+ * accept_tree with one workgroup per round for every walk (the same operation: DARTree
+ * background "speculative sampling"; course notes unit 11). Arguments, outputs, workspace and
+ * errors are those of accept_tree; no device-side failure (no workgroup waits for another).
+ * accept_tree shares each round's passes among four workgroups when they fit on the device
+ * at once, which shortens a call that has the device to itself; this variant keeps one
+ * compute unit per round, for callers that run the walk beside other work on the device
+ * (the one-trial walk at temperature > 0 and the greedy walk each hold a quarter of the
+ * compute units that accept_tree holds, for longer). Results: the greedy walk and every
+ * acceptance test are identical to accept_tree's; the residual's normaliser and the final
+ * draw's block prefix are summed in another order (within float rounding of accept_tree).
+ */
+int accept_tree_narrow(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype,
+                       int R, int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials,
+                       int32_t *accept_len, int32_t *accept_node, int32_t *next_token, void *ws, size_t ws_bytes,
+                       dtree_stream_t s);
+
+/*
  * Exact target-sample matching (DARTree background "speculative sampling": DFlash verifies
  * by matching exact samples of the target), for any tree.
  * At node j draw x from p = softmax(target[r][j] / T) by inverse CDF (smallest v with

@@ -161,6 +161,48 @@ def test_sampled_walk_full_config_one_trial_against_oracle():
     assert n == 512 and bad <= n // 1000, (bad, n)
 
 
+def test_narrow_walks_full_config_against_oracle():
+    """accept_tree_narrow (one workgroup per round for every walk) on the full verification
+    config: the greedy walk on all 64 rounds exactly, and the one-trial walk at T = 1 for trial
+    indices 0..3 on every round, a mismatch allowed only where the oracle's decision margin is
+    <= 1e-6 (at most 0.1 %)."""
+    draft, trees, target = full_verification_case()
+    dtree, tg, dr = oracle_to_device(trees, 64), dev_bf16(target), dev_bf16(draft)
+    alen, anode, nxt = host_outs(dt.accept_tree_narrow(dtree, tg, None, 0.0, SEED, 0, 1))
+    ref0 = op.pmap(op.greedy_task, [(t.parent, t.token, t.depth, target[r, :t.n + 1]) for r, t in enumerate(trees)])
+    for r in range(64):
+        assert (alen[0, r], anode[0, r], nxt[0, r]) == ref0[r]
+    trials = range(4)
+    ref = sampled_oracle(trees, target, draft, trials)
+    bad = n = 0
+    for t in trials:
+        alen, anode, nxt = host_outs(dt.accept_tree_narrow(dtree, tg, dr, 1.0, SEED, t, 1))
+        for r in range(64):
+            b, k = compare_with_margins([(alen[0, r], anode[0, r], nxt[0, r])], [ref[r][0][t]])
+            bad += b
+            n += k
+    assert n == 256 and bad <= n // 1000, (bad, n)
+
+
+def test_narrow_and_default_walks_agree():
+    """accept_tree_narrow and accept_tree on the same inputs: the greedy walks are identical;
+    the one-trial walks at T = 1 agree but for decisions within float rounding (the two sum
+    the LSE and the draw's block prefix in different orders): at most one of 48 differs."""
+    R, L, V, B = 8, 16, 5000, 64
+    draft, trees, target = verification_case(R, L, V, B)
+    dtree, tg, dr = oracle_to_device(trees, B), dev_bf16(target), dev_bf16(draft)
+    a = host_outs(dt.accept_tree(dtree, tg, None, 0.0, SEED, 0, 1))
+    b = host_outs(dt.accept_tree_narrow(dtree, tg, None, 0.0, SEED, 0, 1))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    diff = 0
+    for t in range(6):
+        a = host_outs(dt.accept_tree(dtree, tg, dr, 1.0, SEED, t, 1))
+        b = host_outs(dt.accept_tree_narrow(dtree, tg, dr, 1.0, SEED, t, 1))
+        diff += int(np.sum((a[0] != b[0]) | (a[1] != b[1]) | (a[2] != b[2])))
+    assert diff <= 1, diff
+
+
 MAX_ACCEPT_V = 262144  # DTREE_MAX_ACCEPT_V in include/dtree.h
 
 
