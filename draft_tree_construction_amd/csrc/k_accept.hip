@@ -554,9 +554,9 @@ DT_INLINE void wg_c_sums(const Row<T> &A, const Row<T> &B, const Norm &nt, const
 // the approximation can be further off -- q = 0, or a reciprocal out of range -- the exact
 // ratio is beyond the last edge, or p < 2^-60 and the term adds nothing to either sum.) For a
 // query t in bin bt, every member of a bin below bt has p < t q and every member of a bin
-// above it p > t q, so only bin bt needs the exact test. (The one-workgroup walk still tests
-// bins bt - 1 .. bt + 1, which stays exact.) With the bins' members listed contiguously, a
-// query removes the bins it has left behind (each member once per node).
+// above it p > t q, so only bin bt needs the exact test. With the bins' members listed
+// contiguously and exact per-bin sums turned into suffix sums over the bins, a query reads
+// the suffix sums above bt and the members of bin bt.
 DT_INLINE float bin_edge(int b, uint32_t tbb) { return __uint_as_float(tbb + ((uint32_t)b << AC_BSH)); }
 DT_INLINE int ratio_bin(float p, float q, uint32_t tbb) {
   const float rho = q > 0.f ? p * __builtin_amdgcn_rcpf(q) : kInf;
@@ -599,75 +599,7 @@ struct Bins {
   int *cnt, *off;  // LDS: [AC_NB] counts / cursors, [AC_NB + 1] offsets
   float2 *list;    // global: this round's members of S(t0), (p, q), grouped by bin
   uint32_t tbb;    // bits of t0
-  int lo;          // bins below lo have been removed from (P, Q)
-  uint64_t P, Q;   // sums over the members of bins >= lo
-  uint64_t Pt, Qt; // sums over S(t) for the last t asked (build or query)
 };
-
-// Sort S(t0) into the bins (two passes over the rows: counts, then placement, which also
-// sums p and q over S(t0)); returns C(t0).
-template <typename T>
-DT_INLINE double wg_bins_build(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t0, Bins &bn,
-                               Red &red) {
-  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) bn.cnt[i] = 0;
-  bn.tbb = uni(__float_as_uint(t0));
-  __syncthreads();
-  stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = prob(za[e], nt), q = prob(zb[e], nd);
-      const int b = ratio_bin(p, q, bn.tbb);
-      if (in_s(p, q, t0)) atomicAdd(&bn.cnt[b], 1);
-    }
-  });
-  __syncthreads();
-  wg_scan_int(bn.cnt, bn.off, AC_NB, red);
-  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) bn.cnt[i] = bn.off[i];
-  __syncthreads();
-  // placement, with the sums over S(t0) (exact, so in any order)
-  uint64_t v[2] = {0, 0};
-  stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = prob(za[e], nt), q = prob(zb[e], nd);
-      const int b = ratio_bin(p, q, bn.tbb);
-      if (in_s(p, q, t0)) {
-        bn.list[atomicAdd(&bn.cnt[b], 1)] = make_float2(p, q);
-        v[0] += fx60(p);
-        v[1] += fx60(q);
-      }
-    }
-  });
-  wg_sum_u64<2>(v, red);
-  bn.lo = 0;
-  bn.P = bn.Pt = uni(v[0]);
-  bn.Q = bn.Qt = uni(v[1]);
-  return uni(c_from(bn.P, bn.Q, t0));
-}
-
-// C(t) for t >= the last query's t (>= t0) from the bins.
-DT_INLINE double wg_bins_query(Bins &bn, float t, Red &red) {
-  const int bt = t_bin(t, bn.tbb);
-  const int lo = max(bn.lo, bt - 1);  // bins below lo are left behind
-  const int a0 = bn.off[bn.lo], a1 = bn.off[lo], b1 = bn.off[min(bt + 2, AC_NB)];
-  uint64_t v[4] = {0, 0, 0, 0};  // removed bins (p, q); members of bin bt outside S(t) (p, q)
-  for (int i = a0 + threadIdx.x; i < b1; i += AC_NT) {
-    const float2 x = bn.list[i];
-    const bool below = i < a1, out = !below && !in_s(x.x, x.y, t);
-    const uint64_t fp = fx60(x.x), fq = fx60(x.y);
-    v[0] += below ? fp : 0ull;
-    v[1] += below ? fq : 0ull;
-    v[2] += out ? fp : 0ull;
-    v[3] += out ? fq : 0ull;
-  }
-  wg_sum_u64<4>(v, red);
-  bn.P = uni(bn.P - v[0]);
-  bn.Q = uni(bn.Q - v[1]);
-  bn.lo = uni(lo);
-  bn.Pt = uni(bn.P - uni(v[2]));
-  bn.Qt = uni(bn.Q - uni(v[3]));
-  return uni(c_from(bn.Pt, bn.Qt, t));
-}
 
 // Inclusive prefix sums (float64) of the n block sums, into pre[]; one workgroup.
 DT_INLINE void wg_prefix(const float *blk, double *pre, int n, Red &red) {
@@ -812,17 +744,123 @@ DT_INLINE int clamp_nodes(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : 
 DT_INLINE int draft_row(int depth, int L) { return depth < 0 ? 0 : (depth > L - 1 ? L - 1 : depth); }
 DT_INLINE float log2_scale(float T) { return (float)(1.4426950408889634 / (double)T); }
 
+DT_INLINE uint64_t dbits(double x) { return (uint64_t)__double_as_longlong(x); }
+DT_INLINE double bitsd(uint64_t x) { return __longlong_as_double((long long)x); }
+
+// Suffix sums in place: a[b] <- sum of a[b .. n-1], a[n] = 0 (n = 2 AC_NT, exact).
+DT_INLINE void wg_suffix_u64(uint64_t *a, int n, Red &red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i0 = n - 2 - 2 * (int)threadIdx.x;  // thread k takes entries i0, i0 + 1 (from the top)
+  const uint64_t x0 = a[i0], x1 = a[i0 + 1];
+  const uint64_t s = x0 + x1;
+  uint64_t incl = s;  // inclusive prefix over threads 0..k (entries from the top down)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)incl, o, 64), hi = __shfl_up((uint32_t)(incl >> 32), o, 64);
+    if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
+  }
+  __syncthreads();
+  if (lane == 63) red.u[w] = incl;
+  __syncthreads();
+  uint64_t run = 0;
+  for (int i = 0; i < w; ++i) run += red.u[i];
+  run += incl - s;  // sum of the entries above i0 + 1
+  a[i0 + 1] = run + x1;
+  a[i0] = run + x1 + x0;
+  if (threadIdx.x == 0) a[n] = 0ull;
+  __syncthreads();
+}
+
+// One-workgroup bins with per-bin sums (the one-workgroup walk's form of the merged bins):
+// members of S(t0) to the round's list, grouped by bin, with the exact per-bin sums of p and q
+// in sufP / sufQ (LDS) turned into suffix sums over the bins; returns C(t0).
+template <typename T>
+DT_INLINE double wg_bins_build_sums(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t0,
+                                   Bins &bn, uint64_t *sufP, uint64_t *sufQ, Red &red) {
+  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) {
+    bn.cnt[i] = 0;
+    sufP[i] = 0ull;
+    sufQ[i] = 0ull;
+  }
+  bn.tbb = uni(__float_as_uint(t0));
+  __syncthreads();
+  stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = prob(za[e], nt), q = prob(zb[e], nd);
+      const int b = ratio_bin(p, q, bn.tbb);
+      if (in_s(p, q, t0)) atomicAdd(&bn.cnt[b], 1);
+    }
+  });
+  __syncthreads();
+  wg_scan_int(bn.cnt, bn.off, AC_NB, red);
+  for (int i = threadIdx.x; i < AC_NB; i += AC_NT) bn.cnt[i] = bn.off[i];
+  __syncthreads();
+  stream2<T, 2>(A, B, [&](int, const float *za, const float *zb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = prob(za[e], nt), q = prob(zb[e], nd);
+      const int b = ratio_bin(p, q, bn.tbb);
+      if (in_s(p, q, t0)) {
+        bn.list[atomicAdd(&bn.cnt[b], 1)] = make_float2(p, q);
+        atomicAdd(reinterpret_cast<unsigned long long *>(&sufP[b]), (unsigned long long)fx60(p));
+        atomicAdd(reinterpret_cast<unsigned long long *>(&sufQ[b]), (unsigned long long)fx60(q));
+      }
+    }
+  });
+  __syncthreads();
+  static_assert(AC_NB == 2 * AC_NT, "wg_suffix_u64 takes two entries per thread");
+  wg_suffix_u64(sufP, AC_NB, red);
+  wg_suffix_u64(sufQ, AC_NB, red);
+  return uni(c_from(sufP[0], sufQ[0], t0));
+}
+
+// C(t) from such bins (exact): the bins above t's bin whole from the suffix sums, the members
+// of t's bin tested; the whole workgroup over the list in device memory.
+DT_INLINE double wg_bins_query1(float t, const Bins &bn, const uint64_t *sufP, const uint64_t *sufQ, Red &red) {
+  const int bt = t_bin(t, bn.tbb);
+  uint64_t v[2] = {0, 0};
+  for (int i = bn.off[bt] + (int)threadIdx.x; i < bn.off[bt + 1]; i += AC_NT) {
+    const float2 x = bn.list[i];
+    const bool m = in_s(x.x, x.y, t);
+    v[0] += m ? fx60(x.x) : 0ull;
+    v[1] += m ? fx60(x.y) : 0ull;
+  }
+  wg_sum_u64<2>(v, red);
+  return uni(c_from(sufP[bt + 1] + v[0], sufQ[bt + 1] + v[1], t));
+}
+
+// The same by the calling wave alone, from an LDS copy of the list from bin bs on (t's bin
+// at or above bs): the same members and the same exact sums.
+DT_INLINE double wave_bins_query1(float t, const Bins &bn, int bs, const uint64_t *sufP, const uint64_t *sufQ,
+                                  const float2 *cache) {
+  const int bt = max(t_bin(t, bn.tbb), bs);
+  const int a0 = bn.off[bt] - bn.off[bs], a1 = bn.off[bt + 1] - bn.off[bs];
+  uint64_t v0 = 0, v1 = 0;
+  for (int i = a0 + (int)(threadIdx.x & 63); i < a1; i += 64) {
+    const float2 x = cache[i];
+    const bool m = in_s(x.x, x.y, t);
+    v0 += m ? fx60(x.x) : 0ull;
+    v1 += m ? fx60(x.y) : 0ull;
+  }
+  v0 = wave_sum_u64(v0);
+  v1 = wave_sum_u64(v1);
+  return uni(c_from(sufP[bt + 1] + v0, sufQ[bt + 1] + v1, t));
+}
+
 // ---------------------------------------------------------------- lazy walk (one trial / T = 0)
 // MODE selects the walk at compile time: 0 greedy (a.T == 0), 1 target-sample matching,
 // 2 residual sampling; each kernel's registers are allocated for its own walk alone.
 template <typename T, int MODE>
-__global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_list) {
+__global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_list, int cache_cap) {
   __shared__ int par[DTREE_MAX_CAP + 1], tok[DTREE_MAX_CAP + 1], dep[DTREE_MAX_CAP + 1];
   __shared__ int fc[DTREE_MAX_CAP + 1], ns[DTREE_MAX_CAP + 1], sr[DTREE_MAX_CAP + 1], pv[DTREE_MAX_CAP + 1];
   __shared__ Red red;
   __shared__ float cz1[DTREE_MAX_CAP + 1], cz2[DTREE_MAX_CAP + 1], cu[DTREE_MAX_CAP + 1];
   __shared__ int bcnt[AC_NB], boff[AC_NB + 1];
-  extern __shared__ double dyn[];  // [nblk] prefix (double) then [nblk] block sums (float)
+  // [nblk] prefix (double) then [nblk] block sums (float); in the residual walk, during a
+  // node's chain, the copy of the late bins' members (cache_cap float2)
+  extern __shared__ double dyn[];
   const int r = blockIdx.x;
   const int cap = a.tree.cap;
   const int n = clamp_nodes(a.tree.n_nodes[r], cap);
@@ -892,6 +930,9 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
       j = nxt;
     }
   } else {
+    __shared__ uint64_t sufP[AC_NB + 1], sufQ[AC_NB + 1];  // suffix sums over the bins
+    __shared__ int s_bs;                                   // first bin of the LDS copy
+    __shared__ uint64_t s_res[4];                          // the wave's chain result
     const float s = log2_scale(a.T);
     const T *draft = static_cast<const T *>(a.draft) + (size_t)r * a.L * a.V;
     const uint64_t trial = a.trial0;
@@ -926,7 +967,6 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
       const Norm nt = make_norm(s, la), nd = make_norm(s, lb);
       float t = 0.f;
       double C = 1.0;
-      bool built = false;     // the bins hold this node's residual support
       bool blk_at_t = false;  // blk[] holds the block sums of the residual at t
       int nxt = -1;
       for (int c = fc[j]; c >= 0; c = ns[c]) {
@@ -945,18 +985,88 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
         const float t2 = t + (float)C;
         int left = 0;
         for (int k = ns[c]; k >= 0 && left < AC_BINS_MIN; k = ns[k]) ++left;
-        double C2;
-        if (built) {
-          C2 = wg_bins_query(bn, t2, red);
+        if (left >= AC_BINS_MIN) {
+          // bins with per-bin sums, then every remaining child of the node from them: the
+          // whole workgroup while a query's bin lies below the LDS copy of the late bins, then
+          // the first wave alone from the copy (no barrier per query); each step moves to the
+          // next sibling, so both loops end within the node's children
+          double C2 = wg_bins_build_sums(A, B, nt, nd, t2, bn, sufP, sufQ, red);
+          for (int k = threadIdx.x; k <= n; k += AC_NT)
+            if (pv[k] == j && k > c) {
+              cz1[k] = prob(cz1[k], nt);
+              cz2[k] = prob(cz2[k], nd);
+            }
+          auto above = [&](int b) { return bn.off[AC_NB] - bn.off[b]; };  // members of bins b ..
+          for (int b = threadIdx.x; b <= AC_NB; b += AC_NT)
+            if (above(b) <= cache_cap && (b == 0 || above(b - 1) > cache_cap)) s_bs = b;
+          __syncthreads();
+          const int bs = s_bs;
+          float2 *cache = reinterpret_cast<float2 *>(dyn);
+          for (int i = threadIdx.x; i < above(bs); i += AC_NT) cache[i] = bn.list[bn.off[bs] + i];
+          __syncthreads();
+          float tt = t2;
+          int cc = c;
+          bool done = false;
+          for (bool first = true;; first = false) {
+            if (t_bin(tt, bn.tbb) >= bs) break;
+            if (!first) C2 = wg_bins_query1(tt, bn, sufP, sufQ, red);
+            if (C2 > 0.0) {
+              t = uni(tt);
+              C = uni(C2);
+            }
+            cc = ns[cc];
+            if (cc < 0) {
+              done = true;
+              break;
+            }
+            const float qc = cz2[cc];
+            const float pcc = resid(cz1[cc], qc, t) / (float)C;
+            ++step;
+            if (cu[cc] * qc < pcc) {
+              nxt = cc;
+              done = true;
+              break;
+            }
+            tt = t + (float)C;
+            C2 = -1.0;
+          }
+          if (!done) {
+            if (threadIdx.x < 64) {
+              for (bool first = C2 >= 0.0;; first = false) {
+                if (!first) C2 = wave_bins_query1(tt, bn, bs, sufP, sufQ, cache);
+                if (C2 > 0.0) {
+                  t = tt;
+                  C = C2;
+                }
+                cc = ns[cc];
+                if (cc < 0) break;
+                const float qc = cz2[cc];
+                const float pcc = resid(cz1[cc], qc, t) / (float)C;
+                ++step;
+                if (cu[cc] * qc < pcc) {
+                  nxt = cc;
+                  break;
+                }
+                tt = t + (float)C;
+              }
+              if (threadIdx.x == 0) {
+                s_res[0] = (uint64_t)(uint32_t)nxt;
+                s_res[1] = (uint64_t)__float_as_uint(t);
+                s_res[2] = dbits(C);
+                s_res[3] = (uint64_t)step;
+              }
+            }
+            __syncthreads();
+            nxt = (int)(uint32_t)s_res[0];
+            t = __uint_as_float((uint32_t)s_res[1]);
+            C = bitsd(s_res[2]);
+            step = (uint32_t)s_res[3];
+          }
           blk_at_t = false;
-        } else if (left >= AC_BINS_MIN) {
-          C2 = wg_bins_build(A, B, nt, nd, t2, bn, red);
-          built = true;
-          blk_at_t = false;
-        } else {
-          C2 = wg_c_pass(A, B, nt, nd, t2, blk, nblk, red);
-          blk_at_t = C2 > 0.0;
+          break;
         }
+        const double C2 = wg_c_pass(A, B, nt, nd, t2, blk, nblk, red);
+        blk_at_t = C2 > 0.0;
         if (C2 > 0.0) {
           t = uni(t2);
           C = uni(C2);
@@ -987,7 +1097,7 @@ __global__ __launch_bounds__(AC_NT) void k_accept_lazy(AcceptArgs a, float2 *a_l
 // ---------------------------------------------------------------- merged bins (four-workgroup walk)
 // When a node of the four-workgroup walk has several children left after a rejection,
 // every workgroup sorts the members of S(t0) in its own range into ratio bins (as
-// wg_bins_build) and also records the exact per-bin sums of p and q (fixed point, see fx60).
+// wg_bins_build_sums) and also records the exact per-bin sums of p and q (fixed point, see fx60).
 // It publishes its bin offsets and sums; one workgroup (the leader) then adds the four sets
 // of sums into suffix sums over the bins and answers every further C(t) of the node by
 // itself: the bins from bt + 1 up come whole from the suffix sums, and only the members of
@@ -1015,7 +1125,7 @@ struct CoopBins {
   uint64_t *sum;  // [R][AC_NS][2][AC_NB]: each workgroup's per-bin sums of p and q
 };
 
-// wg_bins_build plus the per-bin sums (into bsP / bsQ, LDS) and their publication.
+// wg_bins_build_sums' bins and per-bin sums (into bsP / bsQ, LDS) and their publication.
 template <typename T>
 DT_INLINE void wg_bins_build_publish(const Row<T> &A, const Row<T> &B, const Norm &nt, const Norm &nd, float t0,
                                      Bins &bn, uint64_t *bsP, uint64_t *bsQ, int *gl_off, uint64_t *gl_sum,
@@ -1059,30 +1169,6 @@ DT_INLINE void wg_bins_build_publish(const Row<T> &A, const Row<T> &B, const Nor
   }
   // every store above has completed (device-coherent) before the exchange announces them
   __builtin_amdgcn_s_waitcnt(0);
-}
-
-// Suffix sums in place: a[b] <- sum of a[b .. n-1], a[n] = 0 (n = 2 AC_NT, exact).
-DT_INLINE void wg_suffix_u64(uint64_t *a, int n, Red &red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i0 = n - 2 - 2 * (int)threadIdx.x;  // thread k takes entries i0, i0 + 1 (from the top)
-  const uint64_t x0 = a[i0], x1 = a[i0 + 1];
-  const uint64_t s = x0 + x1;
-  uint64_t incl = s;  // inclusive prefix over threads 0..k (entries from the top down)
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t lo = __shfl_up((uint32_t)incl, o, 64), hi = __shfl_up((uint32_t)(incl >> 32), o, 64);
-    if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
-  }
-  __syncthreads();
-  if (lane == 63) red.u[w] = incl;
-  __syncthreads();
-  uint64_t run = 0;
-  for (int i = 0; i < w; ++i) run += red.u[i];
-  run += incl - s;  // sum of the entries above i0 + 1
-  a[i0 + 1] = run + x1;
-  a[i0] = run + x1 + x0;
-  if (threadIdx.x == 0) a[n] = 0ull;
-  __syncthreads();
 }
 
 // Leader: the four workgroups' offsets into xoff, the summed per-bin sums as suffix sums.
@@ -1198,8 +1284,6 @@ DT_INLINE bool xch_wait(uint64_t *p, int *err, int spin, uint64_t &v) {
     __builtin_amdgcn_s_sleep(1);
   }
 }
-DT_INLINE uint64_t dbits(double x) { return (uint64_t)__double_as_longlong(x); }
-DT_INLINE double bitsd(uint64_t x) { return __longlong_as_double((long long)x); }
 
 __global__ void k_accept_xch_init(uint64_t *slot, size_t n, int *err, int R) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -1771,12 +1855,13 @@ size_t accept_lds_bytes(int V) {
   return (size_t)nblk * (sizeof(double) + sizeof(float));
 }
 
-// Dynamic LDS of k_accept_coop<T, true>: the draw's block sums and prefix (accept_lds_bytes), or
-// all the LDS a workgroup may hold beside the kernel's static arrays when that is more (the
-// leader's copy of the late bins lives there). The answer depends only on the device and
-// the kernel, so it is kept per device; 0 when a query fails.
-template <typename T>
-static size_t coop_lds_avail() {
+// Dynamic LDS of the residual walks (k_accept_coop<T, true> when COOP, else k_accept_lazy<T, 2>):
+// the draw's block sums and prefix (accept_lds_bytes), or all the LDS a workgroup may hold
+// beside the kernel's static arrays when that is more (the copy of the late bins lives
+// there). The answer depends only on the device and the kernel, so it is kept per device; 0
+// when a query fails.
+template <typename T, bool COOP>
+static size_t walk_lds_avail() {
   static std::atomic<size_t> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -1784,7 +1869,8 @@ static size_t coop_lds_avail() {
   int max_lds = 0;
   hipFuncAttributes fa;
   if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-      hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k_accept_coop<T, true>)) != hipSuccess) {
+      hipFuncGetAttributes(&fa, COOP ? reinterpret_cast<const void *>(k_accept_coop<T, true>)
+                                     : reinterpret_cast<const void *>(k_accept_lazy<T, 2>)) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -1839,7 +1925,7 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
       const bool bf = a.dtype == DTREE_BF16;
       size_t shm_c = 0;
       if (sampled) {
-        const size_t avail = bf ? coop_lds_avail<uint16_t>() : coop_lds_avail<float>();
+        const size_t avail = bf ? walk_lds_avail<uint16_t, true>() : walk_lds_avail<float, true>();
         shm_c = avail > shm ? avail : shm;
       }
       const int capacity = sampled ? (bf ? coop_capacity<uint16_t, true>(shm_c) : coop_capacity<float, true>(shm_c))
@@ -1876,14 +1962,22 @@ hipError_t launch_accept(const AcceptArgs &a, void *ws, hipStream_t st) {
     }
     float2 *lp = static_cast<float2 *>(ws);
     const int mode = a.T == 0.f ? 0 : a.match ? 1 : 2;
-    if (a.dtype == DTREE_BF16) {
-      if (mode == 0) hipLaunchKernelGGL((k_accept_lazy<uint16_t, 0>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
-      else if (mode == 1) hipLaunchKernelGGL((k_accept_lazy<uint16_t, 1>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
-      else hipLaunchKernelGGL((k_accept_lazy<uint16_t, 2>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
+    const bool bf = a.dtype == DTREE_BF16;
+    size_t shm_l = shm;
+    if (mode == 2) {
+      const size_t avail = bf ? walk_lds_avail<uint16_t, false>() : walk_lds_avail<float, false>();
+      shm_l = avail > shm ? avail : shm;
+    }
+    const int cache_cap = mode == 2 ? (int)(shm_l / sizeof(float2)) : 0;
+    const dim3 g(a.R), blk(AC_NT);
+    if (bf) {
+      if (mode == 0) hipLaunchKernelGGL((k_accept_lazy<uint16_t, 0>), g, blk, shm_l, st, a, lp, cache_cap);
+      else if (mode == 1) hipLaunchKernelGGL((k_accept_lazy<uint16_t, 1>), g, blk, shm_l, st, a, lp, cache_cap);
+      else hipLaunchKernelGGL((k_accept_lazy<uint16_t, 2>), g, blk, shm_l, st, a, lp, cache_cap);
     } else {
-      if (mode == 0) hipLaunchKernelGGL((k_accept_lazy<float, 0>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
-      else if (mode == 1) hipLaunchKernelGGL((k_accept_lazy<float, 1>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
-      else hipLaunchKernelGGL((k_accept_lazy<float, 2>), dim3(a.R), dim3(AC_NT), shm, st, a, lp);
+      if (mode == 0) hipLaunchKernelGGL((k_accept_lazy<float, 0>), g, blk, shm_l, st, a, lp, cache_cap);
+      else if (mode == 1) hipLaunchKernelGGL((k_accept_lazy<float, 1>), g, blk, shm_l, st, a, lp, cache_cap);
+      else hipLaunchKernelGGL((k_accept_lazy<float, 2>), g, blk, shm_l, st, a, lp, cache_cap);
     }
     return hipGetLastError();
   }
