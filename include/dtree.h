@@ -336,9 +336,11 @@ int accept_tree(const dtree_tree *tree, const void *target_logits, const void *d
  * at once, which shortens a call that has the device to itself; this variant keeps one
  * compute unit per round, for callers that run the walk beside other work on the device
  * (the one-trial walk at temperature > 0 and the greedy walk each hold a quarter of the
- * compute units that accept_tree holds, for longer). Results: the greedy walk and every
- * acceptance test are identical to accept_tree's; the residual's normaliser and the final
- * draw's block prefix are summed in another order (within float rounding of accept_tree).
+ * compute units that accept_tree holds, for longer). Results: the greedy walk is identical
+ * to accept_tree's. At temperature > 0 the residual masses are the same exact fixed-point
+ * sums, but the rows' log-sum-exps and the final draw's block prefix are summed in another
+ * order, so a trial can differ from accept_tree's only where one of its decisions lies
+ * within float rounding of its threshold.
  */
 int accept_tree_narrow(const dtree_tree *tree, const void *target_logits, const void *draft_logits, int dtype,
                        int R, int L, int V, float temperature, uint64_t seed, uint64_t trial0, int n_trials,
