@@ -13,9 +13,10 @@
 // as a 16-bit code rounded up, so the record can only over-select. Nothing else happens
 // per element: the top-K is found from the record.
 // Four chunks before the end the workgroup takes a bound on the row's K-th largest value
-// -- each wave the ceil(K/4)-th largest of its lanes' running maxima (ballots on the top 16
-// bits of the order-preserving code, rounded down), the smallest over the four waves (each
-// certifies ceil(K/4) distinct elements, so together K). It lists the recorded spans that
+// -- the K-th largest of its 256 lanes' running maxima (each lane's maximum is a distinct
+// element, so K elements reach it; found with ballots on the top 16 bits of the
+// order-preserving code, rounded down, over the lanes' codes that every wave reads back
+// from LDS). It lists the recorded spans that
 // reach the bound and issues their loads at once (lane j of a wave the wave's j-th span),
 // hidden behind the last chunks; those last chunks are checked against the bound while in
 // registers and the spans that reach it are kept in LDS. The candidates -- elements at or
@@ -58,16 +59,23 @@ constexpr double kLn2d = 0.6931471805599453;
 constexpr double kLog2ed = 1.4426950408889634;
 constexpr float kFltLowest = -3.402823466e38f;
 
-// The kw-th largest (1 <= kw <= 64) of the lanes' 16-bit prefixes of the order-preserving
-// code, found bit by bit with ballots (wave-uniform; no LDS traffic). Every value whose
-// prefix is >= it is >= bound16(prefix).
-DT_INLINE uint32_t wave_kth_prefix16(float v, int kw) {
-  const uint32_t key = ord_f32(v) >> 16;
+// The K-th largest (1 <= K <= RS_NT) of the workgroup's per-lane keys (16-bit prefixes of
+// the order-preserving code, keys[i] for lane i), found bit by bit: each wave reads all of
+// them (four per lane) and counts with one ballot per four. Every wave gets the same value,
+// so no barrier follows. Every value whose prefix is >= it is >= bound16(prefix).
+DT_INLINE uint32_t wg_kth_prefix16(const uint16_t *keys, int K) {
+  const int lane = threadIdx.x & 63;
+  uint32_t k[RS_NW];
+#pragma unroll
+  for (int i = 0; i < RS_NW; ++i) k[i] = keys[i * 64 + lane];
   uint32_t t = 0;
 #pragma unroll
   for (int b = 15; b >= 0; --b) {
     const uint32_t c = t | (1u << b);
-    if (__popcll(__ballot(key >= c)) >= kw) t = c;
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < RS_NW; ++i) n += __popcll(__ballot(k[i] >= c));
+    if (n >= K) t = c;
   }
   return t;
 }
@@ -127,7 +135,8 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   __shared__ u32x4 s_span[RS_U][RS_NW * RS_WSP];  // spans of the last chunks that reach the bound
   __shared__ int s_spid[RS_NW * RS_WSP];          // (chunk << 8) | lane of each stored span
   __shared__ uint64_t keys[RS_KEYS];
-  __shared__ float s_wb[RS_NW], s_wm[RS_NW];
+  __shared__ float s_wm[RS_NW];
+  __shared__ uint16_t s_key[RS_NT];  // lanes' running maxima (16-bit codes) for the bound
   __shared__ double s_ws[RS_NW];
   __shared__ int s_kn[RS_NW], s_over[RS_NW];
   __shared__ int s_nkey;  // re-stream fallback counter
@@ -147,7 +156,6 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   const int cB = max(0, nround - RS_PRE);       // chunks [0, cB) are recorded and re-read
   const int cpg = max(1, (cB + RS_NG - 1) / RS_NG);  // chunks per recorded group
   const int ng = (cB + cpg - 1) / cpg;
-  const int kw = (K + RS_NW - 1) / RS_NW;
 
   // element layout: vector u of chunk c on lane ln starts at element c*CH + (u*256 + ln)*EPV
   auto elem0 = [&](int c, int u, int ln) { return v0 + c * CH + (ln * RS_U + u) * EPV; };
@@ -258,10 +266,9 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     }
   }
 
-  // ---- bound: chunks cB and cB + 1 are taken in first; then each wave's ceil(K/4)-th
-  // largest running lane maximum, the smallest over the waves (each certifies ceil(K/4)
-  // distinct elements, so together K). Every later bound would be higher, so th holds for
-  // the rest of the row.
+  // ---- bound: chunks cB and cB + 1 are taken in first; then the K-th largest of the 256
+  // running lane maxima (distinct elements). Every later bound would be higher, so th holds
+  // for the rest of the row.
   float cm0, cm1;
   {
     float x[E];
@@ -272,12 +279,9 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   }
   float th;
   {
-    const float b = bound16(wave_kth_prefix16(m, kw));
-    if (lane == 0) s_wb[w] = b;
+    s_key[tid] = (uint16_t)(ord_f32(m) >> 16);
     __syncthreads();
-    th = s_wb[0];
-#pragma unroll
-    for (int i = 1; i < RS_NW; ++i) th = fminf(th, s_wb[i]);
+    th = bound16(wg_kth_prefix16(s_key, K));
   }
   // ---- the recorded groups (chunks before cB) that reach th: listed per wave, lane j of a
   // wave loads the wave's j-th listed span at once (consumed after the last chunks)
