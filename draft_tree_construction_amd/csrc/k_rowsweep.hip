@@ -13,10 +13,10 @@
 // as a 16-bit code rounded up, so the record can only over-select. Nothing else happens
 // per element: the top-K is found from the record.
 // Four chunks before the end the workgroup takes a bound on the row's K-th largest value
-// -- the K-th largest of its 256 lanes' running maxima (each lane's maximum is a distinct
-// element, so K elements reach it; found with ballots on the top 16 bits of the
-// order-preserving code, rounded down, over the lanes' codes that every wave reads back
-// from LDS). It lists the recorded spans that
+// -- the K-th largest of the 512 values formed by its 256 lanes' two largest span maxima
+// (maxima of different spans are distinct elements, so K elements reach it; found with
+// ballots on the top 16 bits of the order-preserving code, rounded down, over the codes that
+// every wave reads back from LDS). It lists the recorded spans that
 // reach the bound and issues their loads at once (lane j of a wave the wave's j-th span),
 // hidden behind the last chunks; those last chunks are checked against the bound while in
 // registers and the spans that reach it are kept in LDS. The candidates -- elements at or
@@ -59,22 +59,24 @@ constexpr double kLn2d = 0.6931471805599453;
 constexpr double kLog2ed = 1.4426950408889634;
 constexpr float kFltLowest = -3.402823466e38f;
 
-// The K-th largest (1 <= K <= RS_NT) of the workgroup's per-lane keys (16-bit prefixes of
-// the order-preserving code, keys[i] for lane i), found bit by bit: each wave reads all of
-// them (four per lane) and counts with one ballot per four. Every wave gets the same value,
-// so no barrier follows. Every value whose prefix is >= it is >= bound16(prefix).
+// The K-th largest (1 <= K <= N) of N keys (16-bit prefixes of the order-preserving code;
+// N a multiple of 64), found bit by bit: each wave reads all of them (N / 64 per lane) and
+// counts with one ballot per N / 64. Every wave gets the same value, so no barrier follows.
+// Every value whose prefix is >= it is >= bound16(prefix).
+template <int N>
 DT_INLINE uint32_t wg_kth_prefix16(const uint16_t *keys, int K) {
+  constexpr int P = N / 64;
   const int lane = threadIdx.x & 63;
-  uint32_t k[RS_NW];
+  uint32_t k[P];
 #pragma unroll
-  for (int i = 0; i < RS_NW; ++i) k[i] = keys[i * 64 + lane];
+  for (int i = 0; i < P; ++i) k[i] = keys[i * 64 + lane];
   uint32_t t = 0;
 #pragma unroll
   for (int b = 15; b >= 0; --b) {
     const uint32_t c = t | (1u << b);
     int n = 0;
 #pragma unroll
-    for (int i = 0; i < RS_NW; ++i) n += __popcll(__ballot(k[i] >= c));
+    for (int i = 0; i < P; ++i) n += __popcll(__ballot(k[i] >= c));
     if (n >= K) t = c;
   }
   return t;
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   __shared__ int s_spid[RS_NW * RS_WSP];          // (chunk << 8) | lane of each stored span
   __shared__ uint64_t keys[RS_KEYS];
   __shared__ float s_wm[RS_NW];
-  __shared__ uint16_t s_key[RS_NT];  // lanes' running maxima (16-bit codes) for the bound
+  __shared__ uint16_t s_key[2 * RS_NT];  // lanes' two largest span maxima (16-bit codes) for the bound
   __shared__ double s_ws[RS_NW];
   __shared__ int s_kn[RS_NW], s_over[RS_NW];
   __shared__ int s_nkey;  // re-stream fallback counter
@@ -190,6 +192,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   };
 
   float m = -kInf, mh = 0.f;  // running max; mh = fp32(m log2 e) once m is finite
+  float m2 = -kInf;           // second largest span maximum (of another span than m's)
   double s = 0.0;             // sum of exp2(x log2e - mh): the true sum times 2^(m log2e - mh)
   float gm = -kInf;           // maximum of the current recorded group
   int gi = 0, gk = 0;         // recorded group and position in it (wave-uniform)
@@ -199,6 +202,7 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     float cm = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) cm = fmaxf(cm, x[e]);
+    m2 = fmaxf(m2, fminf(m, cm));
     if (cm > m) {
       const float nh = cm * kLog2e;
       // the factor's rounding scales a sum that the factor itself shrinks
@@ -266,9 +270,9 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
     }
   }
 
-  // ---- bound: chunks cB and cB + 1 are taken in first; then the K-th largest of the 256
-  // running lane maxima (distinct elements). Every later bound would be higher, so th holds
-  // for the rest of the row.
+  // ---- bound: chunks cB and cB + 1 are taken in first; then the K-th largest of the lanes'
+  // two largest span maxima (512 distinct elements). Every later bound would be higher, so
+  // th holds for the rest of the row.
   float cm0, cm1;
   {
     float x[E];
@@ -280,8 +284,9 @@ __global__ __launch_bounds__(RS_NT, 4) void k_rowsweep(const T *__restrict__ log
   float th;
   {
     s_key[tid] = (uint16_t)(ord_f32(m) >> 16);
+    s_key[RS_NT + tid] = (uint16_t)(ord_f32(m2) >> 16);
     __syncthreads();
-    th = bound16(wg_kth_prefix16(s_key, K));
+    th = bound16(wg_kth_prefix16<2 * RS_NT>(s_key, K));
   }
   // ---- the recorded groups (chunks before cB) that reach th: listed per wave, lane j of a
   // wave loads the wave's j-th listed span at once (consumed after the last chunks)
