@@ -80,3 +80,24 @@ def test_rowsweep_full_ddtree_shape_sampled():
     np.testing.assert_allclose(lp[pick], r_lp, rtol=0, atol=TOL)
     # every row: ids distinct, lp non-increasing and <= 0
     assert np.all(np.diff(lp, axis=1) <= 0) and np.all(lp <= 0)
+
+
+@pytest.mark.parametrize("rows", [3, 40])
+def test_rowsweep_top_values_in_one_lane(rows):
+    """The row's largest values all in the 16-element spans of one thread of every 4096-element
+    chunk (a stride the sweep's layout maps to one lane): the lanes' own maxima then certify a
+    low bound, far more spans reach it than a wave lists, and the sweep must still return the
+    exact top-K. Also a second pattern with the large values on a 64-element stride. Few rows
+    split each row over several workgroups; 40 rows give one workgroup per row."""
+    V = 151936
+    rng = np.random.default_rng(31 + rows)
+    x = rng.standard_normal((rows, V)).astype(np.float32)
+    v = np.arange(V)
+    one_lane = ((v % 4096) // 16) == 5
+    x[0, one_lane] += (8.0 + rng.uniform(0.0, 2.0, one_lane.sum())).astype(np.float32)
+    strided = (v % 64) == 3
+    x[1, strided] += (6.0 + rng.uniform(0.0, 1.0, strided.sum())).astype(np.float32)
+    x[2, ::4096] += 12.0
+    host = synth.bf16_from_f32(x)
+    for K in (8, 64, 128):
+        run_and_compare(host, "bf16", K)
