@@ -14,6 +14,7 @@ One step = one pass of the whole hot path over a batch of R = 64 rounds
                            logits (one workgroup per round: the walks run beside the
                            depth-wise builder, so they take a CU per round, not four)
   5. accept_tree_narrow T = 1   same, one Philox-seeded trial per round (trial index = step)
+  (in the overlapped step the T = 1 walk runs before the T = 0 walk on the main stream)
 Each configuration's builder as a user calls it alone (its own sweep included) is timed too:
 per_config_ms, the median of as many calls as timed steps; the walks there are accept_tree
 (four workgroups per round, the lower latency for a call that has the device to itself).
@@ -173,7 +174,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     names = ["row_sweep_draft", "marginal", "depthwise", "gated", "accept_t0", "accept_t1"]
     # the step's schedule: the draft logits' row sweep, the marginal tree from its lists and
-    # the two walks on that tree (a chain) on the main stream; the depth-wise tree from the
+    # the two walks on that tree (T = 1, then T = 0; a chain) on the main stream; the depth-wise tree from the
     # same lists on a second stream once they are written; the gated tree (other logits, its
     # own sweep) on a third from the start; joined at the end. Of the orders tried this one
     # finished soonest.
@@ -193,8 +194,9 @@ def main():
             dt.build_tree_depthwise_lists(draft, lists, E, head_d, 1024, 64, root, 8, 32, 128, -0.5, ws=ws_dl,
                                           out=t_d)
         dt.build_tree_marginal_lists(lists, R, L, 64, 0.0, out=t_m)
-        dt.accept_tree_narrow(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
+        # the longer walk first: it then overlaps more of the side streams' work
         dt.accept_tree_narrow(t_m, target, draft, 1.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o1)
+        dt.accept_tree_narrow(t_m, target, None, 0.0, synth.PHILOX_SEED, i, 1, ws=ws_a, outs=o0)
         for s2 in (s_dw, s_g):
             join = torch.cuda.Event()
             join.record(s2)
@@ -487,7 +489,7 @@ def main():
                    "rounds": R, "L": L, "V": V},
         "per_config_ms": {n: round(v, 4) for n, v in per_config.items()},
         "per_config_us_per_round": {n: round(v * 1e3 / R, 3) for n, v in per_config.items()},
-        "schedule": "draft row sweep -> marginal (its lists) -> accept_tree_narrow T=0 -> T=1 on one stream, depthwise "
+        "schedule": "draft row sweep -> marginal (its lists) -> accept_tree_narrow T=1 -> T=0 on one stream, depthwise "
                     "(the same lists) on a second once they are written, gated (own sweep) on a third (default "
                     "priority), forked and joined per step",
         "walk_failures": walk_failures,
